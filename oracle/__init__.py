@@ -1,0 +1,26 @@
+"""CPU oracle for the W4A16 quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this package; the product path never does.
+It shares no code with the HIP library.
+
+The arithmetic lives in ``w4a16_oracle.c`` (plain C, built with gcc); this
+package holds the ctypes marshalling and the build step.
+"""
+from .oracle import (  # noqa: F401
+    BF16,
+    F16,
+    F32,
+    GROUP,
+    bf16_to_double,
+    build,
+    codes_to_nibbles,
+    dequantize,
+    f16_to_double,
+    library_path,
+    linear,
+    linear_entries,
+    nibbles_to_codes,
+    num_threads,
+    quantize,
+)

@@ -1,0 +1,245 @@
+/*
+ * CPU oracle for the W4A16 quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this file.  Only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no code, header, table or
+ * constant with the HIP library: it is a plain, slow, obviously correct
+ * restatement of what the method computes.
+ *
+ * What it computes, and where that is defined:
+ *
+ *  - Post-training quantization at load time by round-to-nearest, to INT4,
+ *    with one scale for every group of 128 weights, activations left in
+ *    BF16/FP16: "Kernel dispatch and Humming quantization in PhyAI", section
+ *    "Humming makes the separation useful".
+ *  - Quantization arithmetic in FP32 and FP32 reference arithmetic:
+ *    "Piper Kernels" (piper-kernels 0.7.3), introduction.
+ *  - Weight shape [out_features, in_features], input [..., in_features],
+ *    output [..., out_features]: "Piper Kernels", section "ConvRot INT8".
+ *  - Bias added in FP32 before the final 16-bit conversion:
+ *    "Piper Kernels", section "NVFP4 construction".
+ *  - A usable scale for an all-zero group is part of the algorithm:
+ *    "Piper Kernels", section "Validation contract".
+ *
+ * Readings taken where the pages are silent (the pages fix only RTN, INT4 and
+ * the group size):
+ *  - symmetric codes, no zero point; scale s = max|w| / 7 over the group, an
+ *    FP32 value obtained by one correctly rounded FP32 division;
+ *  - the group runs along K (in_features), 128 consecutive elements of one
+ *    output row;
+ *  - code q = clamp(round_half_even(fl32(w / s)), -8, 7); s == 0 gives q = 0;
+ *  - canonical byte layout: codes[n][j] holds q[n][2j] in the low nibble and
+ *    q[n][2j+1] in the high nibble, two's complement;
+ *  - dequantized weight W^[n][k] = q[n][k] * s[n][k/128] (exact in double);
+ *  - y[m][n] = sum_k x[m][k] * W^[n][k] + bias[n], accumulated in double
+ *    (the plain definition; it is more accurate than any FP32 order) and
+ *    returned unrounded.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared
+ * The quantizer relies on IEEE binary32 division and on nearbyintf under the
+ * default round-to-nearest-even mode; -ffp-contract=off keeps every step a
+ * separately rounded operation.
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_GROUP 128
+
+/* dtype tags used by the entry points below (their own numbering) */
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+#define ORACLE_F16 2
+
+/* ---- 16-bit floating-point decoding, written from the format definitions ---- */
+
+/* bfloat16 is, by definition, the upper half of an IEEE binary32 pattern. */
+double oracle_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);              /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);  /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static double decode16(uint16_t bits, int dtype)
+{
+    return dtype == ORACLE_BF16 ? oracle_bf16_to_double(bits) : oracle_f16_to_double(bits);
+}
+
+/* A weight element as FP32.  16-bit inputs widen exactly to FP32. */
+static float weight_as_float(const void *w, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F32)
+        return ((const float *)w)[idx];
+    return (float)decode16(((const uint16_t *)w)[idx], dtype);
+}
+
+/* ---- round-to-nearest INT4 quantization, one FP32 scale per group of 128 ---- */
+
+/*
+ * w: [n][ldw] elements of dtype w_dtype (only the first k of each row are used)
+ * q: [n][k] one signed code per byte, s: [n][k/128] FP32 scales.
+ * Returns 0, or -1 when k is not a positive multiple of 128.
+ */
+int oracle_quantize(const void *w, int w_dtype, int64_t n, int64_t k, int64_t ldw,
+                    int8_t *q, float *s)
+{
+    if (k <= 0 || k % ORACLE_GROUP != 0 || ldw < k || n < 0)
+        return -1;
+    if (fegetround() != FE_TONEAREST)
+        fesetround(FE_TONEAREST);
+    const int64_t groups = k / ORACLE_GROUP;
+    for (int64_t row = 0; row < n; ++row) {
+        for (int64_t g = 0; g < groups; ++g) {
+            /* step 1: the group's largest magnitude */
+            float amax = 0.0f;
+            for (int64_t j = 0; j < ORACLE_GROUP; ++j) {
+                float a = fabsf(weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j));
+                if (a > amax)
+                    amax = a;
+            }
+            /* step 2: the scale maps the largest magnitude onto code 7 */
+            float scale = amax / 7.0f;
+            s[row * groups + g] = scale;
+            /* step 3: each code is the quotient rounded to the nearest integer */
+            for (int64_t j = 0; j < ORACLE_GROUP; ++j) {
+                int64_t kk = g * ORACLE_GROUP + j;
+                int code = 0;
+                if (scale != 0.0f) {
+                    float ratio = weight_as_float(w, w_dtype, row * ldw + kk) / scale;
+                    float r = nearbyintf(ratio);   /* ties go to the even integer */
+                    if (r < -8.0f)
+                        r = -8.0f;
+                    if (r > 7.0f)
+                        r = 7.0f;
+                    code = (int)r;
+                }
+                q[row * k + kk] = (int8_t)code;
+            }
+        }
+    }
+    return 0;
+}
+
+/* Canonical storage: two codes per byte, even k in the low nibble. */
+void oracle_codes_to_nibbles(const int8_t *q, int64_t n, int64_t k, uint8_t *codes)
+{
+    for (int64_t row = 0; row < n; ++row)
+        for (int64_t j = 0; j < k / 2; ++j) {
+            unsigned lo = (unsigned)q[row * k + 2 * j] & 0xFu;
+            unsigned hi = (unsigned)q[row * k + 2 * j + 1] & 0xFu;
+            codes[row * (k / 2) + j] = (uint8_t)(lo | (hi << 4));
+        }
+}
+
+/* Inverse of the canonical storage: sign-extend each nibble. */
+void oracle_nibbles_to_codes(const uint8_t *codes, int64_t n, int64_t k, int8_t *q)
+{
+    for (int64_t row = 0; row < n; ++row)
+        for (int64_t kk = 0; kk < k; ++kk) {
+            unsigned byte = codes[row * (k / 2) + kk / 2];
+            int v = (kk % 2 == 0) ? (int)(byte & 0xFu) : (int)(byte >> 4);
+            q[row * k + kk] = (int8_t)(v >= 8 ? v - 16 : v);
+        }
+}
+
+/* Dequantized weight W^[n][k] = q * s, exact in double. */
+void oracle_dequantize(const int8_t *q, const float *s, int64_t n, int64_t k, double *w_hat)
+{
+    const int64_t groups = k / ORACLE_GROUP;
+    for (int64_t row = 0; row < n; ++row)
+        for (int64_t kk = 0; kk < k; ++kk)
+            w_hat[row * k + kk] = (double)q[row * k + kk] * (double)s[row * groups + kk / ORACLE_GROUP];
+}
+
+/* ---- the quantized linear layer: y = x . W^T + bias ---- */
+
+/* One output element, straight from the definition, k ascending. */
+static double one_output(const uint16_t *x, int x_dtype, int64_t ldx, int64_t i,
+                         const int8_t *q, const float *s, int64_t k, int64_t j,
+                         const uint16_t *bias)
+{
+    const int64_t groups = k / ORACLE_GROUP;
+    double acc = 0.0;
+    for (int64_t kk = 0; kk < k; ++kk) {
+        double xv = decode16(x[i * ldx + kk], x_dtype);
+        double wv = (double)q[j * k + kk] * (double)s[j * groups + kk / ORACLE_GROUP];
+        acc += xv * wv;
+    }
+    if (bias)
+        acc += decode16(bias[j], x_dtype);
+    return acc;
+}
+
+/*
+ * x: [m][ldx] 16-bit activations of dtype x_dtype (BF16 or F16)
+ * q, s: codes [n][k] and scales [n][k/128] as produced by oracle_quantize
+ * bias: [n] of x_dtype, or NULL.  y: [m][n] doubles (not rounded to 16 bits).
+ */
+int oracle_linear(const uint16_t *x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
+                  const int8_t *q, const float *s, int64_t n, const uint16_t *bias, double *y)
+{
+    if (k <= 0 || k % ORACLE_GROUP != 0 || ldx < k || m < 0 || n < 0)
+        return -1;
+    if (x_dtype != ORACLE_BF16 && x_dtype != ORACLE_F16)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            y[i * n + j] = one_output(x, x_dtype, ldx, i, q, s, k, j, bias);
+    return 0;
+}
+
+/* The same computation for a list of (row, column) output positions. */
+int oracle_linear_entries(const uint16_t *x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
+                          const int8_t *q, const float *s, int64_t n, const uint16_t *bias,
+                          const int64_t *rows, const int64_t *cols, int64_t count, double *out)
+{
+    if (k <= 0 || k % ORACLE_GROUP != 0 || ldx < k || m < 0 || n < 0)
+        return -1;
+    if (x_dtype != ORACLE_BF16 && x_dtype != ORACLE_F16)
+        return -1;
+    for (int64_t e = 0; e < count; ++e)
+        if (rows[e] < 0 || rows[e] >= m || cols[e] < 0 || cols[e] >= n)
+            return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < count; ++e)
+        out[e] = one_output(x, x_dtype, ldx, rows[e], q, s, k, cols[e], bias);
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region uses (reported by the baseline). */
+int oracle_num_threads(void)
+{
+    int t = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            t = omp_get_num_threads();
+#endif
+        }
+    }
+    return t;
+}

@@ -1,0 +1,240 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` takes a loaded oracle library (``oracle.oracle.load(path)``) and
+raises AssertionError on a mismatch.  They are run on the real oracle by
+``test_oracle.py`` and on deliberately broken copies of the oracle (mutants,
+built on the CPU) to show that each plausible mistake is caught.
+
+What each pin checks against:
+  * hand-worked groups and bytes (tests/golden/), worked from the method's
+    definition by hand;
+  * exact rational arithmetic (tests/exact.py): the correctly rounded FP32
+    scale and quotient, and a brute-force nearest-code search;
+  * closed forms: identity-like weights give y = c*x exactly, and integer
+    weights and activations give an exact integer matrix product;
+  * a library routine: numpy's float64 matmul on the dequantized weights;
+  * numpy/torch decoders for every 16-bit pattern.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+from tests import exact
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+def _pairs(text, conv):
+    out = {}
+    for tok in text.split():
+        i, v = tok.split(":")
+        out[int(i)] = conv(v)
+    return out
+
+
+def pin_hand_worked_groups(lib):
+    """Golden: hand-worked RTN groups (ties to even, s = amax/7, zero group)."""
+    for line in _read_lines("rtn_hand_worked.txt"):
+        name, wtxt, stxt, qtxt = [p.strip() for p in line.split("|")]
+        w = np.zeros((1, 128), dtype=np.float32)
+        for i, v in _pairs(wtxt, float).items():
+            w[0, i] = np.float32(v)
+        want_q = np.zeros(128, dtype=np.int8)
+        for i, v in _pairs(qtxt, int).items():
+            want_q[i] = v
+        q, s = oracle.quantize(w, lib=lib)
+        assert s[0, 0] == np.float32(stxt), f"{name}: scale {s[0,0]!r} != {stxt}"
+        assert np.array_equal(q[0], want_q), f"{name}: codes {q[0][:16]} != {want_q[:16]}"
+        if float(stxt) == 0.0:
+            assert np.signbit(s[0, 0]) == False, f"{name}: zero scale must be +0"  # noqa: E712
+
+
+def pin_negative_zero_group(lib):
+    """A group of -0.0 values quantizes like an all-zero group: s = +0, q = 0."""
+    w = np.full((2, 256), -0.0, dtype=np.float32)
+    w[1, 128:] = 0.0
+    q, s = oracle.quantize(w, lib=lib)
+    assert np.all(q == 0)
+    assert np.all(s == 0) and not np.any(np.signbit(s)), s
+
+
+def pin_canonical_nibbles(lib):
+    """Golden: hand-worked canonical byte layout, and its inverse."""
+    for line in _read_lines("canonical_nibbles.txt"):
+        ctxt, btxt = [p.strip() for p in line.split("|")]
+        q = np.array([int(v) for v in ctxt.split()], dtype=np.int8)[None, :]
+        want = np.array([int(v, 16) for v in btxt.split()], dtype=np.uint8)[None, :]
+        got = oracle.codes_to_nibbles(q, lib=lib)
+        assert np.array_equal(got, want), f"{got} != {want}"
+        back = oracle.nibbles_to_codes(want, lib=lib)
+        assert np.array_equal(back, q), f"{back} != {q}"
+
+
+def pin_exact_scales_and_codes(lib, seed=11, n=24, k=384):
+    """Exact rationals: s is amax/7 correctly rounded to FP32; each code is the
+    ties-to-even rounding of the correctly rounded FP32 quotient; brute-force
+    nearest codes differ only where the quotient lies within one FP32 ulp of a
+    half-integer."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    # a few groups with planted exact and near half-integer quotients
+    w[0, :128] = 0.0
+    w[0, 0] = np.float32(0.7)
+    w[0, 1:8] = np.float32(0.7) * np.arange(1, 8, dtype=np.float32) / np.float32(14.0)
+    w[1, 128:256] *= np.float32(1e-38)  # subnormal magnitudes
+    q, s = oracle.quantize(w, lib=lib)
+    near_ties = 0
+    for r in range(n):
+        for g in range(k // 128):
+            seg = w[r, g * 128:(g + 1) * 128]
+            amax = max(abs(exact.f32_fraction(v)) for v in seg)
+            want_s = exact.round_to_f32(amax / 7)
+            assert float(s[r, g]) == want_s, (r, g, float(s[r, g]), want_s)
+            sf = Fraction(want_s)
+            for j, v in enumerate(seg):
+                wf = exact.f32_fraction(v)
+                got = int(q[r, g * 128 + j])
+                if sf == 0:
+                    assert got == 0
+                    continue
+                ratio = wf / sf
+                quotient = exact.round_to_f32(ratio)
+                want = max(-8, min(7, exact.round_half_even(Fraction(quotient))))
+                assert got == want, (r, g, j, got, want)
+                brute = exact.argmin_code(wf, sf)
+                if brute != got:
+                    half = Fraction(2 * exact.round_half_even(ratio - Fraction(1, 2)) + 1, 2)
+                    assert abs(ratio - half) <= exact.ulp_f32(float(ratio)), (r, g, j, got, brute)
+                    near_ties += 1
+    assert near_ties <= 3, near_ties
+
+
+def pin_invariants(lib, w=None, seed=5):
+    """Codes in [-7, 7]; |w - q s| <= s (1/2 + 2^-21); every nonzero group has a
+    code of magnitude 7; zero groups give s = +0 and q = 0; quantize(-w) = (-q, s);
+    quantize(2^j w) = (q, 2^j s)."""
+    if w is None:
+        rng = np.random.default_rng(seed)
+        w = (rng.standard_normal((64, 1024)) * 0.02).astype(np.float32)
+        w[3, 256:384] = 0.0
+        w[7, :] = 0.0
+        mask = rng.random(w.shape) < 0.01
+        w[mask] = (rng.standard_normal(mask.sum()) * 0.2).astype(np.float32)
+    n, k = w.shape
+    q, s = oracle.quantize(w, lib=lib)
+    assert q.min() >= -7 and q.max() <= 7, (q.min(), q.max())
+    s_full = np.repeat(s.astype(np.float64), 128, axis=1)
+    err = np.abs(w.astype(np.float64) - q.astype(np.float64) * s_full)
+    assert np.all(err <= s_full * (0.5 + 2.0 ** -21)), float((err / np.maximum(s_full, 1e-300)).max())
+    qg = np.abs(q.reshape(n, k // 128, 128)).max(axis=2)
+    zero = np.all(w.reshape(n, k // 128, 128) == 0, axis=2)
+    assert np.all(qg[~zero] == 7)
+    assert np.all(s[zero] == 0) and not np.any(np.signbit(s[zero]))
+    assert np.all(q.reshape(n, k // 128, 128)[zero] == 0)
+    qn, sn = oracle.quantize(-w, lib=lib)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    for j in (5, -5):
+        f = np.float32(2.0 ** j)
+        qj, sj = oracle.quantize(w * f, lib=lib)
+        assert np.array_equal(qj, q) and np.array_equal(sj, s * f)
+
+
+def pin_decoders(lib):
+    """bf16 and fp16 decoding agrees with torch/numpy for all 65536 patterns."""
+    bits = np.arange(65536, dtype=np.uint16)
+    want_f16 = bits.view(np.float16).astype(np.float64)
+    want_bf16 = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    # sample every pattern through the C entry points (cheap: scalar calls)
+    got_f16 = np.array([lib.oracle_f16_to_double(int(b)) for b in bits])
+    got_bf16 = np.array([lib.oracle_bf16_to_double(int(b)) for b in bits])
+    for got, want in ((got_f16, want_f16), (got_bf16, want_bf16)):
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], want[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_identity_like(lib):
+    """W = c I with c = 7 * 2^-3: s = 2^-3 on the diagonal groups, q = 7 on the
+    diagonal, every other group all-zero, so y = c x exactly (bf16 and fp16)."""
+    n = 384
+    c = np.float32(7.0 * 2.0 ** -3)
+    w = np.zeros((n, n), dtype=np.float32)
+    np.fill_diagonal(w, c)
+    q, s = oracle.quantize(w, lib=lib)
+    rng = np.random.default_rng(3)
+    for tag, tdt in ((oracle.BF16, torch.bfloat16), (oracle.F16, torch.float16)):
+        x = torch.from_numpy(rng.standard_normal((5, n)).astype(np.float32)).to(tdt)
+        xb = x.view(torch.int16).numpy().view(np.uint16)
+        y = oracle.linear(xb, tag, q, s, lib=lib)
+        want = x.to(torch.float64).numpy() * float(c)
+        assert np.array_equal(y, want), float(np.abs(y - want).max())
+
+
+def pin_exact_integer_gemm(lib, seed=9):
+    """W = q_int 2^-3 with one |q| = 7 per group, x and bias small integers: the
+    layer output is an exact integer matrix product (numpy int64) times 2^-3."""
+    rng = np.random.default_rng(seed)
+    m, k, n = 6, 512, 40
+    qi = rng.integers(-7, 8, size=(n, k))
+    qi[:, ::128] = 7 * np.where(rng.random((n, k // 128)) < 0.5, 1, -1)
+    w = (qi * 2.0 ** -3).astype(np.float32)
+    q, s = oracle.quantize(w, lib=lib)
+    assert np.array_equal(q, qi.astype(np.int8))
+    assert np.all(s == np.float32(2.0 ** -3))
+    xi = rng.integers(-4, 5, size=(m, k))
+    bi = rng.integers(-9, 10, size=n)
+    for tag, tdt in ((oracle.BF16, torch.bfloat16), (oracle.F16, torch.float16)):
+        xb = torch.from_numpy(xi.astype(np.float32)).to(tdt).view(torch.int16).numpy().view(np.uint16)
+        bb = torch.from_numpy(bi.astype(np.float32)).to(tdt).view(torch.int16).numpy().view(np.uint16)
+        y = oracle.linear(xb, tag, q, s, bb, lib=lib)
+        want = (xi @ qi.T) * 2.0 ** -3 + bi
+        assert np.array_equal(y, want.astype(np.float64)), float(np.abs(y - want).max())
+        ent = oracle.linear_entries(xb, tag, q, s, bb, np.array([0, 5, 3]), np.array([39, 0, 17]), lib=lib)
+        assert np.array_equal(ent, want[[0, 5, 3], [39, 0, 17]].astype(np.float64))
+
+
+def pin_matches_library_matmul(lib, seed=4):
+    """Random case: the oracle equals numpy's float64 matmul of the dequantized
+    weight (plus bias) to float64 rounding."""
+    rng = np.random.default_rng(seed)
+    m, k, n = 7, 640, 96
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    q, s = oracle.quantize(w, lib=lib)
+    w_hat = oracle.dequantize(q, s, lib=lib)
+    want_hat = q.astype(np.float64) * np.repeat(s.astype(np.float64), 128, axis=1)
+    assert np.array_equal(w_hat, want_hat)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    b = torch.from_numpy((rng.standard_normal(n) * 0.01).astype(np.float32)).to(torch.bfloat16)
+    y = oracle.linear(x.view(torch.int16).numpy().view(np.uint16), oracle.BF16, q, s,
+                      b.view(torch.int16).numpy().view(np.uint16), lib=lib)
+    xd = x.to(torch.float64).numpy()
+    want = xd @ want_hat.T + b.to(torch.float64).numpy()
+    bound = 1e-13 * (np.abs(xd) @ np.abs(want_hat).T + 1.0)
+    assert np.all(np.abs(y - want) <= bound)
+
+
+ALL_PINS = [
+    pin_hand_worked_groups,
+    pin_negative_zero_group,
+    pin_canonical_nibbles,
+    pin_exact_scales_and_codes,
+    pin_invariants,
+    pin_decoders,
+    pin_identity_like,
+    pin_exact_integer_gemm,
+    pin_matches_library_matmul,
+]

@@ -1,0 +1,130 @@
+"""The CPU oracle against its pins (no GPU).
+
+The oracle is test infrastructure: these tests are what make it trustworthy.
+Each pin is described in ``tests/oracle_pins.py``.  The mutation test plants
+plausible mistakes into copies of the oracle's C source (on the CPU, in a
+child process) and checks that at least one pin fails for every one of them.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.oracle.load()
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(lib, pin):
+    pin(lib)
+
+
+@pytest.mark.parametrize("name", ["c1_m1_k1024_n1024", "c2_down_m50_k4096_n1024",
+                                  "c3_qkv_m1_k2048_n2560", "c5_m1_k1024_n4096"])
+def test_invariants_on_workload_weights(lib, name):
+    """The invariants hold on each workload's own weights (outliers, zero groups)."""
+    c = synth.case_by_name(name)
+    w = synth.make_weight(c).numpy()
+    oracle_pins.pin_invariants(lib, w=w)
+
+
+def test_bf16_and_f16_weights_upcast_exactly(lib):
+    """16-bit weights quantize exactly like their FP32 widening."""
+    import torch
+    rng = np.random.default_rng(2)
+    w32 = torch.from_numpy((rng.standard_normal((8, 256)) * 0.02).astype(np.float32))
+    for tdt, tag in ((torch.bfloat16, oracle.BF16), (torch.float16, oracle.F16)):
+        w16 = w32.to(tdt)
+        bits = w16.view(torch.int16).numpy().view(np.uint16)
+        q16, s16 = oracle.quantize(bits, tag)
+        q32, s32 = oracle.quantize(w16.to(torch.float32).numpy())
+        assert np.array_equal(q16, q32) and np.array_equal(s16, s32)
+
+
+def test_rejects_bad_group_size(lib):
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((2, 200), dtype=np.float32))
+
+
+# (description, text in w4a16_oracle.c, replacement) -- each is a plausible slip.
+MUTANTS = [
+    ("divisor 8 instead of 7", "float scale = amax / 7.0f;", "float scale = amax / 8.0f;"),
+    ("divisor 7.5", "float scale = amax / 7.0f;", "float scale = amax / 7.5f;"),
+    ("ties away from zero", "float r = nearbyintf(ratio);", "float r = roundf(ratio);"),
+    ("truncation", "float r = nearbyintf(ratio);", "float r = truncf(ratio);"),
+    ("reciprocal multiply", "float ratio = weight_as_float(w, w_dtype, row * ldw + kk) / scale;",
+     "float ratio = weight_as_float(w, w_dtype, row * ldw + kk) * (1.0f / scale);"),
+    ("signed max instead of magnitude", "float a = fabsf(weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j));",
+     "float a = weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j);"),
+    ("clamp at 6", "if (r > 7.0f)\n                        r = 7.0f;", "if (r > 6.0f)\n                        r = 6.0f;"),
+    ("group of 64 for the absmax", "for (int64_t j = 0; j < ORACLE_GROUP; ++j) {\n                float a",
+     "for (int64_t j = 0; j < 64; ++j) {\n                float a"),
+    ("nibbles swapped", "codes[row * (k / 2) + j] = (uint8_t)(lo | (hi << 4));",
+     "codes[row * (k / 2) + j] = (uint8_t)(hi | (lo << 4));"),
+    ("no sign extension", "q[row * k + kk] = (int8_t)(v >= 8 ? v - 16 : v);", "q[row * k + kk] = (int8_t)v;"),
+    ("scale index by k % 128", "double wv = (double)q[j * k + kk] * (double)s[j * groups + kk / ORACLE_GROUP];",
+     "double wv = (double)q[j * k + kk] * (double)s[j * groups + (kk % ORACLE_GROUP) % groups];"),
+    ("transposed weight", "double wv = (double)q[j * k + kk] *", "double wv = (double)q[(kk % n_) * k + j] *"),
+    ("dropped last term", "for (int64_t kk = 0; kk < k; ++kk) {\n        double xv", "for (int64_t kk = 0; kk < k - 1; ++kk) {\n        double xv"),
+    ("bias dropped", "acc += decode16(bias[j], x_dtype);", "acc += 0.0;"),
+    ("bias sign", "acc += decode16(bias[j], x_dtype);", "acc -= decode16(bias[j], x_dtype);"),
+    ("fp16 exponent bias", "v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    ("fp16 subnormal scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    ("bf16 decoded as fp16", "return dtype == ORACLE_BF16 ? oracle_bf16_to_double(bits) : oracle_f16_to_double(bits);",
+     "return oracle_f16_to_double(bits);"),
+    ("zero guard missing", "if (scale != 0.0f) {", "if (1) {"),
+    ("dequant drops the scale", "w_hat[row * k + kk] = (double)q[row * k + kk] * (double)s[row * groups + kk / ORACLE_GROUP];",
+     "w_hat[row * k + kk] = (double)q[row * k + kk];"),
+    ("x row stride ignored", "double xv = decode16(x[i * ldx + kk], x_dtype);", "double xv = decode16(x[kk], x_dtype);"),
+]
+
+_RUNNER = r"""
+import sys
+sys.path.insert(0, {root!r})
+from oracle import oracle as O
+from tests import oracle_pins
+lib = O.load({path!r})
+failed = []
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(lib)
+    except Exception as e:  # a pin caught the mutant (or the mutant broke)
+        failed.append(pin.__name__)
+print("FAILED:" + ",".join(failed))
+"""
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(desc, old, new):
+    src = open(os.path.join(ROOT, "oracle", "w4a16_oracle.c")).read()
+    assert src.count(old) == 1, f"mutation site not found exactly once: {desc}"
+    mutated = src.replace(old, new)
+    if "n_" in new:  # the transposed-index mutant needs the row count in scope
+        mutated = mutated.replace("static double one_output(", "static int64_t n_ = 1;\nstatic double one_output(", 1)
+        mutated = mutated.replace("#pragma omp parallel for schedule(static)\n    for (int64_t i = 0; i < m; ++i)",
+                                  "n_ = n < k ? n : k;\n#pragma omp parallel for schedule(static)\n    for (int64_t i = 0; i < m; ++i)", 1)
+    with tempfile.TemporaryDirectory() as d:
+        src_path = os.path.join(d, "mutant.c")
+        so_path = os.path.join(d, "libmutant.so")
+        with open(src_path, "w") as f:
+            f.write(mutated)
+        oracle.build(src=src_path, out=so_path, extra_flags=["-w"])
+        proc = subprocess.run([sys.executable, "-c", _RUNNER.format(root=ROOT, path=so_path)],
+                              capture_output=True, text=True, timeout=300)
+    line = [ln for ln in proc.stdout.splitlines() if ln.startswith("FAILED:")]
+    if proc.returncode != 0 and not line:
+        return  # the mutant crashed the child: caught
+    assert line, proc.stdout + proc.stderr
+    caught = [p for p in line[0][len("FAILED:"):].split(",") if p]
+    assert caught, f"no pin caught the planted mistake: {desc}"
