@@ -1,0 +1,172 @@
+/*
+ * w4a16.h -- C ABI of the W4A16 quantized linear layer for AMD MI355X (gfx950).
+ *
+ * The layer, as the pages define it:
+ *   - weights are quantized once, when a FP16/BF16/FP32 checkpoint is loaded,
+ *     by round-to-nearest to INT4 with one scale per group of 128 weights;
+ *     activations stay BF16 or FP16 ("Kernel dispatch and Humming
+ *     quantization in PhyAI", section "Humming makes the separation useful");
+ *   - a quantized weight carries its own packed layout, which a plain 16-bit
+ *     GEMM cannot execute (same page and section);
+ *   - y = x . dequant(Wq, s)^T + bias, weight [out_features, in_features],
+ *     input [..., in_features], output [..., out_features] ("Piper Kernels",
+ *     section "ConvRot INT8"); scales and bias are applied in FP32 before the
+ *     one final conversion to the output dtype ("Piper Kernels", section
+ *     "NVFP4 construction").
+ *
+ * Readings fixed by this library where the pages are silent: symmetric codes
+ * without a zero point; scale s = max|w| / 7 over 128 consecutive weights of
+ * one output row (one correctly rounded FP32 division); code
+ * q = clamp(round_half_even(fl32(w / s)), -8, 7), and q = 0 where s == 0.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device; every call is asynchronous on `stream` (a
+ *     hipStream_t; NULL is the null stream).
+ *   - The caller allocates and owns every buffer.  The library never
+ *     allocates, frees or synchronizes, and never reads device contents on
+ *     the host ("Piper Kernels", section "Validation contract"): arguments
+ *     are checked from their values (shapes, dtypes, alignment, sizes) only,
+ *     and a failed check returns an error before anything is launched.
+ *   - Tensor contents are caller preconditions: NaN or Inf in weights,
+ *     activations or bias give unspecified results and no error.
+ *   - All calls can be captured into a HIP graph.
+ *   - Calls on different streams may run concurrently as long as they do not
+ *     share output buffers or a workspace.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_EINVAL = 1,        /* bad shape, stride, pointer, alignment or overlap */
+    W4A16_EUNSUPPORTED = 2,  /* valid request this build does not implement (e.g. dtype) */
+    W4A16_EWORKSPACE = 3,    /* workspace missing or smaller than required */
+    W4A16_EHIP = 4           /* the HIP runtime reported an error at launch */
+} w4a16_status_t;
+
+typedef enum {
+    W4A16_F32 = 0,
+    W4A16_BF16 = 1,
+    W4A16_F16 = 2
+} w4a16_dtype_t;
+
+/* Kernel families w4a16_linear chooses between (by M, N, K). */
+typedef enum {
+    W4A16_PATH_AUTO = 0,    /* let the library choose */
+    W4A16_PATH_GEMV = 1,    /* M <= 4: VALU dot products, split-K, wave reductions */
+    W4A16_PATH_SKINNY = 2,  /* small and mid M: register-dequantized MFMA, split-K */
+    W4A16_PATH_GEMM = 3     /* large M: LDS-staged dequantized tiles into MFMA */
+} w4a16_path_t;
+
+/* Group size along K: one FP32 scale per 128 consecutive weights of a row. */
+#define W4A16_GROUP 128
+
+/*
+ * Round-to-nearest INT4 quantization with one FP32 scale per group of 128
+ * ("Kernel dispatch and Humming quantization in PhyAI", section "Humming
+ * makes the separation useful"; the readings listed at the top of this file).
+ *
+ *   w       device, [n][ldw] elements of w_dtype (F32, BF16 or F16), row-major
+ *           [out_features, in_features]; 16-byte aligned; ldw * element size
+ *           a multiple of 16 bytes.  16-bit weights are widened to FP32
+ *           exactly before quantization.
+ *   n, k    rows and columns; n >= 0, k > 0, k % 128 == 0, ldw >= k.
+ *   codes   device, [n][k/2] bytes, the canonical layout: byte j of a row
+ *           holds the code of column 2j in its low nibble and of column 2j+1
+ *           in its high nibble, 4-bit two's complement; 4-byte aligned.
+ *   scales  device, [n][k/128] FP32, row-major; 4-byte aligned.
+ * Returns W4A16_OK (also for n == 0, which launches nothing), W4A16_EINVAL,
+ * W4A16_EUNSUPPORTED (unknown dtype) or W4A16_EHIP.
+ */
+w4a16_status_t quantize_rtn_int4_g128(const void* w, w4a16_dtype_t w_dtype, int64_t n, int64_t k,
+                                      int64_t ldw, uint8_t* codes, float* scales, void* stream);
+
+/*
+ * Size in bytes of the packed weight for an [n][k] layer (k % 128 == 0),
+ * or 0 for invalid sizes.  The packed layout is the library's own execution
+ * format (the "physical" form of the weight); it is not a storage format:
+ * store codes and scales, and pack after loading.
+ */
+size_t w4a16_packed_bytes(int64_t n, int64_t k);
+
+/*
+ * Canonical codes and scales -> the packed execution layout.
+ *   codes   device, [n][k/2] canonical bytes (see quantize_rtn_int4_g128); 4-byte aligned.
+ *   scales  device, [n][k/128] FP32; 4-byte aligned.
+ *   packed  device, w4a16_packed_bytes(n, k) bytes; 16-byte aligned; must not
+ *           overlap codes or scales.
+ * Codes are taken as given (any 4-bit value, including -8).  Returns
+ * W4A16_OK, W4A16_EINVAL or W4A16_EHIP.
+ */
+w4a16_status_t pack_weights(const uint8_t* codes, const float* scales, int64_t n, int64_t k,
+                            void* packed, void* stream);
+
+/*
+ * Inverse of pack_weights: packed layout -> canonical codes and scales,
+ * bit-exact.  Same argument rules as pack_weights.
+ */
+w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t* codes,
+                              float* scales, void* stream);
+
+/*
+ * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
+ * kernel path (0 if none).  The workspace holds split-K partial sums and
+ * per-tile arrival counters.  It must be zero-filled once before its first
+ * use; every call leaves the counters zero again when it completes.  Two calls
+ * that may run at the same time must not share a workspace.
+ */
+size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/*
+ * y[m][n] = x[m][k] . dequant(packed)^T + bias[n], with
+ * dequant(q, s)[n][k] = q[n][k] * s[n][k / 128]; FP32 accumulation; the bias
+ * is added in FP32 once; the result is rounded to act_dtype (nearest even).
+ *
+ *   x         device, [m][ldx] of act_dtype (BF16 or F16), 16-byte aligned, ldx >= k,
+ *             ldx % 8 == 0.
+ *   m, k      m >= 0; k > 0, k % 128 == 0 (the layer's in_features).
+ *   packed    device, from pack_weights for (n, k); 16-byte aligned.
+ *   n         out_features, n >= 0.
+ *   bias      device [n] of act_dtype, or NULL; 2-byte aligned.
+ *   y         device, [m][ldy] of act_dtype, ldy >= n, 2-byte aligned; must not
+ *             overlap x, packed, bias or workspace.
+ *   workspace device, >= w4a16_linear_workspace_bytes(m, n, k) bytes, 16-byte
+ *             aligned, zero-filled before first use (may be NULL when that size is 0).
+ * m == 0 or n == 0 returns W4A16_OK and launches nothing.  Returns W4A16_OK,
+ * W4A16_EINVAL, W4A16_EUNSUPPORTED (act_dtype), W4A16_EWORKSPACE or W4A16_EHIP.
+ * The result is bit-identical from run to run (no floating-point atomics).
+ */
+w4a16_status_t w4a16_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, int64_t k,
+                            int64_t ldx, const void* packed, int64_t n, const void* bias,
+                            void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * w4a16_linear with an explicit kernel path (W4A16_PATH_AUTO behaves exactly
+ * like w4a16_linear).  Every path accepts every valid m; the automatic choice
+ * is the fast one.  For tests and measurements of each kernel.
+ */
+w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                                      int64_t m, int64_t k, int64_t ldx, const void* packed,
+                                      int64_t n, const void* bias, void* y, int64_t ldy,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* The path w4a16_linear would take for these sizes (never W4A16_PATH_AUTO). */
+w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k);
+
+/* Static, human-readable text for a status code. */
+const char* w4a16_status_string(w4a16_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

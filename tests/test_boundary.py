@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments from host metadata alone (no GPU needed: every check here
+returns before anything is launched).
+
+The validation contract: arguments are checked from shapes, dtypes,
+alignment and sizes only, never from tensor contents ("Piper Kernels",
+section "Validation contract")."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+import weight_only_int4_rtn_amd as w4  # noqa: E402
+from weight_only_int4_rtn_amd import _binding as B  # noqa: E402
+
+A = 1 << 20  # a 16-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return w4.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"quantize_rtn_int4_g128", "pack_weights", "w4a16_linear", "unpack_weights",
+            "w4a16_packed_bytes", "w4a16_linear_workspace_bytes", "w4a16_status_string",
+            "w4a16_linear_with_path", "w4a16_linear_choose_path"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_single_hip_runtime_loaded(lib):
+    maps = open("/proc/self/maps").read()
+    runtimes = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(runtimes) == 1, runtimes
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert w4.status_string(s)
+    assert w4.status_string(99) == "unknown status"
+
+
+def test_packed_bytes(lib):
+    # 16-row tiles x 128-column groups, 1024 code bytes + 64 scale bytes each
+    assert w4.packed_bytes(16, 128) == 1088
+    assert w4.packed_bytes(17, 256) == 2 * 2 * 1088
+    assert w4.packed_bytes(32768, 2048) == 2048 * 16 * 1088
+    assert w4.packed_bytes(0, 128) == 0
+    assert w4.packed_bytes(16, 100) == 0
+    assert w4.packed_bytes(16, 0) == 0
+    assert w4.packed_bytes(-1, 128) == 0
+
+
+def test_choose_path(lib):
+    for m in (1, 2, 3, 4):
+        assert w4.choose_path(m, 2048, 2048) == w4.Path.GEMV
+    assert w4.choose_path(16, 2048, 2048) != w4.Path.AUTO
+    assert w4.choose_path(4096, 2048, 2048) != w4.Path.AUTO
+
+
+def test_workspace_bytes(lib):
+    assert w4.workspace_bytes(0, 2048, 2048) == 0
+    assert w4.workspace_bytes(1, 2048, 100) == 0
+    # a long-K decode shape splits K across workgroups and needs a workspace
+    assert w4.workspace_bytes(1, 2048, 16384) > 0
+
+
+def q(lib, w, dt, n, k, ldw, codes, scales):
+    return lib.quantize_rtn_int4_g128(w, dt, n, k, ldw, codes, scales, None)
+
+
+def test_quantize_rejects(lib):
+    assert q(lib, A, B.F32, 4, 100, 100, A * 2, A * 3) == B.EINVAL      # k % 128
+    assert q(lib, A, B.F32, 4, 0, 128, A * 2, A * 3) == B.EINVAL        # k == 0
+    assert q(lib, A, B.F32, -1, 128, 128, A * 2, A * 3) == B.EINVAL     # n < 0
+    assert q(lib, A, B.F32, 4, 256, 128, A * 2, A * 3) == B.EINVAL      # ldw < k
+    assert q(lib, A, 7, 4, 128, 128, A * 2, A * 3) == B.EUNSUPPORTED    # dtype
+    assert q(lib, None, B.F32, 4, 128, 128, A * 2, A * 3) == B.EINVAL   # null
+    assert q(lib, A, B.F32, 4, 128, 128, None, A * 3) == B.EINVAL
+    assert q(lib, A + 4, B.F32, 4, 128, 128, A * 2, A * 3) == B.EINVAL  # misaligned w
+    assert q(lib, A, B.F32, 4, 128, 130, A * 2, A * 3) == B.EINVAL      # row stride not 16 B
+    assert q(lib, A, B.F32, 4, 128, 128, A * 2 + 1, A * 3) == B.EINVAL  # misaligned codes
+    assert q(lib, A, B.F32, 4, 128, 128, A, A * 3) == B.EINVAL          # codes overlap w
+    assert q(lib, A, B.F32, 0, 128, 128, None, None) == B.OK            # empty: no-op
+
+
+def test_pack_rejects(lib):
+    assert lib.pack_weights(A, A * 2, 4, 100, A * 3, None) == B.EINVAL
+    assert lib.pack_weights(None, A * 2, 4, 128, A * 3, None) == B.EINVAL
+    assert lib.pack_weights(A, A * 2, 4, 128, A * 3 + 8, None) == B.EINVAL
+    assert lib.pack_weights(A, A * 2, 4, 128, A, None) == B.EINVAL       # packed overlaps codes
+    assert lib.pack_weights(A, A * 2, 0, 128, A * 3, None) == B.OK
+    assert lib.unpack_weights(A * 3, 4, 100, A, A * 2, None) == B.EINVAL
+    assert lib.unpack_weights(A * 3, 4, 128, A, A, None) == B.EINVAL      # codes overlap scales
+    assert lib.unpack_weights(A * 3, 0, 128, A, A * 2, None) == B.OK
+
+
+def lin(lib, x=A, act=B.BF16, m=1, k=128, ldx=128, packed=A * 4, n=16, bias=None, y=A * 8, ldy=16,
+        ws=None, ws_bytes=0, path=0):
+    return lib.w4a16_linear_with_path(path, x, act, m, k, ldx, packed, n, bias, y, ldy, ws, ws_bytes, None)
+
+
+def test_linear_rejects(lib):
+    assert lin(lib, k=100, ldx=104) == B.EINVAL                   # k % 128
+    assert lin(lib, act=B.F32) == B.EUNSUPPORTED                  # activation dtype
+    assert lin(lib, ldx=64) == B.EINVAL                           # ldx < k
+    assert lin(lib, k=128, ldx=130) == B.EINVAL                   # ldx % 8
+    assert lin(lib, ldy=8) == B.EINVAL                            # ldy < n
+    assert lin(lib, m=-1) == B.EINVAL
+    assert lin(lib, x=None) == B.EINVAL
+    assert lin(lib, packed=None) == B.EINVAL
+    assert lin(lib, y=None) == B.EINVAL
+    assert lin(lib, x=A + 2) == B.EINVAL                          # misaligned x
+    assert lin(lib, y=A + 1) == B.EINVAL                          # misaligned y
+    assert lin(lib, y=A) == B.EINVAL                              # y overlaps x
+    assert lin(lib, y=A * 4) == B.EINVAL                          # y overlaps packed
+    assert lin(lib, path=9) == B.EINVAL                           # unknown path
+    assert lin(lib, m=0) == B.OK                                  # empty: no-op
+    assert lin(lib, n=0, ldy=0) == B.OK
+    # long K at M=1 needs a workspace
+    need = w4.workspace_bytes(1, 2048, 16384)
+    assert lin(lib, m=1, k=16384, ldx=16384, n=2048, ldy=2048, y=A * 64) == B.EWORKSPACE
+    assert need > 256
+    assert lin(lib, m=1, k=16384, ldx=16384, n=2048, ldy=2048, y=A * 64, ws=A * 128,
+               ws_bytes=256) == B.EWORKSPACE
+    assert lin(lib, m=1, k=16384, ldx=16384, n=2048, ldy=2048, y=A * 64, ws=A * 128 + 8,
+               ws_bytes=need) == B.EINVAL                     # misaligned workspace
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        w4.quantize(torch.zeros(16, 128))

@@ -1,0 +1,175 @@
+"""GPU linear layer against the CPU oracle.
+
+  * exact-arithmetic cases: integer codes with scale 2^-3 and small integer
+    activations make every partial sum exact in FP32 in any order, so each
+    kernel path must return the correctly rounded exact result bit for bit
+    (a misplaced nibble, scale, row or split fails exactly);
+  * random cases at sizes the oracle finishes quickly, spanning several
+    tiles with ragged tails, for every kernel path and both dtypes;
+  * the 36 workload cases at full size through the automatic path, compared
+    elementwise where the oracle is cheap and on sampled outputs otherwise.
+Tolerance (elementwise and mean relative) is defined in tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import bits, check_close, require_gpu, row_max_dequant, say, tag, to_rne16
+
+pytestmark = pytest.mark.gpu
+
+PATHS = ["GEMV", "SKINNY"]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def w4():
+    import weight_only_int4_rtn_amd as m
+    return m
+
+
+def prepare(w_cpu: torch.Tensor, dev):
+    """Quantize on the GPU (checked byte-exact elsewhere) and with the oracle."""
+    lib = w4()
+    codes, scales = lib.quantize(w_cpu.to(dev))
+    packed = lib.pack(codes, scales)
+    q, s = oracle.quantize(w_cpu.numpy())
+    return packed, q, s
+
+
+def run(x, packed, n, bias=None, path="AUTO"):
+    lib = w4()
+    y = lib.linear(x, packed, n, bias, path=lib.Path[path])
+    torch.cuda.synchronize()
+    return y
+
+
+def exact_case(m, n, k, seed, dtype, with_bias):
+    rng = np.random.default_rng(seed)
+    qi = rng.integers(-7, 8, size=(n, k))
+    qi[:, ::128] = 7 * np.where(rng.random((n, k // 128)) < 0.5, 1, -1)
+    w = torch.from_numpy((qi * 2.0 ** -3).astype(np.float32))
+    x = torch.from_numpy(rng.integers(-4, 5, size=(m, k)).astype(np.float32)).to(dtype)
+    b = torch.from_numpy(rng.integers(-9, 10, size=n).astype(np.float32)).to(dtype) if with_bias else None
+    return w, x, b
+
+
+EXACT_SHAPES = [(1, 16, 128), (2, 40, 384), (3, 1000, 2048), (4, 2056, 16384), (5, 72, 256),
+                (17, 130, 640), (33, 64, 1152), (64, 2048, 8192), (130, 100, 1152)]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", EXACT_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k in EXACT_SHAPES])
+def test_exact_arithmetic_bit_exact(dev, path, dtype, m, n, k):
+    w, x, b = exact_case(m, n, k, seed=m * 7 + n + k, dtype=dtype, with_bias=(m % 2 == 1))
+    say(f"exact case path={path} dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare(w, dev)
+    assert np.all(s == np.float32(2.0 ** -3))
+    y = run(x.to(dev), packed, n, b.to(dev) if b is not None else None, path)
+    y_ref = oracle.linear(bits(x), tag(dtype), q, s, bits(b) if b is not None else None)
+    want = to_rne16(y_ref, dtype)
+    got = y.cpu().to(torch.float64).numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
+def random_case(m, n, k, seed, dtype, with_bias):
+    g = torch.Generator().manual_seed(seed)
+    w = torch.randn(n, k, generator=g) * 0.02
+    mask = torch.rand(n, k, generator=g) < 0.01
+    w = torch.where(mask, torch.randn(n, k, generator=g) * 0.2, w)
+    w[:, :128][::7] = 0.0  # some all-zero groups
+    x = torch.randn(m, k, generator=g)
+    x[:, ::64] *= 10.0
+    x = x.to(dtype)
+    b = (torch.randn(n, generator=g) * 0.01).to(dtype) if with_bias else None
+    return w, x, b
+
+
+RANDOM_SHAPES = [(1, 24, 256), (2, 1000, 1024), (3, 100, 4096), (4, 520, 2048), (1, 2048, 16384),
+                 (6, 200, 640), (16, 1000, 2048), (31, 77, 1280), (50, 1024, 4096), (64, 264, 3072),
+                 (100, 520, 1024), (257, 130, 512)]
+
+
+@pytest.mark.parametrize("path", PATHS + ["AUTO"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", RANDOM_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k in RANDOM_SHAPES])
+def test_random_within_tolerance(dev, path, dtype, m, n, k):
+    w, x, b = random_case(m, n, k, seed=1000 + m + n + k, dtype=dtype, with_bias=(n % 2 == 0))
+    say(f"random case path={path} dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare(w, dev)
+    y = run(x.to(dev), packed, n, b.to(dev) if b is not None else None, path)
+    y_ref = oracle.linear(bits(x), tag(dtype), q, s, bits(b) if b is not None else None)
+    xnorm = np.linalg.norm(x.to(torch.float64).numpy(), axis=1)[:, None]
+    wmax = row_max_dequant(q, s)[None, :]
+    check_close(y.cpu().numpy() if y.dtype == torch.float32 else y.cpu().to(torch.float64).numpy(),
+                y_ref, xnorm, wmax, f"{path} m={m} n={n} k={k}")
+
+
+def test_leading_dims_and_strided_out(dev):
+    lib = w4()
+    w, x, b = random_case(6, 48, 256, seed=3, dtype=torch.bfloat16, with_bias=True)
+    packed, q, s = prepare(w, dev)
+    x3 = x.reshape(2, 3, 256).to(dev)
+    y = lib.linear(x3, packed, 48, b.to(dev))
+    torch.cuda.synchronize()
+    assert y.shape == (2, 3, 48)
+    y2 = run(x.to(dev), packed, 48, b.to(dev))
+    assert torch.equal(y.reshape(6, 48), y2)
+
+
+def test_results_are_deterministic(dev):
+    c = synth.case_by_name("c3_down_m4_k16384_n2048")
+    packed, q, s = prepare(synth.make_weight(c), dev)
+    x = synth.make_x(c).to(dev)
+    say("determinism: c3 down m4")
+    for path in PATHS:
+        a = run(x, packed, c.n, path=path)
+        b = run(x, packed, c.n, path=path)
+        assert torch.equal(a, b), path
+
+
+# --- the 36 workload cases at full size --------------------------------------
+
+_weights = {}
+
+
+def workload_weight(c, dev):
+    key = (c.config, c.shape_index)
+    if key not in _weights:
+        _weights.clear()  # keep at most one layer's weights resident
+        w = synth.make_weight(c)
+        packed, q, s = prepare(w, dev)
+        _weights[key] = (packed, q, s, row_max_dequant(q, s))
+    return _weights[key]
+
+
+FULL_LIMIT = 1 << 31  # m*n*k above which outputs are sampled
+
+
+@pytest.mark.parametrize("name", [c.name for c in synth.all_cases()])
+def test_workload_case(dev, name):
+    c = synth.case_by_name(name)
+    say(f"workload case {name}: m={c.m} k={c.k} n={c.n} {c.dtype} bias={c.bias}")
+    packed, q, s, wmax = workload_weight(c, dev)
+    x = synth.make_x(c)
+    b = synth.make_bias(c)
+    y = run(x.to(dev), packed, c.n, b.to(dev) if b is not None else None).cpu().to(torch.float64).numpy()
+    xb = bits(x)
+    bb = bits(b) if b is not None else None
+    xnorm = np.linalg.norm(x.to(torch.float64).numpy(), axis=1)
+    if c.m * c.n * c.k <= FULL_LIMIT:
+        y_ref = oracle.linear(xb, tag(c.torch_dtype), q, s, bb)
+        check_close(y, y_ref, xnorm[:, None], wmax[None, :], name)
+    else:
+        rng = np.random.default_rng(7)
+        rows = np.concatenate([rng.integers(0, c.m, 4096), [0, c.m - 1, c.m - 1, 0]])
+        cols = np.concatenate([rng.integers(0, c.n, 4096), [0, c.n - 1, 0, c.n - 1]])
+        y_ref = oracle.linear_entries(xb, tag(c.torch_dtype), q, s, bb, rows, cols)
+        check_close(y[rows, cols], y_ref, xnorm[rows], wmax[cols], name)

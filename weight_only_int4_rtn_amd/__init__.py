@@ -1,0 +1,27 @@
+"""W4A16 quantized linear layer for AMD MI355X (gfx950).
+
+Weights are round-to-nearest quantized to INT4 with one FP32 scale per group
+of 128 along K when they are loaded; activations stay BF16/FP16; the layer
+computes y = x . dequant(Wq, s)^T (+ bias) in hand-written HIP kernels
+behind the C ABI of ``include/w4a16.h``.
+
+    codes, scales = quantize(w)          # load time, w [n, k] on the GPU
+    packed = pack(codes, scales)         # load time
+    y = linear(x, packed, n, bias)       # every forward step
+"""
+import torch  # noqa: F401  (load torch's HIP runtime before the library)
+
+from ._binding import (  # noqa: F401
+    GROUP,
+    Path,
+    W4A16Error,
+    choose_path,
+    lib,
+    linear,
+    pack,
+    packed_bytes,
+    quantize,
+    status_string,
+    unpack,
+    workspace_bytes,
+)

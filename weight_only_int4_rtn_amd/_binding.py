@@ -1,0 +1,217 @@
+"""ctypes binding over the C ABI (include/w4a16.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch provides device memory and the current stream.  The library must be
+loaded after torch so both share torch's HIP runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4a16.so")
+GROUP = 128
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+F32, BF16, F16 = 0, 1, 2
+
+
+class Path(enum.IntEnum):
+    AUTO = 0
+    GEMV = 1
+    SKINNY = 2
+    GEMM = 3
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def _declare(lib):
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.quantize_rtn_int4_g128.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.quantize_rtn_int4_g128.restype = i32
+    lib.w4a16_packed_bytes.argtypes = [i64, i64]
+    lib.w4a16_packed_bytes.restype = sz
+    lib.pack_weights.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.pack_weights.restype = i32
+    lib.unpack_weights.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.unpack_weights.restype = i32
+    lib.w4a16_linear_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.w4a16_linear_workspace_bytes.restype = sz
+    lib.w4a16_linear.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, sz, vp]
+    lib.w4a16_linear.restype = i32
+    lib.w4a16_linear_with_path.argtypes = [i32, vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, sz, vp]
+    lib.w4a16_linear_with_path.restype = i32
+    lib.w4a16_linear_choose_path.argtypes = [i64, i64, i64]
+    lib.w4a16_linear_choose_path.restype = i32
+    lib.w4a16_status_string.argtypes = [i32]
+    lib.w4a16_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def lib():
+    """The loaded C library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"HIP library not built ({LIB_PATH} missing): run "
+                        "`python -m weight_only_int4_rtn_amd.build`")
+                _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().w4a16_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise W4A16Error(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _act_tag(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float16:
+        return F16
+    raise ValueError(f"activations must be bfloat16 or float16, got {dtype}")
+
+
+def _w_tag(dtype) -> int:
+    if dtype == torch.float32:
+        return F32
+    return _act_tag(dtype)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+
+
+# ---------------------------------------------------------------------------
+
+
+def packed_bytes(n: int, k: int) -> int:
+    return int(lib().w4a16_packed_bytes(n, k))
+
+
+def workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().w4a16_linear_workspace_bytes(m, n, k))
+
+
+def choose_path(m: int, n: int, k: int) -> Path:
+    return Path(lib().w4a16_linear_choose_path(m, n, k))
+
+
+def quantize(w: torch.Tensor):
+    """RTN INT4 g128: w [n, k] (f32/bf16/f16, rows contiguous) -> (codes [n, k/2] uint8, scales [n, k/128] f32)."""
+    _require_cuda(w)
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D tensor with contiguous rows")
+    n, k = w.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=w.device)
+    st = lib().quantize_rtn_int4_g128(_ptr(w), _w_tag(w.dtype), n, k, w.stride(0), _ptr(codes),
+                                      _ptr(scales), _stream(w.device))
+    _check(st, "quantize_rtn_int4_g128")
+    return codes, scales
+
+
+def pack(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """Canonical codes [n, k/2] + scales [n, k/128] -> packed execution layout (uint8, 1-D)."""
+    _require_cuda(codes, scales)
+    n, half = codes.shape
+    k = 2 * half
+    codes = codes.contiguous()
+    scales = scales.contiguous()
+    nbytes = packed_bytes(n, k)
+    if nbytes == 0 and n > 0:
+        raise ValueError(f"invalid layer shape n={n}, k={k}")
+    packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    st = lib().pack_weights(_ptr(codes), _ptr(scales), n, k, _ptr(packed), _stream(codes.device))
+    _check(st, "pack_weights")
+    return packed
+
+
+def unpack(packed: torch.Tensor, n: int, k: int):
+    _require_cuda(packed)
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=packed.device)
+    scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=packed.device)
+    st = lib().unpack_weights(_ptr(packed), n, k, _ptr(codes), _ptr(scales), _stream(packed.device))
+    _check(st, "unpack_weights")
+    return codes, scales
+
+
+_workspaces: dict = {}
+
+
+def workspace_for(device, stream_handle: int, nbytes: int) -> torch.Tensor | None:
+    """A zero-initialised workspace of at least ``nbytes`` for one (device, stream)."""
+    if nbytes == 0:
+        return None
+    key = (torch.device(device).index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | None = None,
+           out: torch.Tensor | None = None, path: Path = Path.AUTO,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x . dequant(packed)^T + bias for x [..., k] (bf16/f16) -> y [..., n] (x's dtype)."""
+    _require_cuda(x, packed, bias, out)
+    if x.requires_grad or (bias is not None and bias.requires_grad):
+        raise ValueError("inference only: autograd inputs are not supported")
+    act = _act_tag(x.dtype)
+    k = x.shape[-1]
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, k)
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    m = x2.shape[0]
+    if bias is not None:
+        if bias.dtype != x.dtype or bias.shape != (n,):
+            raise ValueError("bias must have shape [n] and x's dtype")
+        bias = bias.contiguous()
+    if out is None:
+        out = torch.empty((*lead, n), dtype=x.dtype, device=x.device)
+    elif out.shape != (*lead, n) or out.dtype != x.dtype:
+        raise ValueError("out must have shape [..., n] and x's dtype")
+    y2 = out.view(-1, n) if out.is_contiguous() else None
+    if y2 is None:
+        raise ValueError("out must be contiguous")
+    stream = _stream(x.device)
+    need = workspace_bytes(m, n, k)
+    if workspace is None:
+        workspace = workspace_for(x.device, stream.value, need)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().w4a16_linear_with_path(int(path), _ptr(x2), act, m, k, x2.stride(0), _ptr(packed), n,
+                                      _ptr(bias), _ptr(y2), n, _ptr(workspace), ws_bytes, stream)
+    _check(st, "w4a16_linear")
+    return out

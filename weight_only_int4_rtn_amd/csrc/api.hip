@@ -1,0 +1,179 @@
+// C ABI of the library (include/w4a16.h): argument checks from host metadata
+// only, kernel choice, launches.  Nothing here allocates, synchronizes or
+// reads device memory ("Piper Kernels", section "Validation contract").
+#include "../../include/w4a16.h"
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace w4a16;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [lo, hi) byte ranges overlap?
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t(rows - 1) * size_t(ld) + size_t(cols)) * elem;
+}
+
+// Sizes are limited so every internal offset fits comfortably in int64 and
+// grid dimensions stay within HIP's limits.
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+bool valid_nk(int64_t n, int64_t k) {
+    return n >= 0 && n <= kMaxDim && k > 0 && k <= kMaxDim && k % kGroup == 0;
+}
+
+w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_EHIP; }
+
+size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k) {
+    switch (path) {
+        case W4A16_PATH_GEMV: return plan_gemv(m < 4 ? m : 4, n, k).workspace;
+        case W4A16_PATH_SKINNY: return plan_skinny(m, n, k).workspace;
+        case W4A16_PATH_GEMM: return plan_gemm(m, n, k).workspace;
+        default: return 0;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(w4a16_status_t s) {
+    switch (s) {
+        case W4A16_OK: return "ok";
+        case W4A16_EINVAL: return "invalid argument (shape, stride, pointer, alignment or overlap)";
+        case W4A16_EUNSUPPORTED: return "unsupported request (dtype or path)";
+        case W4A16_EWORKSPACE: return "workspace missing or too small";
+        case W4A16_EHIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+size_t w4a16_packed_bytes(int64_t n, int64_t k) {
+    if (!valid_nk(n, k)) return 0;
+    return size_t(Layout(n, k).bytes());
+}
+
+w4a16_status_t quantize_rtn_int4_g128(const void* w, w4a16_dtype_t w_dtype, int64_t n, int64_t k,
+                                      int64_t ldw, uint8_t* codes, float* scales, void* stream) {
+    if (w_dtype != W4A16_F32 && w_dtype != W4A16_BF16 && w_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
+    if (!valid_nk(n, k) || ldw < k || ldw > kMaxDim) return W4A16_EINVAL;
+    if (n == 0) return W4A16_OK;
+    const size_t elem = w_dtype == W4A16_F32 ? 4 : 2;
+    if (!w || !codes || !scales) return W4A16_EINVAL;
+    if (!aligned(w, 16) || (size_t(ldw) * elem) % 16 != 0) return W4A16_EINVAL;
+    if (!aligned(codes, 4) || !aligned(scales, 4)) return W4A16_EINVAL;
+    const size_t wbytes = span_bytes(n, k, ldw, elem), cbytes = size_t(n) * size_t(k) / 2,
+                 sbytes = size_t(n) * size_t(k / kGroup) * 4;
+    if (overlap(w, wbytes, codes, cbytes) || overlap(w, wbytes, scales, sbytes) ||
+        overlap(codes, cbytes, scales, sbytes))
+        return W4A16_EINVAL;
+    return from_hip(launch_quantize(w, int(w_dtype), n, k, ldw, codes, scales,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status_t pack_weights(const uint8_t* codes, const float* scales, int64_t n, int64_t k,
+                            void* packed, void* stream) {
+    if (!valid_nk(n, k)) return W4A16_EINVAL;
+    if (n == 0) return W4A16_OK;
+    if (!codes || !scales || !packed) return W4A16_EINVAL;
+    if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(packed, 16)) return W4A16_EINVAL;
+    const size_t cbytes = size_t(n) * size_t(k) / 2, sbytes = size_t(n) * size_t(k / kGroup) * 4,
+                 pbytes = w4a16_packed_bytes(n, k);
+    if (overlap(packed, pbytes, codes, cbytes) || overlap(packed, pbytes, scales, sbytes)) return W4A16_EINVAL;
+    return from_hip(launch_pack(codes, scales, n, k, packed, static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t* codes, float* scales,
+                              void* stream) {
+    if (!valid_nk(n, k)) return W4A16_EINVAL;
+    if (n == 0) return W4A16_OK;
+    if (!codes || !scales || !packed) return W4A16_EINVAL;
+    if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(packed, 16)) return W4A16_EINVAL;
+    const size_t cbytes = size_t(n) * size_t(k) / 2, sbytes = size_t(n) * size_t(k / kGroup) * 4,
+                 pbytes = w4a16_packed_bytes(n, k);
+    if (overlap(packed, pbytes, codes, cbytes) || overlap(packed, pbytes, scales, sbytes) ||
+        overlap(codes, cbytes, scales, sbytes))
+        return W4A16_EINVAL;
+    return from_hip(launch_unpack(packed, n, k, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
+    (void)n;
+    (void)k;
+    if (m <= 4) return W4A16_PATH_GEMV;
+    return W4A16_PATH_SKINNY;
+}
+
+size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m <= 0 || !valid_nk(n, k) || n == 0 || m > kMaxDim) return 0;
+    size_t best = 0;
+    const w4a16_path_t paths[3] = {W4A16_PATH_GEMV, W4A16_PATH_SKINNY, W4A16_PATH_GEMM};
+    for (w4a16_path_t p : paths) {
+        const size_t b = path_workspace(p, m, n, k);
+        best = b > best ? b : best;
+    }
+    return best;
+}
+
+w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                                      int64_t m, int64_t k, int64_t ldx, const void* packed,
+                                      int64_t n, const void* bias, void* y, int64_t ldy,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (act_dtype != W4A16_BF16 && act_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_SKINNY &&
+        path != W4A16_PATH_GEMM)
+        return W4A16_EINVAL;
+    if (!valid_nk(n, k) || m < 0 || m > kMaxDim) return W4A16_EINVAL;
+    if (ldx < k || ldx > kMaxDim || ldx % 8 != 0 || ldy < n || ldy > kMaxDim) return W4A16_EINVAL;
+    if (m == 0 || n == 0) return W4A16_OK;
+    if (!x || !packed || !y) return W4A16_EINVAL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2) || (bias && !aligned(bias, 2)))
+        return W4A16_EINVAL;
+    if (path == W4A16_PATH_AUTO) path = w4a16_linear_choose_path(m, n, k);
+    if (path == W4A16_PATH_GEMM) return W4A16_EUNSUPPORTED;
+
+    const size_t xbytes = span_bytes(m, k, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
+                 pbytes = w4a16_packed_bytes(n, k), bbytes = bias ? size_t(n) * 2 : 0;
+    const size_t need = path_workspace(path, m, n, k);
+    if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, packed, pbytes) ||
+        overlap(y, ybytes, bias, bbytes) || overlap(y, ybytes, workspace, need))
+        return W4A16_EINVAL;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return W4A16_EWORKSPACE;
+        if (!aligned(workspace, 16)) return W4A16_EINVAL;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int act = act_dtype == W4A16_BF16 ? kActBf16 : kActF16;
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    uint16_t* yp = static_cast<uint16_t*>(y);
+    if (path == W4A16_PATH_GEMV) {
+        // row blocks of at most 4; launches on one stream share the workspace
+        for (int64_t r0 = 0; r0 < m; r0 += 4) {
+            const int64_t mm = m - r0 < 4 ? m - r0 : 4;
+            const hipError_t e = launch_gemv(xp + r0 * ldx, act, mm, k, ldx, packed, n, bias,
+                                             yp + r0 * ldy, ldy, workspace, s);
+            if (e != hipSuccess) return W4A16_EHIP;
+        }
+        return W4A16_OK;
+    }
+    return from_hip(launch_skinny(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
+}
+
+w4a16_status_t w4a16_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, int64_t k, int64_t ldx,
+                            const void* packed, int64_t n, const void* bias, void* y, int64_t ldy,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return w4a16_linear_with_path(W4A16_PATH_AUTO, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy,
+                                  workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Shared definitions of the HIP library: the packed weight layout, 16-bit
+// conversions and launch planning.  gfx950 (CDNA4) only: wave64, MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// ---------------------------------------------------------------------------
+// Packed execution layout ("the physical form" of a quantized weight).
+//
+// The [N][K] weight is cut into chunks of 16 rows x 128 columns (one scale
+// group per row).  T = ceil(N/16) row tiles, G = K/128 groups.
+//
+//   codes region : T*G chunks of 1024 bytes, chunk (t, g) at (t*G + g)*1024.
+//   scale region : after the codes, 16 FP32 per chunk, chunk (t, g) at
+//                  T*G*1024 + (t*G + g)*64, entry r = row 16t + r.
+//
+// Inside a chunk, lane L of a wave (0..63) owns bytes [16L, 16L + 16): four
+// 32-bit words w[s], s = 0..3.  Lane L stands for row r = L % 16 and quarter
+// kq = L / 16; word s holds the 8 codes of columns
+//     k = 128g + 32s + 8kq + j,   j = 0..7,
+// as offset-binary nibbles u = q + 8: nibble i (bits 4i..4i+3, i = 0..3)
+// holds column j = 2i and nibble i + 4 holds column j = 2i + 1.  So
+//     ((w >> 4i) & 0x000F000F)
+// puts columns (2i, 2i+1) into the low and high 16-bit halves, ready to be
+// turned into a packed pair of 16-bit floats.  This is also exactly the
+// B-operand layout of v_mfma_f32_16x16x32_{bf16,f16} for k-step s (lane L:
+// column n = L % 16, k = 8*(L/16) + j).  Rows n >= N of the last tile hold
+// code 0 (u = 8) and scale 0.
+// ---------------------------------------------------------------------------
+constexpr int kGroup = 128;
+constexpr int kTileRows = 16;
+constexpr int kChunkBytes = 1024;
+constexpr int kChunkScaleBytes = 64;
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Layout {
+    int64_t n, k, tiles, groups;
+    __host__ __device__ Layout(int64_t n_, int64_t k_)
+        : n(n_), k(k_), tiles(ceil_div(n_, kTileRows)), groups(k_ / kGroup) {}
+    __host__ __device__ int64_t chunks() const { return tiles * groups; }
+    __host__ __device__ int64_t scale_offset() const { return chunks() * kChunkBytes; }
+    __host__ __device__ int64_t bytes() const { return chunks() * (kChunkBytes + kChunkScaleBytes); }
+};
+
+// Offset-binary nibble value of the packed-pair magic numbers.
+//  bf16 0x4300 = 128.0 (spacing 1), so 0x4300 | u = 128 + u = 136 + q.
+//  f16  0x6400 = 1024.0 (spacing 1), so 0x6400 | u = 1024 + u = 1032 + q.
+constexpr uint32_t kMagicBf16x2 = 0x43004300u;
+constexpr uint32_t kMagicF16x2 = 0x64006400u;
+constexpr float kOffsetBf16 = 136.0f;
+constexpr float kOffsetF16 = 1032.0f;
+
+enum ActType { kActBf16 = 1, kActF16 = 2 };
+
+// ---------------------------------------------------------------------------
+// 16-bit float helpers (device).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int ACT>
+__device__ inline float to_f32(uint16_t bits) {
+    if constexpr (ACT == kActBf16) {
+        return __uint_as_float(uint32_t(bits) << 16);
+    } else {
+        return float(__builtin_bit_cast(_Float16, bits));
+    }
+}
+
+// Round-to-nearest-even conversion of an FP32 value to the activation dtype.
+template <int ACT>
+__device__ inline uint16_t from_f32(float v) {
+    if constexpr (ACT == kActBf16) {
+        return __builtin_bit_cast(uint16_t, (__bf16)v);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+}
+
+// Dot product of two packed pairs accumulated in FP32:
+// acc + a.lo*b.lo + a.hi*b.hi (v_dot2_f32_bf16 / v_dot2_f32_f16).
+template <int ACT>
+__device__ inline float dot2(uint32_t a, uint32_t b, float acc) {
+    if constexpr (ACT == kActBf16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), acc, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
+                                      __builtin_bit_cast(f16x2_t, b), acc, false);
+    }
+}
+
+// (a & mask) | bits in one v_and_or_b32.  gfx9 VOP3 encodings take no
+// literal constants, so the compiler would otherwise emit a separate and + or
+// pair; the operands here are registers (constants hoisted out of loops).
+__device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(mask), "v"(bits));
+    return d;
+}
+
+// Packed pair (columns 2i, 2i+1 of a word) as two 16-bit floats off + q.
+template <int ACT>
+__device__ inline uint32_t magic_pair(uint32_t word, int i) {
+    constexpr uint32_t magic = ACT == kActBf16 ? kMagicBf16x2 : kMagicF16x2;
+    return and_or(i == 0 ? word : word >> (4 * i), 0x000F000Fu, magic);
+}
+
+template <int ACT>
+__device__ inline constexpr float code_offset() {
+    return ACT == kActBf16 ? kOffsetBf16 : kOffsetF16;
+}
+
+}  // namespace w4a16

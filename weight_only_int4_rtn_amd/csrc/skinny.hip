@@ -1,0 +1,231 @@
+// Mid-M forward (and any M): register-dequantized weights into MFMA.
+//
+// A workgroup of 4 waves owns 4 adjacent 16-row weight tiles (64 output
+// columns), a block of up to 64 activation rows and a K split.  Per 128-column
+// group:
+//   1. the workgroup stages the activation block's 128 columns in LDS and sums
+//      each row (for the offset correction below);
+//   2. each wave loads its tile's 1 KB chunk with one 128-bit load per lane and
+//      turns every word into one MFMA B operand: the chunk layout is the
+//      B-operand layout of v_mfma_f32_16x16x32_{bf16,f16} (common.h), and
+//      each nibble pair becomes a packed pair of 16-bit floats holding
+//      off + q exactly (off = 136 for bf16, 1032 for f16);
+//   3. four MFMAs (k-steps of 32) per 16-row m-subtile give the group's
+//      sum_k x (off + q); the wave subtracts off * sum_k x, multiplies by the
+//      column's FP32 scale and adds into its FP32 totals.
+// The weights never pass through LDS; x tiles are shared by the 4 waves.
+// K splits are reduced like the small-M path: partials in the workspace, and
+// the last workgroup to arrive (integer counter) sums them in split order,
+// adds the bias in FP32 and rounds once.
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a16 {
+
+struct SkinnyArgs {
+    const uint16_t* x;
+    int64_t ldx, m;
+    const uint8_t* packed;
+    int64_t n, k;
+    const uint16_t* bias;
+    uint16_t* y;
+    int64_t ldy;
+    float* partials;
+    uint32_t* counters;
+    int splits, gps;
+    int64_t tile_groups;
+};
+
+constexpr int kSkWaves = 4;
+constexpr int kSkThreads = 64 * kSkWaves;
+constexpr int kSkCols = 16 * kSkWaves;     // output columns per workgroup
+constexpr int kAStride = kGroup + 8;       // LDS row stride of the x tile (elements): 16 B pad
+
+template <int ACT>
+__device__ inline f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+    if constexpr (ACT == kActBf16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+template <int MB, int ACT>
+__global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
+    constexpr int BM = 16 * MB;
+    __shared__ __align__(16) uint16_t xa[BM * kAStride];
+    __shared__ __align__(16) float xrow[BM];
+    __shared__ int last;
+
+    const Layout L(a.n, a.k);
+    const int split = int(blockIdx.x % unsigned(a.splits));
+    const int64_t tg = int64_t(blockIdx.x / unsigned(a.splits));
+    const int64_t mblk = blockIdx.y;
+    const int64_t m0 = mblk * BM;
+    const int64_t g0 = int64_t(split) * a.gps;
+    const int ng = int(min<int64_t>(a.gps, L.groups - g0));
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int64_t t = tg * kSkWaves + wave;
+    const bool tile_ok = t < L.tiles;
+    const int64_t tt = tile_ok ? t : L.tiles - 1;  // loads stay in bounds; results unused
+    const uint8_t* cbase = a.packed + (tt * L.groups + g0) * kChunkBytes + lane * 16;
+    const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (tt * L.groups + g0) * kTileRows + r;
+    constexpr float off = code_offset<ACT>();
+
+    f32x4_t tot[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) tot[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int gl = 0; gl < ng; ++gl) {
+        const int64_t g = g0 + gl;
+        // weights first, so the HBM load overlaps the x staging below
+        const uint4 cw = *reinterpret_cast<const uint4*>(cbase + int64_t(gl) * kChunkBytes);
+        const float sc = sbase[int64_t(gl) * kTileRows];
+
+        // stage x[m0 : m0+BM][g*128 : g*128+128]; 16 threads per row, 8 columns each
+#pragma unroll
+        for (int pass = 0; pass < BM / 16; ++pass) {
+            const int row = pass * 16 + (tid >> 4), piece = tid & 15;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (m0 + row < a.m)
+                v = *reinterpret_cast<const uint4*>(a.x + (m0 + row) * a.ldx + g * kGroup + piece * 8);
+            *reinterpret_cast<uint4*>(xa + row * kAStride + piece * 8) = v;
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s += to_f32<ACT>(uint16_t(w[i] & 0xFFFFu)) + to_f32<ACT>(uint16_t(w[i] >> 16));
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 16);
+            if (piece == 0) xrow[row] = s;
+        }
+        __syncthreads();
+
+        const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+        uint4 b[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            b[s] = make_uint4(magic_pair<ACT>(words[s], 0), magic_pair<ACT>(words[s], 1),
+                              magic_pair<ACT>(words[s], 2), magic_pair<ACT>(words[s], 3));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t* ap = xa + (mb * 16 + r) * kAStride + 8 * kq;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma16<ACT>(*reinterpret_cast<const uint4*>(ap + 32 * s), b[s], acc);
+            const float4 xs4 = *reinterpret_cast<const float4*>(xrow + mb * 16 + 4 * kq);
+            tot[mb][0] = fmaf(sc, fmaf(-off, xs4.x, acc[0]), tot[mb][0]);
+            tot[mb][1] = fmaf(sc, fmaf(-off, xs4.y, acc[1]), tot[mb][1]);
+            tot[mb][2] = fmaf(sc, fmaf(-off, xs4.z, acc[2]), tot[mb][2]);
+            tot[mb][3] = fmaf(sc, fmaf(-off, xs4.w, acc[3]), tot[mb][3]);
+        }
+        __syncthreads();
+    }
+
+    // Lane holds output rows 16mb + 4kq + i (i = 0..3) of column r of its tile.
+    const int64_t col = t * kTileRows + r;
+    if (a.splits == 1) {
+        if (tile_ok && col < a.n) {
+            const float bv = a.bias ? to_f32<ACT>(a.bias[col]) : 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t row = m0 + mb * 16 + 4 * kq + i;
+                    if (row < a.m) a.y[row * a.ldy + col] = from_f32<ACT>(tot[mb][i] + bv);
+                }
+        }
+        return;
+    }
+
+    const int64_t slot = mblk * a.tile_groups + tg;
+    float* mine = a.partials + (slot * a.splits + split) * (BM * kSkCols);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[(mb * 16 + 4 * kq + i) * kSkCols + wave * 16 + r] = tot[mb][i];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.counters + slot, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last = prev == uint32_t(a.splits - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    const float* all = a.partials + slot * a.splits * (BM * kSkCols);
+    for (int idx = tid; idx < BM * kSkCols; idx += kSkThreads) {
+        const int ml = idx / kSkCols, cl = idx - ml * kSkCols;
+        float v = 0.0f;
+        for (int sp = 0; sp < a.splits; ++sp)
+            v += __hip_atomic_load(all + sp * (BM * kSkCols) + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t row = m0 + ml, c = tg * kSkCols + cl;
+        if (row < a.m && c < a.n) {
+            if (a.bias) v += to_f32<ACT>(a.bias[c]);
+            a.y[row * a.ldy + c] = from_f32<ACT>(v);
+        }
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
+    SkinnyPlan p{};
+    const Layout L(n, k);
+    p.mb = m <= 16 ? 1 : m <= 32 ? 2 : m <= 48 ? 3 : 4;
+    const int64_t bm = 16 * p.mb;
+    p.mblocks = ceil_div(m, bm);
+    p.tile_groups = ceil_div(L.tiles, kSkWaves);
+    // ~1024 workgroups, each at least 4 groups deep where K allows.
+    const int64_t base = p.tile_groups * p.mblocks;
+    int64_t gps = ceil_div(base * L.groups, 1024);
+    gps = gps < 4 ? 4 : gps;
+    gps = gps > L.groups ? L.groups : gps;
+    // split K only while every (tile group, m block) slot has its own counter
+    if (base > kMaxSlots) gps = L.groups;
+    p.gps = int(gps);
+    p.splits = int(ceil_div(L.groups, gps));
+    p.workspace = p.splits > 1 ? workspace_layout_bytes(size_t(base) * p.splits * bm * kSkCols) : 0;
+    return p;
+}
+
+template <int MB, int ACT>
+static void launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
+    dim3 grid(unsigned(p.tile_groups * p.splits), unsigned(p.mblocks));
+    skinny_kernel<MB, ACT><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+}
+
+hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
+                         int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+                         hipStream_t stream) {
+    const SkinnyPlan p = plan_skinny(m, n, k);
+    SkinnyArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.m = m;
+    a.packed = static_cast<const uint8_t*>(packed);
+    a.n = n;
+    a.k = k;
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.y = static_cast<uint16_t*>(y);
+    a.ldy = ldy;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.partials = workspace ? workspace_partials(workspace) : nullptr;
+    a.splits = p.splits;
+    a.gps = p.gps;
+    a.tile_groups = p.tile_groups;
+    const bool bf = act == kActBf16;
+    switch (p.mb) {
+        case 1: bf ? launch_one<1, kActBf16>(a, p, stream) : launch_one<1, kActF16>(a, p, stream); break;
+        case 2: bf ? launch_one<2, kActBf16>(a, p, stream) : launch_one<2, kActF16>(a, p, stream); break;
+        case 3: bf ? launch_one<3, kActBf16>(a, p, stream) : launch_one<3, kActF16>(a, p, stream); break;
+        default: bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w4a16
