@@ -1,0 +1,289 @@
+"""Throughput of the W4A16 linear layer on one MI355X.
+
+Step: one decoder layer's four projections at M = 1 (qkv 2048->2560,
+o 2048->2048, gate_up 2048->32768, down 16384->2048; bf16 activations,
+weights N(0,0.02) with 1% N(0,0.2) outliers, RTN INT4 with group 128),
+the decode workload the M = 1 HBM metric is quoted on.  The layer's weights
+rotate over a pool of distinct copies (>= 1 GiB, more than the 256 MB
+Infinity Cache plus L2) so every step streams its weights from HBM, as a
+model with many layers would.  Inputs are resident in HBM before timing.
+
+value  = algorithmic bytes of the step (packed codes + FP32 scales + x + y)
+         / measured time, in GB/s.
+Also reported (same JSON line):
+  roofline      the dominant kernel (gate_up, M = 1) against 8 TB/s, its
+                average duration from HIP events on its stream;
+  m1024         the prefill projections at M = 1024 (fp16, bias) in TFLOP/s
+                against the dense 2.5 PFLOP/s fp16 MFMA peak;
+  load          quantize + pack throughput (load-time rows of the path);
+  cpu_baseline  the CPU oracle on a bounded sample of the same step.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16/fp16
+POOL_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_cases():
+    import synth
+    return [synth.case_by_name(n) for n in
+            ("c3_qkv_m1_k2048_n2560", "c3_o_m1_k2048_n2048",
+             "c3_gate_up_m1_k2048_n32768", "c3_down_m1_k16384_n2048")]
+
+
+def prefill_cases():
+    import synth
+    return [c for c in synth.all_cases() if c.config == 4]
+
+
+def build_pool(cases, dev):
+    """Quantize + pack each case's weight once, then copy it until the pool
+    of layers exceeds POOL_BYTES.  Returns (layers, load_stats)."""
+    import torch
+
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    packed0 = []
+    load_bytes = 0
+    load_time = 0.0
+    for c in cases:
+        w = synth.make_weight(c).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        codes, scales = w4.quantize(w)
+        p = w4.pack(codes, scales)
+        torch.cuda.synchronize()
+        load_time += time.perf_counter() - t0
+        # quantize reads W (4 B) and writes codes + scales; pack reads those and writes packed
+        load_bytes += c.n * c.k * 4 + 2 * (c.n * c.k // 2 + c.n * (c.k // 128) * 4) + p.numel()
+        packed0.append(p)
+        del w, codes, scales
+    per_layer = sum(p.numel() for p in packed0)
+    copies = max(2, -(-POOL_BYTES // per_layer))
+    layers = [packed0] + [[p.clone() for p in packed0] for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    return layers, {"bytes": load_bytes, "seconds": load_time}
+
+
+def capture(fn):
+    """A HIP graph of fn() (torch.cuda.graph over the current device)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def make_step(cases, layer, xs, biases, ys, workspace):
+    import weight_only_int4_rtn_amd as w4
+
+    def step():
+        for j, c in enumerate(cases):
+            w4.linear(xs[j], layer[j], c.n, biases[j], out=ys[j], workspace=workspace)
+    return step
+
+
+def time_graphs(graphs, steps, warmup):
+    """Replay graphs round-robin: warmup, then `steps` timed replays."""
+    import torch
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_kernel(case, layers, j, x, bias, y, workspace, launches=24, replays=10):
+    """Average duration of one projection's launch, from HIP events on its
+    stream around replays of a graph of back-to-back launches (weights rotate
+    over distinct copies)."""
+    import torch
+
+    import weight_only_int4_rtn_amd as w4
+
+    def many():
+        for i in range(launches):
+            w4.linear(x, layers[i % len(layers)][j], case.n, bias, out=y, workspace=workspace)
+    g = capture(many)
+    g.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / (launches * replays)
+
+
+def eager_ms(cases, layers, xs, biases, ys, workspace, steps=20):
+    import torch
+    for i in range(3):
+        make_step(cases, layers[i % len(layers)], xs, biases, ys, workspace)()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        make_step(cases, layers[i % len(layers)], xs, biases, ys, workspace)()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def run_workload(cases, dev, steps, warmup, dominant):
+    """Pool, graphs, timings for one workload.  Returns a dict of figures."""
+    import torch
+
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    layers, load = build_pool(cases, dev)
+    xs = [synth.make_x(c).to(dev) for c in cases]
+    biases = [synth.make_bias(c).to(dev) if c.bias else None for c in cases]
+    ys = [torch.empty((c.m, c.n), dtype=c.torch_dtype, device=dev) for c in cases]
+    ws_bytes = max(w4.workspace_bytes(c.m, c.n, c.k) for c in cases)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    log(f"pool: {len(layers)} layers of {sum(p.numel() for p in layers[0]) / 1e6:.1f} MB; "
+        f"paths {[w4.choose_path(c.m, c.n, c.k).name for c in cases]}")
+    graphs = [capture(make_step(cases, layer, xs, biases, ys, workspace)) for layer in layers]
+    ms = time_graphs(graphs, steps, warmup)
+    dom = cases[dominant]
+    dom_ms = time_kernel(dom, layers, dominant, xs[dominant], biases[dominant], ys[dominant], workspace)
+    eager = eager_ms(cases, layers, xs, biases, ys, workspace)
+    out = {"ms": ms, "dom_ms": dom_ms, "eager_ms": eager, "load": load}
+    del graphs, layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(cases, target_seconds=12.0):
+    """The oracle (as it stands) on the same M = 1 decode layer, repeated."""
+    import oracle
+    import synth
+    prepared = []
+    for c in cases:
+        q, s = oracle.quantize(synth.make_weight(c).numpy())
+        xb = synth.to_bits16(synth.make_x(c))
+        prepared.append((c, xb, q, s))
+    bytes_per_pass = sum(c.alg_bytes() for c in cases)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for c, xb, q, s in prepared:
+            oracle.linear(xb, oracle.BF16, q, s)
+        reps += 1
+        if time.perf_counter() - t0 >= target_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(bytes_per_pass * reps / el / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full M=1 decode layer (4 projections, {bytes_per_pass / 1e6:.1f} MB of "
+                      f"algorithmic bytes) run {reps} times in {el:.1f} s",
+            "ms_per_step": round(el * 1e3 / reps, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer is benchmarked on one MI355X "
+              "(multi-GPU sharding is a design note, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    w4.lib()
+
+    # --- decode step (M = 1) --------------------------------------------------
+    cases = decode_cases()
+    dominant = 2  # gate_up: the largest stream
+    log(f"decode workload: {[c.name for c in cases]}")
+    dec = run_workload(cases, dev, args.steps, args.warmup, dominant)
+    ms, dom_ms = dec["ms"], dec["dom_ms"]
+    step_bytes = sum(c.alg_bytes() for c in cases)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    dom = cases[dominant]
+    dom_gbs = dom.alg_bytes() / (dom_ms * 1e-3) / 1e9
+    log(f"decode: {ms * 1e3:.2f} us/step (graph replay), {value:.1f} GB/s; eager {dec['eager_ms'] * 1e3:.1f} us/step; "
+        f"gate_up {dom_ms * 1e3:.2f} us/launch, {dom_gbs:.1f} GB/s")
+
+    # --- prefill (M = 1024) ---------------------------------------------------
+    pcases = prefill_cases()
+    pdom = 1  # N = 32768: the largest GEMM
+    log(f"prefill workload: {[c.name for c in pcases]}")
+    pre = run_workload(pcases, dev, args.prefill_steps, 5, pdom)
+    pms, pdom_ms = pre["ms"], pre["dom_ms"]
+    pflops = sum(c.flops() for c in pcases)
+    ptf = pflops / (pms * 1e-3) / 1e12
+    pd = pcases[pdom]
+    pd_tf = pd.flops() / (pdom_ms * 1e-3) / 1e12
+    log(f"prefill: {pms * 1e3:.1f} us/step, {ptf:.1f} TFLOP/s; N=32768 {pdom_ms * 1e3:.1f} us, {pd_tf:.1f} TFLOP/s")
+    load = dec["load"]
+
+    out = {
+        "metric": "W4A16 GEMM: HBM GB/s & %peak at M=1; TFLOP/s & %MFMA peak at M=1024",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; weights rotate over a >=1 GiB pool of layer copies; steps replayed as HIP graphs)",
+        "config": {"workload": "decode layer M=1: qkv 2048x2560, o 2048x2048, gate_up 2048x32768, "
+                               "down 16384x2048; bf16 x, int4 g128 weights",
+                   "m": 1, "bytes_per_step": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "kernel_path": w4.choose_path(1, 2048, 2048).name,
+                   "eager_ms_per_step": round(dec["eager_ms"], 4)},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"{w4.choose_path(1, dom.n, dom.k).name} {dom.name}",
+                     "avg_launch_us": round(dom_ms * 1e3, 3), "bytes_per_launch": dom.alg_bytes()},
+        "m1024": {"workload": "prefill M=1024 fp16 with bias: K2048xN2560, K2048xN32768, K16384xN2048",
+                  "tflops": round(ptf, 2), "ms_per_step": round(pms, 4),
+                  "pct_mfma_peak": round(100 * ptf / MFMA_PEAK_TFLOPS, 2),
+                  "roofline": {"bound": "mfma", "achieved": round(pd_tf, 2), "peak": MFMA_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(pd_tf / MFMA_PEAK_TFLOPS, 4),
+                               "kernel": f"{w4.choose_path(pd.m, pd.n, pd.k).name} {pd.name}",
+                               "avg_launch_us": round(pdom_ms * 1e3, 3)}},
+        "load": {"rows": "quantize + pack, decode layer weights",
+                 "GBps": round(load["bytes"] / load["seconds"] / 1e9, 2) if load["seconds"] else None},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(cases)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

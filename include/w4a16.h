@@ -61,9 +61,10 @@ typedef enum {
 /* Kernel families w4a16_linear chooses between (by M, N, K). */
 typedef enum {
     W4A16_PATH_AUTO = 0,    /* let the library choose */
-    W4A16_PATH_GEMV = 1,    /* M <= 4: VALU dot products, split-K, wave reductions */
-    W4A16_PATH_SKINNY = 2,  /* small and mid M: register-dequantized MFMA, split-K */
-    W4A16_PATH_GEMM = 3     /* large M: LDS-staged dequantized tiles into MFMA */
+    W4A16_PATH_GEMV = 1,    /* small M: VALU v_dot2 products, split-K, cross-lane reductions */
+    W4A16_PATH_MGEMV = 2,   /* small M: the same weight stream contracted on MFMA */
+    W4A16_PATH_SKINNY = 3,  /* mid M: register-dequantized MFMA, x tiles through LDS */
+    W4A16_PATH_GEMM = 4     /* large M: LDS-staged dequantized tiles into MFMA */
 } w4a16_path_t;
 
 /* Group size along K: one FP32 scale per 128 consecutive weights of a row. */
@@ -118,10 +119,10 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
 
 /*
  * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
- * kernel path (0 if none).  The workspace holds split-K partial sums and
- * per-tile arrival counters.  It must be zero-filled once before its first
- * use; every call leaves the counters zero again when it completes.  Two calls
- * that may run at the same time must not share a workspace.
+ * kernel path (0 if none).  The workspace holds the FP32 partial sums of a K
+ * split, which a second small kernel adds in split order (no inter-workgroup
+ * synchronisation, no floating-point atomics).  It needs no initialisation.
+ * Two calls that may run at the same time must not share a workspace.
  */
 size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
@@ -139,7 +140,7 @@ size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *   y         device, [m][ldy] of act_dtype, ldy >= n, 2-byte aligned; must not
  *             overlap x, packed, bias or workspace.
  *   workspace device, >= w4a16_linear_workspace_bytes(m, n, k) bytes, 16-byte
- *             aligned, zero-filled before first use (may be NULL when that size is 0).
+ *             aligned, contents ignored (may be NULL when that size is 0).
  * m == 0 or n == 0 returns W4A16_OK and launches nothing.  Returns W4A16_OK,
  * W4A16_EINVAL, W4A16_EUNSUPPORTED (act_dtype), W4A16_EWORKSPACE or W4A16_EHIP.
  * The result is bit-identical from run to run (no floating-point atomics).

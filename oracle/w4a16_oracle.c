@@ -202,7 +202,7 @@ int oracle_linear(const uint16_t *x, int x_dtype, int64_t m, int64_t k, int64_t 
         return -1;
     if (x_dtype != ORACLE_BF16 && x_dtype != ORACLE_F16)
         return -1;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t i = 0; i < m; ++i)
         for (int64_t j = 0; j < n; ++j)
             y[i * n + j] = one_output(x, x_dtype, ldx, i, q, s, k, j, bias);

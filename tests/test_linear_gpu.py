@@ -20,7 +20,7 @@ from tests.gpu_util import bits, check_close, require_gpu, row_max_dequant, say,
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ["GEMV", "SKINNY"]
+PATHS = ["GEMV", "MGEMV", "SKINNY", "GEMM"]
 
 
 @pytest.fixture(scope="module")

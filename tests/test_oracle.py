@@ -112,8 +112,8 @@ def test_pins_catch_planted_mistake(desc, old, new):
     mutated = src.replace(old, new)
     if "n_" in new:  # the transposed-index mutant needs the row count in scope
         mutated = mutated.replace("static double one_output(", "static int64_t n_ = 1;\nstatic double one_output(", 1)
-        mutated = mutated.replace("#pragma omp parallel for schedule(static)\n    for (int64_t i = 0; i < m; ++i)",
-                                  "n_ = n < k ? n : k;\n#pragma omp parallel for schedule(static)\n    for (int64_t i = 0; i < m; ++i)", 1)
+        mutated = mutated.replace("#pragma omp parallel for collapse(2) schedule(static)\n    for (int64_t i = 0; i < m; ++i)",
+                                  "n_ = n < k ? n : k;\n#pragma omp parallel for collapse(2) schedule(static)\n    for (int64_t i = 0; i < m; ++i)", 1)
     with tempfile.TemporaryDirectory() as d:
         src_path = os.path.join(d, "mutant.c")
         so_path = os.path.join(d, "libmutant.so")

@@ -24,8 +24,9 @@ F32, BF16, F16 = 0, 1, 2
 class Path(enum.IntEnum):
     AUTO = 0
     GEMV = 1
-    SKINNY = 2
-    GEMM = 3
+    MGEMV = 2
+    SKINNY = 3
+    GEMM = 4
 
 
 class W4A16Error(RuntimeError):
@@ -170,13 +171,13 @@ _workspaces: dict = {}
 
 
 def workspace_for(device, stream_handle: int, nbytes: int) -> torch.Tensor | None:
-    """A zero-initialised workspace of at least ``nbytes`` for one (device, stream)."""
+    """A workspace of at least ``nbytes`` for one (device, stream)."""
     if nbytes == 0:
         return None
     key = (torch.device(device).index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

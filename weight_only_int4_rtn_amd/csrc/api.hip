@@ -1,7 +1,7 @@
 // C ABI of the library (include/w4a16.h): argument checks from host metadata
 // only, kernel choice, launches.  Nothing here allocates, synchronizes or
 // reads device memory ("Piper Kernels", section "Validation contract").
-#include "../../include/w4a16.h"
+#include "w4a16.h"
 
 #include "common.h"
 #include "kernels.h"
@@ -37,6 +37,7 @@ w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A1
 size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k) {
     switch (path) {
         case W4A16_PATH_GEMV: return plan_gemv(m < 4 ? m : 4, n, k).workspace;
+        case W4A16_PATH_MGEMV: return plan_mgemv(m < 16 ? m : 16, n, k).workspace;
         case W4A16_PATH_SKINNY: return plan_skinny(m, n, k).workspace;
         case W4A16_PATH_GEMM: return plan_gemm(m, n, k).workspace;
         default: return 0;
@@ -110,14 +111,16 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     (void)n;
     (void)k;
-    if (m <= 4) return W4A16_PATH_GEMV;
-    return W4A16_PATH_SKINNY;
+    if (m <= 3) return W4A16_PATH_GEMV;
+    if (m <= 8) return W4A16_PATH_MGEMV;
+    if (m < 128) return W4A16_PATH_SKINNY;
+    return W4A16_PATH_GEMM;
 }
 
 size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     if (m <= 0 || !valid_nk(n, k) || n == 0 || m > kMaxDim) return 0;
     size_t best = 0;
-    const w4a16_path_t paths[3] = {W4A16_PATH_GEMV, W4A16_PATH_SKINNY, W4A16_PATH_GEMM};
+    const w4a16_path_t paths[4] = {W4A16_PATH_GEMV, W4A16_PATH_MGEMV, W4A16_PATH_SKINNY, W4A16_PATH_GEMM};
     for (w4a16_path_t p : paths) {
         const size_t b = path_workspace(p, m, n, k);
         best = b > best ? b : best;
@@ -130,8 +133,8 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
                                       int64_t n, const void* bias, void* y, int64_t ldy,
                                       void* workspace, size_t workspace_bytes, void* stream) {
     if (act_dtype != W4A16_BF16 && act_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
-    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_SKINNY &&
-        path != W4A16_PATH_GEMM)
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MGEMV &&
+        path != W4A16_PATH_SKINNY && path != W4A16_PATH_GEMM)
         return W4A16_EINVAL;
     if (!valid_nk(n, k) || m < 0 || m > kMaxDim) return W4A16_EINVAL;
     if (ldx < k || ldx > kMaxDim || ldx % 8 != 0 || ldy < n || ldy > kMaxDim) return W4A16_EINVAL;
@@ -140,7 +143,6 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2) || (bias && !aligned(bias, 2)))
         return W4A16_EINVAL;
     if (path == W4A16_PATH_AUTO) path = w4a16_linear_choose_path(m, n, k);
-    if (path == W4A16_PATH_GEMM) return W4A16_EUNSUPPORTED;
 
     const size_t xbytes = span_bytes(m, k, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
                  pbytes = w4a16_packed_bytes(n, k), bbytes = bias ? size_t(n) * 2 : 0;
@@ -166,6 +168,17 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
         }
         return W4A16_OK;
     }
+    if (path == W4A16_PATH_MGEMV) {
+        for (int64_t r0 = 0; r0 < m; r0 += 16) {
+            const int64_t mm = m - r0 < 16 ? m - r0 : 16;
+            const hipError_t e = launch_mgemv(xp + r0 * ldx, act, mm, k, ldx, packed, n, bias,
+                                              yp + r0 * ldy, ldy, workspace, s);
+            if (e != hipSuccess) return W4A16_EHIP;
+        }
+        return W4A16_OK;
+    }
+    if (path == W4A16_PATH_GEMM)
+        return from_hip(launch_gemm(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
     return from_hip(launch_skinny(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
 }
 

@@ -113,6 +113,14 @@ __device__ inline uint32_t magic_pair(uint32_t word, int i) {
     return and_or(i == 0 ? word : word >> (4 * i), 0x000F000Fu, magic);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, then s_barrier.  __syncthreads() also waits for every
+// outstanding global load (vmcnt(0)), which would serialise the weight
+// prefetch that is in flight when x is staged.
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int ACT>
 __device__ inline constexpr float code_offset() {
     return ACT == kActBf16 ? kOffsetBf16 : kOffsetF16;

@@ -7,26 +7,20 @@
 
 namespace w4a16 {
 
-// Workspace = [arrival counters: kMaxSlots uint32][FP32 partial sums].
-// The counter region has a fixed size so that partial sums of one call can
-// never land on the counters of a later call with another shape: counters
-// start zeroed (the caller zero-fills a new workspace) and every call leaves
-// the counters it used at zero.  A launch uses at most kMaxSlots counters.
-constexpr int64_t kMaxSlots = 16384;
-constexpr size_t kCounterBytes = size_t(kMaxSlots) * 4;
-inline size_t workspace_layout_bytes(size_t partial_floats) {
-    return kCounterBytes + partial_floats * 4;
-}
-inline float* workspace_partials(void* ws) {
-    return reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kCounterBytes);
-}
+// The workspace of a K-split launch holds FP32 partial sums [splits][m][npad];
+// it needs no initialisation (every element read is written first).
 
 struct GemvPlan {
-    int gps, splits;
-    int64_t tiles_per_launch;  // tile range of one launch (<= kMaxSlots when split)
+    int waves, gps, splits, cpw;  // cpw: chunks each wave loads up front
     size_t lds, workspace;
 };
 GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k);
+
+struct MgemvPlan {
+    int mmax, gps, splits, cpw;
+    size_t lds, workspace;
+};
+MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k);
 
 struct SkinnyPlan {
     int mb;             // 16-row m-subtiles per workgroup (1..4)
@@ -38,6 +32,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k);
 
 struct GemmPlan {
     int64_t mtiles, ntiles;
+    int gps, splits;
     size_t workspace;
 };
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k);
@@ -49,10 +44,19 @@ hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t n, int
 hipError_t launch_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, float* scales,
                          hipStream_t stream);
 
+// y[m][n] = round(sum over splits of partials[s][m][npad] + bias): finishes K-split launches.
+hipError_t launch_splitk_reduce(const float* partials, int splits, int64_t m, int64_t n, int64_t npad,
+                                const uint16_t* bias, uint16_t* y, int64_t ldy, int act,
+                                hipStream_t stream);
+
 // m <= 4 per launch (the caller splits larger m into row blocks).
 hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream);
+// m <= 16 per launch (the caller splits larger m into row blocks).
+hipError_t launch_mgemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
+                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+                        hipStream_t stream);
 hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
                          int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                          hipStream_t stream);

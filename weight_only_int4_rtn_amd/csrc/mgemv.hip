@@ -1,0 +1,246 @@
+// Small-M forward on the matrix cores (M <= 16): the same weight stream as
+// the v_dot2 kernel (gemv.hip), with the contraction done by MFMA.
+//
+// A workgroup of 4 waves owns one 16-row weight tile and a K split.  The
+// workgroup stages its slice of x (M rows) in LDS once, with each row's sum
+// over every 128-column group.  Per chunk, a wave turns its four words into
+// four B operands of v_mfma_f32_16x16x32_{bf16,f16} (the chunk layout is that
+// operand layout: lane L holds column L % 16 of the tile, columns
+// 8*(L/16) + j of each 32-wide k-step), reads the matching A operands (row
+// L % 16 of x, zero for rows >= M) from LDS, and runs four MFMAs into a fresh
+// accumulator.  The packed pairs hold off + q exactly (off = 136 for bf16,
+// 1032 for f16), so per group
+//     sum_k x_k q_k = mfma result - off * sum_k x_k,
+// and the group's FP32 scale multiplies that into the FP32 totals.  The
+// accumulator layout of the MFMA gives lane L the rows 4*(L/16) + i, i = 0..3,
+// of column L % 16.  Per weight element this costs 7/8 of a VALU instruction
+// for the nibble conversion, against 11/8 for the v_dot2 kernel at M = 1.
+//
+// Waves are summed through LDS in a fixed order; K splits store FP32 partial
+// sums for the split-K reduce kernel (reduce.hip).
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a16 {
+
+struct MgemvArgs {
+    const uint16_t* x;
+    int64_t ldx, m;
+    const uint8_t* packed;
+    int64_t n, k;
+    const uint16_t* bias;
+    uint16_t* y;
+    int64_t ldy;
+    float* partials;  // [splits][m][tiles*16] when splits > 1
+    int splits, gps;
+};
+
+constexpr int kMgWaves = 4;
+constexpr int kMgThreads = 64 * kMgWaves;
+constexpr int kMgChunks = 8;  // chunks per wave, all loaded up front
+constexpr int kXRegs = 8;  // 16-byte x loads per thread while staging
+
+template <int ACT>
+__device__ inline f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
+    if constexpr (ACT == kActBf16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+// MMAX: rows of x staged (>= m, <= 16).
+template <int MMAX, int ACT, int CPW>
+__global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const Layout L(a.n, a.k);
+    const int split = int(blockIdx.x % unsigned(a.splits));
+    const int64_t t = int64_t(blockIdx.x / unsigned(a.splits));
+    const int64_t g0 = int64_t(split) * a.gps;
+    const int ng = int(min<int64_t>(a.gps, L.groups - g0));
+    const int klen = ng * kGroup;
+    const int m = int(a.m);
+
+    // x rows are padded by 16 bytes so the 16 rows an A-operand read touches
+    // fall in different LDS banks.
+    const int xstride = klen + 8;
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                                      // [MMAX][xstride]
+    float* xg = reinterpret_cast<float*>(smem + size_t(MMAX) * (a.gps * kGroup + 8) * 2);    // [ng][16]
+    float* red = xg + a.gps * 16;                                                          // [waves][16][16]
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+
+    const uint8_t* cbase = a.packed + (t * L.groups + g0) * kChunkBytes + lane * 16;
+    const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (t * L.groups + g0) * kTileRows + r;
+
+    // Every chunk of the wave (CPW of them) is loaded before any is used.
+    // The loads are unconditional straight-line code (clamped addresses), so
+    // the compiler's wait counts stay exact: each use waits for its own load.
+    uint4 cw[CPW];
+    float sc[CPW];
+
+    // x slice first, then the first weight batch (loads complete in issue
+    // order: staging waits for x only).  The plan keeps m * klen / 8 <=
+    // kXRegs * threads.
+    const int per_row = klen / 8;
+    const int total = m * per_row;
+    uint4 xv[kXRegs];
+#pragma unroll
+    for (int j = 0; j < kXRegs; ++j) {
+        if (j * kMgThreads >= total) break;
+        const int i = j * kMgThreads + tid;
+        const int ic = i < total ? i : total - 1;
+        const int row = ic / per_row, c = ic - row * per_row;
+        xv[j] = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + g0 * kGroup + c * 8);
+    }
+    // keep the compiler from hoisting the weight loads above the x loads
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+        const int gl = wave + u * kMgWaves;
+        const int gc = gl < ng ? gl : ng - 1;  // a valid chunk; unused when gl >= ng
+        cw[u] = *reinterpret_cast<const uint4*>(cbase + int64_t(gc) * kChunkBytes);
+        sc[u] = sbase[int64_t(gc) * kTileRows];
+    }
+
+    // Stage rows [0, m); group sums over the 16 threads that cover one row's
+    // 128 columns of a group (lanes 1, 2, 4, 8 apart).
+#pragma unroll
+    for (int j = 0; j < kXRegs; ++j) {
+        if (j * kMgThreads >= total) break;
+        const int i = j * kMgThreads + tid;
+        const bool on = i < total;
+        const int row = on ? i / per_row : 0, c = on ? i - row * per_row : 0;
+        if (on) *reinterpret_cast<uint4*>(xs + row * xstride + c * 8) = xv[j];
+        if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            s += to_f32<ACT>(uint16_t(w[q] & 0xFFFFu)) + to_f32<ACT>(uint16_t(w[q] >> 16));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 16);
+        if (on && (c & 15) == 0) xg[(c >> 4) * 16 + row] = s;
+    }
+    // rows m..15 of the group sums are zero (their A operands are zero)
+    for (int i = tid; i < ng * 16; i += kMgThreads)
+        if ((i & 15) >= m) xg[i] = 0.0f;
+    lds_barrier();
+
+    constexpr float off = code_offset<ACT>();
+    const bool row_on = r < m;
+    const uint16_t* xrow = xs + (row_on ? r : 0) * xstride + 8 * kq;
+    f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+        const int gl = wave + u * kMgWaves;
+        if (gl < ng) {
+            const uint32_t words[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+            const float scale = sc[u];
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                uint4 av = make_uint4(0u, 0u, 0u, 0u);
+                if (row_on) av = *reinterpret_cast<const uint4*>(xrow + gl * kGroup + 32 * s);
+                const uint4 bv = make_uint4(magic_pair<ACT>(words[s], 0), magic_pair<ACT>(words[s], 1),
+                                            magic_pair<ACT>(words[s], 2), magic_pair<ACT>(words[s], 3));
+                acc = mfma_16x16x32<ACT>(av, bv, acc);
+            }
+            const float4 xsum = *reinterpret_cast<const float4*>(xg + gl * 16 + 4 * kq);
+            tot[0] = fmaf(scale, fmaf(-off, xsum.x, acc[0]), tot[0]);
+            tot[1] = fmaf(scale, fmaf(-off, xsum.y, acc[1]), tot[1]);
+            tot[2] = fmaf(scale, fmaf(-off, xsum.z, acc[2]), tot[2]);
+            tot[3] = fmaf(scale, fmaf(-off, xsum.w, acc[3]), tot[3]);
+        }
+    }
+
+    // Lane holds rows 4kq + i of column r; sum the waves through LDS.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * kq + i) * 16 + r] = tot[i];
+    __syncthreads();
+    const int orow = tid >> 4, ocol = tid & 15;  // 256 threads = 16 x 16 outputs
+    if (orow >= m) return;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMgWaves; ++w) v += red[(w * 16 + orow) * 16 + ocol];
+    const int64_t col = t * kTileRows + ocol;
+    if (a.splits > 1) {
+        a.partials[(int64_t(split) * m + orow) * (L.tiles * kTileRows) + col] = v;
+        return;
+    }
+    if (col < a.n) {
+        if (a.bias) v += to_f32<ACT>(a.bias[col]);
+        a.y[orow * a.ldy + col] = from_f32<ACT>(v);
+    }
+}
+
+// Same plan shape as the v_dot2 kernel: split K only when the row tiles
+// cannot fill the chip; the x slice stays within 16 rows x 2048 columns.
+MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k) {
+    MgemvPlan p{};
+    const Layout L(n, k);
+    p.mmax = m <= 4 ? 4 : m <= 8 ? 8 : 16;
+    int64_t splits = 1;
+    if (L.tiles < 512) splits = ceil_div(512, L.tiles);
+    int64_t gps = ceil_div(L.groups, splits);
+    if (gps < 2 * kMgWaves) gps = 2 * kMgWaves;
+    int64_t max_gps = 128 / m;                       // x slice <= kXRegs loads per thread
+    if (max_gps > kMgChunks * kMgWaves) max_gps = kMgChunks * kMgWaves;  // chunks per wave
+    if (gps > max_gps) gps = max_gps;
+    if (gps > L.groups) gps = L.groups;
+    p.gps = int(gps);
+    p.splits = int(ceil_div(L.groups, gps));
+    const int64_t per_wave = ceil_div(gps, kMgWaves);
+    p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+    p.lds = size_t(p.mmax) * (gps * kGroup + 8) * 2 + size_t(gps) * 16 * 4 + size_t(kMgWaves) * 256 * 4;
+    p.workspace = p.splits > 1 ? size_t(p.splits) * m * L.tiles * kTileRows * 4 : 0;
+    return p;
+}
+
+template <int MMAX, int ACT>
+static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t stream) {
+    const Layout L(a.n, a.k);
+    const dim3 grid(unsigned(L.tiles * p.splits)), block(kMgThreads);
+    switch (p.cpw) {
+        case 1: mgemv_kernel<MMAX, ACT, 1><<<grid, block, p.lds, stream>>>(a); break;
+        case 2: mgemv_kernel<MMAX, ACT, 2><<<grid, block, p.lds, stream>>>(a); break;
+        case 4: mgemv_kernel<MMAX, ACT, 4><<<grid, block, p.lds, stream>>>(a); break;
+        default: mgemv_kernel<MMAX, ACT, 8><<<grid, block, p.lds, stream>>>(a); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_reduce(a.partials, p.splits, a.m, a.n, L.tiles * kTileRows, a.bias, a.y, a.ldy,
+                                ACT, stream);
+}
+
+hipError_t launch_mgemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
+                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+                        hipStream_t stream) {
+    const MgemvPlan p = plan_mgemv(m, n, k);
+    MgemvArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.m = m;
+    a.packed = static_cast<const uint8_t*>(packed);
+    a.n = n;
+    a.k = k;
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.y = static_cast<uint16_t*>(y);
+    a.ldy = ldy;
+    a.partials = static_cast<float*>(workspace);
+    a.splits = p.splits;
+    a.gps = p.gps;
+    const bool bf = act == kActBf16;
+    switch (p.mmax) {
+        case 4: return bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream);
+        case 8: return bf ? launch_one<8, kActBf16>(a, p, stream) : launch_one<8, kActF16>(a, p, stream);
+        default: return bf ? launch_one<16, kActBf16>(a, p, stream) : launch_one<16, kActF16>(a, p, stream);
+    }
+}
+
+}  // namespace w4a16

@@ -14,9 +14,8 @@
 //      sum_k x (off + q); the wave subtracts off * sum_k x, multiplies by the
 //      column's FP32 scale and adds into its FP32 totals.
 // The weights never pass through LDS; x tiles are shared by the 4 waves.
-// K splits are reduced like the small-M path: partials in the workspace, and
-// the last workgroup to arrive (integer counter) sums them in split order,
-// adds the bias in FP32 and rounds once.
+// K splits store FP32 partial sums that the split-K reduce kernel adds in
+// split order (reduce.hip), adding the bias in FP32 and rounding once.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,8 +29,7 @@ struct SkinnyArgs {
     const uint16_t* bias;
     uint16_t* y;
     int64_t ldy;
-    float* partials;
-    uint32_t* counters;
+    float* partials;  // [splits][m][tile_groups*64] when splits > 1
     int splits, gps;
     int64_t tile_groups;
 };
@@ -57,7 +55,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     constexpr int BM = 16 * MB;
     __shared__ __align__(16) uint16_t xa[BM * kAStride];
     __shared__ __align__(16) float xrow[BM];
-    __shared__ int last;
 
     const Layout L(a.n, a.k);
     const int split = int(blockIdx.x % unsigned(a.splits));
@@ -143,34 +140,17 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
         return;
     }
 
-    const int64_t slot = mblk * a.tile_groups + tg;
-    float* mine = a.partials + (slot * a.splits + split) * (BM * kSkCols);
+    // K split: store the FP32 partial sums; the split-K reduce kernel adds
+    // them in split order, adds the bias and rounds (reduce.hip).
+    if (!tile_ok) return;
+    const int64_t npad = a.tile_groups * kSkCols;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mine[(mb * 16 + 4 * kq + i) * kSkCols + wave * 16 + r] = tot[mb][i];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(a.counters + slot, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == uint32_t(a.splits - 1);
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const float* all = a.partials + slot * a.splits * (BM * kSkCols);
-    for (int idx = tid; idx < BM * kSkCols; idx += kSkThreads) {
-        const int ml = idx / kSkCols, cl = idx - ml * kSkCols;
-        float v = 0.0f;
-        for (int sp = 0; sp < a.splits; ++sp)
-            v += __hip_atomic_load(all + sp * (BM * kSkCols) + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int64_t row = m0 + ml, c = tg * kSkCols + cl;
-        if (row < a.m && c < a.n) {
-            if (a.bias) v += to_f32<ACT>(a.bias[c]);
-            a.y[row * a.ldy + c] = from_f32<ACT>(v);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + mb * 16 + 4 * kq + i;
+            if (row < a.m) a.partials[(int64_t(split) * a.m + row) * npad + col] = tot[mb][i];
         }
-    }
-    if (tid == 0) __hip_atomic_store(a.counters + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
@@ -185,18 +165,20 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
     int64_t gps = ceil_div(base * L.groups, 1024);
     gps = gps < 4 ? 4 : gps;
     gps = gps > L.groups ? L.groups : gps;
-    // split K only while every (tile group, m block) slot has its own counter
-    if (base > kMaxSlots) gps = L.groups;
     p.gps = int(gps);
     p.splits = int(ceil_div(L.groups, gps));
-    p.workspace = p.splits > 1 ? workspace_layout_bytes(size_t(base) * p.splits * bm * kSkCols) : 0;
+    p.workspace = p.splits > 1 ? size_t(p.splits) * m * p.tile_groups * kSkCols * 4 : 0;
     return p;
 }
 
 template <int MB, int ACT>
-static void launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
+static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
     dim3 grid(unsigned(p.tile_groups * p.splits), unsigned(p.mblocks));
     skinny_kernel<MB, ACT><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_reduce(a.partials, p.splits, a.m, a.n, p.tile_groups * kSkCols, a.bias, a.y, a.ldy,
+                                ACT, stream);
 }
 
 hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
@@ -213,19 +195,17 @@ hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t l
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.partials = workspace ? workspace_partials(workspace) : nullptr;
+    a.partials = static_cast<float*>(workspace);
     a.splits = p.splits;
     a.gps = p.gps;
     a.tile_groups = p.tile_groups;
     const bool bf = act == kActBf16;
     switch (p.mb) {
-        case 1: bf ? launch_one<1, kActBf16>(a, p, stream) : launch_one<1, kActF16>(a, p, stream); break;
-        case 2: bf ? launch_one<2, kActBf16>(a, p, stream) : launch_one<2, kActF16>(a, p, stream); break;
-        case 3: bf ? launch_one<3, kActBf16>(a, p, stream) : launch_one<3, kActF16>(a, p, stream); break;
-        default: bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream); break;
+        case 1: return bf ? launch_one<1, kActBf16>(a, p, stream) : launch_one<1, kActF16>(a, p, stream);
+        case 2: return bf ? launch_one<2, kActBf16>(a, p, stream) : launch_one<2, kActF16>(a, p, stream);
+        case 3: return bf ? launch_one<3, kActBf16>(a, p, stream) : launch_one<3, kActF16>(a, p, stream);
+        default: return bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream);
     }
-    return hipGetLastError();
 }
 
 }  // namespace w4a16
