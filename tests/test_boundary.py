@@ -64,10 +64,10 @@ def test_packed_bytes(lib):
 
 
 def test_choose_path(lib):
-    for m in (1, 2, 3, 4):
-        assert w4.choose_path(m, 2048, 2048) == w4.Path.GEMV
-    assert w4.choose_path(16, 2048, 2048) != w4.Path.AUTO
-    assert w4.choose_path(4096, 2048, 2048) != w4.Path.AUTO
+    assert w4.choose_path(1, 2048, 2048) == w4.Path.GEMV
+    for m in (1, 2, 3, 4, 8, 16, 50, 64, 256, 1024, 4096):
+        assert w4.choose_path(m, 2048, 2048) != w4.Path.AUTO
+    assert w4.choose_path(4096, 2048, 2048) == w4.Path.GEMM
 
 
 def test_workspace_bytes(lib):
