@@ -32,7 +32,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k);
 
 struct GemmPlan {
     int64_t mtiles, ntiles;
-    int gps, splits;
+    int mb, gps, splits;  // mb: 16-row blocks per workgroup (128 or 256 rows)
     size_t workspace;
 };
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k);
