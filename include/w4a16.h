@@ -153,7 +153,9 @@ w4a16_status_t w4a16_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, i
 /*
  * w4a16_linear with an explicit kernel path (W4A16_PATH_AUTO behaves exactly
  * like w4a16_linear).  Every path accepts every valid m; the automatic choice
- * is the fast one.  For tests and measurements of each kernel.
+ * is the fast one.  For tests and measurements of each kernel.  The GEMM path
+ * addresses its x tiles with 32-bit offsets and returns W4A16_EUNSUPPORTED for
+ * ldx > 4194304 (2^22); the automatic choice then takes the SKINNY path.
  */
 w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
                                       int64_t m, int64_t k, int64_t ldx, const void* packed,

@@ -137,6 +137,10 @@ def test_linear_rejects(lib):
                ws_bytes=256) == B.EWORKSPACE
     assert lin(lib, m=1, k=16384, ldx=16384, n=2048, ldy=2048, y=A * 64, ws=A * 128 + 8,
                ws_bytes=need) == B.EINVAL                     # misaligned workspace
+    # the GEMM path takes row strides up to 2^22 elements (32-bit tile offsets)
+    big = (1 << 22) + 8
+    assert lin(lib, m=256, k=128, ldx=big, n=16, y=A * 4096, path=int(w4.Path.GEMM)) == B.EUNSUPPORTED
+    assert w4.choose_path(256, 16, (1 << 22) + 128) == w4.Path.SKINNY
 
 
 def test_binding_rejects_cpu_tensors():

@@ -79,6 +79,69 @@ def test_exact_arithmetic_bit_exact(dev, path, dtype, m, n, k):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
 
 
+# GEMM tilings the planner picks by shape: 256 x 256 tiles with ragged M and
+# N, a K split whose parts hold odd and even group counts, a single group
+# (LDS-staged epilogue), a row stride that is not a multiple of 8 (direct
+# epilogue); and 128 x 256 tiles, one group deep and split.  Exact
+# arithmetic, checked bit for bit on whole rows and columns (first, last,
+# either side of a tile edge).
+GEMM_TILE_SHAPES = [(513, 16424, 1152), (769, 12296, 128), (300, 4104, 640), (1000, 2056, 2176),
+                    (512, 32772, 256)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", GEMM_TILE_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k in GEMM_TILE_SHAPES])
+def test_gemm_tilings_bit_exact(dev, dtype, m, n, k):
+    w, x, b = exact_case(m, n, k, seed=m + n + k, dtype=dtype, with_bias=True)
+    say(f"gemm tiling case dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare(w, dev)
+    y = run(x.to(dev), packed, n, b.to(dev), "GEMM").cpu().to(torch.float64).numpy()
+    edge_rows = sorted({0, 127, 128, 255, 256, m - 2, m - 1} & set(range(m)))
+    edge_cols = sorted({0, 15, 16, 255, 256, n - 17, n - 1} & set(range(n)))
+    rows = np.concatenate([np.repeat(edge_rows, n), np.tile(np.arange(m), len(edge_cols))])
+    cols = np.concatenate([np.tile(np.arange(n), len(edge_rows)), np.repeat(edge_cols, m)])
+    y_ref = oracle.linear_entries(bits(x), tag(dtype), q, s, bits(b), rows, cols)
+    want = to_rne16(y_ref, dtype)
+    got = y[rows, cols]
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (f"{bad.size} mismatches, first at row {rows[bad[0]]} col {cols[bad[0]]}: "
+                           f"got {got[bad[0]]} want {want[bad[0]]}")
+
+
+def test_strided_output_bit_exact(dev):
+    """Row stride ldy > n through the C-ABI: every path writes exactly the
+    n outputs of each row (the padding keeps its sentinel), bit-exact.
+    1024 x 16388 takes the 256 x 256 GEMM tiles with one K split, the
+    LDS-staged epilogue and a ragged last 8-column unit."""
+    from weight_only_int4_rtn_amd import _binding as B
+    m, n, k = 1024, 16388, 256
+    ldy = n + 4
+    w, x, b = exact_case(m, n, k, seed=5, dtype=torch.bfloat16, with_bias=True)
+    packed, q, s = prepare(w, dev)
+    xd, bd = x.to(dev), b.to(dev)
+    need = B.workspace_bytes(m, n, k)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    rows = np.array(sorted({0, 1, 255, 256, 511, 1022, 1023}))
+    cols = np.array(sorted({0, 7, 8, 255, 256, 16383, 16384, 16385, 16386, 16387}))
+    rr, cc = np.meshgrid(rows, cols, indexing="ij")
+    want = to_rne16(oracle.linear_entries(bits(x), tag(torch.bfloat16), q, s, bits(b), rr.ravel(), cc.ravel()),
+                    torch.bfloat16)
+    sentinel = -12352.0  # exact in bf16
+    for path in PATHS:
+        say(f"strided output path={path} m={m} n={n} k={k} ldy={ldy}")
+        ybuf = torch.full((m, ldy), sentinel, dtype=torch.bfloat16, device=dev)
+        st = B.lib().w4a16_linear_with_path(int(B.Path[path]), B._ptr(xd), B._act_tag(xd.dtype), m, k, k,
+                                            B._ptr(packed), n, B._ptr(bd), B._ptr(ybuf), ldy, B._ptr(ws),
+                                            ws.numel(), B._stream(dev))
+        torch.cuda.synchronize()
+        assert st == 0, (path, B.status_string(st))
+        yc = ybuf.cpu().to(torch.float64).numpy()
+        assert np.all(yc[:, n:] == sentinel), path
+        got = yc[rr.ravel(), cc.ravel()]
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"{path}: {bad.size} mismatches, first at {rr.ravel()[bad[0]]},{cc.ravel()[bad[0]]}"
+
+
 def random_case(m, n, k, seed, dtype, with_bias):
     g = torch.Generator().manual_seed(seed)
     w = torch.randn(n, k, generator=g) * 0.02

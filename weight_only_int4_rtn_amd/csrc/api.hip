@@ -27,6 +27,9 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
 // Sizes are limited so every internal offset fits comfortably in int64 and
 // grid dimensions stay within HIP's limits.
 constexpr int64_t kMaxDim = int64_t(1) << 24;
+// The GEMM path addresses a 256-row x tile through one buffer resource
+// (32-bit byte offsets): row stride at most 2^22 elements.
+constexpr int64_t kGemmMaxLd = int64_t(1) << 22;
 
 bool valid_nk(int64_t n, int64_t k) {
     return n >= 0 && n <= kMaxDim && k > 0 && k <= kMaxDim && k % kGroup == 0;
@@ -110,10 +113,9 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
 
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     (void)n;
-    (void)k;
     if (m <= 3) return W4A16_PATH_GEMV;
     if (m <= 8) return W4A16_PATH_MGEMV;
-    if (m < 128) return W4A16_PATH_SKINNY;
+    if (m < 128 || k > kGemmMaxLd) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
 }
 
@@ -142,7 +144,11 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
     if (!x || !packed || !y) return W4A16_EINVAL;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2) || (bias && !aligned(bias, 2)))
         return W4A16_EINVAL;
-    if (path == W4A16_PATH_AUTO) path = w4a16_linear_choose_path(m, n, k);
+    if (path == W4A16_PATH_AUTO) {
+        path = w4a16_linear_choose_path(m, n, k);
+        if (path == W4A16_PATH_GEMM && ldx > kGemmMaxLd) path = W4A16_PATH_SKINNY;
+    }
+    if (path == W4A16_PATH_GEMM && ldx > kGemmMaxLd) return W4A16_EUNSUPPORTED;
 
     const size_t xbytes = span_bytes(m, k, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
                  pbytes = w4a16_packed_bytes(n, k), bbytes = bias ? size_t(n) * 2 : 0;

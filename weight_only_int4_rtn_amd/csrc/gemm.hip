@@ -1,20 +1,28 @@
-// Large-M forward: the layer as a dense contraction on the matrix cores.
+// Large-M forward: the layer as a dense contraction on the matrix cores
+// (v_mfma_f32_16x16x32_{bf16,f16}, FP32 accumulation).
 //
-// A workgroup of 4 waves computes a BM x 256 tile of y; wave w owns the 64
-// columns of row tiles 4w .. 4w+3 and all BM rows (BM / 16 blocks of
-// v_mfma_f32_16x16x32_{bf16,f16} per column tile).  K advances one
-// 128-column scale group per iteration.
+// Each 16 x 16 output block is computed as D = W . x^T: the dequantized
+// weights are the A operand and the x rows the B operand.  A packed chunk
+// (16 output columns x 128 k, one 16-byte run per lane) is exactly an MFMA
+// operand: lane L holds row L % 16 of the tile and k = 8 (L / 16) + j of each
+// 32-wide k-step, one 32-bit word per k-step.  Dequantization happens once per
+// word as q * s rounded once to the 16-bit input type (byte -> float of the
+// offset code u = q + 8, then fma(u, s, -8 s), -8 s being exact).  With D
+// transposed, a lane ends with four consecutive outputs of one row, which
+// the epilogue stores together.
 //
-// Weights never pass through LDS: the packed chunk is the MFMA B-operand
-// layout (lane L: column L % 16 of the tile, columns 8*(L/16) + j of each
-// 32-wide k-step), so each wave loads its four chunks with one 128-bit load
-// per lane each and dequantizes them in registers as q * s rounded once to
-// the 16-bit input type (byte -> float of the offset code u = q + 8, then
-// fma(u, s, -8 s), -8 s being exact).  The x tile is shared by the 4 waves
-// through LDS, double-buffered: while the waves run the MFMAs of group g, the
-// loads of group g + 1 (x rows and weight chunks) are in flight, so one
-// barrier per group suffices.  LDS rows are padded by 16 bytes against bank
-// conflicts.
+// Two kernels, chosen by tile count:
+//   gemm_kernel<ACT, 8>: 128 x 256 tiles, four waves (two workgroups per
+//     CU); wave w owns 64 columns and all 128 rows, and dequantizes its own
+//     chunks in registers between its MFMAs.
+//   gemm8_kernel: 256 x 256 tiles, eight waves (two per SIMD); the
+//     workgroup dequantizes each weight once into an LDS operand tile that
+//     all waves read, so each weight is decoded once per 256 rows.
+// Both stage x in LDS by direct-to-LDS buffer loads (rows past M fall
+// outside the buffer and fetch nothing), double-buffered with one barrier
+// per stage, and spread the next stage's loads and dequantization between
+// the MFMAs of the current one.  Accumulators live in AGPRs (inline-asm
+// MFMA with an "a" constraint).
 //
 // The epilogue adds the bias in FP32 and rounds once to the output dtype, or,
 // for a K split, stores FP32 partial sums for the split-K reduce kernel.
@@ -31,12 +39,32 @@ struct GemmArgs {
     const uint16_t* bias;
     uint16_t* y;
     int64_t ldy;
-    float* partials;  // [splits][m][ntiles*128] when splits > 1
+    float* partials;  // [splits][m][ntiles*256] when splits > 1
     int splits, gps;
+    int vec_store;    // y 8-byte aligned and ldy % 4 == 0: 4 outputs per store
+    int vec16;        // y 16-byte aligned and ldy % 8 == 0: 8 outputs per store
     int64_t mtiles, ntiles;
 };
 
 constexpr int kGmBN = 256, kGmThreads = 256;  // rows per workgroup: 16 * MB
+#ifndef GM_PREFETCH
+#define GM_PREFETCH 2
+#endif
+constexpr int kGmPrefetch = GM_PREFETCH;  // A fragments read ahead of their MFMAs
+
+template <int ACT>
+__device__ inline void gm_mfma_acc(uint4 a, uint4 b, f32x4_t& c) {
+    // accumulator pinned to AGPRs; the two wait states cover a VALU write of
+    // an operand just before
+    if constexpr (ACT == kActBf16)
+        asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+            : "+a"(c)
+            : "v"(__builtin_bit_cast(bf16x8_t, a)), "v"(__builtin_bit_cast(bf16x8_t, b)));
+    else
+        asm("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+            : "+a"(c)
+            : "v"(__builtin_bit_cast(f16x8_t, a)), "v"(__builtin_bit_cast(f16x8_t, b)));
+}
 
 template <int ACT>
 __device__ inline f32x4_t gm_mfma(uint4 a, uint4 b, f32x4_t c) {
@@ -98,12 +126,34 @@ __device__ inline uint4 dequant_word(uint32_t w, float s, float neg8s) {
 // be filled by one global_load_lds_dwordx4 (lane i -> LDS bytes 16i..16i+15).
 __device__ inline int swz(int row, int seg) { return row * 128 + ((seg ^ (row & 15)) << 3); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// A value the same in every lane, kept in a scalar register (buffer
+// resources and offsets must be).
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = uint32_t(uniform(int(uint32_t(b)))), hi = uint32_t(uniform(int(uint32_t(b >> 32))));
+    void* p = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, uniform(int(uint32_t(bytes))), 0x00020000);
+}
+
+// A wave's four 1 KB weight chunks of one group and their dequantization
+// into MFMA B operands, one k-step (one word per lane per chunk) at a time.
+template <int ACT>
+struct GroupWords {
+    uint4 w[4];      // this lane's 16 bytes of each chunk: word s = k-step s
+    float s[4], o[4];  // scale and -8 * scale per chunk
+};
+
 template <int ACT, int MB>
 __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmArgs a) {
     constexpr int BM = 16 * MB;
-    constexpr int DMA = BM * kGroup * 2 / 1024 / 4;  // 1 KB direct loads per wave per group
+    constexpr int DMA = BM * kGroup * 2 / 1024 / 4;  // 1 KB x pieces per wave per group
+    constexpr int NF = 4 * MB;                       // A fragments per wave per group
     __shared__ __align__(16) uint16_t As0[BM * kGroup];
     __shared__ __align__(16) uint16_t As1[BM * kGroup];
+    __shared__ __align__(16) uint8_t Bs[16 * kChunkBytes];  // wave w: chunks 4w .. 4w+3
 
     const Layout L(a.n, a.k);
     const int split = int(blockIdx.x % unsigned(a.splits));
@@ -114,47 +164,64 @@ __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmA
     const int ng = int(min<int64_t>(a.gps, L.groups - g0));
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    const float* scales = reinterpret_cast<const float*>(a.packed + L.scale_offset());
+
+    // x rows m0 .. m0 + BM - 1 through a buffer resource whose size ends at
+    // row M: loads of rows past M are out of range and fetch nothing (those
+    // rows only feed outputs that are never stored).  Piece p of a wave
+    // covers tile rows 4 * (wave * DMA + p) .. +3; lane i lands at row
+    // + i / 16, position i % 16, which holds segment (i % 16) ^ (row & 15).
+    // Row & 15 repeats every four pieces, so four lane offsets serve all.
+    const int64_t rows_valid = min<int64_t>(BM, a.m - m0);
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(a.x + m0 * a.ldx, rows_valid * a.ldx * 2);
+    uint32_t xoff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = wave * DMA * 4 + 4 * p + (lane >> 4);
+        xoff[p] = uint32_t(row * a.ldx * 2 + (((lane & 15) ^ (row & 15)) << 4));
+    }
+    const uint32_t xstep16 = uint32_t(16 * a.ldx * 2);  // 16 rows
+    auto load_x_piece = [&](uint16_t* dst, int64_t g, int p) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_ptr_t)(dst + (wave * DMA + p) * 512), 16,
+                                                 xoff[p & 3] + uint32_t(p >> 2) * xstep16,
+                                                 uniform(int(g * kGroup * 2)), 0, 0);
+    };
 
     // This wave's four row tiles t0 + j (j = 0..3) are consecutive, so their
-    // chunks of a group are kGroups * 1 KB apart.  Tiles past N are clamped to
-    // the last one; their outputs are never stored.
+    // chunks of a group are kGroups * 1 KB apart.  Tiles past N read the last
+    // tile again (clamped); their scales are zeroed and outputs never stored.
+    // A chunk is exactly the lane-ordered 1 KB a wave's 16-byte direct load
+    // writes, so lane L later reads back its own 16 bytes; scales go to
+    // registers.
     const int64_t t0 = nt * 16 + wave * 4;
-    const int64_t tile_step = L.groups * kChunkBytes;
-    const uint8_t* cbase = a.packed + (min<int64_t>(t0, L.tiles - 1) * L.groups) * kChunkBytes + lane * 16;
-    const float* sbase = scales + min<int64_t>(t0, L.tiles - 1) * L.groups * kTileRows + r;
-    const int valid = int(min<int64_t>(4, max<int64_t>(0, L.tiles - t0)));  // tiles of this wave inside N
-
-    // Direct x loads: piece p covers tile rows 4 * (wave * DMA + p) .. +3;
-    // lane i lands at row + i / 16, position i % 16, which holds segment
-    // (i % 16) ^ (row & 15).  Rows past M are clamped (they feed outputs that
-    // are never stored).
-    const int drow0 = wave * DMA * 4 + (lane >> 4);
-    auto load_x = [&](uint16_t* dst, int64_t g) {
-        // recompute the source addresses every group rather than keeping
-        // DMA 64-bit pointers live across the loop (they would spill)
-        int rbase = drow0;
-        asm volatile("" : "+v"(rbase));
+    const int valid = int(min<int64_t>(4, max<int64_t>(0, L.tiles - t0)));
+    const int64_t tfirst = min<int64_t>(t0, L.tiles - 1);
+    const __amdgpu_buffer_rsrc_t wres =
+        buffer_rsrc(a.packed + tfirst * L.groups * kChunkBytes, 4 * L.groups * kChunkBytes);
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
+        a.packed + L.scale_offset() + tfirst * L.groups * kChunkScaleBytes, 4 * L.groups * kChunkScaleBytes);
+    uint32_t woff[4], soff[4];
 #pragma unroll
-        for (int p = 0; p < DMA; ++p) {
-            const int row = rbase + 4 * p;
-            const int seg = (lane & 15) ^ (row & 15);
-            const int64_t gr = m0 + row < a.m ? m0 + row : a.m - 1;
-            __builtin_amdgcn_global_load_lds(a.x + gr * a.ldx + g * kGroup + seg * 8,
-                                             (__attribute__((address_space(3))) void*)(dst + (wave * DMA + p) * 512),
-                                             16, 0, 0);
-        }
-    };
-    uint4 cw[4];
+    for (int j = 0; j < 4; ++j) {
+        const int jj = j < valid ? j : (valid > 0 ? valid - 1 : 0);
+        woff[j] = uint32_t(jj * L.groups * kChunkBytes + lane * 16);
+        soff[j] = uint32_t(jj * L.groups * kChunkScaleBytes + r * 4);
+    }
     float sc[4];
-    auto load_w = [&](int64_t g) {
+    auto load_w_chunk = [&](int64_t g, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr_t)(Bs + (wave * 4 + j) * kChunkBytes), 16,
+                                                 woff[j], uniform(int(g * kChunkBytes)), 0, 0);
+        sc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              sres, soff[j], uniform(int(g * kChunkScaleBytes)), 0));
+    };
+    // this wave's chunk words and scales of a group, once its loads landed
+    auto take_words = [&](GroupWords<ACT>& gw) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int jj = j < valid ? j : (valid > 0 ? valid - 1 : 0);
-            cw[j] = *reinterpret_cast<const uint4*>(cbase + jj * tile_step + g * kChunkBytes);
-            sc[j] = sbase[jj * L.groups * kTileRows + g * kTileRows];
+            gw.w[j] = *reinterpret_cast<const uint4*>(Bs + (wave * 4 + j) * kChunkBytes + lane * 16);
+            gw.s[j] = j < valid ? sc[j] : 0.0f;
+            gw.o[j] = -8.0f * gw.s[j];
         }
     };
 
@@ -164,78 +231,467 @@ __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmA
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // One group: wait for its x pieces and weights, barrier (A complete, and
-    // nobody reads Anext any more), start the next group's loads into Anext
-    // and registers, then run the MFMAs on A.  The two buffers keep fixed
-    // roles in each half of the unrolled pair below, so the compiler can
-    // tell the direct loads into Anext from the reads of A.
+    // One group, software-pipelined.  On entry the group's x tile sits in A
+    // (after the barrier below), its chunk words in cur and k-step 0's B
+    // operands in bc.  The four k-steps run as MB blocks each: four MFMAs on
+    // one A fragment (read two blocks ahead) plus one slice of other work,
+    // fenced so that the slices stay spread between the MFMAs:
+    //   k-step 0: one of the next group's x pieces into Anext;
+    //   k-step 1: one of its weight chunks and scales (blocks 0..3);
+    //   k-steps 0..2: a quarter word of the next k-step's B operands;
+    //   k-step 3: once the next group's chunks landed, a quarter word of its
+    //             k-step 0 B operands.
+    // The two x buffers keep fixed roles in each half of the unrolled pair
+    // below so the compiler can tell the direct loads into Anext from the
+    // reads of A.
+    GroupWords<ACT> cur, nxt;
+    uint4 bc[4], bn[4];
     auto group = [&](const uint16_t* A, uint16_t* Anext, int gl) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        uint4 cur[4];
-        float s4[4];
+        __builtin_amdgcn_s_barrier();  // every wave's x pieces of this group landed
+        const bool more = gl + 1 < ng;
+        const int64_t gn = g0 + gl + 1;
+        uint4 af[kGmPrefetch + 1];
+        auto read_a = [&](int f) {
+            const int sk = f / MB, i = f % MB;
+            return *reinterpret_cast<const uint4*>(A + swz(i * 16 + r, 4 * sk + kq));
+        };
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            cur[j] = cw[j];
-            s4[j] = j < valid ? sc[j] : 0.0f;
-        }
-        if (gl + 1 < ng) {
-            load_x(Anext, g0 + gl + 1);
-            load_w(g0 + gl + 1);
-        }
+        for (int f = 0; f < kGmPrefetch; ++f) af[f] = read_a(f);
 #pragma unroll
         for (int sk = 0; sk < 4; ++sk) {
-            uint4 bop[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t w = sk == 0 ? cur[j].x : sk == 1 ? cur[j].y : sk == 2 ? cur[j].z : cur[j].w;
-                bop[j] = dequant_word<ACT>(w, s4[j], -8.0f * s4[j]);
+            if (sk == 3 && more) {
+                // the next group's chunks, scales and x pieces were issued
+                // two k-steps ago
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                take_words(nxt);
             }
+            // dequantization temporaries carried between the quarter slices
+            uint32_t lo = 0, hi = 0;
+            float c0 = 0.f, c4 = 0.f, c2 = 0.f, c6 = 0.f;
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
-                const uint4 aop = *reinterpret_cast<const uint4*>(A + swz(i * 16 + r, 4 * sk + kq));
+                const int f = sk * MB + i;
+                const uint4 aop = af[f % (kGmPrefetch + 1)];
+                if (f + kGmPrefetch < NF) af[(f + kGmPrefetch) % (kGmPrefetch + 1)] = read_a(f + kGmPrefetch);
+                if (sk == 0 && i < DMA && more) load_x_piece(Anext, gn, i);
+                if (sk == 1 && i < 4 && more) load_w_chunk(gn, i);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = gm_mfma<ACT>(aop, bop[j], acc[i][j]);
+                for (int j = 0; j < 4; ++j) gm_mfma_acc<ACT>(bc[j], aop, acc[i][j]);
+                // word j of the next k-step (k-step 3: the next group's
+                // k-step 0) in MB / 4 slices, quarters q0 .. q0 + 4 / PER - 1
+                constexpr int PER = MB / 4;
+                const int j = i / PER, q0 = (i % PER) * (4 / PER);
+                if (sk < 3 || more) {
+                    const GroupWords<ACT>& src = sk < 3 ? cur : nxt;
+                    const uint32_t w = sk == 0 ? src.w[j].y : sk == 1 ? src.w[j].z : sk == 2 ? src.w[j].w : src.w[j].x;
+                    const float sj = src.s[j], oj = src.o[j];
+#pragma unroll
+                    for (int q = q0; q < q0 + 4 / PER; ++q) {
+                        if (q == 0) {
+                            lo = w & 0x0F0F0F0Fu;  // bytes: columns 0, 4, 1, 5
+                            c0 = fmaf(byte_f32<0>(lo), sj, oj);
+                            c4 = fmaf(byte_f32<1>(lo), sj, oj);
+                        } else if (q == 1) {
+                            const float c1 = fmaf(byte_f32<2>(lo), sj, oj);
+                            const float c5 = fmaf(byte_f32<3>(lo), sj, oj);
+                            bn[j].x = pack2<ACT>(c0, c1);
+                            bn[j].z = pack2<ACT>(c4, c5);
+                        } else if (q == 2) {
+                            hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: columns 2, 6, 3, 7
+                            c2 = fmaf(byte_f32<0>(hi), sj, oj);
+                            c6 = fmaf(byte_f32<1>(hi), sj, oj);
+                        } else {
+                            const float c3 = fmaf(byte_f32<2>(hi), sj, oj);
+                            const float c7 = fmaf(byte_f32<3>(hi), sj, oj);
+                            bn[j].y = pack2<ACT>(c2, c3);
+                            bn[j].w = pack2<ACT>(c6, c7);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // keep each k-step's operands from piling up in registers
-            if constexpr (MB > 8) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bc[j] = bn[j];
         }
+        cur = nxt;
     };
 
-    load_x(As0, g0);
-    load_w(g0);
-    for (int gl = 0; gl < ng; gl += 2) {
-        group(As0, As1, gl);
-        if (gl + 1 < ng) group(As1, As0, gl + 1);
-    }
+    // prologue: group g0's loads, its words and k-step 0 operands
+#pragma unroll
+    for (int p = 0; p < DMA; ++p) load_x_piece(As0, g0, p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_w_chunk(g0, j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    take_words(cur);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bc[j] = dequant_word<ACT>(cur.w[j].x, cur.s[j], cur.o[j]);
+    // Bs is refilled (next group's chunks) only after every word was read
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-    // --- epilogue: lane holds rows 4kq + e of column r of each 16 x 16 block
+    int gl = 0;
+    for (; gl + 1 < ng; gl += 2) {
+        group(As0, As1, gl);
+        group(As1, As0, gl + 1);
+    }
+    if (gl < ng) group(As0, As1, gl);
+    // results of the last MFMAs are read by ordinary instructions below:
+    // wait out the pipeline first, then mark every accumulator as produced
+    // after the wait
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+
+    // --- epilogue.  Each 16 x 16 block is D = W . x^T: lane (r, kq) holds
+    // outputs 4kq .. 4kq + 3 of tile t0 + j for x row r of row block i, four
+    // consecutive columns (one 8-byte store, 16 bytes for FP32 partials).
     const int64_t npad = a.ntiles * kGmBN;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int64_t col = (t0 + j) * 16 + r;
-        if (col >= a.n) continue;
-        const float bv = (a.splits == 1 && a.bias) ? to_f32<ACT>(a.bias[col]) : 0.0f;
+        const int64_t c0 = (t0 + j) * 16 + 4 * kq;
+        if (c0 >= a.n) continue;
+        const bool full = c0 + 4 <= a.n;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (a.splits == 1 && a.bias) {
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+            for (int e = 0; e < 4; ++e)
+                if (c0 + e < a.n) bv[e] = to_f32<ACT>(a.bias[c0 + e]);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + i * 16 + 4 * kq + e;
-                if (row >= a.m) continue;
-                if (a.splits == 1)
-                    a.y[row * a.ldy + col] = from_f32<ACT>(acc[i][j][e] + bv);
-                else
-                    a.partials[(int64_t(split) * a.m + row) * npad + col] = acc[i][j][e];
+        for (int i = 0; i < MB; ++i) {
+            const int64_t row = m0 + i * 16 + r;
+            if (row >= a.m) continue;
+            const f32x4_t v = acc[i][j];
+            if (a.splits > 1) {
+                *reinterpret_cast<f32x4_t*>(a.partials + (int64_t(split) * a.m + row) * npad + c0) = v;
+            } else if (full && a.vec_store) {
+                *reinterpret_cast<uint2*>(a.y + row * a.ldy + c0) =
+                    make_uint2(pack2<ACT>(v[0] + bv[0], v[1] + bv[1]), pack2<ACT>(v[2] + bv[2], v[3] + bv[3]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + e < a.n) a.y[row * a.ldy + c0 + e] = from_f32<ACT>(v[e] + bv[e]);
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Eight-wave variant: a 256 x 256 output tile per workgroup, two waves per
+// SIMD, each wave 128 rows x 64 columns (128 accumulators).  The K loop runs
+// in stages of 64 (half a quantization group).  Per stage the workgroup
+// stages in LDS the x tile (256 rows x 64, by direct loads) and the B tile:
+// the stage's weights dequantized to 16-bit MFMA operands, 16 tiles x 2
+// k-steps x 64 lanes x 16 bytes.  Each wave dequantizes two of the 16 weight
+// tiles (one word per lane per k-step, written where the reading lane finds
+// it), so each weight is dequantized once per 256 rows of x while every wave
+// keeps only 128 accumulators.
+// ---------------------------------------------------------------------------
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+constexpr int kG8Threads = 512, kG8Rows = 256, kG8K = 64;
+constexpr int kG8XStage = kG8Rows * kG8K;          // 16-bit elements per x stage
+constexpr int kG8WStage = 16 * 2 * 64 * 16;        // bytes per B stage
+
+// x stage layout: row r holds its 64 columns as 8 segments of 16 bytes,
+// segment c at position c ^ ((r >> 1) & 7): the 16 lanes of an operand read
+// (16 consecutive rows, one segment) cover all 64 banks once.
+__device__ inline int swz8(int row, int seg) { return row * kG8K + ((seg ^ ((row >> 1) & 7)) << 3); }
+
+template <int ACT, bool STAGED>
+__global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
+    __shared__ __align__(16) uint16_t X0[kG8XStage];
+    __shared__ __align__(16) uint16_t X1[kG8XStage];
+    __shared__ __align__(16) uint8_t W0[kG8WStage];
+    __shared__ __align__(16) uint8_t W1[kG8WStage];
+
+    const Layout L(a.n, a.k);
+    const int split = int(blockIdx.x % unsigned(a.splits));
+    const int64_t tile = int64_t(blockIdx.x / unsigned(a.splits));
+    const int64_t mt = tile % a.mtiles, nt = tile / a.mtiles;  // consecutive workgroups share weights
+    const int64_t m0 = mt * kG8Rows;
+    const int64_t g0 = int64_t(split) * a.gps;
+    const int ng = int(min<int64_t>(a.gps, L.groups - g0));
+    const int nstages = 2 * ng;
+
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int wm = wave >> 2, wn = wave & 3;  // 128-row half, 64-column quarter
+
+    // x: rows m0 .. m0 + 255 through a buffer resource ending at row M (loads
+    // of rows past M fetch nothing; those rows only feed outputs never
+    // stored).  Piece p of wave w fills stage rows 8 (4w + p) .. +7; lane i
+    // lands at row + i / 8, position i % 8.
+    const int64_t rows_valid = min<int64_t>(kG8Rows, a.m - m0);
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(a.x + m0 * a.ldx, rows_valid * a.ldx * 2);
+    uint32_t xoff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = 8 * (4 * wave + p) + (lane >> 3);
+        xoff[p] = uint32_t(row * a.ldx * 2 + (((lane & 7) ^ ((row >> 1) & 7)) << 4));
+    }
+    auto load_x = [&](uint16_t* dst, int s) {
+        const int soff = uniform(int((g0 + (s >> 1)) * kGroup * 2 + (s & 1) * kG8K * 2));
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_ptr_t)(dst + (4 * wave + p) * 512), 16, xoff[p],
+                                                     soff, 0, 0);
+    };
+
+    // Weights: this wave dequantizes the workgroup's tiles 2w and 2w + 1.
+    // Tiles past N read the last tile again (clamped) with their scales
+    // zeroed.
+    const int64_t tw = nt * 16 + 2 * wave;
+    const int validw = int(min<int64_t>(2, max<int64_t>(0, L.tiles - tw)));
+    const int64_t twfirst = min<int64_t>(tw, L.tiles - 1);
+    const __amdgpu_buffer_rsrc_t wres =
+        buffer_rsrc(a.packed + twfirst * L.groups * kChunkBytes, 2 * L.groups * kChunkBytes);
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
+        a.packed + L.scale_offset() + twfirst * L.groups * kChunkScaleBytes, 2 * L.groups * kChunkScaleBytes);
+    uint32_t woff[2], soff[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int cc = c < validw ? c : (validw > 0 ? validw - 1 : 0);
+        woff[c] = uint32_t(cc * L.groups * kChunkBytes + lane * 16);
+        soff[c] = uint32_t(cc * L.groups * kChunkScaleBytes + r * 4);
+    }
+    struct Words {
+        uint32_t w[2][4];
+        float s[2];
+    };
+    // one group's words and scales (groups past the split's end reload its
+    // last group, keeping the count of loads in flight fixed)
+    auto load_words = [&](Words& d, int gl) {
+        const int64_t g = g0 + min(gl, ng - 1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[c], uniform(int(g * kChunkBytes)), 0);
+            d.w[c][0] = v[0];
+            d.w[c][1] = v[1];
+            d.w[c][2] = v[2];
+            d.w[c][3] = v[3];
+            d.s[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   sres, soff[c], uniform(int(g * kChunkScaleBytes)), 0));
+        }
+    };
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    Words wcur, wnext, wfut;
+    // B-stage slot of (tile, k-step) for this lane
+    auto wslot = [&](int tt, int ks) { return ((tt * 2 + ks) * 64 + lane) * 16; };
+
+    // One stage: wait for its x pieces and B tile, barrier, start the next
+    // stage's x loads (and at a group's first stage the weight words two
+    // groups ahead), then 16 blocks of four MFMAs, each with a quarter word
+    // of the next stage's dequantization; a finished word goes to the next
+    // B tile.  Fixed buffer roles per call let the compiler tell the direct
+    // loads and B writes into the next stage from the reads of this one.
+    // The last stage also loads and dequantizes (its own x and B again, into
+    // buffers nobody reads any more), which keeps the loop free of branches.
+    auto stage = [&](const uint16_t* Xp, const uint8_t* Wp, uint16_t* Xq, uint8_t* Wq, int s, auto odd_c) {
+        constexpr bool odd = decltype(odd_c)::value;
+        // an even stage issued its successor's x pieces and then four word
+        // loads; an odd stage only x pieces
+        if constexpr (odd)
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        load_x(Xq, min(s + 1, nstages - 1));
+        if constexpr (!odd) load_words(wfut, (s >> 1) + 2);
+        // words of stage s + 1: the second half of this group, or the first
+        // half of the next
+        const Words& src = odd ? wnext : wcur;
+        constexpr int h1 = odd ? 0 : 1;
+
+        uint4 xf[3];
+        auto read_x = [&](int f) {
+            const int ks = f >> 3, i = f & 7;
+            return *reinterpret_cast<const uint4*>(Xp + swz8(wm * 128 + i * 16 + r, 4 * ks + kq));
+        };
+        xf[0] = read_x(0);
+        xf[1] = read_x(1);
+        uint4 wf[4];
+        uint32_t lo = 0, hi = 0;
+        float c0 = 0.f, c4 = 0.f, c2 = 0.f, c6 = 0.f;
+        uint4 out = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int f = 0; f < 16; ++f) {
+            const int ks = f >> 3, i = f & 7;
+            if (i == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    wf[j] = *reinterpret_cast<const uint4*>(Wp + wslot(wn * 4 + j, ks));
+            }
+            const uint4 xop = xf[f % 3];
+            if (f + 2 < 16) xf[(f + 2) % 3] = read_x(f + 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gm_mfma_acc<ACT>(wf[j], xop, acc[i][j]);
+            {
+                // word (c, ks') of stage s + 1: c = f / 8, ks' = (f / 4) % 2,
+                // quarter f % 4
+                const int c = f >> 3, kn = (f >> 2) & 1, q = f & 3;
+                const uint32_t w = src.w[c][2 * h1 + kn];
+                const float sj = c < validw ? src.s[c] : 0.0f;
+                const float oj = -8.0f * sj;
+                if (q == 0) {
+                    lo = w & 0x0F0F0F0Fu;  // bytes: columns 0, 4, 1, 5
+                    c0 = fmaf(byte_f32<0>(lo), sj, oj);
+                    c4 = fmaf(byte_f32<1>(lo), sj, oj);
+                } else if (q == 1) {
+                    const float c1 = fmaf(byte_f32<2>(lo), sj, oj);
+                    const float c5 = fmaf(byte_f32<3>(lo), sj, oj);
+                    out.x = pack2<ACT>(c0, c1);
+                    out.z = pack2<ACT>(c4, c5);
+                } else if (q == 2) {
+                    hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: columns 2, 6, 3, 7
+                    c2 = fmaf(byte_f32<0>(hi), sj, oj);
+                    c6 = fmaf(byte_f32<1>(hi), sj, oj);
+                } else {
+                    const float c3 = fmaf(byte_f32<2>(hi), sj, oj);
+                    const float c7 = fmaf(byte_f32<3>(hi), sj, oj);
+                    out.y = pack2<ACT>(c2, c3);
+                    out.w = pack2<ACT>(c6, c7);
+                    *reinterpret_cast<uint4*>(Wq + wslot(2 * wave + c, kn)) = out;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (odd) {
+            wcur = wnext;
+            wnext = wfut;
+        }
+    };
+
+    // prologue: stage 0's x, the first two groups' words, stage 0's B tile
+    load_x(X0, 0);
+    load_words(wcur, 0);
+    load_words(wnext, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const float sj = c < validw ? wcur.s[c] : 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            *reinterpret_cast<uint4*>(W0 + wslot(2 * wave + c, ks)) = dequant_word<ACT>(wcur.w[c][ks], sj, -8.0f * sj);
+    }
+
+    for (int s = 0; s < nstages; s += 2) {
+        stage(X0, W0, X1, W1, s, BoolC<false>{});
+        stage(X1, W1, X0, W0, s + 1, BoolC<true>{});
+    }
+    // results of the last MFMAs are read by ordinary instructions below:
+    // wait out the pipeline first, then mark every accumulator as produced
+    // after the wait
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+
+    // --- epilogue: lane (r, kq) holds outputs 4kq .. 4kq + 3 of tile t0 + j
+    // for x row r of row block i
+    const int64_t npad = a.ntiles * kGmBN;
+    const int64_t t0 = nt * 16 + wn * 4;
+    if constexpr (STAGED) {
+        // Through LDS (one K split, 16-byte aligned rows): the 256 x 256 tile of 16-bit outputs (512 bytes a row)
+        // fills the four stage buffers, 64 rows each, and leaves as whole
+        // rows in 16-byte stores.  Within a row, 16-byte unit u sits at
+        // position u ^ (row & 31), so the sixteen rows one write touches and
+        // the 32 units one row read touches spread over all banks.
+        __builtin_amdgcn_s_barrier();  // every wave is done with the last stage
+        auto tile_row = [&](int row) -> uint8_t* {
+            uint8_t* q = (row >> 6) == 0   ? reinterpret_cast<uint8_t*>(X0)
+                         : (row >> 6) == 1 ? reinterpret_cast<uint8_t*>(X1)
+                         : (row >> 6) == 2 ? W0
+                                           : W1;
+            return q + (row & 63) * 512;
+        };
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t c0 = (t0 + j) * 16 + 4 * kq;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (a.bias) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + e < a.n) bv[e] = to_f32<ACT>(a.bias[c0 + e]);
+            }
+            const int u = (wn * 4 + j) * 2 + (kq >> 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = wm * 128 + i * 16 + r;
+                const f32x4_t v = acc[i][j];
+                *reinterpret_cast<uint2*>(tile_row(row) + ((u ^ (row & 31)) << 4) + (kq & 1) * 8) =
+                    make_uint2(pack2<ACT>(v[0] + bv[0], v[1] + bv[1]), pack2<ACT>(v[2] + bv[2], v[3] + bv[3]));
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        const int u = tid & 31;
+        const int64_t col = nt * kGmBN + u * 8;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int row = it * 16 + (tid >> 5);
+            const int64_t grow = m0 + row;
+            const uint4 v = *reinterpret_cast<const uint4*>(tile_row(row) + ((u ^ (row & 31)) << 4));
+            if (grow >= a.m || col >= a.n) continue;
+            uint16_t* dst = a.y + grow * a.ldy + col;
+            if (col + 8 <= a.n) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                for (int e = 0; e < 8 && col + e < a.n; ++e) dst[e] = uint16_t(w4[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t c0 = (t0 + j) * 16 + 4 * kq;
+        if (c0 >= a.n) continue;
+        const bool full = c0 + 4 <= a.n;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (a.splits == 1 && a.bias) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c0 + e < a.n) bv[e] = to_f32<ACT>(a.bias[c0 + e]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t row = m0 + wm * 128 + i * 16 + r;
+            if (row >= a.m) continue;
+            const f32x4_t v = acc[i][j];
+            if (a.splits > 1) {
+                *reinterpret_cast<f32x4_t*>(a.partials + (int64_t(split) * a.m + row) * npad + c0) = v;
+            } else if (full && a.vec_store) {
+                *reinterpret_cast<uint2*>(a.y + row * a.ldy + c0) =
+                    make_uint2(pack2<ACT>(v[0] + bv[0], v[1] + bv[1]), pack2<ACT>(v[2] + bv[2], v[3] + bv[3]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + e < a.n) a.y[row * a.ldy + c0 + e] = from_f32<ACT>(v[e] + bv[e]);
+            }
+        }
+    }
     }
 }
 
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
     GemmPlan p{};
     const Layout L(n, k);
-    // 256 rows per workgroup halve the dequantization work per MFMA; 128
-    // rows keep two workgroups per CU where M is small.
-    p.mb = 8;
+    // 256 x 256 tiles (eight waves, each weight dequantized once per 256
+    // rows) where they alone give every CU work; else 128 x 256 tiles of
+    // four waves, two workgroups per CU.
+    p.waves = ceil_div(m, kG8Rows) * ceil_div(n, kGmBN) >= 128 ? 8 : 4;
+    p.mb = p.waves == 8 ? 16 : 8;
     p.mtiles = ceil_div(m, 16 * p.mb);
     p.ntiles = ceil_div(n, kGmBN);
     const int64_t tiles = p.mtiles * p.ntiles;
@@ -253,6 +709,8 @@ hipError_t launch_gemm(const void* x, int act, int64_t m, int64_t k, int64_t ldx
                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream) {
     const GemmPlan p = plan_gemm(m, n, k);
+    // the x tile's buffer resource takes 32-bit byte offsets
+    if (int64_t(16 * p.mb) * ldx * 2 > int64_t(0xFFFFFFFF)) return hipErrorInvalidValue;
     GemmArgs a;
     a.x = static_cast<const uint16_t*>(x);
     a.ldx = ldx;
@@ -264,18 +722,23 @@ hipError_t launch_gemm(const void* x, int act, int64_t m, int64_t k, int64_t ldx
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
     a.partials = static_cast<float*>(workspace);
+    a.vec_store = reinterpret_cast<uintptr_t>(y) % 8 == 0 && ldy % 4 == 0;
+    a.vec16 = reinterpret_cast<uintptr_t>(y) % 16 == 0 && ldy % 8 == 0;
     a.splits = p.splits;
     a.gps = p.gps;
     a.mtiles = p.mtiles;
     a.ntiles = p.ntiles;
     const dim3 grid(unsigned(p.mtiles * p.ntiles * p.splits)), block(kGmThreads);
     const bool bf = act == kActBf16;
-    if (p.mb == 16) {
-        if (bf) gemm_kernel<kActBf16, 16><<<grid, block, 0, stream>>>(a);
-        else gemm_kernel<kActF16, 16><<<grid, block, 0, stream>>>(a);
-    } else if (p.mb == 12) {
-        if (bf) gemm_kernel<kActBf16, 12><<<grid, block, 0, stream>>>(a);
-        else gemm_kernel<kActF16, 12><<<grid, block, 0, stream>>>(a);
+    if (p.waves == 8) {
+        const dim3 b8(kG8Threads);
+        if (p.splits == 1 && a.vec16) {
+            if (bf) gemm8_kernel<kActBf16, true><<<grid, b8, 0, stream>>>(a);
+            else gemm8_kernel<kActF16, true><<<grid, b8, 0, stream>>>(a);
+        } else {
+            if (bf) gemm8_kernel<kActBf16, false><<<grid, b8, 0, stream>>>(a);
+            else gemm8_kernel<kActF16, false><<<grid, b8, 0, stream>>>(a);
+        }
     } else {
         if (bf) gemm_kernel<kActBf16, 8><<<grid, block, 0, stream>>>(a);
         else gemm_kernel<kActF16, 8><<<grid, block, 0, stream>>>(a);
