@@ -161,7 +161,7 @@ def run_workload(cases, dev, steps, warmup, dominant):
     biases = [synth.make_bias(c).to(dev) if c.bias else None for c in cases]
     ys = [torch.empty((c.m, c.n), dtype=c.torch_dtype, device=dev) for c in cases]
     ws_bytes = max(w4.workspace_bytes(c.m, c.n, c.k) for c in cases)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     log(f"pool: {len(layers)} layers of {sum(p.numel() for p in layers[0]) / 1e6:.1f} MB; "
         f"paths {[w4.choose_path(c.m, c.n, c.k).name for c in cases]}")
     graphs = [capture(make_step(cases, layer, xs, biases, ys, workspace)) for layer in layers]
@@ -174,6 +174,64 @@ def run_workload(cases, dev, steps, warmup, dominant):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
+
+
+# HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+# `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE), scaled by what the
+# same counters read for an elementwise kernel of known size.  The summary
+# records a hash of the kernel's sources; a changed kernel reports null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_m1_traffic.md")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "weight_only_int4_rtn_amd", "csrc", f) for f in ("gemv.hip", "common.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the gate_up GEMV from the committed counter
+    summary, or None when it is missing or was taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            fields = dict(ln.split(":", 1) for ln in fh.read().splitlines() if ln.startswith("- ") and ":" in ln)
+    except OSError:
+        return None
+    fields = {k[2:].strip(): v.strip().strip("`") for k, v in fields.items()}
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_probe(dev):
+    """Launches for the counter runs: the gate_up GEMV on 16 pool copies, then
+    an elementwise kernel over 256 MiB (reads and writes exactly that much),
+    the scale for the counters."""
+    import torch
+
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    c = synth.case_by_name("c3_gate_up_m1_k2048_n32768")
+    layers, _ = build_pool([c], dev)
+    x = synth.make_x(c).to(dev)
+    y = torch.empty((c.m, c.n), dtype=c.torch_dtype, device=dev)
+    for i in range(16):
+        w4.linear(x, layers[i % len(layers)][0], c.n, out=y)
+    torch.cuda.synchronize()
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"traffic probe: 16 GEMV launches ({c.alg_bytes()} algorithmic bytes each), "
+        f"4 elementwise launches of {src.numel() * 4} bytes read + written; sources {kernel_source_hash()}")
 
 
 def cpu_baseline(cases, target_seconds=12.0):
@@ -209,6 +267,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only the launches the HBM counter runs measure (see TRAFFIC_FILE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer is benchmarked on one MI355X "
@@ -220,6 +280,9 @@ def main():
     import weight_only_int4_rtn_amd as w4
     dev = torch.device("cuda:0")
     w4.lib()
+    if args.traffic_probe:
+        traffic_probe(dev)
+        return
 
     # --- decode step (M = 1) --------------------------------------------------
     cases = decode_cases()
@@ -266,7 +329,7 @@ def main():
                    "kernel_path": w4.choose_path(1, 2048, 2048).name,
                    "eager_ms_per_step": round(dec["eager_ms"], 4)},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": f"{w4.choose_path(1, dom.n, dom.k).name} {dom.name}",
                      "avg_launch_us": round(dom_ms * 1e3, 3), "bytes_per_launch": dom.alg_bytes()},
         "m1024": {"workload": "prefill M=1024 fp16 with bias: K2048xN2560, K2048xN32768, K16384xN2048",

@@ -120,9 +120,12 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
 /*
  * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
  * kernel path (0 if none).  The workspace holds the FP32 partial sums of a K
- * split, which a second small kernel adds in split order (no inter-workgroup
- * synchronisation, no floating-point atomics).  It needs no initialisation.
- * Two calls that may run at the same time must not share a workspace.
+ * split, added in split order (no floating-point atomics), after a 4096-byte
+ * header of completion counters with which the small-M kernel finishes its
+ * split inside one launch.  The caller zero-fills a workspace once, before
+ * its first use; every call leaves the header zero again, so a workspace is
+ * reused without clearing (also by calls of other shapes and paths).  Two
+ * calls that may run at the same time must not share a workspace.
  */
 size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
@@ -140,7 +143,8 @@ size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *   y         device, [m][ldy] of act_dtype, ldy >= n, 2-byte aligned; must not
  *             overlap x, packed, bias or workspace.
  *   workspace device, >= w4a16_linear_workspace_bytes(m, n, k) bytes, 16-byte
- *             aligned, contents ignored (may be NULL when that size is 0).
+ *             aligned, zero-filled before its first use and then only
+ *             passed to these calls (may be NULL when that size is 0).
  * m == 0 or n == 0 returns W4A16_OK and launches nothing.  Returns W4A16_OK,
  * W4A16_EINVAL, W4A16_EUNSUPPORTED (act_dtype), W4A16_EWORKSPACE or W4A16_EHIP.
  * The result is bit-identical from run to run (no floating-point atomics).

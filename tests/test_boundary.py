@@ -129,14 +129,15 @@ def test_linear_rejects(lib):
     assert lin(lib, path=9) == B.EINVAL                           # unknown path
     assert lin(lib, m=0) == B.OK                                  # empty: no-op
     assert lin(lib, n=0, ldy=0) == B.OK
-    # long K at M=1 needs a workspace
-    need = w4.workspace_bytes(1, 2048, 16384)
-    assert lin(lib, m=1, k=16384, ldx=16384, n=2048, ldy=2048, y=A * 64) == B.EWORKSPACE
+    # a K beyond one workgroup's reach (256 groups at M=1) splits and needs a workspace
+    gemv = int(w4.Path.GEMV)
+    need = w4.workspace_bytes(1, 2048, 32768)
+    assert lin(lib, m=1, k=32768, ldx=32768, n=2048, ldy=2048, y=A * 64, path=gemv) == B.EWORKSPACE
     assert need > 256
-    assert lin(lib, m=1, k=16384, ldx=16384, n=2048, ldy=2048, y=A * 64, ws=A * 128,
-               ws_bytes=256) == B.EWORKSPACE
-    assert lin(lib, m=1, k=16384, ldx=16384, n=2048, ldy=2048, y=A * 64, ws=A * 128 + 8,
-               ws_bytes=need) == B.EINVAL                     # misaligned workspace
+    assert lin(lib, m=1, k=32768, ldx=32768, n=2048, ldy=2048, y=A * 64, ws=A * 128,
+               ws_bytes=256, path=gemv) == B.EWORKSPACE
+    assert lin(lib, m=1, k=32768, ldx=32768, n=2048, ldy=2048, y=A * 64, ws=A * 128 + 8,
+               ws_bytes=need, path=gemv) == B.EINVAL          # misaligned workspace
     # the GEMM path takes row strides up to 2^22 elements (32-bit tile offsets)
     big = (1 << 22) + 8
     assert lin(lib, m=256, k=128, ldx=big, n=16, y=A * 4096, path=int(w4.Path.GEMM)) == B.EUNSUPPORTED

@@ -120,7 +120,7 @@ def test_strided_output_bit_exact(dev):
     packed, q, s = prepare(w, dev)
     xd, bd = x.to(dev), b.to(dev)
     need = B.workspace_bytes(m, n, k)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     rows = np.array(sorted({0, 1, 255, 256, 511, 1022, 1023}))
     cols = np.array(sorted({0, 7, 8, 255, 256, 16383, 16384, 16385, 16386, 16387}))
     rr, cc = np.meshgrid(rows, cols, indexing="ij")
@@ -140,6 +140,38 @@ def test_strided_output_bit_exact(dev):
         got = yc[rr.ravel(), cc.ravel()]
         bad = np.flatnonzero(got != want)
         assert bad.size == 0, f"{path}: {bad.size} mismatches, first at {rr.ravel()[bad[0]]},{cc.ravel()[bad[0]]}"
+
+
+# Calls of different shapes and paths sharing one zero-filled workspace, in an
+# order where a later call's counter header lies where an earlier call could
+# have written partial sums: every result bit-exact, and the 4096-byte counter
+# header zero again after every call.
+SHARED_WS_CALLS = [("GEMV", 1, 2048, 16384), ("SKINNY", 50, 1000, 4096), ("GEMV", 3, 16, 1280),
+                   ("MGEMV", 6, 520, 2048), ("GEMM", 300, 4104, 640), ("GEMV", 2, 2056, 16384),
+                   ("GEMV", 1, 2048, 16384)]
+
+
+def test_shared_workspace_counters_stay_clear(dev):
+    from weight_only_int4_rtn_amd import _binding as B
+    lib = w4()
+    need = max(B.workspace_bytes(m, n, k) for _, m, n, k in SHARED_WS_CALLS)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    splits_seen = 0
+    for i, (path, m, n, k) in enumerate(SHARED_WS_CALLS):
+        say(f"shared workspace call {i}: path={path} m={m} n={n} k={k}")
+        w, x, b = exact_case(m, n, k, seed=40 + i, dtype=torch.bfloat16, with_bias=(i % 2 == 0))
+        packed, q, s = prepare(w, dev)
+        splits_seen += B.workspace_bytes(m, n, k) > 0
+        y = lib.linear(x.to(dev), packed, n, b.to(dev) if b is not None else None, path=lib.Path[path],
+                       workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4096].count_nonzero()) == 0, f"call {i}: counter header not left zero"
+        want = to_rne16(oracle.linear(bits(x), tag(torch.bfloat16), q, s, bits(b) if b is not None else None),
+                        torch.bfloat16)
+        got = y.cpu().to(torch.float64).numpy()
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"call {i} ({path} {m}x{n}x{k}): {len(bad)} mismatches, first {bad[:3].tolist()}"
+    assert splits_seen >= 5
 
 
 def random_case(m, n, k, seed, dtype, with_bias):

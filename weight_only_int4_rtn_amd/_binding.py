@@ -171,13 +171,14 @@ _workspaces: dict = {}
 
 
 def workspace_for(device, stream_handle: int, nbytes: int) -> torch.Tensor | None:
-    """A workspace of at least ``nbytes`` for one (device, stream)."""
+    """A workspace of at least ``nbytes`` for one (device, stream), zero-filled
+    when allocated (the calls leave its counter header zero)."""
     if nbytes == 0:
         return None
     key = (torch.device(device).index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

@@ -24,9 +24,10 @@
 // Reduction: the 4 lanes that share a row (L, L+16, L+32, L+48) are summed
 // with two cross-lane exchanges and the waves through LDS in a fixed order.
 // Without a K split the workgroup then adds the bias in FP32 and rounds once
-// to the output dtype.  With a K split it stores its FP32 row sums and the
-// split-K reduce kernel (reduce.hip) finishes the outputs: no inter-workgroup
-// synchronisation, no floating-point atomics, reproducible results.
+// to the output dtype.  With a K split (few row tiles, long K) the split's
+// workgroups post FP32 row sums and take tickets from the tile's counter; the
+// one holding the last ticket adds the posted sums in split order, adds the
+// bias and rounds: one launch, no floating-point atomics, reproducible.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,7 +41,8 @@ struct GemvArgs {
     const uint16_t* bias;
     uint16_t* y;
     int64_t ldy;
-    float* partials;  // [splits][M][tiles*16] when splits > 1
+    float* partials;     // [splits][M][tiles*16] when splits > 1
+    unsigned* counters;  // [tiles] completion tickets, zero before and after a call
     int splits;
     int gps;          // groups per split
 };
@@ -50,9 +52,9 @@ constexpr int kGemvChunks = 8;  // chunks per wave, all loaded up front
 template <int M, int ACT, int WAVES, int CPW>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     constexpr int THREADS = 64 * WAVES;
-    // 16-byte x loads per thread while staging: the plan keeps the slice at
-    // M * 32 groups * 128 columns, i.e. 2 * M loads per thread for 4 waves.
-    constexpr int kXRegs = 2 * M * 4 / WAVES;
+    // 16-byte x loads per thread while staging: the slice is M rows of at
+    // most WAVES * CPW groups of 128 columns, M * CPW / 4 loads per thread.
+    constexpr int kXRegs = (M * CPW + 3) / 4;
     extern __shared__ __align__(16) unsigned char smem[];
     const Layout L(a.n, a.k);
     const int split = int(blockIdx.x % unsigned(a.splits));
@@ -163,17 +165,48 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         if (lane < 16) red[(wave * M + m) * 16 + lane] = tot[m];
     }
     __syncthreads();
-    if (tid >= M * 16) return;
+    const bool out_thread = tid < M * 16;
     const int om = tid >> 4, orow = tid & 15;
     float v = 0.0f;
+    if (out_thread) {
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[(w * M + om) * 16 + orow];
+        for (int w = 0; w < WAVES; ++w) v += red[(w * M + om) * 16 + orow];
+    }
     const int64_t ncol = t * kTileRows + orow;
     if (a.splits > 1) {
-        a.partials[(int64_t(split) * M + om) * (L.tiles * kTileRows) + ncol] = v;
-        return;
+        // K split, finished in this kernel.  Each workgroup posts its row sums
+        // with device-scope atomic stores (written through to the point where
+        // every XCD sees them), waits until they are acknowledged, then takes
+        // a ticket from the tile's counter (device-scope atomic add).  The
+        // workgroup holding the last ticket resets the counter to zero and
+        // reads the posted sums back with device-scope atomic loads (never
+        // served from a stale L2 line of its own XCD), in split order.  No
+        // release/acquire fence is needed: the data itself moves only through
+        // device-coherent accesses, and the kernel's own wait orders the posts
+        // before the ticket.  (Such fences write back and invalidate a whole
+        // XCD L2 on gfx950, which costs far more than this kernel.)
+        const int64_t npad = L.tiles * kTileRows;
+        if (out_thread)
+            __hip_atomic_store(a.partials + (int64_t(split) * M + om) * npad + ncol, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        int* last = reinterpret_cast<int*>(red);
+        if (tid == 0) {
+            const unsigned ticket =
+                __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool is_last = ticket == unsigned(a.splits - 1);
+            if (is_last) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *last = is_last;
+        }
+        __syncthreads();
+        if (!*last || !out_thread) return;
+        v = 0.0f;
+        for (int sp = 0; sp < a.splits; ++sp)
+            v += __hip_atomic_load(a.partials + (int64_t(sp) * M + om) * npad + ncol, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (ncol < a.n) {
+    if (out_thread && ncol < a.n) {
         if (a.bias) v += to_f32<ACT>(a.bias[ncol]);
         a.y[om * a.ldy + ncol] = from_f32<ACT>(v);
     }
@@ -181,34 +214,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 
 // --- planning ---------------------------------------------------------------
 //
-// Workgroups of 4 waves.  A K split is used only when the row tiles alone
-// cannot fill the chip (fewer than ~512 workgroups); it keeps every wave at
-// two or more chunks and every workgroup's x slice within 32 KB.
+// Workgroups of 4 waves, one row tile each.  A K split is used only while the
+// row tiles alone leave the chip short of ~512 workgroups; every wave keeps
+// two or more chunks, at most 8, so a workgroup covers at most 32 groups and
+// its x slice stays small.  Split launches have fewer than 512 tiles, so
+// their counters fit the workspace's ticket header.
 
 GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
     GemvPlan p{};
     const Layout L(n, k);
+    const int64_t G = L.groups;
+    const int mm = int(m);
     p.waves = 4;
-    int64_t splits = 1;
-    if (L.tiles < 512) splits = ceil_div(512, L.tiles);
-    int64_t gps = ceil_div(L.groups, splits);
-    if (gps < 2 * p.waves) gps = 2 * p.waves;  // at least two chunks per wave
-    const int64_t max_gps = kGemvChunks * p.waves;  // 8 chunks per wave; x slice <= 2M loads per thread
-    if (gps > max_gps) gps = max_gps;
-    if (gps > L.groups) gps = L.groups;
+    int64_t splits = L.tiles < 512 ? ceil_div(512, L.tiles) : 1;
+    int64_t gps = ceil_div(G, splits);
+    if (gps < 2 * p.waves) gps = 2 * p.waves;
+    if (gps > kGemvChunks * p.waves) gps = kGemvChunks * p.waves;
+    if (gps > G) gps = G;
     p.gps = int(gps);
-    p.splits = int(ceil_div(L.groups, gps));
+    p.splits = int(ceil_div(G, gps));
     const int64_t per_wave = ceil_div(gps, p.waves);
     p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
-    const int mm = int(m);
     p.lds = size_t(mm) * gps * kGroup * 2 + size_t(mm) * gps * 4 * 4 + size_t(p.waves) * mm * 16 * 4;
-    p.workspace = p.splits > 1 ? size_t(p.splits) * mm * L.tiles * kTileRows * 4 : 0;
+    p.workspace = p.splits > 1 ? kTicketBytes + size_t(p.splits) * mm * L.tiles * kTileRows * 4 : 0;
     return p;
 }
 
 template <int M, int ACT>
 static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k);
+    if (p.splits > 1 && L.tiles > kTicketCounters) return hipErrorInvalidValue;
     const dim3 grid(unsigned(L.tiles * p.splits)), block(256);
     switch (p.cpw) {
         case 1: gemv_kernel<M, ACT, 4, 1><<<grid, block, p.lds, stream>>>(a); break;
@@ -216,10 +251,7 @@ static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s
         case 4: gemv_kernel<M, ACT, 4, 4><<<grid, block, p.lds, stream>>>(a); break;
         default: gemv_kernel<M, ACT, 4, 8><<<grid, block, p.lds, stream>>>(a); break;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
-    return launch_splitk_reduce(a.partials, p.splits, M, a.n, L.tiles * kTileRows, a.bias, a.y, a.ldy,
-                                ACT, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
@@ -235,7 +267,8 @@ hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
-    a.partials = static_cast<float*>(workspace);
+    a.counters = static_cast<unsigned*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kTicketBytes);
     a.splits = p.splits;
     a.gps = p.gps;
     const bool bf = act == kActBf16;

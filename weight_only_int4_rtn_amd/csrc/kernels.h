@@ -7,8 +7,14 @@
 
 namespace w4a16 {
 
-// The workspace of a K-split launch holds FP32 partial sums [splits][m][npad];
-// it needs no initialisation (every element read is written first).
+// Workspace of a K-split launch: a ticket header of kTicketBytes (one 32-bit
+// counter per row tile of a launch that finishes its split in-kernel), then
+// FP32 partial sums [splits][m][npad].  The header must be zero before a call
+// and every call leaves it zero (the last workgroup of a tile resets its
+// counter); the partial sums need no initialisation (every element read is
+// written first).  Every path places its partial sums after the header.
+constexpr size_t kTicketBytes = 4096;
+constexpr int64_t kTicketCounters = int64_t(kTicketBytes / 4);
 
 struct GemvPlan {
     int waves, gps, splits, cpw;  // cpw: chunks each wave loads up front
