@@ -119,13 +119,14 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
 
 /*
  * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
- * kernel path (0 if none).  The workspace holds the FP32 partial sums of a K
- * split, added in split order (no floating-point atomics), after a 4096-byte
- * header of completion counters with which the small-M kernel finishes its
- * split inside one launch.  The caller zero-fills a workspace once, before
- * its first use; every call leaves the header zero again, so a workspace is
- * reused without clearing (also by calls of other shapes and paths).  Two
- * calls that may run at the same time must not share a workspace.
+ * kernel path (0 if none).  A K split needs it: a 256 KiB header of exchange
+ * slots through which the small-M kernel adds the parts' sums inside one
+ * launch, then FP32 partial sums that a second small kernel adds in split
+ * order (no floating-point atomics either way).  The caller zero-fills a
+ * workspace once, before its first use; every call leaves the header zero
+ * again, so a workspace is reused without clearing (also by calls of other
+ * shapes and paths).  Two calls that may run at the same time must not share
+ * a workspace.
  */
 size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 

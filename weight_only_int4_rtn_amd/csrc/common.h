@@ -113,6 +113,14 @@ __device__ inline uint32_t magic_pair(uint32_t word, int i) {
     return and_or(i == 0 ? word : word >> (4 * i), 0x000F000Fu, magic);
 }
 
+// 16-byte load of streamed data (read once: nontemporal, so it does not
+// displace data the kernel reuses from the caches).
+__device__ inline uint4 load_stream16(const uint8_t* p) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, then s_barrier.  __syncthreads() also waits for every
 // outstanding global load (vmcnt(0)), which would serialise the weight

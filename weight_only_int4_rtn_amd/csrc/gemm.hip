@@ -701,7 +701,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
     int64_t gps = ceil_div(L.groups, splits);
     p.gps = int(gps);
     p.splits = int(ceil_div(L.groups, gps));
-    p.workspace = p.splits > 1 ? kTicketBytes + size_t(p.splits) * m * p.ntiles * kGmBN * 4 : 0;
+    p.workspace = p.splits > 1 ? kSyncBytes + size_t(p.splits) * m * p.ntiles * kGmBN * 4 : 0;
     return p;
 }
 
@@ -721,7 +721,7 @@ hipError_t launch_gemm(const void* x, int act, int64_t m, int64_t k, int64_t ldx
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
-    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kTicketBytes);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSyncBytes);
     a.vec_store = reinterpret_cast<uintptr_t>(y) % 8 == 0 && ldy % 4 == 0;
     a.vec16 = reinterpret_cast<uintptr_t>(y) % 16 == 0 && ldy % 8 == 0;
     a.splits = p.splits;

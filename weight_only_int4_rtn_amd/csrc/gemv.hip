@@ -9,11 +9,11 @@
 // packed pair of 16-bit floats with one shift and one v_and_or, and multiplies
 // them into the activations with v_dot2 (FP32 accumulation).
 //
-// Latency: each thread first loads its part of the x slice, then its wave's
-// first batch of chunks, then stages x in LDS; a wave issues the next batch
-// before it works on the current one.  Loads complete in issue order, so
-// the staging waits only for x and every chunk is used as soon as it lands:
-// the nibble arithmetic overlaps the weight stream instead of trailing it.
+// Latency: each thread first loads its part of the x slice, then every chunk
+// of its wave (nontemporal loads: the weights are read once), then stages x
+// in LDS.  Loads complete in issue order, so the staging waits only for x and
+// every chunk is used as soon as it lands: the nibble arithmetic overlaps the
+// weight stream instead of trailing it.
 //
 // The packed pairs hold 136 + q (bf16) or 1032 + q (f16) exactly; the offset
 // is removed once per group with the sum of the lane's 32 activations, which
@@ -24,10 +24,12 @@
 // Reduction: the 4 lanes that share a row (L, L+16, L+32, L+48) are summed
 // with two cross-lane exchanges and the waves through LDS in a fixed order.
 // Without a K split the workgroup then adds the bias in FP32 and rounds once
-// to the output dtype.  With a K split (few row tiles, long K) the split's
-// workgroups post FP32 row sums and take tickets from the tile's counter; the
-// one holding the last ticket adds the posted sums in split order, adds the
-// bias and rounds: one launch, no floating-point atomics, reproducible.
+// to the output dtype.  A K longer than one workgroup covers (32 groups) is
+// split over workgroups whose row sums meet in a fixed binary tree of
+// exchange slots: at each node the two children's sums are added (FP32
+// addition is commutative, so the result does not depend on which child
+// arrives first); the root adds the bias and rounds.  One launch, no
+// floating-point atomics, reproducible results.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,10 +43,11 @@ struct GemvArgs {
     const uint16_t* bias;
     uint16_t* y;
     int64_t ldy;
-    float* partials;     // [splits][M][tiles*16] when splits > 1
-    unsigned* counters;  // [tiles] completion tickets, zero before and after a call
+    unsigned long long* slots;  // [tiles][splits - 1][M * 16] exchange slots, zero before and after a call
+    float* partials;            // [splits][M][tiles * 16] when the slots do not fit: split-K reduce kernel
     int splits;
-    int gps;          // groups per split
+    int gps;                    // groups per split
+    int exchange;               // splits > 1: finish through the slots (else through partials)
 };
 
 constexpr int kGemvChunks = 8;  // chunks per wave, all loaded up front
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * WAVES;
         const int gc = gl < ng ? gl : ng - 1;  // a valid chunk; unused when gl >= ng
-        cw[u] = *reinterpret_cast<const uint4*>(cbase + int64_t(gc) * kChunkBytes);
+        cw[u] = load_stream16(cbase + int64_t(gc) * kChunkBytes);
         sc[u] = sbase[int64_t(gc) * kTileRows];
     }
 
@@ -173,38 +176,37 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         for (int w = 0; w < WAVES; ++w) v += red[(w * M + om) * 16 + orow];
     }
     const int64_t ncol = t * kTileRows + orow;
+    if (a.splits > 1 && !a.exchange) {
+        if (out_thread) a.partials[(int64_t(split) * M + om) * (L.tiles * kTileRows) + ncol] = v;
+        return;
+    }
     if (a.splits > 1) {
-        // K split, finished in this kernel.  Each workgroup posts its row sums
-        // with device-scope atomic stores (written through to the point where
-        // every XCD sees them), waits until they are acknowledged, then takes
-        // a ticket from the tile's counter (device-scope atomic add).  The
-        // workgroup holding the last ticket resets the counter to zero and
-        // reads the posted sums back with device-scope atomic loads (never
-        // served from a stale L2 line of its own XCD), in split order.  No
-        // release/acquire fence is needed: the data itself moves only through
-        // device-coherent accesses, and the kernel's own wait orders the posts
-        // before the ticket.  (Such fences write back and invalidate a whole
-        // XCD L2 on gfx950, which costs far more than this kernel.)
-        const int64_t npad = L.tiles * kTileRows;
-        if (out_thread)
-            __hip_atomic_store(a.partials + (int64_t(split) * M + om) * npad + ncol, v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        int* last = reinterpret_cast<int*>(red);
-        if (tid == 0) {
-            const unsigned ticket =
-                __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool is_last = ticket == unsigned(a.splits - 1);
-            if (is_last) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *last = is_last;
+        // Binary tree over the splits: leaf i = split i, node j of a level
+        // joins children 2j and 2j + 1 of the level below (an odd last child
+        // moves up alone).  Each output thread swaps its sum, tagged, into
+        // its row's slot of the node with one device-scope 64-bit atomic
+        // exchange.  An empty slot (tag 0) means the sibling has not arrived:
+        // this thread is done.  Otherwise the old value is the sibling's sum:
+        // the thread clears the slot for the next call, adds, and climbs.
+        // The sums travel inside the atomics, so no fence is needed, and no
+        // thread ever waits for another.
+        if (!out_thread) return;
+        int node_base = 0, idx = split, width = a.splits;
+        while (width > 1) {
+            if (!((width & 1) && idx == width - 1)) {
+                unsigned long long* slot =
+                    a.slots + (t * (a.splits - 1) + node_base + (idx >> 1)) * (M * kTileRows) + tid;
+                const unsigned long long mine = (1ull << 32) | __float_as_uint(v);
+                const unsigned long long old =
+                    __hip_atomic_exchange(slot, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((old >> 32) == 0ull) return;
+                __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v += __uint_as_float(uint32_t(old));
+            }
+            node_base += width >> 1;
+            idx >>= 1;
+            width = (width + 1) >> 1;
         }
-        __syncthreads();
-        if (!*last || !out_thread) return;
-        v = 0.0f;
-        for (int sp = 0; sp < a.splits; ++sp)
-            v += __hip_atomic_load(a.partials + (int64_t(sp) * M + om) * npad + ncol, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
     }
     if (out_thread && ncol < a.n) {
         if (a.bias) v += to_f32<ACT>(a.bias[ncol]);
@@ -214,11 +216,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 
 // --- planning ---------------------------------------------------------------
 //
-// Workgroups of 4 waves, one row tile each.  A K split is used only while the
-// row tiles alone leave the chip short of ~512 workgroups; every wave keeps
-// two or more chunks, at most 8, so a workgroup covers at most 32 groups and
-// its x slice stays small.  Split launches have fewer than 512 tiles, so
-// their counters fit the workspace's ticket header.
+// Workgroups of 4 waves, one row tile each, at most 8 chunks per wave: a
+// workgroup covers up to 32 groups (K <= 4096) and a longer K is split into
+// equal parts.  Splitting only to fill the chip costs more than it gains:
+// the exchange adds a device round trip per tree level, while a tile's
+// chunks are all in flight at once anyway.  The exchange slots live in the
+// workspace's zero header; a launch whose tree does not fit there stores
+// partial sums for the split-K reduce kernel instead.
 
 GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
     GemvPlan p{};
@@ -226,24 +230,23 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
     const int64_t G = L.groups;
     const int mm = int(m);
     p.waves = 4;
-    int64_t splits = L.tiles < 512 ? ceil_div(512, L.tiles) : 1;
-    int64_t gps = ceil_div(G, splits);
-    if (gps < 2 * p.waves) gps = 2 * p.waves;
-    if (gps > kGemvChunks * p.waves) gps = kGemvChunks * p.waves;
-    if (gps > G) gps = G;
+    const int64_t gps = G < kGemvChunks * p.waves ? G : kGemvChunks * p.waves;
     p.gps = int(gps);
     p.splits = int(ceil_div(G, gps));
     const int64_t per_wave = ceil_div(gps, p.waves);
     p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
     p.lds = size_t(mm) * gps * kGroup * 2 + size_t(mm) * gps * 4 * 4 + size_t(p.waves) * mm * 16 * 4;
-    p.workspace = p.splits > 1 ? kTicketBytes + size_t(p.splits) * mm * L.tiles * kTileRows * 4 : 0;
+    const int64_t slots = L.tiles * (p.splits - 1) * mm * kTileRows;
+    p.exchange = p.splits > 1 && slots * 8 <= int64_t(kSyncBytes);
+    p.workspace = p.splits == 1 ? 0
+                  : p.exchange ? kSyncBytes
+                               : kSyncBytes + size_t(p.splits) * mm * L.tiles * kTileRows * 4;
     return p;
 }
 
 template <int M, int ACT>
 static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k);
-    if (p.splits > 1 && L.tiles > kTicketCounters) return hipErrorInvalidValue;
     const dim3 grid(unsigned(L.tiles * p.splits)), block(256);
     switch (p.cpw) {
         case 1: gemv_kernel<M, ACT, 4, 1><<<grid, block, p.lds, stream>>>(a); break;
@@ -251,7 +254,10 @@ static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s
         case 4: gemv_kernel<M, ACT, 4, 4><<<grid, block, p.lds, stream>>>(a); break;
         default: gemv_kernel<M, ACT, 4, 8><<<grid, block, p.lds, stream>>>(a); break;
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1 || p.exchange) return e;
+    return launch_splitk_reduce(a.partials, p.splits, M, a.n, L.tiles * kTileRows, a.bias, a.y, a.ldy, ACT,
+                                stream);
 }
 
 hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
@@ -267,10 +273,11 @@ hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
-    a.counters = static_cast<unsigned*>(workspace);
-    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kTicketBytes);
+    a.slots = static_cast<unsigned long long*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSyncBytes);
     a.splits = p.splits;
     a.gps = p.gps;
+    a.exchange = p.exchange;
     const bool bf = act == kActBf16;
     switch (m) {
         case 1: return bf ? launch_one<1, kActBf16>(a, p, stream) : launch_one<1, kActF16>(a, p, stream);

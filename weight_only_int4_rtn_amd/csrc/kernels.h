@@ -7,17 +7,18 @@
 
 namespace w4a16 {
 
-// Workspace of a K-split launch: a ticket header of kTicketBytes (one 32-bit
-// counter per row tile of a launch that finishes its split in-kernel), then
-// FP32 partial sums [splits][m][npad].  The header must be zero before a call
-// and every call leaves it zero (the last workgroup of a tile resets its
-// counter); the partial sums need no initialisation (every element read is
-// written first).  Every path places its partial sums after the header.
-constexpr size_t kTicketBytes = 4096;
-constexpr int64_t kTicketCounters = int64_t(kTicketBytes / 4);
+// Workspace of a K-split launch: a header of kSyncBytes holding the 64-bit
+// exchange slots through which small-M launches finish their split in-kernel,
+// then FP32 partial sums [splits][m][npad] for the split-K reduce kernel.
+// The header must be zero before a call and every call leaves it zero (the
+// thread that empties a slot clears it); the partial sums need no
+// initialisation (every element read is written first).  Every path places
+// its partial sums after the header.
+constexpr size_t kSyncBytes = size_t(256) << 10;
 
 struct GemvPlan {
     int waves, gps, splits, cpw;  // cpw: chunks each wave loads up front
+    bool exchange;                // split finished through the header's exchange slots
     size_t lds, workspace;
 };
 GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k);

@@ -198,7 +198,7 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k) {
     const int64_t per_wave = ceil_div(gps, kMgWaves);
     p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
     p.lds = size_t(p.mmax) * (gps * kGroup + 8) * 2 + size_t(gps) * 16 * 4 + size_t(kMgWaves) * 256 * 4;
-    p.workspace = p.splits > 1 ? kTicketBytes + size_t(p.splits) * m * L.tiles * kTileRows * 4 : 0;
+    p.workspace = p.splits > 1 ? kSyncBytes + size_t(p.splits) * m * L.tiles * kTileRows * 4 : 0;
     return p;
 }
 
@@ -232,7 +232,7 @@ hipError_t launch_mgemv(const void* x, int act, int64_t m, int64_t k, int64_t ld
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
-    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kTicketBytes);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSyncBytes);
     a.splits = p.splits;
     a.gps = p.gps;
     const bool bf = act == kActBf16;

@@ -167,7 +167,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
     gps = gps > L.groups ? L.groups : gps;
     p.gps = int(gps);
     p.splits = int(ceil_div(L.groups, gps));
-    p.workspace = p.splits > 1 ? kTicketBytes + size_t(p.splits) * m * p.tile_groups * kSkCols * 4 : 0;
+    p.workspace = p.splits > 1 ? kSyncBytes + size_t(p.splits) * m * p.tile_groups * kSkCols * 4 : 0;
     return p;
 }
 
@@ -195,7 +195,7 @@ hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t l
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
-    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kTicketBytes);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSyncBytes);
     a.splits = p.splits;
     a.gps = p.gps;
     a.tile_groups = p.tile_groups;
