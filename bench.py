@@ -101,17 +101,28 @@ def make_step(cases, layer, xs, biases, ys, workspace):
     return step
 
 
-def time_graphs(graphs, steps, warmup):
-    """Replay graphs round-robin: warmup, then `steps` timed replays."""
+def steps_per_graph(steps: int) -> int:
+    """Consecutive steps (layers) per captured graph: the largest divisor of
+    `steps` up to 16, so the timed region replays whole graphs."""
+    return max(d for d in range(1, 17) if steps % d == 0)
+
+
+def time_graphs(graphs, per_graph, steps, warmup):
+    """Replay graphs of `per_graph` consecutive steps round-robin: warmup,
+    then exactly `steps` timed steps between two device synchronisations,
+    measured with HIP events on the replay stream.  Returns ms per step."""
     import torch
-    for i in range(warmup):
+    for i in range(-(-warmup // per_graph)):
         graphs[i % len(graphs)].replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
+    e0.record(stream)
+    for i in range(steps // per_graph):
         graphs[i % len(graphs)].replay()
+    e1.record(stream)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps
 
 
 def time_kernel(case, layers, j, x, bias, y, workspace, launches=24, replays=10):
@@ -164,12 +175,23 @@ def run_workload(cases, dev, steps, warmup, dominant):
     workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     log(f"pool: {len(layers)} layers of {sum(p.numel() for p in layers[0]) / 1e6:.1f} MB; "
         f"paths {[w4.choose_path(c.m, c.n, c.k).name for c in cases]}")
-    graphs = [capture(make_step(cases, layer, xs, biases, ys, workspace)) for layer in layers]
-    ms = time_graphs(graphs, steps, warmup)
+    # Each graph runs `per` consecutive layers of the pool, as a decode loop
+    # runs a model's layers back to back; the graphs together cover the pool.
+    per = steps_per_graph(steps)
+
+    def layer_run(first):
+        fns = [make_step(cases, layers[(first + i) % len(layers)], xs, biases, ys, workspace) for i in range(per)]
+
+        def run():
+            for f in fns:
+                f()
+        return run
+    graphs = [capture(layer_run(first)) for first in range(0, len(layers), per)]
+    ms = time_graphs(graphs, per, steps, warmup)
     dom = cases[dominant]
     dom_ms = time_kernel(dom, layers, dominant, xs[dominant], biases[dominant], ys[dominant], workspace)
     eager = eager_ms(cases, layers, xs, biases, ys, workspace)
-    out = {"ms": ms, "dom_ms": dom_ms, "eager_ms": eager, "load": load}
+    out = {"ms": ms, "dom_ms": dom_ms, "eager_ms": eager, "load": load, "steps_per_graph": per}
     del graphs, layers
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -234,6 +256,63 @@ def traffic_probe(dev):
         f"4 elementwise launches of {src.numel() * 4} bytes read + written; sources {kernel_source_hash()}")
 
 
+def _rocpd_rows(db, sql):
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        return con.execute(sql).fetchall()
+    finally:
+        con.close()
+
+
+def summarize_trace(db):
+    """Markdown table of a rocprofv3 --kernel-trace database: launches and
+    durations per kernel name and grid size (the `kernels` view)."""
+    import statistics
+    rows = _rocpd_rows(db, "select name, grid_x, duration from kernels")
+    groups = {}
+    for name, grid, dur in rows:
+        groups.setdefault((name, grid), []).append(dur / 1e3)
+    lines = ["| kernel | grid (threads) | launches | mean us | median us | min us |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name.split("(")[0]
+        lines.append(f"| `{short}` | {grid} | {len(d)} | {statistics.mean(d):.2f} | "
+                     f"{statistics.median(d):.2f} | {min(d):.2f} |")
+    return "\n".join(lines)
+
+
+def summarize_traffic(fetch_db, write_db):
+    """HBM bytes per launch of the gate_up GEMV from two counter databases of
+    `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what its counter reads for the elementwise
+    kernel that reads and writes exactly 256 MiB."""
+    known_kib = (64 << 20) * 4 / 1024
+
+    def per_dispatch(db, counter):
+        rows = _rocpd_rows(db, "select dispatch_id, kernel_name, grid_size, value from counters_collection "
+                               f"where counter_name = '{counter}'")
+        acc = {}
+        for d, name, grid, v in rows:
+            key = (d, name, grid)
+            acc[key] = acc.get(key, 0.0) + v
+        return acc
+
+    out = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        acc = per_dispatch(db, counter)
+        gemv = [v for (d, name, g), v in acc.items() if "gemv_kernel" in name]
+        copy = [v for (d, name, g), v in acc.items()
+                if "elementwise" in name and g == (64 << 20) // 4 and v > known_kib / 8]
+        if not gemv or not copy:
+            raise SystemExit(f"{db}: no GEMV or no 256 MiB elementwise dispatch with {counter}")
+        scale = known_kib / (sum(copy) / len(copy))
+        out[counter] = (sum(gemv) / len(gemv), scale, len(gemv), len(copy))
+    fetch = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][1] * 1024
+    write = out["WRITE_SIZE"][0] * out["WRITE_SIZE"][1] * 1024
+    return out, int(round(fetch + write))
+
+
 def cpu_baseline(cases, target_seconds=12.0):
     """The oracle (as it stands) on the same M = 1 decode layer, repeated."""
     import oracle
@@ -269,7 +348,44 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the launches the HBM counter runs measure (see TRAFFIC_FILE)")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace database and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write TRAFFIC_FILE from the two counter databases of --traffic-probe and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_traffic:
+        parts, traffic = summarize_traffic(*args.summarize_traffic)
+        fk, fs, fn, fc = parts["FETCH_SIZE"]
+        wk, wsc, wn, wc = parts["WRITE_SIZE"]
+        text = "\n".join([
+            "# HBM traffic of the gate_up GEMV at M = 1 (K 2048, N 32768, bf16)",
+            "",
+            "Commands (MI355X, one GPU; R = repository root, databases under $R/gpurun_out):",
+            "",
+            "    cd /tmp && export TMPDIR=/tmp",
+            "    timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch -o run -- python3 $R/bench.py --traffic-probe",
+            "    timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write -o run -- python3 $R/bench.py --traffic-probe",
+            "    python3 $R/bench.py --summarize-traffic $R/gpurun_out/pmc_fetch/run_results.db $R/gpurun_out/pmc_write/run_results.db",
+            "",
+            "The probe launches the GEMV 16 times over distinct weight copies and an",
+            "elementwise kernel that reads and writes exactly 256 MiB; each counter is",
+            "scaled by what it reads for that kernel.",
+            "",
+            f"- FETCH_SIZE per GEMV launch (KiB, mean of {fn}): {fk:.2f}; scale {fs:.5f} (from {fc} copies)",
+            f"- WRITE_SIZE per GEMV launch (KiB, mean of {wn}): {wk:.2f}; scale {wsc:.5f} (from {wc} copies)",
+            "- algorithmic_bytes_per_launch: `35721216`",
+            f"- traffic_bytes_per_launch: `{traffic}`",
+            f"- traffic / algorithmic: {traffic / 35721216:.4f}",
+            f"- kernel_source_sha256: `{kernel_source_hash()}`",
+            ""])
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as fh:
+            fh.write(text)
+        print(text)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer is benchmarked on one MI355X "
               "(multi-GPU sharding is a design note, not part of this build)", file=sys.stderr)
@@ -322,7 +438,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; weights rotate over a >=1 GiB pool of layer copies; steps replayed as HIP graphs)",
+        "data": "synthetic (seeded; weights rotate over a >=1 GiB pool of layer copies; "
+                f"steps replayed as HIP graphs of {dec['steps_per_graph']} consecutive layers)",
         "config": {"workload": "decode layer M=1: qkv 2048x2560, o 2048x2048, gate_up 2048x32768, "
                                "down 16384x2048; bf16 x, int4 g128 weights",
                    "m": 1, "bytes_per_step": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
