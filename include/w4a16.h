@@ -119,8 +119,8 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
 
 /*
  * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
- * kernel path (0 if none).  A K split needs it: a 256 KiB header of exchange
- * slots through which the small-M kernel adds the parts' sums inside one
+ * kernel path (0 if none).  A K split needs it: a 1 MiB header of exchange
+ * slots through which the small-M kernels add the parts' sums inside one
  * launch, then FP32 partial sums that a second small kernel adds in split
  * order (no floating-point atomics either way).  The caller zero-fills a
  * workspace once, before its first use; every call leaves the header zero

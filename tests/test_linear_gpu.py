@@ -51,7 +51,7 @@ def run(x, packed, n, bias=None, path="AUTO"):
 
 def exact_case(m, n, k, seed, dtype, with_bias):
     rng = np.random.default_rng(seed)
-    qi = rng.integers(-7, 8, size=(n, k))
+    qi = rng.integers(-7, 8, size=(n, k), dtype=np.int8)
     qi[:, ::128] = 7 * np.where(rng.random((n, k // 128)) < 0.5, 1, -1)
     w = torch.from_numpy((qi * 2.0 ** -3).astype(np.float32))
     x = torch.from_numpy(rng.integers(-4, 5, size=(m, k)).astype(np.float32)).to(dtype)
@@ -144,14 +144,15 @@ def test_strided_output_bit_exact(dev):
 
 # Calls of different shapes and paths sharing one zero-filled workspace, in an
 # order where a later call's partial sums land where an earlier call's could
-# have been: every result bit-exact, and the 256 KiB exchange-slot header
-# zero again after every call.  The GEMV calls split K into 4, 3 (a tree with
-# an odd child), 8 (too many slots: partial sums and the reduce kernel) and
-# 5 parts.
-SYNC_HEADER = 256 << 10
+# have been: every result bit-exact, and the 1 MiB exchange-slot header zero
+# again after every call.  Small-M splits: GEMV into 4, 3 (a tree with an odd
+# child), 8 (too many slots: partial sums and the reduce kernel) and 5 parts;
+# MGEMV into 8 (three tree levels), 16 (partial sums) and 2 parts.
+SYNC_HEADER = 1 << 20
 SHARED_WS_CALLS = [("GEMV", 1, 2048, 16384), ("SKINNY", 50, 1000, 4096), ("GEMV", 3, 40, 12288),
-                   ("MGEMV", 6, 520, 2048), ("GEMM", 300, 4104, 640), ("GEMV", 4, 1200, 32768),
-                   ("GEMV", 2, 100, 20480), ("GEMV", 1, 2048, 16384)]
+                   ("MGEMV", 8, 2048, 16384), ("GEMM", 300, 4104, 640), ("GEMV", 4, 4688, 32768),
+                   ("MGEMV", 16, 1040, 16384), ("GEMV", 2, 100, 20480), ("MGEMV", 6, 520, 2048),
+                   ("GEMV", 1, 2048, 16384)]
 
 
 def test_shared_workspace_header_stays_clear(dev):
@@ -174,7 +175,7 @@ def test_shared_workspace_header_stays_clear(dev):
         got = y.cpu().to(torch.float64).numpy()
         bad = np.argwhere(got != want)
         assert bad.size == 0, f"call {i} ({path} {m}x{n}x{k}): {len(bad)} mismatches, first {bad[:3].tolist()}"
-    assert splits_seen >= 7
+    assert splits_seen >= 9
 
 
 def random_case(m, n, k, seed, dtype, with_bias):

@@ -695,8 +695,10 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
     p.mtiles = ceil_div(m, 16 * p.mb);
     p.ntiles = ceil_div(n, kGmBN);
     const int64_t tiles = p.mtiles * p.ntiles;
-    // split K while the tiles alone leave CUs idle (aim for >= 256 workgroups)
-    int64_t splits = tiles >= 256 ? 1 : ceil_div(256, tiles);
+    // split K while the tiles alone leave CUs idle, into as many parts as
+    // still fit one round of 256 workgroups (a second, partial round would
+    // cost a whole round's time)
+    int64_t splits = tiles >= 256 ? 1 : 256 / tiles;
     if (splits > L.groups) splits = L.groups;
     int64_t gps = ceil_div(L.groups, splits);
     p.gps = int(gps);

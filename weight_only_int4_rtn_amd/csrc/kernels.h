@@ -14,7 +14,7 @@ namespace w4a16 {
 // thread that empties a slot clears it); the partial sums need no
 // initialisation (every element read is written first).  Every path places
 // its partial sums after the header.
-constexpr size_t kSyncBytes = size_t(256) << 10;
+constexpr size_t kSyncBytes = size_t(1) << 20;
 
 struct GemvPlan {
     int waves, gps, splits, cpw;  // cpw: chunks each wave loads up front
@@ -25,6 +25,7 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k);
 
 struct MgemvPlan {
     int mmax, gps, splits, cpw;
+    bool exchange;  // split finished through the header's exchange slots
     size_t lds, workspace;
 };
 MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k);

@@ -16,8 +16,10 @@
 // of column L % 16.  Per weight element this costs 7/8 of a VALU instruction
 // for the nibble conversion, against 11/8 for the v_dot2 kernel at M = 1.
 //
-// Waves are summed through LDS in a fixed order; K splits store FP32 partial
-// sums for the split-K reduce kernel (reduce.hip).
+// Waves are summed through LDS in a fixed order.  K splits meet in a binary
+// tree of exchange slots in the workspace header (as in gemv.hip), or, when
+// the tree does not fit there, store FP32 partial sums for the split-K reduce
+// kernel (reduce.hip).
 #include "common.h"
 #include "kernels.h"
 
@@ -31,8 +33,10 @@ struct MgemvArgs {
     const uint16_t* bias;
     uint16_t* y;
     int64_t ldy;
-    float* partials;  // [splits][m][tiles*16] when splits > 1
+    unsigned long long* slots;  // [tiles][splits - 1][m * 16] exchange slots, zero before and after a call
+    float* partials;            // [splits][m][tiles * 16] when the slots do not fit: split-K reduce kernel
     int splits, gps;
+    int exchange;               // splits > 1: finish through the slots (else through partials)
 };
 
 constexpr int kMgWaves = 4;
@@ -169,9 +173,30 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
 #pragma unroll
     for (int w = 0; w < kMgWaves; ++w) v += red[(w * 16 + orow) * 16 + ocol];
     const int64_t col = t * kTileRows + ocol;
-    if (a.splits > 1) {
+    if (a.splits > 1 && !a.exchange) {
         a.partials[(int64_t(split) * m + orow) * (L.tiles * kTileRows) + col] = v;
         return;
+    }
+    if (a.splits > 1) {
+        // the split's parts meet in a binary tree of exchange slots, as in
+        // the v_dot2 kernel (gemv.hip): one device atomic per level, the
+        // second arrival adds (commutative, so reproducible) and climbs
+        int node_base = 0, idx = split, width = a.splits;
+        while (width > 1) {
+            if (!((width & 1) && idx == width - 1)) {
+                unsigned long long* slot =
+                    a.slots + (t * (a.splits - 1) + node_base + (idx >> 1)) * (int64_t(m) * kTileRows) + tid;
+                const unsigned long long mine = (1ull << 32) | __float_as_uint(v);
+                const unsigned long long old =
+                    __hip_atomic_exchange(slot, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((old >> 32) == 0ull) return;
+                __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v += __uint_as_float(uint32_t(old));
+            }
+            node_base += width >> 1;
+            idx >>= 1;
+            width = (width + 1) >> 1;
+        }
     }
     if (col < a.n) {
         if (a.bias) v += to_f32<ACT>(a.bias[col]);
@@ -198,7 +223,11 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k) {
     const int64_t per_wave = ceil_div(gps, kMgWaves);
     p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
     p.lds = size_t(p.mmax) * (gps * kGroup + 8) * 2 + size_t(gps) * 16 * 4 + size_t(kMgWaves) * 256 * 4;
-    p.workspace = p.splits > 1 ? kSyncBytes + size_t(p.splits) * m * L.tiles * kTileRows * 4 : 0;
+    const int64_t slots = L.tiles * (p.splits - 1) * m * kTileRows;
+    p.exchange = p.splits > 1 && slots * 8 <= int64_t(kSyncBytes);
+    p.workspace = p.splits == 1 ? 0
+                  : p.exchange ? kSyncBytes
+                               : kSyncBytes + size_t(p.splits) * m * L.tiles * kTileRows * 4;
     return p;
 }
 
@@ -213,7 +242,7 @@ static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t
         default: mgemv_kernel<MMAX, ACT, 8><<<grid, block, p.lds, stream>>>(a); break;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
+    if (e != hipSuccess || p.splits == 1 || p.exchange) return e;
     return launch_splitk_reduce(a.partials, p.splits, a.m, a.n, L.tiles * kTileRows, a.bias, a.y, a.ldy,
                                 ACT, stream);
 }
@@ -232,9 +261,11 @@ hipError_t launch_mgemv(const void* x, int act, int64_t m, int64_t k, int64_t ld
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.ldy = ldy;
+    a.slots = static_cast<unsigned long long*>(workspace);
     a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSyncBytes);
     a.splits = p.splits;
     a.gps = p.gps;
+    a.exchange = p.exchange;
     const bool bf = act == kActBf16;
     switch (p.mmax) {
         case 4: return bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream);
