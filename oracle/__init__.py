@@ -8,10 +8,14 @@ The arithmetic lives in ``w4a16_oracle.c`` (plain C, built with gcc); this
 package holds the ctypes marshalling and the build step.
 """
 from .oracle import (  # noqa: F401
+    ACT_GELU_TANH,
+    ACT_SWIGLU,
     BF16,
     F16,
     F32,
     GROUP,
+    act_value,
+    activate,
     bf16_to_double,
     build,
     codes_to_nibbles,
@@ -19,8 +23,10 @@ from .oracle import (  # noqa: F401
     f16_to_double,
     library_path,
     linear,
+    linear_act,
     linear_entries,
     nibbles_to_codes,
     num_threads,
     quantize,
+    round16,
 )

@@ -13,6 +13,7 @@ import numpy as np
 
 GROUP = 128
 F32, BF16, F16 = 0, 1, 2
+ACT_SWIGLU, ACT_GELU_TANH = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "w4a16_oracle.c")
@@ -53,6 +54,12 @@ def _declare(lib):
     lib.oracle_bf16_to_double.restype = ctypes.c_double
     lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_f16_to_double.restype = ctypes.c_double
+    lib.oracle_round16.argtypes = [ctypes.c_double, i32]
+    lib.oracle_round16.restype = ctypes.c_uint16
+    lib.oracle_act_value.argtypes = [ctypes.c_double, ctypes.c_double, i32]
+    lib.oracle_act_value.restype = ctypes.c_double
+    lib.oracle_activate.argtypes = [vp, i32, i32, i64, i64, i64, vp]
+    lib.oracle_activate.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     return lib
@@ -167,6 +174,34 @@ def linear_entries(x_bits, x_tag, q, s, bias_bits, rows, cols, lib=None) -> np.n
     if rc != 0:
         raise ValueError("oracle_linear_entries rejected its arguments")
     return out
+
+
+def activate(x_bits: np.ndarray, x_tag: int, act: int, lib=None) -> np.ndarray:
+    """The activated layer input as 16-bit patterns [m, k].  SwiGLU rows of
+    ``x_bits`` hold [up | gate] (2k columns); GELU rows hold k columns."""
+    lib = lib or load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    m, width = x_bits.shape
+    k = width // 2 if act == ACT_SWIGLU else width
+    out = np.empty((m, k), dtype=np.uint16)
+    rc = lib.oracle_activate(_p(x_bits), x_tag, act, m, k, width, _p(out))
+    if rc != 0:
+        raise ValueError("oracle_activate rejected its arguments")
+    return out
+
+
+def linear_act(x_bits, x_tag, act, q, s, bias_bits=None, lib=None) -> np.ndarray:
+    """y = act(x) . (q*s)^T + bias in double, act(x) rounded to x's dtype first."""
+    a = activate(x_bits, x_tag, act, lib=lib)
+    return linear(a, x_tag, q, s, bias_bits, lib=lib)
+
+
+def round16(v: float, tag: int, lib=None) -> int:
+    return int((lib or load()).oracle_round16(float(v), tag))
+
+
+def act_value(v: float, up: float, act: int, lib=None) -> float:
+    return float((lib or load()).oracle_act_value(float(v), float(up), act))
 
 
 def bf16_to_double(bits: int, lib=None) -> float:

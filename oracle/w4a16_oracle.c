@@ -36,11 +36,22 @@
  *    (the plain definition; it is more accurate than any FP32 order) and
  *    returned unrounded.
  *
+ * Activations fused into a linear's input ("Piper Kernels", section "ConvRot
+ * INT8": the SwiGLU input row is [up | gate] of twice the layer's in_features
+ * and gives up * silu(gate); the GELU input is tanh-approximate GELU of the
+ * row; fused activation preparation keeps FP32 arithmetic, section "ConvRot
+ * INT8 ... FFN", and outputs keep the input dtype).  Readings: the activation
+ * is evaluated in double here (more accurate than the FP32 it asks for) and
+ * rounded once, to the nearest 16-bit value of the input dtype (ties to
+ * even), which is then the layer's input, as a separately materialised
+ * activation would be.
+ *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared
  * The quantizer relies on IEEE binary32 division and on nearbyintf under the
  * default round-to-nearest-even mode; -ffp-contract=off keeps every step a
  * separately rounded operation.
  */
+#define _GNU_SOURCE
 #include <fenv.h>
 #include <math.h>
 #include <stdint.h>
@@ -224,6 +235,102 @@ int oracle_linear_entries(const uint16_t *x, int x_dtype, int64_t m, int64_t k, 
 #pragma omp parallel for schedule(static)
     for (int64_t e = 0; e < count; ++e)
         out[e] = one_output(x, x_dtype, ldx, rows[e], q, s, k, cols[e], bias);
+    return 0;
+}
+
+/* ---- activations fused into the input of a linear layer ---- */
+
+#define ORACLE_ACT_SWIGLU 1
+#define ORACLE_ACT_GELU_TANH 2
+
+/*
+ * Nearest 16-bit value of a double, ties to the even significand, from the
+ * format definitions:
+ *   BF16: 8 significant bits, normal numbers from 2^-126 (the binary32
+ *         exponent range), subnormal spacing 2^-133, exponent bias 127;
+ *   F16:  11 significant bits, normal numbers from 2^-14, subnormal spacing
+ *         2^-24, exponent bias 15, largest finite 65504.
+ * Magnitudes that round beyond the largest finite value give infinity.
+ * Returns the bit pattern.
+ */
+uint16_t oracle_round16(double v, int dtype)
+{
+    const int p = dtype == ORACLE_BF16 ? 8 : 11;          /* significant bits */
+    const int emin = dtype == ORACLE_BF16 ? -126 : -14;   /* smallest normal exponent */
+    const int emax = dtype == ORACLE_BF16 ? 127 : 15;     /* largest exponent */
+    const int bias = dtype == ORACLE_BF16 ? 127 : 15;
+    const int mbits = p - 1;                               /* stored fraction bits */
+    const unsigned sign = signbit(v) ? 1u : 0u;
+    if (isnan(v))
+        return (uint16_t)((sign << 15) | (dtype == ORACLE_BF16 ? 0x7fc0u : 0x7e00u));
+    double a = fabs(v);
+    const uint16_t inf = (uint16_t)((sign << 15) | (((1u << (15 - mbits)) - 1u) << mbits));
+    if (isinf(a))
+        return inf;
+    if (a == 0.0)
+        return (uint16_t)(sign << 15);
+    int e2;
+    frexp(a, &e2);                       /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                      /* exponent of the leading bit */
+    int q = (e < emin ? emin : e) - mbits;          /* exponent of one unit in the last place */
+    double units = nearbyint(ldexp(a, -q));         /* ties to even under the default mode */
+    double r = ldexp(units, q);
+    if (r >= ldexp(1.0, emax + 1))
+        return inf;
+    if (r < ldexp(1.0, emin))            /* subnormal (or rounded to zero) */
+        return (uint16_t)((sign << 15) | (unsigned)units);
+    frexp(r, &e2);
+    e = e2 - 1;
+    unsigned frac = (unsigned)(ldexp(r, mbits - e) - ldexp(1.0, mbits));
+    return (uint16_t)((sign << 15) | ((unsigned)(e + bias) << mbits) | frac);
+}
+
+/*
+ * The activation's value for one element (double arithmetic):
+ *   SwiGLU:    up * silu(gate), silu(g) = g / (1 + e^-g);
+ *   GELU_TANH: x/2 * (1 + tanh(u)), u = sqrt(2/pi) * (x + 0.044715 x^3),
+ *              x = v, evaluated as x / (1 + e^-2u): the same function
+ *              ((1 + tanh u) / 2 = 1 / (1 + e^-2u)) without the cancellation
+ *              of 1 + tanh(u) for large negative x.
+ * For GELU_TANH the second argument is ignored.
+ */
+double oracle_act_value(double v, double up, int act)
+{
+    if (act == ORACLE_ACT_SWIGLU)
+        return up * (v / (1.0 + exp(-v)));
+    const double u = sqrt(2.0 / M_PI) * (v + 0.044715 * v * v * v);
+    return v / (1.0 + exp(-2.0 * u));
+}
+
+/*
+ * x: [m][ldx] 16-bit values of dtype x_dtype.  SwiGLU rows hold [up | gate],
+ * up in columns 0..k-1 and gate in columns k..2k-1 (ldx >= 2k); GELU rows
+ * hold k values.  a: [m][k] bit patterns of the activated input, each value
+ * rounded once to x_dtype.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_activate(const uint16_t *x, int x_dtype, int act, int64_t m, int64_t k, int64_t ldx,
+                    uint16_t *a)
+{
+    if (k <= 0 || m < 0 || (x_dtype != ORACLE_BF16 && x_dtype != ORACLE_F16))
+        return -1;
+    if (act != ORACLE_ACT_SWIGLU && act != ORACLE_ACT_GELU_TANH)
+        return -1;
+    if (ldx < (act == ORACLE_ACT_SWIGLU ? 2 * k : k))
+        return -1;
+    if (fegetround() != FE_TONEAREST)
+        fesetround(FE_TONEAREST);
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < k; ++j) {
+            double v;
+            if (act == ORACLE_ACT_SWIGLU) {
+                double up = decode16(x[i * ldx + j], x_dtype);
+                double gate = decode16(x[i * ldx + k + j], x_dtype);
+                v = oracle_act_value(gate, up, act);
+            } else {
+                v = oracle_act_value(decode16(x[i * ldx + j], x_dtype), 0.0, act);
+            }
+            a[i * k + j] = oracle_round16(v, x_dtype);
+        }
     return 0;
 }
 

@@ -66,3 +66,24 @@ def argmin_code(w: Fraction, s: Fraction, lo: int = -8, hi: int = 7) -> int:
         if best is None or d < best[0] or (d == best[0] and q % 2 == 0):
             best = (d, q)
     return best[1]
+
+
+def round_to_16(r: Fraction, fmt: str) -> float:
+    """Correctly rounded (nearest-even) value of an exact rational in the
+    16-bit format ``fmt`` ("bf16": 8 significant bits, normal from 2^-126;
+    "f16": 11 significant bits, normal from 2^-14).  Results whose magnitude
+    reaches 2^(emax+1) after rounding are returned as +-inf."""
+    p, emin, emax = (8, -126, 127) if fmt == "bf16" else (11, -14, 15)
+    if r == 0:
+        return 0.0
+    sign = -1.0 if r < 0 else 1.0
+    a = abs(r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp_exp = max(e, emin) - (p - 1)
+    n = round_half_even(a / (Fraction(2) ** ulp_exp))
+    v = Fraction(n) * Fraction(2) ** ulp_exp
+    if v >= Fraction(2) ** (emax + 1):
+        return sign * float("inf")
+    return sign * float(v)

@@ -13,10 +13,14 @@ What each pin checks against:
   * closed forms: identity-like weights give y = c*x exactly, and integer
     weights and activations give an exact integer matrix product;
   * a library routine: numpy's float64 matmul on the dequantized weights;
-  * numpy/torch decoders for every 16-bit pattern.
+  * numpy/torch decoders for every 16-bit pattern;
+  * the fused activations: torch's float64 silu and tanh-GELU (library
+    routines), their odd-part identity, and exact rational rounding of the
+    activated value to bf16/fp16 (also against torch/numpy FP32 conversions).
 """
 from __future__ import annotations
 
+import ctypes
 import os
 from fractions import Fraction
 
@@ -227,6 +231,111 @@ def pin_matches_library_matmul(lib, seed=4):
     assert np.all(np.abs(y - want) <= bound)
 
 
+def _decode(bits: int, tag: int) -> float:
+    arr = np.array([bits], dtype=np.uint16)
+    if tag == oracle.F16:
+        return float(arr.view(np.float16)[0])
+    return float(torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)[0])
+
+
+def pin_round16_exact(lib, seed=21):
+    """Rounding a double to bf16/fp16 equals the exact rational nearest-even
+    rounding (tests/exact.py), over random magnitudes from the subnormal range
+    to overflow, exact ties, and the edges of both formats."""
+    rng = np.random.default_rng(seed)
+    vals = list(rng.standard_normal(400) * np.exp2(rng.integers(-150, 130, 400)))
+    vals += [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 65536.0, 2.0 ** -24, 2.0 ** -25,
+             3 * 2.0 ** -26, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8,
+             1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 3.3895313892515355e38, 3.4e38, -1e-30]
+    for tag, fmt in ((oracle.BF16, "bf16"), (oracle.F16, "f16")):
+        for v in vals:
+            got = _decode(lib.oracle_round16(float(v), tag), tag)
+            want = exact.round_to_16(Fraction(float(v)), fmt)
+            assert got == want and np.signbit(got) == np.signbit(v), (fmt, v, got, want)
+
+
+def pin_round16_matches_fp32_conversion(lib, seed=22):
+    """For every binary32 value (random bit patterns) the rounding equals the
+    libraries' own single-rounding conversions: torch float32 -> bfloat16 and
+    numpy float32 -> float16."""
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 2 ** 32, 4000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    want_bf = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    with np.errstate(over="ignore"):
+        want_h = f.astype(np.float16).view(np.uint16)
+    for i, v in enumerate(f):
+        assert lib.oracle_round16(float(v), oracle.BF16) == want_bf[i], (float(v), hex(want_bf[i]))
+        assert lib.oracle_round16(float(v), oracle.F16) == want_h[i], (float(v), hex(want_h[i]))
+
+
+def pin_activation_library(lib):
+    """The activations agree with torch's float64 silu and tanh-approximate GELU
+    on a grid from -40 to 40 (library routines), to 1e-14 relative plus
+    1e-15 |x| absolute (torch evaluates 1 + tanh(u), which cancels for large
+    negative x)."""
+    grid = np.concatenate([np.linspace(-40, 40, 801), [0.0, 1e-8, -1e-8, 0.5, -3.25, 6.0]])
+    t = torch.from_numpy(grid)
+    silu = torch.nn.functional.silu(t).numpy()
+    gelu = torch.nn.functional.gelu(t, approximate="tanh").numpy()
+    for i, v in enumerate(grid):
+        for up in (1.0, -2.5):
+            got = lib.oracle_act_value(float(v), up, oracle.ACT_SWIGLU)
+            assert abs(got - up * silu[i]) <= 1e-14 * abs(up * silu[i]) + 1e-15 * abs(up * v), (v, up, got)
+        got = lib.oracle_act_value(float(v), 0.0, oracle.ACT_GELU_TANH)
+        assert abs(got - gelu[i]) <= 1e-14 * abs(gelu[i]) + 1e-15 * abs(v), (v, got, gelu[i])
+
+
+def pin_activation_odd_part(lib):
+    """Both activations have odd part x/2 (their gates are logistic-type): silu(x) -
+    silu(-x) = x and gelu(x) - gelu(-x) = x; silu(0) = gelu(0) = 0."""
+    for v in (0.25, 1.0, 2.75, 7.5, 19.0):
+        s = lib.oracle_act_value(v, 1.0, oracle.ACT_SWIGLU) - lib.oracle_act_value(-v, 1.0, oracle.ACT_SWIGLU)
+        g = lib.oracle_act_value(v, 0.0, oracle.ACT_GELU_TANH) - lib.oracle_act_value(-v, 0.0, oracle.ACT_GELU_TANH)
+        assert abs(s - v) <= 4e-16 * v and abs(g - v) <= 4e-16 * v, (v, s, g)
+    assert lib.oracle_act_value(0.0, 3.0, oracle.ACT_SWIGLU) == 0.0
+    assert lib.oracle_act_value(0.0, 0.0, oracle.ACT_GELU_TANH) == 0.0
+
+
+def pin_activate_rows(lib, seed=23):
+    """The activated input takes up from the first half of a SwiGLU row and
+    gate from the second, reads GELU rows in place, honours the row stride,
+    and rounds each value once: equal to torch's float64 activation followed
+    by the exact rounding, element by element."""
+    rng = np.random.default_rng(seed)
+    m, k = 3, 256
+    for tag, tdt, fmt in ((oracle.BF16, torch.bfloat16, "bf16"), (oracle.F16, torch.float16, "f16")):
+        x = torch.from_numpy((rng.standard_normal((m, 2 * k + 8)) * 3).astype(np.float32)).to(tdt)
+        x[0, :4] = torch.tensor([3.0, -2.0, 0.5, 0.0], dtype=tdt)          # up values
+        x[0, k:k + 4] = torch.tensor([30.0, 0.0, -30.0, 5.0], dtype=tdt)   # gate values
+        xb = x.view(torch.int16).numpy().view(np.uint16)
+        xd = x.to(torch.float64)
+        up, gate = xd[:, :k], xd[:, k:2 * k]
+        want_sw = (up * torch.nn.functional.silu(gate)).numpy()
+        got = oracle.activate(xb[:, :2 * k], tag, oracle.ACT_SWIGLU, lib=lib)
+        for i in range(m):
+            for j in range(k):
+                assert _decode(got[i, j], tag) == exact.round_to_16(Fraction(float(want_sw[i, j])), fmt), (i, j)
+        # silu(30) = 30 (1 - 9e-14): up 3 with gate 30 gives 90 after rounding
+        # (swapped halves would give 30 silu(3) = 85.7); gate 0 gives an exact zero
+        assert _decode(got[0, 0], tag) == 90.0 and _decode(got[0, 1], tag) == 0.0
+        # GELU inputs within [-3, 3], where torch's 1 + tanh(u) is accurate
+        xg = x[:, :k].clamp(-3.0, 3.0)
+        want_ge = torch.nn.functional.gelu(xg.to(torch.float64), approximate="tanh").numpy()
+        got = oracle.activate(xg.view(torch.int16).numpy().view(np.uint16), tag, oracle.ACT_GELU_TANH, lib=lib)
+        for i in range(m):
+            for j in range(k):
+                assert _decode(got[i, j], tag) == exact.round_to_16(Fraction(float(want_ge[i, j])), fmt), (i, j)
+        # a row stride wider than the row: the C entry point with ldx = 2k + 8
+        out = np.empty((m, k), dtype=np.uint16)
+        xs = np.ascontiguousarray(xb)
+        rc = lib.oracle_activate(xs.ctypes.data_as(ctypes.c_void_p), tag, oracle.ACT_SWIGLU, m, k, 2 * k + 8,
+                                 out.ctypes.data_as(ctypes.c_void_p))
+        assert rc == 0
+        assert np.array_equal(out, oracle.activate(xb[:, :2 * k], tag, oracle.ACT_SWIGLU, lib=lib))
+
+
 ALL_PINS = [
     pin_hand_worked_groups,
     pin_negative_zero_group,
@@ -237,4 +346,9 @@ ALL_PINS = [
     pin_identity_like,
     pin_exact_integer_gemm,
     pin_matches_library_matmul,
+    pin_round16_exact,
+    pin_round16_matches_fp32_conversion,
+    pin_activation_library,
+    pin_activation_odd_part,
+    pin_activate_rows,
 ]

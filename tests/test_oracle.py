@@ -87,6 +87,21 @@ MUTANTS = [
     ("dequant drops the scale", "w_hat[row * k + kk] = (double)q[row * k + kk] * (double)s[row * groups + kk / ORACLE_GROUP];",
      "w_hat[row * k + kk] = (double)q[row * k + kk];"),
     ("x row stride ignored", "double xv = decode16(x[i * ldx + kk], x_dtype);", "double xv = decode16(x[kk], x_dtype);"),
+    ("swiglu halves swapped", "double up = decode16(x[i * ldx + j], x_dtype);\n                double gate = decode16(x[i * ldx + k + j], x_dtype);",
+     "double up = decode16(x[i * ldx + k + j], x_dtype);\n                double gate = decode16(x[i * ldx + j], x_dtype);"),
+    ("swiglu row stride taken as 2k", "double up = decode16(x[i * ldx + j], x_dtype);", "double up = decode16(x[i * 2 * k + j], x_dtype);"),
+    ("sigmoid sign", "return up * (v / (1.0 + exp(-v)));", "return up * (v / (1.0 + exp(v)));"),
+    ("gelu cubic coefficient", "const double u = sqrt(2.0 / M_PI) * (v + 0.044715 * v * v * v);",
+     "const double u = sqrt(2.0 / M_PI) * (v + 0.04715 * v * v * v);"),
+    ("gelu scale sqrt(1/pi)", "const double u = sqrt(2.0 / M_PI) * (v + 0.044715 * v * v * v);",
+     "const double u = sqrt(1.0 / M_PI) * (v + 0.044715 * v * v * v);"),
+    ("gelu tanh argument not doubled", "return v / (1.0 + exp(-2.0 * u));", "return v / (1.0 + exp(-u));"),
+    ("round16 ties away from zero", "double units = nearbyint(ldexp(a, -q));", "double units = round(ldexp(a, -q));"),
+    ("round16 truncates", "double units = nearbyint(ldexp(a, -q));", "double units = trunc(ldexp(a, -q));"),
+    ("bf16 with 7 significant bits", "const int p = dtype == ORACLE_BF16 ? 8 : 11;", "const int p = dtype == ORACLE_BF16 ? 7 : 11;"),
+    ("fp16 normal range from 2^-15", "const int emin = dtype == ORACLE_BF16 ? -126 : -14;",
+     "const int emin = dtype == ORACLE_BF16 ? -126 : -15;"),
+    ("no overflow to infinity", "if (r >= ldexp(1.0, emax + 1))\n        return inf;", "if (0)\n        return inf;"),
 ]
 
 _RUNNER = r"""
