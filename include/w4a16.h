@@ -67,6 +67,20 @@ typedef enum {
     W4A16_PATH_GEMM = 4     /* large M: LDS-staged dequantized tiles into MFMA */
 } w4a16_path_t;
 
+/*
+ * Activation applied to a linear layer's input before the product
+ * ("Piper Kernels", section "ConvRot INT8": an activated linear takes
+ * activation_fn "swiglu", whose input rows are [up | gate] of twice the
+ * layer's in_features and give up * silu(gate), or "gelu_tanh", the
+ * tanh-approximate GELU of the input).  Evaluated in FP32 and rounded once to
+ * the activation dtype (nearest even) before it enters the product.
+ */
+typedef enum {
+    W4A16_ACT_NONE = 0,      /* y = x . W^T + b */
+    W4A16_ACT_SWIGLU = 1,    /* y = (up * silu(gate)) . W^T + b, x rows = [up | gate], silu(g) = g / (1 + e^-g) */
+    W4A16_ACT_GELU_TANH = 2  /* y = gelu(x) . W^T + b, gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))) */
+} w4a16_act_t;
+
 /* Group size along K: one FP32 scale per 128 consecutive weights of a row. */
 #define W4A16_GROUP 128
 
@@ -166,6 +180,36 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
                                       int64_t m, int64_t k, int64_t ldx, const void* packed,
                                       int64_t n, const void* bias, void* y, int64_t ldy,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes w4a16_linear_act needs (0 if none; 0 for an unknown act).
+ * Same header rules as w4a16_linear_workspace_bytes; with an activation the
+ * large-M path also keeps the activated input, m * k 16-bit values, there.
+ */
+size_t w4a16_linear_act_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k);
+
+/*
+ * y[m][n] = act(x)[m][k] . dequant(packed)^T + bias[n]: a linear layer with
+ * its input activation fused ("Piper Kernels", section "ConvRot INT8"; the
+ * down projection of an FFN).  The small- and mid-M paths apply the
+ * activation while they stage x (one launch); the large-M path materialises
+ * the activated input in the workspace first, with the same arithmetic.
+ *
+ *   act       W4A16_ACT_NONE (exactly w4a16_linear_with_path), SWIGLU or
+ *             GELU_TANH; anything else gives W4A16_EINVAL.
+ *   path      as for w4a16_linear_with_path (W4A16_PATH_AUTO: the library
+ *             chooses; the GEMM path then requires k <= 2^22 instead of ldx).
+ *   x         device, [m][ldx] of act_dtype, 16-byte aligned, ldx % 8 == 0;
+ *             SWIGLU: each row holds up in columns [0, k) and gate in
+ *             [k, 2k), ldx >= 2k; GELU_TANH / NONE: ldx >= k.
+ *   workspace >= w4a16_linear_act_workspace_bytes(act, m, n, k) bytes.
+ * Every other argument, the no-op cases, the overlap rules (y against all of
+ * x's rows) and the status codes are those of w4a16_linear.
+ */
+w4a16_status_t w4a16_linear_act(w4a16_act_t act, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                                int64_t m, int64_t k, int64_t ldx, const void* packed, int64_t n,
+                                const void* bias, void* y, int64_t ldy, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* The path w4a16_linear would take for these sizes (never W4A16_PATH_AUTO). */
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k);

@@ -129,7 +129,7 @@ def test_linear_rejects(lib):
     assert lin(lib, path=9) == B.EINVAL                           # unknown path
     assert lin(lib, m=0) == B.OK                                  # empty: no-op
     assert lin(lib, n=0, ldy=0) == B.OK
-    # a K beyond one workgroup's reach (256 groups at M=1) splits and needs a workspace
+    # a K beyond one workgroup's reach (32 groups) splits and needs a workspace
     gemv = int(w4.Path.GEMV)
     need = w4.workspace_bytes(1, 2048, 32768)
     assert lin(lib, m=1, k=32768, ldx=32768, n=2048, ldy=2048, y=A * 64, path=gemv) == B.EWORKSPACE
@@ -142,6 +142,40 @@ def test_linear_rejects(lib):
     big = (1 << 22) + 8
     assert lin(lib, m=256, k=128, ldx=big, n=16, y=A * 4096, path=int(w4.Path.GEMM)) == B.EUNSUPPORTED
     assert w4.choose_path(256, 16, (1 << 22) + 128) == w4.Path.SKINNY
+
+
+def lin_act(lib, fn, path=0, x=A, act=B.BF16, m=1, k=128, ldx=256, packed=A * 4, n=16, bias=None, y=A * 8,
+            ldy=16, ws=None, ws_bytes=0):
+    return lib.w4a16_linear_act(fn, path, x, act, m, k, ldx, packed, n, bias, y, ldy, ws, ws_bytes, None)
+
+
+def test_linear_act_rejects(lib):
+    sw, ge = int(w4.Act.SWIGLU), int(w4.Act.GELU_TANH)
+    assert lin_act(lib, 3) == B.EINVAL                             # unknown activation
+    assert lin_act(lib, -1) == B.EINVAL
+    assert lin_act(lib, sw, ldx=128) == B.EINVAL                   # [up | gate] needs ldx >= 2k
+    assert lin_act(lib, ge, ldx=120) == B.EINVAL                   # ldx < k
+    assert lin_act(lib, sw, act=B.F32) == B.EUNSUPPORTED
+    assert lin_act(lib, sw, path=9) == B.EINVAL
+    # y inside the gate half of x's row span overlaps x
+    assert lin_act(lib, sw, m=2, y=A + 2 * 200) == B.EINVAL
+    assert lin_act(lib, sw, m=0) == B.OK                            # empty: no-op
+    assert lin_act(lib, sw, n=0, ldy=0) == B.OK
+    # the large-M path materialises the activated input in the workspace
+    gemm = int(w4.Path.GEMM)
+    need = w4.workspace_bytes(256, 16, 128, w4.Act.SWIGLU)
+    assert need >= 256 * 128 * 2
+    assert w4.workspace_bytes(256, 16, 128) == 0
+    assert lin_act(lib, sw, path=gemm, m=256, y=A * 16) == B.EWORKSPACE
+    assert lin_act(lib, sw, path=gemm, m=256, y=A * 16, ws=A * 32, ws_bytes=need - 16) == B.EWORKSPACE
+    assert lin_act(lib, sw, path=gemm, m=256, y=A * 16, ws=A, ws_bytes=need) == B.EINVAL  # workspace overlaps x
+    # with an activation the GEMM's row-stride limit applies to k, not ldx
+    big = (1 << 22) + 8
+    assert lin_act(lib, ge, path=gemm, m=256, k=(1 << 22) + 128, ldx=(1 << 22) + 128, n=16,
+                   y=A * 8192) == B.EUNSUPPORTED
+    assert lin_act(lib, ge, path=gemm, m=256, k=128, ldx=big, y=A * 8192, ws=None) == B.EWORKSPACE
+    assert lib.w4a16_linear_act_workspace_bytes(5, 16, 16, 128) == 0
+    assert lib.w4a16_linear_act_workspace_bytes(int(w4.Act.NONE), 1, 2048, 16384) == w4.workspace_bytes(1, 2048, 16384)
 
 
 def test_binding_rejects_cpu_tensors():

@@ -8,11 +8,13 @@ behind the C ABI of ``include/w4a16.h``.
     codes, scales = quantize(w)          # load time, w [n, k] on the GPU
     packed = pack(codes, scales)         # load time
     y = linear(x, packed, n, bias)       # every forward step
+    y = linear(up_gate, packed_down, n, act=Act.SWIGLU)   # activation fused into the input
 """
 import torch  # noqa: F401  (load torch's HIP runtime before the library)
 
 from ._binding import (  # noqa: F401
     GROUP,
+    Act,
     Path,
     W4A16Error,
     choose_path,

@@ -29,6 +29,13 @@ class Path(enum.IntEnum):
     GEMM = 4
 
 
+class Act(enum.IntEnum):
+    """Activation fused into a linear's input (w4a16_act_t)."""
+    NONE = 0
+    SWIGLU = 1      # input rows [up | gate] (2k values) -> up * silu(gate)
+    GELU_TANH = 2   # tanh-approximate GELU of the input
+
+
 class W4A16Error(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -55,6 +62,10 @@ def _declare(lib):
     lib.w4a16_linear.restype = i32
     lib.w4a16_linear_with_path.argtypes = [i32, vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, sz, vp]
     lib.w4a16_linear_with_path.restype = i32
+    lib.w4a16_linear_act_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.w4a16_linear_act_workspace_bytes.restype = sz
+    lib.w4a16_linear_act.argtypes = [i32, i32, vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, sz, vp]
+    lib.w4a16_linear_act.restype = i32
     lib.w4a16_linear_choose_path.argtypes = [i64, i64, i64]
     lib.w4a16_linear_choose_path.restype = i32
     lib.w4a16_status_string.argtypes = [i32]
@@ -93,7 +104,7 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _act_tag(dtype) -> int:
+def _act_tag(dtype) -> int:  # activation dtype tag
     if dtype == torch.bfloat16:
         return BF16
     if dtype == torch.float16:
@@ -120,8 +131,10 @@ def packed_bytes(n: int, k: int) -> int:
     return int(lib().w4a16_packed_bytes(n, k))
 
 
-def workspace_bytes(m: int, n: int, k: int) -> int:
-    return int(lib().w4a16_linear_workspace_bytes(m, n, k))
+def workspace_bytes(m: int, n: int, k: int, act: Act = Act.NONE) -> int:
+    if act == Act.NONE:
+        return int(lib().w4a16_linear_workspace_bytes(m, n, k))
+    return int(lib().w4a16_linear_act_workspace_bytes(int(act), m, n, k))
 
 
 def choose_path(m: int, n: int, k: int) -> Path:
@@ -185,15 +198,20 @@ def workspace_for(device, stream_handle: int, nbytes: int) -> torch.Tensor | Non
 
 def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | None = None,
            out: torch.Tensor | None = None, path: Path = Path.AUTO,
-           workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y = x . dequant(packed)^T + bias for x [..., k] (bf16/f16) -> y [..., n] (x's dtype)."""
+           workspace: torch.Tensor | None = None, act: Act = Act.NONE) -> torch.Tensor:
+    """y = act(x) . dequant(packed)^T + bias for x [..., k] (bf16/f16) -> y [..., n]
+    (x's dtype).  With ``act=Act.SWIGLU`` the rows of x are [up | gate], 2k values."""
     _require_cuda(x, packed, bias, out)
     if x.requires_grad or (bias is not None and bias.requires_grad):
         raise ValueError("inference only: autograd inputs are not supported")
-    act = _act_tag(x.dtype)
-    k = x.shape[-1]
+    act = Act(act)
+    dt = _act_tag(x.dtype)
+    width = x.shape[-1]
+    if act == Act.SWIGLU and width % 2 != 0:
+        raise ValueError("SwiGLU input rows hold [up | gate]: an even number of columns")
+    k = width // 2 if act == Act.SWIGLU else width
     lead = x.shape[:-1]
-    x2 = x.reshape(-1, k)
+    x2 = x.reshape(-1, width)
     if x2.stride(-1) != 1:
         x2 = x2.contiguous()
     m = x2.shape[0]
@@ -209,11 +227,15 @@ def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | N
     if y2 is None:
         raise ValueError("out must be contiguous")
     stream = _stream(x.device)
-    need = workspace_bytes(m, n, k)
+    need = workspace_bytes(m, n, k, act)
     if workspace is None:
         workspace = workspace_for(x.device, stream.value, need)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().w4a16_linear_with_path(int(path), _ptr(x2), act, m, k, x2.stride(0), _ptr(packed), n,
-                                      _ptr(bias), _ptr(y2), n, _ptr(workspace), ws_bytes, stream)
-    _check(st, "w4a16_linear")
+    if act == Act.NONE:
+        st = lib().w4a16_linear_with_path(int(path), _ptr(x2), dt, m, k, x2.stride(0), _ptr(packed), n,
+                                          _ptr(bias), _ptr(y2), n, _ptr(workspace), ws_bytes, stream)
+    else:
+        st = lib().w4a16_linear_act(int(act), int(path), _ptr(x2), dt, m, k, x2.stride(0), _ptr(packed), n,
+                                    _ptr(bias), _ptr(y2), n, _ptr(workspace), ws_bytes, stream)
+    _check(st, "w4a16_linear_act" if act != Act.NONE else "w4a16_linear")
     return out

@@ -119,46 +119,67 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     return W4A16_PATH_GEMM;
 }
 
-size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+}  // extern "C"
+
+namespace {
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace of one path with an activation: the large-M path materialises
+// the activated input [m][k] after its own workspace.
+size_t act_path_workspace(int act_fn, w4a16_path_t path, int64_t m, int64_t n, int64_t k) {
+    const size_t base = path_workspace(path, m, n, k);
+    if (act_fn == kActFnNone || path != W4A16_PATH_GEMM) return base;
+    return round_up(base, 256) + size_t(m) * size_t(k) * 2;
+}
+
+size_t act_workspace_bytes(int act_fn, int64_t m, int64_t n, int64_t k) {
     if (m <= 0 || !valid_nk(n, k) || n == 0 || m > kMaxDim) return 0;
     size_t best = 0;
     const w4a16_path_t paths[4] = {W4A16_PATH_GEMV, W4A16_PATH_MGEMV, W4A16_PATH_SKINNY, W4A16_PATH_GEMM};
     for (w4a16_path_t p : paths) {
-        const size_t b = path_workspace(p, m, n, k);
+        const size_t b = act_path_workspace(act_fn, p, m, n, k);
         best = b > best ? b : best;
     }
     return best;
 }
 
-w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
-                                      int64_t m, int64_t k, int64_t ldx, const void* packed,
-                                      int64_t n, const void* bias, void* y, int64_t ldy,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+// y = act(x) . dequant(packed)^T + bias on one kernel path (act_fn: ActFn).
+w4a16_status_t linear_impl(int act_fn, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype, int64_t m,
+                           int64_t k, int64_t ldx, const void* packed, int64_t n, const void* bias, void* y,
+                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
     if (act_dtype != W4A16_BF16 && act_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
     if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MGEMV &&
         path != W4A16_PATH_SKINNY && path != W4A16_PATH_GEMM)
         return W4A16_EINVAL;
     if (!valid_nk(n, k) || m < 0 || m > kMaxDim) return W4A16_EINVAL;
-    if (ldx < k || ldx > kMaxDim || ldx % 8 != 0 || ldy < n || ldy > kMaxDim) return W4A16_EINVAL;
+    const int64_t xcols = act_fn == kActFnSwiglu ? 2 * k : k;  // SwiGLU rows hold [up | gate]
+    if (ldx < xcols || ldx > kMaxDim || ldx % 8 != 0 || ldy < n || ldy > kMaxDim) return W4A16_EINVAL;
     if (m == 0 || n == 0) return W4A16_OK;
     if (!x || !packed || !y) return W4A16_EINVAL;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2) || (bias && !aligned(bias, 2)))
         return W4A16_EINVAL;
+    // the GEMM reads its x tiles with 32-bit offsets: the row stride it sees
+    // is ldx, or k for the materialised activation
+    const int64_t gemm_ld = act_fn == kActFnNone ? ldx : k;
     if (path == W4A16_PATH_AUTO) {
         path = w4a16_linear_choose_path(m, n, k);
-        if (path == W4A16_PATH_GEMM && ldx > kGemmMaxLd) path = W4A16_PATH_SKINNY;
+        if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) path = W4A16_PATH_SKINNY;
     }
-    if (path == W4A16_PATH_GEMM && ldx > kGemmMaxLd) return W4A16_EUNSUPPORTED;
+    if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) return W4A16_EUNSUPPORTED;
 
-    const size_t xbytes = span_bytes(m, k, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
+    const size_t xbytes = span_bytes(m, xcols, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
                  pbytes = w4a16_packed_bytes(n, k), bbytes = bias ? size_t(n) * 2 : 0;
-    const size_t need = path_workspace(path, m, n, k);
+    const size_t need = act_path_workspace(act_fn, path, m, n, k);
     if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, packed, pbytes) ||
         overlap(y, ybytes, bias, bbytes) || overlap(y, ybytes, workspace, need))
         return W4A16_EINVAL;
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return W4A16_EWORKSPACE;
         if (!aligned(workspace, 16)) return W4A16_EINVAL;
+        if (overlap(workspace, need, x, xbytes) || overlap(workspace, need, packed, pbytes) ||
+            overlap(workspace, need, bias, bbytes))
+            return W4A16_EINVAL;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int act = act_dtype == W4A16_BF16 ? kActBf16 : kActF16;
@@ -168,7 +189,7 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
         // row blocks of at most 4; launches on one stream share the workspace
         for (int64_t r0 = 0; r0 < m; r0 += 4) {
             const int64_t mm = m - r0 < 4 ? m - r0 : 4;
-            const hipError_t e = launch_gemv(xp + r0 * ldx, act, mm, k, ldx, packed, n, bias,
+            const hipError_t e = launch_gemv(xp + r0 * ldx, act, act_fn, mm, k, ldx, packed, n, bias,
                                              yp + r0 * ldy, ldy, workspace, s);
             if (e != hipSuccess) return W4A16_EHIP;
         }
@@ -177,22 +198,58 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
     if (path == W4A16_PATH_MGEMV) {
         for (int64_t r0 = 0; r0 < m; r0 += 16) {
             const int64_t mm = m - r0 < 16 ? m - r0 : 16;
-            const hipError_t e = launch_mgemv(xp + r0 * ldx, act, mm, k, ldx, packed, n, bias,
+            const hipError_t e = launch_mgemv(xp + r0 * ldx, act, act_fn, mm, k, ldx, packed, n, bias,
                                               yp + r0 * ldy, ldy, workspace, s);
             if (e != hipSuccess) return W4A16_EHIP;
         }
         return W4A16_OK;
     }
-    if (path == W4A16_PATH_GEMM)
-        return from_hip(launch_gemm(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
-    return from_hip(launch_skinny(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
+    if (path == W4A16_PATH_GEMM) {
+        if (act_fn == kActFnNone)
+            return from_hip(launch_gemm(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
+        void* xa = static_cast<uint8_t*>(workspace) + round_up(path_workspace(path, m, n, k), 256);
+        const hipError_t e = launch_activate(x, act, act_fn, m, k, ldx, xa, s);
+        if (e != hipSuccess) return W4A16_EHIP;
+        return from_hip(launch_gemm(xa, act, m, k, k, packed, n, bias, y, ldy, workspace, s));
+    }
+    return from_hip(launch_skinny(x, act, act_fn, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    return act_workspace_bytes(kActFnNone, m, n, k);
+}
+
+size_t w4a16_linear_act_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k) {
+    if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return 0;
+    return act_workspace_bytes(int(act), m, n, k);
+}
+
+w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                                      int64_t m, int64_t k, int64_t ldx, const void* packed,
+                                      int64_t n, const void* bias, void* y, int64_t ldy,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    return linear_impl(kActFnNone, path, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
+                       workspace_bytes, stream);
 }
 
 w4a16_status_t w4a16_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, int64_t k, int64_t ldx,
                             const void* packed, int64_t n, const void* bias, void* y, int64_t ldy,
                             void* workspace, size_t workspace_bytes, void* stream) {
-    return w4a16_linear_with_path(W4A16_PATH_AUTO, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy,
-                                  workspace, workspace_bytes, stream);
+    return linear_impl(kActFnNone, W4A16_PATH_AUTO, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy,
+                       workspace, workspace_bytes, stream);
+}
+
+w4a16_status_t w4a16_linear_act(w4a16_act_t act, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                                int64_t m, int64_t k, int64_t ldx, const void* packed, int64_t n,
+                                const void* bias, void* y, int64_t ldy, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return W4A16_EINVAL;
+    return linear_impl(int(act), path, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

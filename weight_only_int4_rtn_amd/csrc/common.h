@@ -113,6 +113,44 @@ __device__ inline uint32_t magic_pair(uint32_t word, int i) {
     return and_or(i == 0 ? word : word >> (4 * i), 0x000F000Fu, magic);
 }
 
+// ---------------------------------------------------------------------------
+// Activations fused into a layer's input ("Piper Kernels", section "ConvRot
+// INT8"): SwiGLU rows hold [up | gate] (2K values) and give up * silu(gate);
+// GELU rows give the tanh-approximate GELU.  Evaluated in FP32 and rounded
+// once to the activation dtype (nearest even).  (1 + tanh u) / 2 is written
+// as 1 / (1 + e^-2u): the same function without the cancellation of
+// 1 + tanh(u) for large negative inputs.
+// ---------------------------------------------------------------------------
+enum ActFn { kActFnNone = 0, kActFnSwiglu = 1, kActFnGeluTanh = 2 };
+
+__device__ inline float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ inline float gelu_tanh_f32(float x) {
+    const float u = 0.7978845608028654f * fmaf(0.044715f * x, x * x, x);  // sqrt(2/pi) (x + 0.044715 x^3)
+    return x / (1.0f + __expf(-2.0f * u));
+}
+
+// Eight 16-bit inputs (and, for SwiGLU, the eight matching gate values) ->
+// eight activated 16-bit values, in place order.
+template <int ACT, int AF>
+__device__ inline uint4 activate8(uint4 v, uint4 g) {
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w}, gt[4] = {g.x, g.y, g.z, g.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float lo = to_f32<ACT>(uint16_t(in[i] & 0xFFFFu)), hi = to_f32<ACT>(uint16_t(in[i] >> 16));
+        if constexpr (AF == kActFnSwiglu) {
+            lo *= silu_f32(to_f32<ACT>(uint16_t(gt[i] & 0xFFFFu)));
+            hi *= silu_f32(to_f32<ACT>(uint16_t(gt[i] >> 16)));
+        } else {
+            lo = gelu_tanh_f32(lo);
+            hi = gelu_tanh_f32(hi);
+        }
+        out[i] = uint32_t(from_f32<ACT>(lo)) | (uint32_t(from_f32<ACT>(hi)) << 16);
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // 16-byte load of streamed data (read once: nontemporal, so it does not
 // displace data the kernel reuses from the caches).
 __device__ inline uint4 load_stream16(const uint8_t* p) {

@@ -52,7 +52,9 @@ struct GemvArgs {
 
 constexpr int kGemvChunks = 8;  // chunks per wave, all loaded up front
 
-template <int M, int ACT, int WAVES, int CPW>
+// AF: activation fused into the x staging (ActFn); for SwiGLU the x rows
+// hold [up | gate] and the gate values sit k columns after the up values.
+template <int M, int ACT, int WAVES, int CPW, int AF>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     constexpr int THREADS = 64 * WAVES;
     // 16-byte x loads per thread while staging: the slice is M rows of at
@@ -89,13 +91,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     const int per_row = klen / 8;  // multiple of 16
     const int total = M * per_row;
     uint4 xv[kXRegs];
+    uint4 xgate[AF == kActFnSwiglu ? kXRegs : 1];
 #pragma unroll
     for (int j = 0; j < kXRegs; ++j) {
         if (j * THREADS >= total) break;
         const int i = j * THREADS + tid;
         const int ic = i < total ? i : total - 1;
         const int m = ic / per_row, c = ic - m * per_row;
-        xv[j] = *reinterpret_cast<const uint4*>(a.x + m * a.ldx + g0 * kGroup + c * 8);
+        const uint16_t* src = a.x + m * a.ldx + g0 * kGroup + c * 8;
+        xv[j] = *reinterpret_cast<const uint4*>(src);
+        if constexpr (AF == kActFnSwiglu) xgate[j] = *reinterpret_cast<const uint4*>(src + a.k);
     }
     // keep the compiler from hoisting the weight loads above the x loads
     __builtin_amdgcn_sched_barrier(0);
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         const int i = j * THREADS + tid;
         const bool on = i < total;
         const int m = on ? i / per_row : 0, c = on ? i - m * per_row : 0;
+        if constexpr (AF != kActFnNone) xv[j] = activate8<ACT, AF>(xv[j], xgate[AF == kActFnSwiglu ? j : 0]);
         if (on) *reinterpret_cast<uint4*>(xs + m * klen + c * 8) = xv[j];
         if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
         const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
@@ -244,15 +250,15 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-template <int M, int ACT>
+template <int M, int ACT, int AF>
 static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k);
     const dim3 grid(unsigned(L.tiles * p.splits)), block(256);
     switch (p.cpw) {
-        case 1: gemv_kernel<M, ACT, 4, 1><<<grid, block, p.lds, stream>>>(a); break;
-        case 2: gemv_kernel<M, ACT, 4, 2><<<grid, block, p.lds, stream>>>(a); break;
-        case 4: gemv_kernel<M, ACT, 4, 4><<<grid, block, p.lds, stream>>>(a); break;
-        default: gemv_kernel<M, ACT, 4, 8><<<grid, block, p.lds, stream>>>(a); break;
+        case 1: gemv_kernel<M, ACT, 4, 1, AF><<<grid, block, p.lds, stream>>>(a); break;
+        case 2: gemv_kernel<M, ACT, 4, 2, AF><<<grid, block, p.lds, stream>>>(a); break;
+        case 4: gemv_kernel<M, ACT, 4, 4, AF><<<grid, block, p.lds, stream>>>(a); break;
+        default: gemv_kernel<M, ACT, 4, 8, AF><<<grid, block, p.lds, stream>>>(a); break;
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.exchange) return e;
@@ -260,8 +266,17 @@ static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s
                                 stream);
 }
 
-hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                       int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+template <int M, int ACT>
+static hipError_t launch_af(const GemvArgs& a, const GemvPlan& p, int act_fn, hipStream_t stream) {
+    switch (act_fn) {
+        case kActFnSwiglu: return launch_one<M, ACT, kActFnSwiglu>(a, p, stream);
+        case kActFnGeluTanh: return launch_one<M, ACT, kActFnGeluTanh>(a, p, stream);
+        default: return launch_one<M, ACT, kActFnNone>(a, p, stream);
+    }
+}
+
+hipError_t launch_gemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+                       const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream) {
     const GemvPlan p = plan_gemv(m, n, k);
     GemvArgs a;
@@ -280,10 +295,10 @@ hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx
     a.exchange = p.exchange;
     const bool bf = act == kActBf16;
     switch (m) {
-        case 1: return bf ? launch_one<1, kActBf16>(a, p, stream) : launch_one<1, kActF16>(a, p, stream);
-        case 2: return bf ? launch_one<2, kActBf16>(a, p, stream) : launch_one<2, kActF16>(a, p, stream);
-        case 3: return bf ? launch_one<3, kActBf16>(a, p, stream) : launch_one<3, kActF16>(a, p, stream);
-        default: return bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream);
+        case 1: return bf ? launch_af<1, kActBf16>(a, p, act_fn, stream) : launch_af<1, kActF16>(a, p, act_fn, stream);
+        case 2: return bf ? launch_af<2, kActBf16>(a, p, act_fn, stream) : launch_af<2, kActF16>(a, p, act_fn, stream);
+        case 3: return bf ? launch_af<3, kActBf16>(a, p, act_fn, stream) : launch_af<3, kActF16>(a, p, act_fn, stream);
+        default: return bf ? launch_af<4, kActBf16>(a, p, act_fn, stream) : launch_af<4, kActF16>(a, p, act_fn, stream);
     }
 }
 

@@ -58,17 +58,22 @@ hipError_t launch_splitk_reduce(const float* partials, int splits, int64_t m, in
                                 const uint16_t* bias, uint16_t* y, int64_t ldy, int act,
                                 hipStream_t stream);
 
+// act_fn (ActFn, common.h): activation fused into the x staging; SwiGLU x
+// rows hold [up | gate], 2k values.
 // m <= 4 per launch (the caller splits larger m into row blocks).
-hipError_t launch_gemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                       int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+hipError_t launch_gemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+                       const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream);
 // m <= 16 per launch (the caller splits larger m into row blocks).
-hipError_t launch_mgemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+hipError_t launch_mgemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+                        const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                         hipStream_t stream);
-hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                         int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+hipError_t launch_skinny(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+                         const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                          hipStream_t stream);
+// The activated input [m][k] (row stride k) of x for the GEMM path.
+hipError_t launch_activate(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx, void* out,
+                           hipStream_t stream);
 hipError_t launch_gemm(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream);

@@ -55,8 +55,9 @@ __device__ inline f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
     }
 }
 
-// MMAX: rows of x staged (>= m, <= 16).
-template <int MMAX, int ACT, int CPW>
+// MMAX: rows of x staged (>= m, <= 16).  AF: activation fused into the x
+// staging (ActFn; SwiGLU gate values sit k columns after the up values).
+template <int MMAX, int ACT, int CPW, int AF>
 __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Layout L(a.n, a.k);
@@ -93,13 +94,16 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     const int per_row = klen / 8;
     const int total = m * per_row;
     uint4 xv[kXRegs];
+    uint4 xgate[AF == kActFnSwiglu ? kXRegs : 1];
 #pragma unroll
     for (int j = 0; j < kXRegs; ++j) {
         if (j * kMgThreads >= total) break;
         const int i = j * kMgThreads + tid;
         const int ic = i < total ? i : total - 1;
         const int row = ic / per_row, c = ic - row * per_row;
-        xv[j] = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + g0 * kGroup + c * 8);
+        const uint16_t* src = a.x + row * a.ldx + g0 * kGroup + c * 8;
+        xv[j] = *reinterpret_cast<const uint4*>(src);
+        if constexpr (AF == kActFnSwiglu) xgate[j] = *reinterpret_cast<const uint4*>(src + a.k);
     }
     // keep the compiler from hoisting the weight loads above the x loads
     __builtin_amdgcn_sched_barrier(0);
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
         const int i = j * kMgThreads + tid;
         const bool on = i < total;
         const int row = on ? i / per_row : 0, c = on ? i - row * per_row : 0;
+        if constexpr (AF != kActFnNone) xv[j] = activate8<ACT, AF>(xv[j], xgate[AF == kActFnSwiglu ? j : 0]);
         if (on) *reinterpret_cast<uint4*>(xs + row * xstride + c * 8) = xv[j];
         if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
         const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
@@ -231,15 +236,15 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-template <int MMAX, int ACT>
+template <int MMAX, int ACT, int AF>
 static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k);
     const dim3 grid(unsigned(L.tiles * p.splits)), block(kMgThreads);
     switch (p.cpw) {
-        case 1: mgemv_kernel<MMAX, ACT, 1><<<grid, block, p.lds, stream>>>(a); break;
-        case 2: mgemv_kernel<MMAX, ACT, 2><<<grid, block, p.lds, stream>>>(a); break;
-        case 4: mgemv_kernel<MMAX, ACT, 4><<<grid, block, p.lds, stream>>>(a); break;
-        default: mgemv_kernel<MMAX, ACT, 8><<<grid, block, p.lds, stream>>>(a); break;
+        case 1: mgemv_kernel<MMAX, ACT, 1, AF><<<grid, block, p.lds, stream>>>(a); break;
+        case 2: mgemv_kernel<MMAX, ACT, 2, AF><<<grid, block, p.lds, stream>>>(a); break;
+        case 4: mgemv_kernel<MMAX, ACT, 4, AF><<<grid, block, p.lds, stream>>>(a); break;
+        default: mgemv_kernel<MMAX, ACT, 8, AF><<<grid, block, p.lds, stream>>>(a); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.exchange) return e;
@@ -247,8 +252,17 @@ static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t
                                 ACT, stream);
 }
 
-hipError_t launch_mgemv(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+template <int MMAX, int ACT>
+static hipError_t launch_af(const MgemvArgs& a, const MgemvPlan& p, int act_fn, hipStream_t stream) {
+    switch (act_fn) {
+        case kActFnSwiglu: return launch_one<MMAX, ACT, kActFnSwiglu>(a, p, stream);
+        case kActFnGeluTanh: return launch_one<MMAX, ACT, kActFnGeluTanh>(a, p, stream);
+        default: return launch_one<MMAX, ACT, kActFnNone>(a, p, stream);
+    }
+}
+
+hipError_t launch_mgemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+                        const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                         hipStream_t stream) {
     const MgemvPlan p = plan_mgemv(m, n, k);
     MgemvArgs a;
@@ -268,9 +282,9 @@ hipError_t launch_mgemv(const void* x, int act, int64_t m, int64_t k, int64_t ld
     a.exchange = p.exchange;
     const bool bf = act == kActBf16;
     switch (p.mmax) {
-        case 4: return bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream);
-        case 8: return bf ? launch_one<8, kActBf16>(a, p, stream) : launch_one<8, kActF16>(a, p, stream);
-        default: return bf ? launch_one<16, kActBf16>(a, p, stream) : launch_one<16, kActF16>(a, p, stream);
+        case 4: return bf ? launch_af<4, kActBf16>(a, p, act_fn, stream) : launch_af<4, kActF16>(a, p, act_fn, stream);
+        case 8: return bf ? launch_af<8, kActBf16>(a, p, act_fn, stream) : launch_af<8, kActF16>(a, p, act_fn, stream);
+        default: return bf ? launch_af<16, kActBf16>(a, p, act_fn, stream) : launch_af<16, kActF16>(a, p, act_fn, stream);
     }
 }
 

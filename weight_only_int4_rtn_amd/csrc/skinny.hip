@@ -50,7 +50,9 @@ __device__ inline f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     }
 }
 
-template <int MB, int ACT>
+// AF: activation fused into the x staging (ActFn; SwiGLU gate values sit k
+// columns after the up values).
+template <int MB, int ACT, int AF>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     constexpr int BM = 16 * MB;
     __shared__ __align__(16) uint16_t xa[BM * kAStride];
@@ -89,8 +91,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
         for (int pass = 0; pass < BM / 16; ++pass) {
             const int row = pass * 16 + (tid >> 4), piece = tid & 15;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m0 + row < a.m)
-                v = *reinterpret_cast<const uint4*>(a.x + (m0 + row) * a.ldx + g * kGroup + piece * 8);
+            if (m0 + row < a.m) {
+                const uint16_t* src = a.x + (m0 + row) * a.ldx + g * kGroup + piece * 8;
+                v = *reinterpret_cast<const uint4*>(src);
+                if constexpr (AF == kActFnSwiglu)
+                    v = activate8<ACT, AF>(v, *reinterpret_cast<const uint4*>(src + a.k));
+                else if constexpr (AF == kActFnGeluTanh)
+                    v = activate8<ACT, AF>(v, v);
+            }
             *reinterpret_cast<uint4*>(xa + row * kAStride + piece * 8) = v;
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
             float s = 0.0f;
@@ -171,18 +179,27 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-template <int MB, int ACT>
+template <int MB, int ACT, int AF>
 static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
     dim3 grid(unsigned(p.tile_groups * p.splits), unsigned(p.mblocks));
-    skinny_kernel<MB, ACT><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+    skinny_kernel<MB, ACT, AF><<<grid, dim3(kSkThreads), 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_splitk_reduce(a.partials, p.splits, a.m, a.n, p.tile_groups * kSkCols, a.bias, a.y, a.ldy,
                                 ACT, stream);
 }
 
-hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                         int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+template <int MB, int ACT>
+static hipError_t launch_af(const SkinnyArgs& a, const SkinnyPlan& p, int act_fn, hipStream_t stream) {
+    switch (act_fn) {
+        case kActFnSwiglu: return launch_one<MB, ACT, kActFnSwiglu>(a, p, stream);
+        case kActFnGeluTanh: return launch_one<MB, ACT, kActFnGeluTanh>(a, p, stream);
+        default: return launch_one<MB, ACT, kActFnNone>(a, p, stream);
+    }
+}
+
+hipError_t launch_skinny(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+                         const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                          hipStream_t stream) {
     const SkinnyPlan p = plan_skinny(m, n, k);
     SkinnyArgs a;
@@ -201,10 +218,10 @@ hipError_t launch_skinny(const void* x, int act, int64_t m, int64_t k, int64_t l
     a.tile_groups = p.tile_groups;
     const bool bf = act == kActBf16;
     switch (p.mb) {
-        case 1: return bf ? launch_one<1, kActBf16>(a, p, stream) : launch_one<1, kActF16>(a, p, stream);
-        case 2: return bf ? launch_one<2, kActBf16>(a, p, stream) : launch_one<2, kActF16>(a, p, stream);
-        case 3: return bf ? launch_one<3, kActBf16>(a, p, stream) : launch_one<3, kActF16>(a, p, stream);
-        default: return bf ? launch_one<4, kActBf16>(a, p, stream) : launch_one<4, kActF16>(a, p, stream);
+        case 1: return bf ? launch_af<1, kActBf16>(a, p, act_fn, stream) : launch_af<1, kActF16>(a, p, act_fn, stream);
+        case 2: return bf ? launch_af<2, kActBf16>(a, p, act_fn, stream) : launch_af<2, kActF16>(a, p, act_fn, stream);
+        case 3: return bf ? launch_af<3, kActBf16>(a, p, act_fn, stream) : launch_af<3, kActF16>(a, p, act_fn, stream);
+        default: return bf ? launch_af<4, kActBf16>(a, p, act_fn, stream) : launch_af<4, kActF16>(a, p, act_fn, stream);
     }
 }
 
