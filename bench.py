@@ -198,6 +198,72 @@ def run_workload(cases, dev, steps, warmup, dominant):
     return out
 
 
+def ffn_block(act, m, hidden, inter, dtype, dev, replays=20):
+    """An FFN block (up or [up | gate] projection, then the down projection
+    with the activation fused into its input) against the same block with
+    the activation as separate torch kernels between two plain projections.
+    Weights rotate over a >= 1 GiB pool; each variant is a HIP graph of 8
+    consecutive blocks, timed with HIP events.  Returns us per block for both
+    and the fused block's algorithmic GB/s."""
+    import torch
+
+    import weight_only_int4_rtn_amd as w4
+    g = torch.Generator().manual_seed(1234)
+    width = 2 * inter if act == w4.Act.SWIGLU else inter
+    packs = []
+    for n, k in ((width, hidden), (hidden, inter)):
+        w = (torch.randn(n, k, generator=g) * 0.02).to(dev)
+        c, sc = w4.quantize(w)
+        packs.append(w4.pack(c, sc))
+        del w, c, sc
+    per = sum(p.numel() for p in packs)
+    copies = max(2, -(-POOL_BYTES // per))
+    pool = [packs] + [[p.clone() for p in packs] for _ in range(copies - 1)]
+    x = torch.randn(m, hidden, generator=g).to(dtype).to(dev)
+    bias = (torch.randn(hidden, generator=g) * 0.01).to(dtype).to(dev)
+    u = torch.empty(m, width, dtype=dtype, device=dev)
+    a = torch.empty(m, inter, dtype=dtype, device=dev)
+    y = torch.empty(m, hidden, dtype=dtype, device=dev)
+    ws = torch.zeros(max(16, w4.workspace_bytes(m, width, hidden), w4.workspace_bytes(m, hidden, inter, act)),
+                     dtype=torch.uint8, device=dev)
+
+    def fused(layer):
+        w4.linear(x, layer[0], width, out=u, workspace=ws)
+        w4.linear(u, layer[1], hidden, bias, out=y, workspace=ws, act=act)
+
+    def unfused(layer):
+        w4.linear(x, layer[0], width, out=u, workspace=ws)
+        if act == w4.Act.SWIGLU:
+            torch.mul(u[:, :inter], torch.nn.functional.silu(u[:, inter:]), out=a)
+        else:
+            a.copy_(torch.nn.functional.gelu(u, approximate="tanh"))
+        w4.linear(a, layer[1], hidden, bias, out=y, workspace=ws)
+
+    def timed(fn):
+        per_graph = 8
+        graphs = [capture(lambda f=first: [fn(pool[(f + i) % len(pool)]) for i in range(per_graph)])
+                  for first in range(0, len(pool), per_graph)]
+        for gr in graphs[:2]:
+            gr.replay()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(replays):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * per_graph)
+    us_fused = timed(fused)
+    us_unfused = timed(unfused)
+    alg = (width * hidden + hidden * inter) * (0.5 + 4 / 128) + 2 * m * (hidden + width + width + hidden) + 2 * hidden
+    del pool, packs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"us_fused": round(us_fused, 3), "us_unfused_torch_activation": round(us_unfused, 3),
+            "fused_GBps": round(alg / (us_fused * 1e-6) / 1e9, 1)}
+
+
 # HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
 # `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE), scaled by what the
 # same counters read for an elementwise kernel of known size.  The summary
@@ -426,6 +492,16 @@ def main():
     log(f"prefill: {pms * 1e3:.1f} us/step, {ptf:.1f} TFLOP/s; N=32768 {pdom_ms * 1e3:.1f} us, {pd_tf:.1f} TFLOP/s")
     load = dec["load"]
 
+    # --- FFN blocks with the activation fused into the down projection ------
+    log("ffn blocks")
+    ffn = {
+        "swiglu_m1": {"workload": "M=1 bf16: [up | gate] 2048x32768, down 16384x2048 with up*silu(gate) fused",
+                      **ffn_block(w4.Act.SWIGLU, 1, 2048, 16384, torch.bfloat16, dev)},
+        "gelu_m50": {"workload": "M=50 bf16: up 1024x4096, down 4096x1024 (+bias) with tanh-GELU fused",
+                     **ffn_block(w4.Act.GELU_TANH, 50, 1024, 4096, torch.bfloat16, dev)},
+    }
+    log(f"ffn: {ffn}")
+
     out = {
         "metric": "W4A16 GEMM: HBM GB/s & %peak at M=1; TFLOP/s & %MFMA peak at M=1024",
         "value": round(value, 2),
@@ -456,6 +532,7 @@ def main():
                                "unit": "TFLOP/s", "frac": round(pd_tf / MFMA_PEAK_TFLOPS, 4),
                                "kernel": f"{w4.choose_path(pd.m, pd.n, pd.k).name} {pd.name}",
                                "avg_launch_us": round(pdom_ms * 1e3, 3)}},
+        "ffn": ffn,
         "load": {"rows": "quantize + pack, decode layer weights",
                  "GBps": round(load["bytes"] / load["seconds"] / 1e9, 2) if load["seconds"] else None},
     }

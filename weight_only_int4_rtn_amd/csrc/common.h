@@ -123,11 +123,14 @@ __device__ inline uint32_t magic_pair(uint32_t word, int i) {
 // ---------------------------------------------------------------------------
 enum ActFn { kActFnNone = 0, kActFnSwiglu = 1, kActFnGeluTanh = 2 };
 
-__device__ inline float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// The logistic factor takes the hardware reciprocal (v_rcp_f32, about one
+// FP32 ulp) rather than a correctly rounded division: the result is rounded
+// to 16 bits next, and every workgroup recomputes the activation of its slice.
+__device__ inline float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 __device__ inline float gelu_tanh_f32(float x) {
     const float u = 0.7978845608028654f * fmaf(0.044715f * x, x * x, x);  // sqrt(2/pi) (x + 0.044715 x^3)
-    return x / (1.0f + __expf(-2.0f * u));
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
 }
 
 // Eight 16-bit inputs (and, for SwiGLU, the eight matching gate values) ->

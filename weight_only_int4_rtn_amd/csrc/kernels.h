@@ -33,6 +33,7 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k);
 struct SkinnyPlan {
     int mb;             // 16-row m-subtiles per workgroup (1..4)
     int gps, splits;
+    int gmax;           // register capacity for chunks (4, 8, 16 groups)
     int64_t tile_groups, mblocks;
     size_t workspace;
 };

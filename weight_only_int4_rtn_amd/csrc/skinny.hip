@@ -1,15 +1,18 @@
 // Mid-M forward (and any M): register-dequantized weights into MFMA.
 //
 // A workgroup of 4 waves owns 4 adjacent 16-row weight tiles (64 output
-// columns), a block of up to 64 activation rows and a K split.  Per 128-column
-// group:
-//   1. the workgroup stages the activation block's 128 columns in LDS and sums
-//      each row (for the offset correction below);
-//   2. each wave loads its tile's 1 KB chunk with one 128-bit load per lane and
-//      turns every word into one MFMA B operand: the chunk layout is the
-//      B-operand layout of v_mfma_f32_16x16x32_{bf16,f16} (common.h), and
-//      each nibble pair becomes a packed pair of 16-bit floats holding
-//      off + q exactly (off = 136 for bf16, 1032 for f16);
+// columns), a block of up to 64 activation rows (MB 16-row blocks) and a K
+// split of up to 16 groups (8 for MB > 2).  Each wave first loads every 1 KB
+// chunk of its tile in the split (one 128-bit load per lane each), so the
+// whole weight stream is in flight at once.  Then per 128-column group:
+//   1. the activation block's 128 columns, loaded into registers two groups
+//      ahead, are staged in one of two LDS buffers (with a fused input
+//      activation applied on the way) and each row is summed (for the offset
+//      correction below);
+//   2. each wave turns every word of its chunk into one MFMA B operand: the
+//      chunk layout is the B-operand layout of v_mfma_f32_16x16x32_{bf16,f16}
+//      (common.h), and each nibble pair becomes a packed pair of 16-bit
+//      floats holding off + q exactly (off = 136 for bf16, 1032 for f16);
 //   3. four MFMAs (k-steps of 32) per 16-row m-subtile give the group's
 //      sum_k x (off + q); the wave subtracts off * sum_k x, multiplies by the
 //      column's FP32 scale and adds into its FP32 totals.
@@ -51,12 +54,13 @@ __device__ inline f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 }
 
 // AF: activation fused into the x staging (ActFn; SwiGLU gate values sit k
-// columns after the up values).
-template <int MB, int ACT, int AF>
+// columns after the up values).  GMAX: most groups one workgroup covers (all
+// of its chunks are held in registers).
+template <int MB, int ACT, int AF, int GMAX>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     constexpr int BM = 16 * MB;
-    __shared__ __align__(16) uint16_t xa[BM * kAStride];
-    __shared__ __align__(16) float xrow[BM];
+    __shared__ __align__(16) uint16_t xa[2][BM * kAStride];
+    __shared__ __align__(16) float xrow[2][BM];
 
     const Layout L(a.n, a.k);
     const int split = int(blockIdx.x % unsigned(a.splits));
@@ -76,30 +80,43 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (tt * L.groups + g0) * kTileRows + r;
     constexpr float off = code_offset<ACT>();
 
-    f32x4_t tot[MB];
+    // Every chunk and scale of the wave's groups, loaded before anything
+    // else, so the weight stream is in flight during all of the x staging.
+    uint4 cw[GMAX];
+    float sc[GMAX];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) tot[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < GMAX; ++u) {
+        const int gc = u < ng ? u : ng - 1;  // a valid chunk; unused when u >= ng
+        cw[u] = load_stream16(cbase + int64_t(gc) * kChunkBytes);
+        sc[u] = sbase[int64_t(gc) * kTileRows];
+    }
 
-    for (int gl = 0; gl < ng; ++gl) {
-        const int64_t g = g0 + gl;
-        // weights first, so the HBM load overlaps the x staging below
-        const uint4 cw = *reinterpret_cast<const uint4*>(cbase + int64_t(gl) * kChunkBytes);
-        const float sc = sbase[int64_t(gl) * kTileRows];
-
-        // stage x[m0 : m0+BM][g*128 : g*128+128]; 16 threads per row, 8 columns each
+    // x of one group: rows m0 .. m0 + BM - 1, columns of the group; 16
+    // threads per row, 8 columns each, MB passes (rows past M read row 0 and
+    // are zeroed when staged).  Loaded into one of two register sets two
+    // groups ahead, then activated, staged in one of two LDS buffers and
+    // summed per row (for the offset correction below).
+    uint4 xr[2][MB];
+    uint4 xgate[AF == kActFnSwiglu ? 2 : 1][AF == kActFnSwiglu ? MB : 1];
+    auto load_x = [&](int set, int gl) {
 #pragma unroll
-        for (int pass = 0; pass < BM / 16; ++pass) {
+        for (int pass = 0; pass < MB; ++pass) {
             const int row = pass * 16 + (tid >> 4), piece = tid & 15;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m0 + row < a.m) {
-                const uint16_t* src = a.x + (m0 + row) * a.ldx + g * kGroup + piece * 8;
-                v = *reinterpret_cast<const uint4*>(src);
-                if constexpr (AF == kActFnSwiglu)
-                    v = activate8<ACT, AF>(v, *reinterpret_cast<const uint4*>(src + a.k));
-                else if constexpr (AF == kActFnGeluTanh)
-                    v = activate8<ACT, AF>(v, v);
-            }
-            *reinterpret_cast<uint4*>(xa + row * kAStride + piece * 8) = v;
+            const bool on = m0 + row < a.m;
+            const uint16_t* src = a.x + (on ? m0 + row : 0) * a.ldx + (g0 + gl) * kGroup + piece * 8;
+            xr[set][pass] = *reinterpret_cast<const uint4*>(src);
+            if constexpr (AF == kActFnSwiglu) xgate[set][pass] = *reinterpret_cast<const uint4*>(src + a.k);
+        }
+    };
+    auto stage_x = [&](int set, int buf) {
+#pragma unroll
+        for (int pass = 0; pass < MB; ++pass) {
+            const int row = pass * 16 + (tid >> 4), piece = tid & 15;
+            uint4 v = xr[set][pass];
+            if constexpr (AF != kActFnNone)
+                v = activate8<ACT, AF>(v, xgate[AF == kActFnSwiglu ? set : 0][AF == kActFnSwiglu ? pass : 0]);
+            if (m0 + row >= a.m) v = make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(&xa[buf][row * kAStride + piece * 8]) = v;
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
             float s = 0.0f;
 #pragma unroll
@@ -107,11 +124,26 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
                 s += to_f32<ACT>(uint16_t(w[i] & 0xFFFFu)) + to_f32<ACT>(uint16_t(w[i] >> 16));
 #pragma unroll
             for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 16);
-            if (piece == 0) xrow[row] = s;
+            if (piece == 0) xrow[buf][row] = s;
         }
-        __syncthreads();
+    };
 
-        const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+    f32x4_t tot[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) tot[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load_x(0, 0);
+    if (ng > 1) load_x(1, 1);
+    stage_x(0, 0);
+    __syncthreads();
+#pragma unroll
+    for (int gl = 0; gl < GMAX; ++gl) {
+        if (gl >= ng) continue;  // (not break: the loop stays fully unrolled, arrays in registers)
+        const int buf = gl & 1;
+        // group gl + 2 into the register set group gl was staged from
+        if (gl + 2 < ng) load_x(gl & 1, gl + 2);
+
+        const uint32_t words[4] = {cw[gl].x, cw[gl].y, cw[gl].z, cw[gl].w};
         uint4 b[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -120,15 +152,18 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t* ap = xa + (mb * 16 + r) * kAStride + 8 * kq;
+            const uint16_t* ap = &xa[buf][(mb * 16 + r) * kAStride + 8 * kq];
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc = mfma16<ACT>(*reinterpret_cast<const uint4*>(ap + 32 * s), b[s], acc);
-            const float4 xs4 = *reinterpret_cast<const float4*>(xrow + mb * 16 + 4 * kq);
-            tot[mb][0] = fmaf(sc, fmaf(-off, xs4.x, acc[0]), tot[mb][0]);
-            tot[mb][1] = fmaf(sc, fmaf(-off, xs4.y, acc[1]), tot[mb][1]);
-            tot[mb][2] = fmaf(sc, fmaf(-off, xs4.z, acc[2]), tot[mb][2]);
-            tot[mb][3] = fmaf(sc, fmaf(-off, xs4.w, acc[3]), tot[mb][3]);
+            const float4 xs4 = *reinterpret_cast<const float4*>(&xrow[buf][mb * 16 + 4 * kq]);
+            tot[mb][0] = fmaf(sc[gl], fmaf(-off, xs4.x, acc[0]), tot[mb][0]);
+            tot[mb][1] = fmaf(sc[gl], fmaf(-off, xs4.y, acc[1]), tot[mb][1]);
+            tot[mb][2] = fmaf(sc[gl], fmaf(-off, xs4.z, acc[2]), tot[mb][2]);
+            tot[mb][3] = fmaf(sc[gl], fmaf(-off, xs4.w, acc[3]), tot[mb][3]);
         }
+        // group gl + 1 into the other LDS buffer, last read in the previous
+        // group, which ended with a barrier
+        if (gl + 1 < ng) stage_x((gl + 1) & 1, buf ^ 1);
         __syncthreads();
     }
 
@@ -168,12 +203,18 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
     const int64_t bm = 16 * p.mb;
     p.mblocks = ceil_div(m, bm);
     p.tile_groups = ceil_div(L.tiles, kSkWaves);
-    // ~1024 workgroups, each at least 4 groups deep where K allows.
+    // A workgroup holds all of its chunks in registers: up to 16 groups with
+    // one or two 16-row m-subtiles, 8 with more.  Split K beyond that, and
+    // further (halving the groups per workgroup) while fewer than 128
+    // workgroups would run (measured: that beats the cost of the reduce
+    // launch a split adds).
+    const int64_t minwg = 128;
+    const int64_t cap = p.mb <= 2 ? 16 : 8;
     const int64_t base = p.tile_groups * p.mblocks;
-    int64_t gps = ceil_div(base * L.groups, 1024);
-    gps = gps < 4 ? 4 : gps;
-    gps = gps > L.groups ? L.groups : gps;
+    int64_t gps = L.groups < cap ? L.groups : cap;
+    while (gps > 2 && base * ceil_div(L.groups, gps) < minwg) gps = ceil_div(gps, 2);
     p.gps = int(gps);
+    p.gmax = gps <= 4 ? 4 : gps <= 8 ? 8 : 16;
     p.splits = int(ceil_div(L.groups, gps));
     p.workspace = p.splits > 1 ? kSyncBytes + size_t(p.splits) * m * p.tile_groups * kSkCols * 4 : 0;
     return p;
@@ -182,7 +223,14 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
 template <int MB, int ACT, int AF>
 static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
     dim3 grid(unsigned(p.tile_groups * p.splits), unsigned(p.mblocks));
-    skinny_kernel<MB, ACT, AF><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+    if (p.gmax == 4) {
+        skinny_kernel<MB, ACT, AF, 4><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+    } else if (p.gmax == 8) {
+        skinny_kernel<MB, ACT, AF, 8><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+    } else {
+        if constexpr (MB <= 2) skinny_kernel<MB, ACT, AF, 16><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+        else return hipErrorInvalidValue;  // the plan keeps 16-group splits to MB <= 2
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_splitk_reduce(a.partials, p.splits, a.m, a.n, p.tile_groups * kSkCols, a.bias, a.y, a.ldy,
