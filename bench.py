@@ -264,6 +264,40 @@ def ffn_block(act, m, hidden, inter, dtype, dev, replays=20):
             "fused_GBps": round(alg / (us_fused * 1e-6) / 1e9, 1)}
 
 
+def shard_rate(dev, parts=8, replays=5):
+    """Tensor-parallel shards of the decode layer's gate_up (rows, dim 0) and
+    down (group-aligned columns, dim 1) weights, `parts` each, from packed
+    weights without requantizing: bytes read + written per second."""
+    import torch
+
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    work = []
+    for name, dim in (("c3_gate_up_m1_k2048_n32768", 0), ("c3_down_m1_k16384_n2048", 1)):
+        c = synth.case_by_name(name)
+        codes, scales = w4.quantize(synth.make_weight(c).to(dev))
+        work.append((w4.pack(codes, scales), c.n, c.k, dim))
+        del codes, scales
+
+    def run():
+        outs = []
+        for packed, n, k, dim in work:
+            size = (n if dim == 0 else k) // parts
+            outs += [w4.shard(packed, n, k, dim, i * size, size) for i in range(parts)]
+        return outs
+    run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        outs = run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    moved = 2 * sum(o.numel() for o in outs)
+    return round(moved * replays / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+
 # HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
 # `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE), scaled by what the
 # same counters read for an elementwise kernel of known size.  The summary
@@ -534,7 +568,10 @@ def main():
                                "avg_launch_us": round(pdom_ms * 1e3, 3)}},
         "ffn": ffn,
         "load": {"rows": "quantize + pack, decode layer weights",
-                 "GBps": round(load["bytes"] / load["seconds"] / 1e9, 2) if load["seconds"] else None},
+                 "GBps": round(load["bytes"] / load["seconds"] / 1e9, 2) if load["seconds"] else None,
+                 "shard_GBps": shard_rate(dev),
+                 "shard": "8 row shards of gate_up 32768x2048 and 8 column shards of down 2048x16384, "
+                          "packed to packed, eager launches"},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

@@ -132,6 +132,26 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
                               float* scales, void* stream);
 
 /*
+ * A shard of an already packed [n][k] weight, without requantizing ("Piper
+ * Kernels", section "NVFP4 construction", partitioning an already quantized
+ * weight: packed data is copied, nibble order and scales are preserved, each
+ * shard owns its storage, a shard is a nonempty contiguous interval, and
+ * input-channel shards align to the format's blocks).
+ *   dim 0 (output features): rows [start, start + length), any start;
+ *          out = packed [length][k], w4a16_packed_bytes(length, k) bytes.
+ *   dim 1 (input features): columns [start, start + length), both multiples
+ *          of 128 (whole quantization groups), length > 0;
+ *          out = packed [n][length], w4a16_packed_bytes(n, length) bytes.
+ * unpack_weights(out) equals the same rows / columns of unpack_weights(packed),
+ * and out is byte-identical to pack_weights of those canonical rows / columns.
+ * packed and out are device pointers, 16-byte aligned, and must not overlap.
+ * n == 0, length <= 0 or an interval outside the weight give W4A16_EINVAL.
+ * Returns W4A16_OK, W4A16_EINVAL or W4A16_EHIP.
+ */
+w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, int dim, int64_t start,
+                                    int64_t length, void* out, void* stream);
+
+/*
  * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
  * kernel path (0 if none).  A K split needs it: a 1 MiB header of exchange
  * slots through which the small-M kernels add the parts' sums inside one

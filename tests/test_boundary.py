@@ -35,7 +35,8 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"quantize_rtn_int4_g128", "pack_weights", "w4a16_linear", "unpack_weights",
             "w4a16_packed_bytes", "w4a16_linear_workspace_bytes", "w4a16_status_string",
-            "w4a16_linear_with_path", "w4a16_linear_choose_path"} <= set(names)
+            "w4a16_linear_with_path", "w4a16_linear_choose_path", "w4a16_linear_act",
+            "w4a16_linear_act_workspace_bytes", "shard_packed_weights"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -176,6 +177,22 @@ def test_linear_act_rejects(lib):
     assert lin_act(lib, ge, path=gemm, m=256, k=128, ldx=big, y=A * 8192, ws=None) == B.EWORKSPACE
     assert lib.w4a16_linear_act_workspace_bytes(5, 16, 16, 128) == 0
     assert lib.w4a16_linear_act_workspace_bytes(int(w4.Act.NONE), 1, 2048, 16384) == w4.workspace_bytes(1, 2048, 16384)
+
+
+def test_shard_rejects(lib):
+    sh = lib.shard_packed_weights
+    assert sh(A, 100, 640, 2, 0, 10, A * 4, None) == B.EINVAL        # dim
+    assert sh(A, 100, 640, 0, -1, 10, A * 4, None) == B.EINVAL       # start < 0
+    assert sh(A, 100, 640, 0, 0, 0, A * 4, None) == B.EINVAL         # empty shard
+    assert sh(A, 100, 640, 0, 95, 10, A * 4, None) == B.EINVAL       # past n
+    assert sh(A, 100, 640, 1, 64, 128, A * 4, None) == B.EINVAL      # start not on a group
+    assert sh(A, 100, 640, 1, 128, 100, A * 4, None) == B.EINVAL     # length not whole groups
+    assert sh(A, 100, 640, 1, 512, 256, A * 4, None) == B.EINVAL     # past k
+    assert sh(A, 100, 600, 0, 0, 10, A * 4, None) == B.EINVAL        # k % 128
+    assert sh(A, 0, 640, 0, 0, 1, A * 4, None) == B.EINVAL           # empty weight
+    assert sh(None, 100, 640, 0, 0, 10, A * 4, None) == B.EINVAL
+    assert sh(A, 100, 640, 0, 0, 10, A + 8, None) == B.EINVAL        # misaligned / overlapping out
+    assert sh(A, 100, 640, 0, 0, 10, A + 4096, None) == B.EINVAL     # out inside the packed weight
 
 
 def test_binding_rejects_cpu_tensors():

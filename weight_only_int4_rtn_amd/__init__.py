@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     pack,
     packed_bytes,
     quantize,
+    shard,
     status_string,
     unpack,
     workspace_bytes,

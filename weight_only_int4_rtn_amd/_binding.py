@@ -56,6 +56,8 @@ def _declare(lib):
     lib.pack_weights.restype = i32
     lib.unpack_weights.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.unpack_weights.restype = i32
+    lib.shard_packed_weights.argtypes = [vp, i64, i64, i32, i64, i64, vp, vp]
+    lib.shard_packed_weights.restype = i32
     lib.w4a16_linear_workspace_bytes.argtypes = [i64, i64, i64]
     lib.w4a16_linear_workspace_bytes.restype = sz
     lib.w4a16_linear.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, sz, vp]
@@ -178,6 +180,17 @@ def unpack(packed: torch.Tensor, n: int, k: int):
     st = lib().unpack_weights(_ptr(packed), n, k, _ptr(codes), _ptr(scales), _stream(packed.device))
     _check(st, "unpack_weights")
     return codes, scales
+
+
+def shard(packed: torch.Tensor, n: int, k: int, dim: int, start: int, length: int) -> torch.Tensor:
+    """Rows [start, start+length) (dim 0) or group-aligned columns (dim 1) of a
+    packed [n, k] weight as a new packed weight (no requantization)."""
+    _require_cuda(packed)
+    rows, cols = (length, k) if dim == 0 else (n, length)
+    out = torch.empty(max(packed_bytes(rows, cols), 16), dtype=torch.uint8, device=packed.device)
+    st = lib().shard_packed_weights(_ptr(packed), n, k, dim, start, length, _ptr(out), _stream(packed.device))
+    _check(st, "shard_packed_weights")
+    return out[:packed_bytes(rows, cols)]
 
 
 _workspaces: dict = {}

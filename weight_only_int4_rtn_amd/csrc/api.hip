@@ -111,6 +111,20 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
     return from_hip(launch_unpack(packed, n, k, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
+w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, int dim, int64_t start,
+                                    int64_t length, void* out, void* stream) {
+    // a shard is a nonempty contiguous interval; input-feature shards hold
+    // whole quantization groups
+    if (!valid_nk(n, k) || n == 0 || (dim != 0 && dim != 1) || start < 0 || length <= 0) return W4A16_EINVAL;
+    if (dim == 0 && start + length > n) return W4A16_EINVAL;
+    if (dim == 1 && (start % kGroup != 0 || length % kGroup != 0 || start + length > k)) return W4A16_EINVAL;
+    if (!packed || !out || !aligned(packed, 16) || !aligned(out, 16)) return W4A16_EINVAL;
+    const size_t in_bytes = w4a16_packed_bytes(n, k);
+    const size_t out_bytes = dim == 0 ? w4a16_packed_bytes(length, k) : w4a16_packed_bytes(n, length);
+    if (overlap(packed, in_bytes, out, out_bytes)) return W4A16_EINVAL;
+    return from_hip(launch_shard(packed, n, k, dim, start, length, out, static_cast<hipStream_t>(stream)));
+}
+
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     (void)n;
     if (m <= 3) return W4A16_PATH_GEMV;

@@ -53,6 +53,10 @@ hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t n, int
                        void* packed, hipStream_t stream);
 hipError_t launch_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, float* scales,
                          hipStream_t stream);
+// Rows [start, start + len) (dim 0) or group-aligned columns (dim 1) of a
+// packed [n][k] weight into a new packed weight.
+hipError_t launch_shard(const void* packed, int64_t n, int64_t k, int dim, int64_t start, int64_t len,
+                        void* out, hipStream_t stream);
 
 // y[m][n] = round(sum over splits of partials[s][m][npad] + bias): finishes K-split launches.
 hipError_t launch_splitk_reduce(const float* partials, int splits, int64_t m, int64_t n, int64_t npad,

@@ -176,6 +176,63 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Shard of a packed weight without requantizing ("Piper Kernels", section
+// "NVFP4 construction", partitioning an already quantized weight: the packed
+// data is copied, nibble order and scales preserved).  One thread per
+// (output chunk, lane): 16 bytes.
+//   dim 0: output rows r of [0, len) are source rows start + r (any start);
+//          a row moves as the four 16-byte lane runs (one per k-quarter) of
+//          each of its chunks, plus its scale.  Rows past len in the last
+//          output tile get code 0 (nibble 8) and scale 0, as pack writes them.
+//   dim 1: output groups are source groups start/128 + g': whole chunks and
+//          their scale blocks are copied.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void shard_kernel(const uint8_t* __restrict__ src, int64_t n, int64_t k,
+                                                    int dim, int64_t start, int64_t len,
+                                                    uint8_t* __restrict__ dst) {
+    const Layout S(n, k);
+    const Layout D(dim == 0 ? len : n, dim == 0 ? k : len);
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (tid >= D.chunks() * 64) return;
+    const int64_t chunk = tid >> 6;
+    const int lane = int(tid & 63);
+    const int64_t t = chunk / D.groups, g = chunk - t * D.groups;
+    const int r = lane & 15, kq = lane >> 4;
+    const float* ss = reinterpret_cast<const float*>(src + S.scale_offset());
+    float* ds = reinterpret_cast<float*>(dst + D.scale_offset());
+    uint4 v;
+    float sc;
+    if (dim == 0) {
+        const int64_t orow = t * kTileRows + r;
+        if (orow < len) {
+            const int64_t srow = start + orow;
+            const int64_t schunk = (srow / kTileRows) * S.groups + g;
+            const int slane = int(srow % kTileRows) + 16 * kq;
+            v = *reinterpret_cast<const uint4*>(src + schunk * kChunkBytes + slane * 16);
+            sc = ss[schunk * kTileRows + srow % kTileRows];
+        } else {
+            v = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+            sc = 0.0f;
+        }
+    } else {
+        const int64_t schunk = t * S.groups + start / kGroup + g;
+        v = *reinterpret_cast<const uint4*>(src + schunk * kChunkBytes + lane * 16);
+        sc = ss[schunk * kTileRows + r];
+    }
+    *reinterpret_cast<uint4*>(dst + chunk * kChunkBytes + lane * 16) = v;
+    if (kq == 0) ds[chunk * kTileRows + r] = sc;
+}
+
+hipError_t launch_shard(const void* packed, int64_t n, int64_t k, int dim, int64_t start, int64_t len,
+                        void* out, hipStream_t stream) {
+    const Layout D(dim == 0 ? len : n, dim == 0 ? k : len);
+    const int64_t blocks = ceil_div(D.chunks() * 64, 256);
+    shard_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(static_cast<const uint8_t*>(packed), n, k, dim, start,
+                                                         len, static_cast<uint8_t*>(out));
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t n, int64_t k,
                        void* packed, hipStream_t stream) {
     const Layout L(n, k);
