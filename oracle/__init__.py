@@ -29,4 +29,7 @@ from .oracle import (  # noqa: F401
     num_threads,
     quantize,
     round16,
+    splitmix64,
+    uniform,
+    update,
 )

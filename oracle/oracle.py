@@ -60,6 +60,13 @@ def _declare(lib):
     lib.oracle_act_value.restype = ctypes.c_double
     lib.oracle_activate.argtypes = [vp, i32, i32, i64, i64, i64, vp]
     lib.oracle_activate.restype = i32
+    lib.oracle_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    lib.oracle_splitmix64.restype = ctypes.c_uint64
+    lib.oracle_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    lib.oracle_uniform.restype = ctypes.c_float
+    lib.oracle_update.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, i32, ctypes.c_float, ctypes.c_float,
+                                  i32, ctypes.c_uint64]
+    lib.oracle_update.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     return lib
@@ -202,6 +209,43 @@ def round16(v: float, tag: int, lib=None) -> int:
 
 def act_value(v: float, up: float, act: int, lib=None) -> float:
     return float((lib or load()).oracle_act_value(float(v), float(up), act))
+
+
+def _upd_array(a: np.ndarray, tag):
+    a = np.ascontiguousarray(a)
+    return a, _dtype_tag(a, tag)
+
+
+def update(q: np.ndarray, s: np.ndarray, upd=None, mat1=None, mat2=None, alpha=1.0, beta=1.0,
+           seed=None, dtype_tag=None, lib=None):
+    """Requantized codes and scales of beta * dequant(q, s) + alpha * U, U a
+    dense [n, k] update or mat1 [n, r] @ mat2 [r, k] (float32, or uint16 bits
+    with a dtype tag); stochastic rounding when ``seed`` is given.
+    Returns new (q, s); the inputs are not modified."""
+    lib = lib or load()
+    q = np.array(q, dtype=np.int8, order="C", copy=True)
+    s = np.array(s, dtype=np.float32, order="C", copy=True)
+    n, k = q.shape
+    if upd is not None:
+        u, tag = _upd_array(upd, dtype_tag)
+        args = (_p(u), k, None, None, 0, tag)
+    else:
+        a, tag = _upd_array(mat1, dtype_tag)
+        b, _ = _upd_array(mat2, dtype_tag)
+        args = (None, 0, _p(a), _p(b), a.shape[1], tag)
+    rc = lib.oracle_update(_p(q), _p(s), n, k, *args, float(alpha), float(beta), int(seed is not None),
+                           int(seed or 0))
+    if rc != 0:
+        raise ValueError("oracle_update rejected its arguments")
+    return q, s
+
+
+def splitmix64(seed: int, e: int, lib=None) -> int:
+    return int((lib or load()).oracle_splitmix64(seed, e))
+
+
+def uniform(seed: int, e: int, lib=None) -> float:
+    return float((lib or load()).oracle_uniform(seed, e))
 
 
 def bf16_to_double(bits: int, lib=None) -> float:

@@ -46,6 +46,24 @@
  * even), which is then the layer's input, as a separately materialised
  * activation would be.
  *
+ * Updates of a quantized weight ("Piper Kernels", sections "ConvRot INT8"
+ * (add_ / addmm_ with an optional rounding_seed, requantizing the result)
+ * and "Stochastic quantization"): W' = beta * dequant(W) + alpha * U, U a
+ * dense update or a low-rank product mat1 @ mat2 accumulated in FP32, then
+ * requantized with the same deterministic scales as round-to-nearest; with a
+ * seed, each code is one of the two adjacent codes with probability
+ * proportional to distance (values outside the code range and exact hits are
+ * never perturbed), drawn by logical element offset from a seeded generator.
+ * Readings: every step is one FP32 operation in this order --
+ *   d = fl32(q * s); p = U widened to FP32, or p = fma(mat1[n][r], mat2[r][k], p)
+ *   over r ascending from p = 0; w' = fma(alpha, p, fl32(beta * d)) --
+ *   then the quantizer above on w'.  The generator is SplitMix64 (Steele, Lea
+ *   and Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014):
+ *   element e of the weight (row-major offset n * K + k) draws the (e+1)-th
+ *   output of SplitMix64 seeded with the 64-bit seed; its top 24 bits give a
+ *   uniform u in [0, 1) (u = bits * 2^-24), and the code rounds up exactly
+ *   when u < v - floor(v), v = fl32(w' / s').
+ *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared
  * The quantizer relies on IEEE binary32 division and on nearbyintf under the
  * default round-to-nearest-even mode; -ffp-contract=off keeps every step a
@@ -331,6 +349,105 @@ int oracle_activate(const uint16_t *x, int x_dtype, int act, int64_t m, int64_t 
             }
             a[i * k + j] = oracle_round16(v, x_dtype);
         }
+    return 0;
+}
+
+/* ---- updates of a quantized weight, with optional stochastic rounding ---- */
+
+/* The (e+1)-th output of SplitMix64 seeded with `seed`. */
+uint64_t oracle_splitmix64(uint64_t seed, uint64_t e)
+{
+    uint64_t z = seed + (e + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* Uniform in [0, 1) with 24 bits, for element e. */
+float oracle_uniform(uint64_t seed, uint64_t e)
+{
+    return (float)(oracle_splitmix64(seed, e) >> 40) * 0x1p-24f;
+}
+
+static float update_value(const void *u, int u_dtype, int64_t idx)
+{
+    return weight_as_float(u, u_dtype, idx);
+}
+
+/*
+ * In place on canonical codes q [n][k] and scales s [n][k/128]:
+ *   rank == 0: W' = beta * dequant + alpha * upd, upd [n][k] (row stride ldu)
+ *   rank  > 0: W' = beta * dequant + alpha * (mat1 @ mat2), mat1 [n][rank],
+ *              mat2 [rank][k], both row-major of dtype u_dtype
+ * then requantized (round to nearest, or stochastic when has_seed).
+ * u_dtype: F32, BF16 or F16.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_update(int8_t *q, float *s, int64_t n, int64_t k, const void *upd, int64_t ldu,
+                  const void *mat1, const void *mat2, int64_t rank, int u_dtype,
+                  float alpha, float beta, int has_seed, uint64_t seed)
+{
+    if (k <= 0 || k % ORACLE_GROUP != 0 || n < 0 || rank < 0)
+        return -1;
+    if (u_dtype != ORACLE_F32 && u_dtype != ORACLE_BF16 && u_dtype != ORACLE_F16)
+        return -1;
+    if (rank == 0 && (!upd || ldu < k))
+        return -1;
+    if (rank > 0 && (!mat1 || !mat2))
+        return -1;
+    if (fegetround() != FE_TONEAREST)
+        fesetround(FE_TONEAREST);
+    const int64_t groups = k / ORACLE_GROUP;
+    float w[ORACLE_GROUP];
+    for (int64_t row = 0; row < n; ++row) {
+        for (int64_t g = 0; g < groups; ++g) {
+            /* the updated group in FP32 */
+            const float sc = s[row * groups + g];
+            for (int64_t j = 0; j < ORACLE_GROUP; ++j) {
+                const int64_t kk = g * ORACLE_GROUP + j;
+                const float d = (float)q[row * k + kk] * sc;
+                float p;
+                if (rank == 0) {
+                    p = update_value(upd, u_dtype, row * ldu + kk);
+                } else {
+                    p = 0.0f;
+                    for (int64_t r = 0; r < rank; ++r)
+                        p = fmaf(update_value(mat1, u_dtype, row * rank + r),
+                                 update_value(mat2, u_dtype, r * k + kk), p);
+                }
+                const float bd = beta * d;
+                w[j] = fmaf(alpha, p, bd);
+            }
+            /* requantize: the scale of round-to-nearest, then the codes */
+            float amax = 0.0f;
+            for (int j = 0; j < ORACLE_GROUP; ++j)
+                if (fabsf(w[j]) > amax)
+                    amax = fabsf(w[j]);
+            const float scale = amax / 7.0f;
+            s[row * groups + g] = scale;
+            for (int64_t j = 0; j < ORACLE_GROUP; ++j) {
+                const int64_t kk = g * ORACLE_GROUP + j;
+                int code = 0;
+                if (scale != 0.0f) {
+                    const float v = w[j] / scale;
+                    const float lo = floorf(v);
+                    if (has_seed && lo >= -8.0f && lo + 1.0f <= 7.0f) {
+                        /* interior: one of the two adjacent codes */
+                        const float frac = v - lo;
+                        const float u = oracle_uniform(seed, (uint64_t)(row * k + kk));
+                        code = (int)lo + (u < frac ? 1 : 0);
+                    } else {
+                        float r = nearbyintf(v);
+                        if (r < -8.0f)
+                            r = -8.0f;
+                        if (r > 7.0f)
+                            r = 7.0f;
+                        code = (int)r;
+                    }
+                }
+                q[row * k + kk] = (int8_t)code;
+            }
+        }
+    }
     return 0;
 }
 

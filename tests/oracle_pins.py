@@ -16,7 +16,11 @@ What each pin checks against:
   * numpy/torch decoders for every 16-bit pattern;
   * the fused activations: torch's float64 silu and tanh-GELU (library
     routines), their odd-part identity, and exact rational rounding of the
-    activated value to bf16/fp16 (also against torch/numpy FP32 conversions).
+    activated value to bf16/fp16 (also against torch/numpy FP32 conversions);
+  * weight updates: exactly emulated FP32 steps fed to the (pinned)
+    quantizer, identities on dyadic weights, the published SplitMix64
+    outputs, and the stochastic rounding's adjacency, offsets,
+    reproducibility and unbiasedness.
 """
 from __future__ import annotations
 
@@ -336,6 +340,162 @@ def pin_activate_rows(lib, seed=23):
         assert np.array_equal(out, oracle.activate(xb[:, :2 * k], tag, oracle.ACT_SWIGLU, lib=lib))
 
 
+def pin_splitmix64_published(lib):
+    """Golden: the generator's published outputs (tests/golden/splitmix64.txt);
+    output i + 1 of a seed is draw i, and a draw's top 24 bits are the uniform."""
+    for line in _read_lines("splitmix64.txt"):
+        seed, outs = [p.strip() for p in line.split("|")]
+        for i, want in enumerate(int(v) for v in outs.split()):
+            got = lib.oracle_splitmix64(int(seed), i)
+            assert got == want, (seed, i, got, want)
+            assert lib.oracle_uniform(int(seed), i) == (want >> 40) * 2.0 ** -24
+
+
+def _fl32(fr: Fraction) -> Fraction:
+    return Fraction(exact.round_to_f32(fr))
+
+
+def _exact_update(q, s, upd=None, m1=None, m2=None, alpha=1.0, beta=1.0):
+    """The update's FP32 steps emulated exactly: each product, sum and fused
+    multiply-add computed in rationals and rounded once to binary32."""
+    n, k = q.shape
+    a, b = Fraction(float(np.float32(alpha))), Fraction(float(np.float32(beta)))
+    out = np.empty((n, k), dtype=np.float32)
+    for i in range(n):
+        for j in range(k):
+            d = _fl32(Fraction(int(q[i, j])) * Fraction(float(s[i, j // 128])))
+            if upd is not None:
+                p = Fraction(float(upd[i, j]))
+            else:
+                p = Fraction(0)
+                for r in range(m1.shape[1]):
+                    p = _fl32(Fraction(float(m1[i, r])) * Fraction(float(m2[r, j])) + p)
+            out[i, j] = np.float32(exact.round_to_f32(a * p + _fl32(b * d)))
+    return out
+
+
+def pin_update_matches_exact_steps(lib, seed=31):
+    """Round-to-nearest updates (dense and low-rank, several alpha/beta) equal
+    the quantizer applied to the exactly emulated FP32 steps."""
+    rng = np.random.default_rng(seed)
+    n, k = 4, 256
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    q, s = oracle.quantize(w, lib=lib)
+    upd = (rng.standard_normal((n, k)) * 0.01).astype(np.float32)
+    m1 = (rng.standard_normal((n, 3)) * 0.1).astype(np.float32)
+    m2 = (rng.standard_normal((3, k)) * 0.1).astype(np.float32)
+    for kind in ("dense", "lowrank"):
+        for alpha, beta in ((1.0, 1.0), (0.375, 1.0), (-2.0, 0.5)):
+            if kind == "dense":
+                got = oracle.update(q, s, upd=upd, alpha=alpha, beta=beta, lib=lib)
+                wn = _exact_update(q, s, upd=upd, alpha=alpha, beta=beta)
+            else:
+                got = oracle.update(q, s, mat1=m1, mat2=m2, alpha=alpha, beta=beta, lib=lib)
+                wn = _exact_update(q, s, m1=m1, m2=m2, alpha=alpha, beta=beta)
+            want = oracle.quantize(wn, lib=lib)
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), (kind, alpha, beta)
+    # a dense update with a row stride wider than the row (the C entry point)
+    wide = np.zeros((n, k + 8), dtype=np.float32)
+    wide[:, :k] = upd
+    wide[:, k:] = 1e3  # never read
+    q2, s2 = q.copy(), s.copy()
+    rc = lib.oracle_update(q2.ctypes.data_as(ctypes.c_void_p), s2.ctypes.data_as(ctypes.c_void_p), n, k,
+                           wide.ctypes.data_as(ctypes.c_void_p), k + 8, None, None, 0, oracle.F32,
+                           ctypes.c_float(1.0), ctypes.c_float(1.0), 0, 0)
+    assert rc == 0
+    want = oracle.update(q, s, upd=upd, lib=lib)
+    assert np.array_equal(q2, want[0]) and np.array_equal(s2, want[1])
+    # the low-rank sum runs r ascending: terms 1, 2^-24, 2^-24 sum to 1 in that
+    # order (each tie rounds to even) but to 1 + 2^-23 in the other; that value
+    # is the group's largest, so it shows in the scale
+    m1 = np.array([[1.0, 2.0 ** -24, 2.0 ** -24]], dtype=np.float32)
+    m2 = np.zeros((3, 128), dtype=np.float32)
+    m2[:, 0] = 1.0
+    zq, zs = np.zeros((1, 128), np.int8), np.zeros((1, 1), np.float32)
+    got = oracle.update(zq, zs, mat1=m1, mat2=m2, lib=lib)
+    wn = _exact_update(zq, zs, m1=m1, m2=m2)
+    assert wn[0, 0] == 1.0 and got[1][0, 0] == np.float32(1.0) / np.float32(7.0), (wn[0, 0], got[1][0, 0])
+
+
+def pin_update_identities(lib, seed=32):
+    """Dyadic weights (codes times 2^-3): a zero update keeps codes and scales
+    in both rounding modes (exact hits are never perturbed); subtracting the
+    dequantized weight gives all-zero groups (s = +0, q = 0); doubling it
+    doubles the scales and keeps the codes."""
+    rng = np.random.default_rng(seed)
+    n, k = 6, 384
+    qi = rng.integers(-7, 8, size=(n, k))
+    qi[:, ::128] = 7
+    w = (qi * 2.0 ** -3).astype(np.float32)
+    q, s = oracle.quantize(w, lib=lib)
+    zero = np.zeros((n, k), dtype=np.float32)
+    for sd in (None, 7):
+        q2, s2 = oracle.update(q, s, upd=zero, seed=sd, lib=lib)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s)
+        q3, s3 = oracle.update(q, s, upd=-w, seed=sd, lib=lib)
+        assert np.all(q3 == 0) and np.all(s3 == 0) and not np.any(np.signbit(s3))
+        q4, s4 = oracle.update(q, s, upd=w, seed=sd, lib=lib)
+        assert np.array_equal(q4, q) and np.array_equal(s4, 2 * s)
+
+
+def pin_stochastic_rounding(lib, seed=33):
+    """Stochastic codes: each is floor(v) or floor(v) + 1 of the exactly
+    emulated quotient v (codes outside the interior keep the nearest code),
+    element (i, j) rounds up exactly when draw i*K + j of the seed falls below
+    v - floor(v), a seed reproduces its result, and over many seeds the mean
+    code approaches v (unbiased)."""
+    rng = np.random.default_rng(seed)
+    n, k = 3, 256
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    q, s = oracle.quantize(w, lib=lib)
+    upd = (rng.standard_normal((n, k)) * 0.005).astype(np.float32)
+    wn = _exact_update(q, s, upd=upd)
+    qn, sn = oracle.quantize(wn, lib=lib)
+    v = np.empty((n, k))
+    for i in range(n):
+        for j in range(k):
+            v[i, j] = exact.round_to_f32(Fraction(float(wn[i, j])) / Fraction(float(sn[i, j // 128])))
+    lo = np.floor(v)
+    interior = (lo >= -8) & (lo + 1 <= 7)
+    trials = []
+    for sd in range(300):
+        q2, s2 = oracle.update(q, s, upd=upd, seed=sd, lib=lib)
+        assert np.array_equal(s2, sn)  # the deterministic scales
+        assert np.all(((q2 == lo) | (q2 == lo + 1))[interior])
+        assert np.array_equal(q2[~interior], qn[~interior])
+        trials.append(q2.astype(np.float64))
+    q_a, _ = oracle.update(q, s, upd=upd, seed=12345, lib=lib)
+    q_b, _ = oracle.update(q, s, upd=upd, seed=12345, lib=lib)
+    assert np.array_equal(q_a, q_b)
+    for i in range(n):
+        for j in range(k):
+            if interior[i, j]:
+                up = lib.oracle_uniform(12345, i * k + j) < v[i, j] - lo[i, j]
+                assert q_a[i, j] == lo[i, j] + up, (i, j)
+    # a quotient equal to its own draw does not round up (u < frac is strict):
+    # from an all-zero weight, the dense update itself is w'; 7 fixes s' = 1
+    u0 = lib.oracle_uniform(77, 0)
+    z = np.zeros((1, 128), dtype=np.float32)
+    craft = np.zeros((1, 128), dtype=np.float32)
+    craft[0, 0], craft[0, 1] = u0, 7.0
+    qc, sc = oracle.update(z.astype(np.int8), np.zeros((1, 1), np.float32), upd=craft, seed=77, lib=lib)
+    assert sc[0, 0] == 1.0 and qc[0, 0] == 0 and qc[0, 1] == 7, (qc[0, :2], sc)
+    # outside the interior the nearest code stands: a = 1.0000007 gives
+    # s' = fl32(a/7) = 0.14285724 and v = 7.0000005 (floor 7, no code 8);
+    # seed 1127518 draws 2 * 2^-24 first, below v - 7, so a rounding that
+    # ignored the code range would produce 8 here
+    craft = np.zeros((1, 128), dtype=np.float32)
+    craft[0, 0] = np.float32(1.0000007)
+    qc, sc = oracle.update(z.astype(np.int8), np.zeros((1, 1), np.float32), upd=craft, seed=1127518, lib=lib)
+    assert lib.oracle_uniform(1127518, 0) == 2 * 2.0 ** -24
+    assert np.float32(craft[0, 0]) / sc[0, 0] > np.float32(7.0) and qc[0, 0] == 7, (qc[0, 0], sc[0, 0])
+    mean = np.mean(trials, axis=0)
+    frac = v - lo
+    sd_err = np.sqrt(frac * (1 - frac) / len(trials)) + 1e-6
+    assert np.all(np.abs(mean - v)[interior] <= 5 * sd_err[interior] + 1e-6)
+    assert np.mean(np.abs(mean - v)[interior]) < 0.02
+
+
 ALL_PINS = [
     pin_hand_worked_groups,
     pin_negative_zero_group,
@@ -351,4 +511,8 @@ ALL_PINS = [
     pin_activation_library,
     pin_activation_odd_part,
     pin_activate_rows,
+    pin_splitmix64_published,
+    pin_update_matches_exact_steps,
+    pin_update_identities,
+    pin_stochastic_rounding,
 ]

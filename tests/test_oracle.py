@@ -59,8 +59,10 @@ def test_rejects_bad_group_size(lib):
 
 # (description, text in w4a16_oracle.c, replacement) -- each is a plausible slip.
 MUTANTS = [
-    ("divisor 8 instead of 7", "float scale = amax / 7.0f;", "float scale = amax / 8.0f;"),
-    ("divisor 7.5", "float scale = amax / 7.0f;", "float scale = amax / 7.5f;"),
+    ("divisor 8 instead of 7", "onto code 7 */\n            float scale = amax / 7.0f;",
+     "onto code 7 */\n            float scale = amax / 8.0f;"),
+    ("divisor 7.5", "onto code 7 */\n            float scale = amax / 7.0f;",
+     "onto code 7 */\n            float scale = amax / 7.5f;"),
     ("ties away from zero", "float r = nearbyintf(ratio);", "float r = roundf(ratio);"),
     ("truncation", "float r = nearbyintf(ratio);", "float r = truncf(ratio);"),
     ("reciprocal multiply", "float ratio = weight_as_float(w, w_dtype, row * ldw + kk) / scale;",
@@ -83,7 +85,7 @@ MUTANTS = [
     ("fp16 subnormal scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     ("bf16 decoded as fp16", "return dtype == ORACLE_BF16 ? oracle_bf16_to_double(bits) : oracle_f16_to_double(bits);",
      "return oracle_f16_to_double(bits);"),
-    ("zero guard missing", "if (scale != 0.0f) {", "if (1) {"),
+    ("zero guard missing", "if (scale != 0.0f) {\n                    float ratio", "if (1) {\n                    float ratio"),
     ("dequant drops the scale", "w_hat[row * k + kk] = (double)q[row * k + kk] * (double)s[row * groups + kk / ORACLE_GROUP];",
      "w_hat[row * k + kk] = (double)q[row * k + kk];"),
     ("x row stride ignored", "double xv = decode16(x[i * ldx + kk], x_dtype);", "double xv = decode16(x[kk], x_dtype);"),
@@ -102,6 +104,28 @@ MUTANTS = [
     ("fp16 normal range from 2^-15", "const int emin = dtype == ORACLE_BF16 ? -126 : -14;",
      "const int emin = dtype == ORACLE_BF16 ? -126 : -15;"),
     ("no overflow to infinity", "if (r >= ldexp(1.0, emax + 1))\n        return inf;", "if (0)\n        return inf;"),
+    ("splitmix64 increment", "uint64_t z = seed + (e + 1) * 0x9E3779B97F4A7C15ull;",
+     "uint64_t z = seed + (e + 1) * 0x9E3779B97F4A7C13ull;"),
+    ("draw index off by one", "uint64_t z = seed + (e + 1) * 0x9E3779B97F4A7C15ull;",
+     "uint64_t z = seed + e * 0x9E3779B97F4A7C15ull;"),
+    ("uniform from the low bits", "return (float)(oracle_splitmix64(seed, e) >> 40) * 0x1p-24f;",
+     "return (float)(oracle_splitmix64(seed, e) & 0xFFFFFF) * 0x1p-24f;"),
+    ("round up when u <= frac", "code = (int)lo + (u < frac ? 1 : 0);", "code = (int)lo + (u <= frac ? 1 : 0);"),
+    ("round up with probability 1 - frac", "code = (int)lo + (u < frac ? 1 : 0);", "code = (int)lo + (u < 1.0f - frac ? 1 : 0);"),
+    ("truncation instead of floor", "const float lo = floorf(v);", "const float lo = truncf(v);"),
+    ("column-major draw offsets", "const float u = oracle_uniform(seed, (uint64_t)(row * k + kk));",
+     "const float u = oracle_uniform(seed, (uint64_t)(kk * n + row));"),
+    ("alpha on the old weight", "w[j] = fmaf(alpha, p, bd);", "w[j] = fmaf(alpha, bd, p);"),
+    ("beta ignored", "const float bd = beta * d;", "const float bd = d;"),
+    ("low-rank index transposed", "p = fmaf(update_value(mat1, u_dtype, row * rank + r),",
+     "p = fmaf(update_value(mat1, u_dtype, r * n + row),"),
+    ("low-rank sum in descending order", "for (int64_t r = 0; r < rank; ++r)\n                        p = fmaf(",
+     "for (int64_t r = rank - 1; r >= 0; --r)\n                        p = fmaf("),
+    ("dense update row stride ignored", "p = update_value(upd, u_dtype, row * ldu + kk);",
+     "p = update_value(upd, u_dtype, row * k + kk);"),
+    ("stochastic outside the interior", "if (has_seed && lo >= -8.0f && lo + 1.0f <= 7.0f) {", "if (has_seed) {"),
+    ("update scale divisor 8", "const float scale = amax / 7.0f;\n            s[row * groups + g] = scale;",
+     "const float scale = amax / 8.0f;\n            s[row * groups + g] = scale;"),
 ]
 
 _RUNNER = r"""
