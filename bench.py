@@ -264,6 +264,35 @@ def ffn_block(act, m, hidden, inter, dtype, dev, replays=20):
             "fused_GBps": round(alg / (us_fused * 1e-6) / 1e9, 1)}
 
 
+def update_rate(dev, rank=16, replays=5):
+    """A seeded low-rank merge (LoRA, rank 16) into the decode layer's gate_up
+    weight, requantized in place with stochastic rounding: microseconds and
+    the packed weight's bytes read + written per second."""
+    import torch
+
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    c = synth.case_by_name("c3_gate_up_m1_k2048_n32768")
+    codes, scales = w4.quantize(synth.make_weight(c).to(dev))
+    packed = w4.pack(codes, scales)
+    del codes, scales
+    g = torch.Generator().manual_seed(7)
+    m1 = (torch.randn(c.n, rank, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    m2 = (torch.randn(rank, c.k, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    w4.update_(packed, c.n, c.k, mat1=m1, mat2=m2, alpha=0.5, seed=1)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(replays):
+        w4.update_(packed, c.n, c.k, mat1=m1, mat2=m2, alpha=0.5, seed=2 + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / replays
+    return {"workload": f"rank-{rank} bf16 merge into gate_up 32768x2048, stochastic rounding",
+            "us": round(us, 2), "packed_GBps": round(2 * packed.numel() / (us * 1e-6) / 1e9, 1)}
+
+
 def shard_rate(dev, parts=8, replays=5):
     """Tensor-parallel shards of the decode layer's gate_up (rows, dim 0) and
     down (group-aligned columns, dim 1) weights, `parts` each, from packed
@@ -570,6 +599,7 @@ def main():
         "load": {"rows": "quantize + pack, decode layer weights",
                  "GBps": round(load["bytes"] / load["seconds"] / 1e9, 2) if load["seconds"] else None,
                  "shard_GBps": shard_rate(dev),
+                 "update": update_rate(dev),
                  "shard": "8 row shards of gate_up 32768x2048 and 8 column shards of down 2048x16384, "
                           "packed to packed, eager launches"},
     }

@@ -132,6 +132,41 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
                               float* scales, void* stream);
 
 /*
+ * In-place update of a packed [n][k] weight ("Piper Kernels", sections
+ * "ConvRot INT8" -- add_ / addmm_ requantize the updated weight; an unsigned
+ * 64-bit rounding_seed selects stochastic rounding without changing the
+ * scales, none selects nearest rounding -- and "Stochastic quantization" --
+ * one of the two adjacent codes with probability proportional to distance,
+ * values outside the code range and exact hits never perturbed, draws by
+ * logical element offset):
+ *   W' = beta * dequant(W) + alpha * U
+ * with U the dense update [n][ldu] (update != NULL, rank == 0) or the
+ * low-rank product mat1 [n][rank] @ mat2 [rank][k] (update == NULL,
+ * 1 <= rank <= 65536), all of update_dtype (F32, BF16 or F16), row-major.
+ * Every step is one FP32 operation: d = fl32(q * s); U widened to FP32, or
+ * p = fma(mat1[n][r], mat2[r][k], p) over r ascending from 0; w' =
+ * fma(alpha, p, fl32(beta * d)).  W' is then quantized with the rules of
+ * quantize_rtn_int4_g128 (scale amax / 7 per group); with a seed, an
+ * interior quotient v (-8 <= floor(v) <= 6) becomes floor(v) + 1 exactly when
+ * u < v - floor(v), u = (SplitMix64 output e+1 of the seed) >> 40, times
+ * 2^-24, e = n * k_total + k the element's row-major offset (SplitMix64:
+ * Steele, Lea and Flood, OOPSLA 2014).  Results are identical from run to
+ * run and independent of the launch.
+ *   packed   device, from pack_weights, 16-byte aligned; updated in place.
+ *   update   device, 16-byte aligned, ldu >= k, ldu * element size a
+ *            multiple of 16 bytes.
+ *   mat1     device, element-aligned; mat2 device, 16-byte aligned.
+ *   rounding_seed  host pointer to the seed, or NULL for nearest rounding.
+ * The update operands must not overlap packed.  n == 0 is a no-op.  Returns
+ * W4A16_OK, W4A16_EINVAL, W4A16_EUNSUPPORTED (update_dtype) or W4A16_EHIP.
+ * Repeated requantization is lossy.
+ */
+w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
+                                   const void* mat1, const void* mat2, int64_t rank,
+                                   w4a16_dtype_t update_dtype, float alpha, float beta,
+                                   const uint64_t* rounding_seed, void* stream);
+
+/*
  * A shard of an already packed [n][k] weight, without requantizing ("Piper
  * Kernels", section "NVFP4 construction", partitioning an already quantized
  * weight: packed data is copied, nibble order and scales are preserved, each

@@ -36,7 +36,7 @@ def test_exports_every_declared_function(lib):
     assert {"quantize_rtn_int4_g128", "pack_weights", "w4a16_linear", "unpack_weights",
             "w4a16_packed_bytes", "w4a16_linear_workspace_bytes", "w4a16_status_string",
             "w4a16_linear_with_path", "w4a16_linear_choose_path", "w4a16_linear_act",
-            "w4a16_linear_act_workspace_bytes", "shard_packed_weights"} <= set(names)
+            "w4a16_linear_act_workspace_bytes", "shard_packed_weights", "w4a16_update_packed"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -177,6 +177,26 @@ def test_linear_act_rejects(lib):
     assert lin_act(lib, ge, path=gemm, m=256, k=128, ldx=big, y=A * 8192, ws=None) == B.EWORKSPACE
     assert lib.w4a16_linear_act_workspace_bytes(5, 16, 16, 128) == 0
     assert lib.w4a16_linear_act_workspace_bytes(int(w4.Act.NONE), 1, 2048, 16384) == w4.workspace_bytes(1, 2048, 16384)
+
+
+def test_update_rejects(lib):
+    import ctypes
+    up = lib.w4a16_update_packed
+    seed = ctypes.pointer(ctypes.c_uint64(5))
+    f1 = ctypes.c_float(1.0)
+    assert up(A, 16, 128, A * 4, 128, None, None, 0, 7, f1, f1, None, None) == B.EUNSUPPORTED   # dtype
+    assert up(A, 16, 100, A * 4, 128, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL     # k % 128
+    assert up(A, 16, 128, None, 0, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL        # no update
+    assert up(A, 16, 128, A * 4, 128, A * 8, A * 9, 4, B.F32, f1, f1, None, None) == B.EINVAL   # both forms
+    assert up(A, 16, 128, None, 0, A * 8, None, 4, B.F32, f1, f1, None, None) == B.EINVAL       # mat2 missing
+    assert up(A, 16, 128, None, 0, A * 8, A * 9, 0, B.F32, f1, f1, None, None) == B.EINVAL      # rank 0 low-rank
+    assert up(A, 16, 128, None, 0, A * 8, A * 9, (1 << 16) + 1, B.F32, f1, f1, seed, None) == B.EINVAL  # rank
+    assert up(A, 16, 128, A * 4, 120, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL     # ldu < k
+    assert up(A, 16, 128, A * 4, 130, None, None, 0, B.BF16, f1, f1, None, None) == B.EINVAL    # ldu bytes % 16
+    assert up(A, 16, 128, A * 4 + 8, 128, None, None, 0, B.BF16, f1, f1, None, None) == B.EINVAL  # alignment
+    assert up(A, 16, 128, A + 64, 128, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL    # overlaps packed
+    assert up(None, 16, 128, A * 4, 128, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL
+    assert up(A, 0, 128, A * 4, 128, None, None, 0, B.F32, f1, f1, seed, None) == B.OK          # empty: no-op
 
 
 def test_shard_rejects(lib):

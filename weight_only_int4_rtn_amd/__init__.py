@@ -26,5 +26,6 @@ from ._binding import (  # noqa: F401
     shard,
     status_string,
     unpack,
+    update_,
     workspace_bytes,
 )

@@ -56,6 +56,9 @@ def _declare(lib):
     lib.pack_weights.restype = i32
     lib.unpack_weights.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.unpack_weights.restype = i32
+    lib.w4a16_update_packed.argtypes = [vp, i64, i64, vp, i64, vp, vp, i64, i32, ctypes.c_float, ctypes.c_float,
+                                        ctypes.POINTER(ctypes.c_uint64), vp]
+    lib.w4a16_update_packed.restype = i32
     lib.shard_packed_weights.argtypes = [vp, i64, i64, i32, i64, i64, vp, vp]
     lib.shard_packed_weights.restype = i32
     lib.w4a16_linear_workspace_bytes.argtypes = [i64, i64, i64]
@@ -180,6 +183,36 @@ def unpack(packed: torch.Tensor, n: int, k: int):
     st = lib().unpack_weights(_ptr(packed), n, k, _ptr(codes), _ptr(scales), _stream(packed.device))
     _check(st, "unpack_weights")
     return codes, scales
+
+
+def update_(packed: torch.Tensor, n: int, k: int, update: torch.Tensor | None = None,
+            mat1: torch.Tensor | None = None, mat2: torch.Tensor | None = None,
+            alpha: float = 1.0, beta: float = 1.0, seed: int | None = None) -> torch.Tensor:
+    """In place: packed <- requantize(beta * dequant(packed) + alpha * U), U the
+    dense ``update`` [n, k] or ``mat1`` [n, r] @ ``mat2`` [r, k]; stochastic
+    rounding when ``seed`` (unsigned 64-bit) is given."""
+    _require_cuda(packed, update, mat1, mat2)
+    src = update if update is not None else mat1
+    dt = _w_tag(src.dtype)
+    rank = 0
+    ldu = 0
+    if update is not None:
+        if update.shape[-1] != k or update.stride(-1) != 1:
+            raise ValueError("update must be [n, k] with unit column stride")
+        ldu = update.stride(0)
+    else:
+        mat1 = mat1.contiguous()
+        mat2 = mat2.contiguous()
+        if mat2.dtype != mat1.dtype or mat1.shape[0] != n or mat2.shape != (mat1.shape[1], k):
+            raise ValueError("mat1 [n, r] and mat2 [r, k] of one dtype")
+        rank = mat1.shape[1]
+    sp = None
+    if seed is not None:
+        sp = ctypes.pointer(ctypes.c_uint64(int(seed) & ((1 << 64) - 1)))
+    st = lib().w4a16_update_packed(_ptr(packed), n, k, _ptr(update), ldu, _ptr(mat1), _ptr(mat2), rank, dt,
+                                   float(alpha), float(beta), sp, _stream(packed.device))
+    _check(st, "w4a16_update_packed")
+    return packed
 
 
 def shard(packed: torch.Tensor, n: int, k: int, dim: int, start: int, length: int) -> torch.Tensor:

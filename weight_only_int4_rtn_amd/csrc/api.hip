@@ -30,6 +30,8 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 // The GEMM path addresses a 256-row x tile through one buffer resource
 // (32-bit byte offsets): row stride at most 2^22 elements.
 constexpr int64_t kGemmMaxLd = int64_t(1) << 22;
+// Largest rank of a low-rank update (mat1 [n][rank] @ mat2 [rank][k]).
+constexpr int64_t kMaxRank = int64_t(1) << 16;
 
 bool valid_nk(int64_t n, int64_t k) {
     return n >= 0 && n <= kMaxDim && k > 0 && k <= kMaxDim && k % kGroup == 0;
@@ -109,6 +111,33 @@ w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t*
         overlap(codes, cbytes, scales, sbytes))
         return W4A16_EINVAL;
     return from_hip(launch_unpack(packed, n, k, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
+                                   const void* mat1, const void* mat2, int64_t rank, w4a16_dtype_t update_dtype,
+                                   float alpha, float beta, const uint64_t* rounding_seed, void* stream) {
+    if (update_dtype != W4A16_F32 && update_dtype != W4A16_BF16 && update_dtype != W4A16_F16)
+        return W4A16_EUNSUPPORTED;
+    if (!valid_nk(n, k) || rank < 0 || rank > kMaxRank) return W4A16_EINVAL;
+    const bool dense = update != nullptr;
+    if (dense == (rank > 0) || (dense && (mat1 || mat2)) || (!dense && (!mat1 || !mat2))) return W4A16_EINVAL;
+    if (n == 0) return W4A16_OK;
+    if (!packed || !aligned(packed, 16)) return W4A16_EINVAL;
+    const size_t elem = update_dtype == W4A16_F32 ? 4 : 2;
+    const size_t pbytes = w4a16_packed_bytes(n, k);
+    if (dense) {
+        if (ldu < k || ldu > kMaxDim || !aligned(update, 16) || (size_t(ldu) * elem) % 16 != 0) return W4A16_EINVAL;
+        if (overlap(packed, pbytes, update, span_bytes(n, k, ldu, elem))) return W4A16_EINVAL;
+    } else {
+        if (!aligned(mat2, 16) || !aligned(mat1, elem)) return W4A16_EINVAL;
+        if (overlap(packed, pbytes, mat1, size_t(n) * size_t(rank) * elem) ||
+            overlap(packed, pbytes, mat2, size_t(rank) * size_t(k) * elem))
+            return W4A16_EINVAL;
+    }
+    const int dt = update_dtype == W4A16_F32 ? 0 : update_dtype == W4A16_BF16 ? kActBf16 : kActF16;
+    return from_hip(launch_update(packed, n, k, update, ldu, mat1, mat2, rank, dt, alpha, beta,
+                                  rounding_seed != nullptr, rounding_seed ? *rounding_seed : 0,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, int dim, int64_t start,

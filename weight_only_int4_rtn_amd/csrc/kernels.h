@@ -53,6 +53,12 @@ hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t n, int
                        void* packed, hipStream_t stream);
 hipError_t launch_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, float* scales,
                          hipStream_t stream);
+// In place: packed <- requantize(beta * dequant(packed) + alpha * U), U the
+// dense update [n][ldu] (rank 0) or mat1 [n][rank] @ mat2 [rank][k]; dtype
+// 0 (FP32), kActBf16 or kActF16; stochastic rounding with `seed` when set.
+hipError_t launch_update(void* packed, int64_t n, int64_t k, const void* upd, int64_t ldu, const void* mat1,
+                         const void* mat2, int64_t rank, int dtype, float alpha, float beta, int stochastic,
+                         uint64_t seed, hipStream_t stream);
 // Rows [start, start + len) (dim 0) or group-aligned columns (dim 1) of a
 // packed [n][k] weight into a new packed weight.
 hipError_t launch_shard(const void* packed, int64_t n, int64_t k, int dim, int64_t start, int64_t len,
