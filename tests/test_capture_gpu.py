@@ -1,0 +1,64 @@
+"""The linear layer's calls captured in a HIP graph (torch.cuda.graph) and
+replayed equal the eager calls bit for bit: the calls allocate nothing,
+synchronise nothing and record no memset, and the K-split exchange slots are
+left zero by every replay.  Replays are interleaved with eager work and
+synchronisations, and every replay is checked."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+# (m, n, k, act): GEMV with a K split finished through the exchange slots,
+# MGEMV split, SKINNY split + reduce kernel, GEMM, a fused SwiGLU input, the
+# GEMM path with a materialised GELU input
+CALLS = [(1, 2048, 16384, "NONE"), (6, 520, 8192, "NONE"), (50, 1000, 4096, "NONE"), (300, 2056, 1152, "NONE"),
+         (1, 1024, 4096, "SWIGLU"), (256, 512, 1024, "GELU_TANH")]
+
+
+def test_graph_replays_equal_eager(dev=None):
+    dev = require_gpu()
+    import weight_only_int4_rtn_amd as w4
+    g = torch.Generator().manual_seed(11)
+    setups = []
+    ws_bytes = 16
+    for m, n, k, act in CALLS:
+        w = torch.randn(n, k, generator=g) * 0.02
+        width = 2 * k if act == "SWIGLU" else k
+        x = torch.randn(m, width, generator=g).to(torch.bfloat16).to(dev)
+        b = (torch.randn(n, generator=g) * 0.01).to(torch.bfloat16).to(dev)
+        c, s = w4.quantize(w.to(dev))
+        p = w4.pack(c, s)
+        y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        setups.append((m, n, k, w4.Act[act], x, p, b, y))
+        ws_bytes = max(ws_bytes, w4.workspace_bytes(m, n, k, w4.Act[act]))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def run():
+        for m, n, k, act, x, p, b, y in setups:
+            w4.linear(x, p, n, b, out=y, workspace=ws, act=act)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [s[-1].clone() for s in setups]
+    for s in setups:
+        s[-1].fill_(0.0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"graph replay {rep}")
+        for s in setups:
+            s[-1].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, s in enumerate(setups):
+            assert torch.equal(s[-1], eager[i]), f"replay {rep}, call {i} {CALLS[i]}"
+        assert int(ws[:1 << 20].count_nonzero()) == 0, f"replay {rep}: exchange slots not left zero"
+        # eager work between replays (same workspace, other shapes)
+        w4.linear(setups[2][4], setups[2][5], setups[2][1], workspace=ws)
+        torch.cuda.synchronize()

@@ -60,7 +60,8 @@ def exact_case(m, n, k, seed, dtype, with_bias):
 
 
 EXACT_SHAPES = [(1, 16, 128), (2, 40, 384), (3, 1000, 2048), (4, 2056, 16384), (5, 72, 256),
-                (17, 130, 640), (33, 64, 1152), (64, 2048, 8192), (130, 100, 1152)]
+                (17, 130, 640), (33, 64, 1152), (63, 130, 512), (64, 2048, 8192), (65, 40, 256),
+                (130, 100, 1152), (255, 72, 384), (257, 136, 256)]
 
 
 @pytest.mark.parametrize("path", PATHS)

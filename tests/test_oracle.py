@@ -167,3 +167,16 @@ def test_pins_catch_planted_mistake(desc, old, new):
     assert line, proc.stdout + proc.stderr
     caught = [p for p in line[0][len("FAILED:"):].split(",") if p]
     assert caught, f"no pin caught the planted mistake: {desc}"
+
+
+def test_pins_pass_under_ubsan():
+    """The oracle built with the undefined-behaviour sanitizer (aborting on the
+    first report) passes every pin: no overflow, shift or conversion UB on
+    the paths the pins exercise."""
+    with tempfile.TemporaryDirectory() as d:
+        so_path = os.path.join(d, "libubsan_oracle.so")
+        oracle.build(out=so_path, extra_flags=["-fsanitize=undefined", "-fno-sanitize-recover=all", "-g"])
+        proc = subprocess.run([sys.executable, "-c", _RUNNER.format(root=ROOT, path=so_path)],
+                              capture_output=True, text=True, timeout=600)
+    line = [ln for ln in proc.stdout.splitlines() if ln.startswith("FAILED:")]
+    assert proc.returncode == 0 and line == ["FAILED:"], proc.stdout[-2000:] + proc.stderr[-2000:]

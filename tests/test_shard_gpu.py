@@ -94,3 +94,30 @@ def test_row_shards_reassemble(dev):
     parts = [lib.linear(x, lib.shard(packed, n, k, 0, a, b - a), b - a) for a, b in zip(cuts[:-1], cuts[1:])]
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(parts, dim=1), full)
+
+
+def test_input_feature_shards_sum(dev):
+    """Row-parallel emulation on one device: the layer on group-aligned input
+    feature shards (the matching x columns each), partial outputs summed in
+    FP32 and the bias added once, equals the unsharded layer within the
+    layer's tolerance (the oracle's outputs as the reference)."""
+    from tests.gpu_util import check_close, row_max_dequant
+    lib = w4()
+    m, n, k = 4, 264, 2048
+    g = torch.Generator().manual_seed(3)
+    w = torch.randn(n, k, generator=g) * 0.02
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    b = (torch.randn(n, generator=g) * 0.01).to(torch.bfloat16)
+    codes, scales = lib.quantize(w.to(dev))
+    packed = lib.pack(codes, scales)
+    xd = x.to(dev)
+    total = torch.zeros(m, n, dtype=torch.float32, device=dev)
+    for start in range(0, k, 512):
+        part = lib.shard(packed, n, k, 1, start, 512)
+        total += lib.linear(xd[:, start:start + 512].contiguous(), part, n).float()
+    y = (total + b.to(dev).float()).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    q, s = oracle.quantize(w.numpy())
+    y_ref = oracle.linear(bits(x), tag(torch.bfloat16), q, s, bits(b))
+    xnorm = np.linalg.norm(x.to(torch.float64).numpy(), axis=1)[:, None]
+    check_close(y.cpu().to(torch.float64).numpy(), y_ref, xnorm, row_max_dequant(q, s)[None, :], "K shards summed")
