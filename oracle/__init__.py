@@ -28,6 +28,7 @@ from .oracle import (  # noqa: F401
     nibbles_to_codes,
     num_threads,
     quantize,
+    quantize_int8,
     round16,
     splitmix64,
     uniform,

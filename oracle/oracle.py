@@ -40,6 +40,8 @@ def _declare(lib):
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.oracle_quantize.argtypes = [vp, i32, i64, i64, i64, vp, vp]
     lib.oracle_quantize.restype = i32
+    lib.oracle_quantize_int8.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+    lib.oracle_quantize_int8.restype = i32
     lib.oracle_codes_to_nibbles.argtypes = [vp, i64, i64, vp]
     lib.oracle_codes_to_nibbles.restype = None
     lib.oracle_nibbles_to_codes.argtypes = [vp, i64, i64, vp]
@@ -110,6 +112,20 @@ def quantize(w: np.ndarray, dtype_tag=None, lib=None):
     rc = lib.oracle_quantize(_p(w), tag, n, k, k, _p(q), _p(s))
     if rc != 0:
         raise ValueError(f"oracle_quantize rejected shape {w.shape}")
+    return q, s
+
+
+def quantize_int8(w: np.ndarray, dtype_tag=None, lib=None):
+    """RTN INT8 g128 quantization: (q int8 [n, k] in [-128, 127], s float32 [n, k/128])."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w)
+    n, k = w.shape
+    tag = _dtype_tag(w, dtype_tag)
+    q = np.empty((n, k), dtype=np.int8)
+    s = np.empty((n, max(k // GROUP, 0)), dtype=np.float32)
+    rc = lib.oracle_quantize_int8(_p(w), tag, n, k, k, _p(q), _p(s))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_int8 rejected shape {w.shape}")
     return q, s
 
 

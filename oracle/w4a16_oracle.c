@@ -46,6 +46,13 @@
  * even), which is then the layer's input, as a separately materialised
  * activation would be.
  *
+ * INT8 weights (the Humming integration also supports INT8 weight schemes:
+ * "Kernel dispatch and Humming quantization in PhyAI", section "Choose
+ * precision by layer and hardware"): the same round-to-nearest quantizer with
+ * one FP32 scale per group of 128, the scale mapping the group's largest
+ * magnitude onto code 127 (reading: symmetric, s = amax / 127, codes
+ * clamp(round_half_even(w / s), -128, 127)), one signed code per byte.
+ *
  * Updates of a quantized weight ("Piper Kernels", sections "ConvRot INT8"
  * (add_ / addmm_ with an optional rounding_seed, requantizing the result)
  * and "Stochastic quantization"): W' = beta * dequant(W) + alpha * U, U a
@@ -163,6 +170,48 @@ int oracle_quantize(const void *w, int w_dtype, int64_t n, int64_t k, int64_t ld
                     code = (int)r;
                 }
                 q[row * k + kk] = (int8_t)code;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Round-to-nearest INT8 quantization with one FP32 scale per group of 128.
+ * w: [n][ldw] of w_dtype; q: [n][k] one signed code per byte (the canonical
+ * INT8 storage), s: [n][k/128].  Returns 0, or -1 on a bad shape.
+ */
+int oracle_quantize_int8(const void *w, int w_dtype, int64_t n, int64_t k, int64_t ldw,
+                         int8_t *q, float *s)
+{
+    if (k <= 0 || k % ORACLE_GROUP != 0 || ldw < k || n < 0)
+        return -1;
+    if (fegetround() != FE_TONEAREST)
+        fesetround(FE_TONEAREST);
+    const int64_t groups = k / ORACLE_GROUP;
+    for (int64_t row = 0; row < n; ++row) {
+        for (int64_t g = 0; g < groups; ++g) {
+            float amax = 0.0f;
+            for (int64_t j = 0; j < ORACLE_GROUP; ++j) {
+                float mag = fabsf(weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j));
+                if (mag > amax)
+                    amax = mag;
+            }
+            /* the scale maps the largest magnitude onto code 127 */
+            float scale8 = amax / 127.0f;
+            s[row * groups + g] = scale8;
+            for (int64_t j = 0; j < ORACLE_GROUP; ++j) {
+                int64_t kk = g * ORACLE_GROUP + j;
+                int code8 = 0;
+                if (scale8 != 0.0f) {
+                    float r8 = nearbyintf(weight_as_float(w, w_dtype, row * ldw + kk) / scale8);
+                    if (r8 < -128.0f)
+                        r8 = -128.0f;
+                    if (r8 > 127.0f)
+                        r8 = 127.0f;
+                    code8 = (int)r8;
+                }
+                q[row * k + kk] = (int8_t)code8;
             }
         }
     }

@@ -6,8 +6,8 @@ raises AssertionError on a mismatch.  They are run on the real oracle by
 built on the CPU) to show that each plausible mistake is caught.
 
 What each pin checks against:
-  * hand-worked groups and bytes (tests/golden/), worked from the method's
-    definition by hand;
+  * hand-worked INT4 and INT8 groups and bytes (tests/golden/), worked from
+    the method's definition by hand;
   * exact rational arithmetic (tests/exact.py): the correctly rounded FP32
     scale and quotient, and a brute-force nearest-code search;
   * closed forms: identity-like weights give y = c*x exactly, and integer
@@ -91,25 +91,16 @@ def pin_canonical_nibbles(lib):
         assert np.array_equal(back, q), f"{back} != {q}"
 
 
-def pin_exact_scales_and_codes(lib, seed=11, n=24, k=384):
-    """Exact rationals: s is amax/7 correctly rounded to FP32; each code is the
-    ties-to-even rounding of the correctly rounded FP32 quotient; brute-force
-    nearest codes differ only where the quotient lies within one FP32 ulp of a
-    half-integer."""
-    rng = np.random.default_rng(seed)
-    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
-    # a few groups with planted exact and near half-integer quotients
-    w[0, :128] = 0.0
-    w[0, 0] = np.float32(0.7)
-    w[0, 1:8] = np.float32(0.7) * np.arange(1, 8, dtype=np.float32) / np.float32(14.0)
-    w[1, 128:256] *= np.float32(1e-38)  # subnormal magnitudes
-    q, s = oracle.quantize(w, lib=lib)
+def _check_exact_rtn(w, q, s, qmax, lo, hi):
+    """Returns the number of codes that differ from the brute-force nearest code
+    (each only where the quotient is within one FP32 ulp of a half-integer)."""
+    n, k = w.shape
     near_ties = 0
     for r in range(n):
         for g in range(k // 128):
             seg = w[r, g * 128:(g + 1) * 128]
             amax = max(abs(exact.f32_fraction(v)) for v in seg)
-            want_s = exact.round_to_f32(amax / 7)
+            want_s = exact.round_to_f32(amax / qmax)
             assert float(s[r, g]) == want_s, (r, g, float(s[r, g]), want_s)
             sf = Fraction(want_s)
             for j, v in enumerate(seg):
@@ -120,14 +111,38 @@ def pin_exact_scales_and_codes(lib, seed=11, n=24, k=384):
                     continue
                 ratio = wf / sf
                 quotient = exact.round_to_f32(ratio)
-                want = max(-8, min(7, exact.round_half_even(Fraction(quotient))))
+                want = max(lo, min(hi, exact.round_half_even(Fraction(quotient))))
                 assert got == want, (r, g, j, got, want)
-                brute = exact.argmin_code(wf, sf)
+                # |w - c s| is convex in c, so the nearest code lies within two
+                # of the clamped rounded ratio: search that window exhaustively
+                c = max(lo, min(hi, int(ratio)))
+                brute = exact.argmin_code(wf, sf, max(lo, c - 2), min(hi, c + 2))
                 if brute != got:
                     half = Fraction(2 * exact.round_half_even(ratio - Fraction(1, 2)) + 1, 2)
                     assert abs(ratio - half) <= exact.ulp_f32(float(ratio)), (r, g, j, got, brute)
                     near_ties += 1
-    assert near_ties <= 3, near_ties
+    return near_ties
+
+
+def _planted_weights(seed, n, k, top):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    # a group with planted exact and near half-integer quotients
+    w[0, :128] = 0.0
+    w[0, 0] = np.float32(0.7)
+    w[0, 1:8] = np.float32(0.7) * np.arange(1, 8, dtype=np.float32) / np.float32(2 * top)
+    w[1, 128:256] *= np.float32(1e-38)  # subnormal magnitudes
+    return w
+
+
+def pin_exact_scales_and_codes(lib, seed=11, n=24, k=384):
+    """Exact rationals: s is amax/7 correctly rounded to FP32; each code is the
+    ties-to-even rounding of the correctly rounded FP32 quotient; brute-force
+    nearest codes differ only where the quotient lies within one FP32 ulp of a
+    half-integer."""
+    w = _planted_weights(seed, n, k, 7)
+    q, s = oracle.quantize(w, lib=lib)
+    assert _check_exact_rtn(w, q, s, 7, -8, 7) <= 3
 
 
 def pin_invariants(lib, w=None, seed=5):
@@ -158,6 +173,65 @@ def pin_invariants(lib, w=None, seed=5):
         f = np.float32(2.0 ** j)
         qj, sj = oracle.quantize(w * f, lib=lib)
         assert np.array_equal(qj, q) and np.array_equal(sj, s * f)
+
+
+def pin_int8_hand_worked_groups(lib):
+    """Golden: hand-worked RTN INT8 groups (ties to even, s = amax/127, zero group)."""
+    for line in _read_lines("rtn8_hand_worked.txt"):
+        name, wtxt, stxt, qtxt = [p.strip() for p in line.split("|")]
+        w = np.zeros((1, 128), dtype=np.float32)
+        for i, v in _pairs(wtxt, float).items():
+            w[0, i] = np.float32(v)
+        want_q = np.zeros(128, dtype=np.int8)
+        for i, v in _pairs(qtxt, int).items():
+            want_q[i] = v
+        q, s = oracle.quantize_int8(w, lib=lib)
+        assert s[0, 0] == np.float32(stxt), f"{name}: scale {s[0,0]!r} != {stxt}"
+        assert np.array_equal(q[0], want_q), f"{name}: codes {q[0][:16]} != {want_q[:16]}"
+
+
+def pin_int8_exact_scales_and_codes(lib, seed=12, n=16, k=384):
+    """Exact rationals for INT8: s is amax/127 correctly rounded to FP32; each
+    code is the ties-to-even rounding of the correctly rounded FP32 quotient,
+    and equals the brute-force nearest code in [-128, 127] except within one
+    FP32 ulp of a half-integer."""
+    w = _planted_weights(seed, n, k, 127)
+    q, s = oracle.quantize_int8(w, lib=lib)
+    assert _check_exact_rtn(w, q, s, 127, -128, 127) <= 3
+
+
+def pin_int8_invariants(lib, w=None, seed=6):
+    """INT8 codes in [-127, 127]; |w - q s| <= s (1/2 + 2^-16); every nonzero
+    group has a code of magnitude 127; zero groups give s = +0 and q = 0;
+    quantize(-w) = (-q, s); quantize(2^j w) = (q, 2^j s); the INT8 scale is the
+    INT4 scale times 7/127 up to FP32 rounding."""
+    if w is None:
+        rng = np.random.default_rng(seed)
+        w = (rng.standard_normal((48, 1024)) * 0.02).astype(np.float32)
+        w[3, 256:384] = 0.0
+        w[5, :] = -0.0
+        mask = rng.random(w.shape) < 0.01
+        w[mask] = (rng.standard_normal(mask.sum()) * 0.2).astype(np.float32)
+    n, k = w.shape
+    q, s = oracle.quantize_int8(w, lib=lib)
+    assert q.min() >= -127 and q.max() <= 127, (q.min(), q.max())
+    s_full = np.repeat(s.astype(np.float64), 128, axis=1)
+    err = np.abs(w.astype(np.float64) - q.astype(np.float64) * s_full)
+    assert np.all(err <= s_full * (0.5 + 2.0 ** -16)), float((err / np.maximum(s_full, 1e-300)).max())
+    qg = np.abs(q.reshape(n, k // 128, 128).astype(np.int32)).max(axis=2)
+    zero = np.all(w.reshape(n, k // 128, 128) == 0, axis=2)
+    assert np.all(qg[~zero] == 127)
+    assert np.all(s[zero] == 0) and not np.any(np.signbit(s[zero]))
+    assert np.all(q.reshape(n, k // 128, 128)[zero] == 0)
+    qn, sn = oracle.quantize_int8(-w, lib=lib)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    for j in (5, -5):
+        f = np.float32(2.0 ** j)
+        qj, sj = oracle.quantize_int8(w * f, lib=lib)
+        assert np.array_equal(qj, q) and np.array_equal(sj, s * f)
+    _, s4 = oracle.quantize(w, lib=lib)
+    ratio = s.astype(np.float64)[~zero] * 127 / (s4.astype(np.float64)[~zero] * 7)
+    assert np.all(np.abs(ratio - 1) < 2.0 ** -22), float(np.abs(ratio - 1).max())
 
 
 def pin_decoders(lib):
@@ -502,6 +576,9 @@ ALL_PINS = [
     pin_canonical_nibbles,
     pin_exact_scales_and_codes,
     pin_invariants,
+    pin_int8_hand_worked_groups,
+    pin_int8_exact_scales_and_codes,
+    pin_int8_invariants,
     pin_decoders,
     pin_identity_like,
     pin_exact_integer_gemm,

@@ -124,6 +124,19 @@ MUTANTS = [
     ("dense update row stride ignored", "p = update_value(upd, u_dtype, row * ldu + kk);",
      "p = update_value(upd, u_dtype, row * k + kk);"),
     ("stochastic outside the interior", "if (has_seed && lo >= -8.0f && lo + 1.0f <= 7.0f) {", "if (has_seed) {"),
+    ("int8 divisor 128", "onto code 127 */\n            float scale8 = amax / 127.0f;",
+     "onto code 127 */\n            float scale8 = amax / 128.0f;"),
+    ("int8 divisor 255", "onto code 127 */\n            float scale8 = amax / 127.0f;",
+     "onto code 127 */\n            float scale8 = amax / 255.0f;"),
+    ("int8 ties away from zero", "float r8 = nearbyintf(", "float r8 = roundf("),
+    ("int8 truncation", "float r8 = nearbyintf(", "float r8 = truncf("),
+    ("int8 clamp at 126", "if (r8 > 127.0f)\n                        r8 = 127.0f;",
+     "if (r8 > 126.0f)\n                        r8 = 126.0f;"),
+    ("int8 signed max", "float mag = fabsf(weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j));",
+     "float mag = weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j);"),
+    ("int8 absmax over the first group", "float mag = fabsf(weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j));",
+     "float mag = fabsf(weight_as_float(w, w_dtype, row * ldw + j));"),
+    ("int8 codes written to the group start", "q[row * k + kk] = (int8_t)code8;", "q[row * k + g * ORACLE_GROUP] = (int8_t)code8;"),
     ("update scale divisor 8", "const float scale = amax / 7.0f;\n            s[row * groups + g] = scale;",
      "const float scale = amax / 8.0f;\n            s[row * groups + g] = scale;"),
 ]
