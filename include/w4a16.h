@@ -269,6 +269,59 @@ w4a16_status_t w4a16_linear_act(w4a16_act_t act, w4a16_path_t path, const void* 
 /* The path w4a16_linear would take for these sizes (never W4A16_PATH_AUTO). */
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k);
 
+/* ------------------------------------------------------------------------
+ * W8A16: INT8 weights.  The same integration lists INT8 beside INT4 among
+ * its weight schemes ("Kernel dispatch and Humming quantization in PhyAI",
+ * section "Choose precision by layer and hardware"); the method is the same
+ * round-to-nearest quantizer with one FP32 scale per group of 128 along K,
+ * with the 8-bit code range.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Round-to-nearest INT8 quantization, group 128:
+ *   s[n][g] = fl32(max_{k in group g} |w[n][k]| / 127)      (FP32 division)
+ *   q[n][k] = clamp(round_half_even(fl32(w[n][k] / s)), -128, 127), 0 if s == 0
+ * (-128 is never produced).  Arguments as for quantize_rtn_int4_g128, except
+ *   codes   device, [n][k] int8, one two's-complement code per byte; 8-byte
+ *           aligned.
+ * Returns W4A16_OK (also for n == 0), W4A16_EINVAL, W4A16_EUNSUPPORTED or
+ * W4A16_EHIP.
+ */
+w4a16_status_t quantize_rtn_int8_g128(const void* w, w4a16_dtype_t w_dtype, int64_t n, int64_t k,
+                                      int64_t ldw, int8_t* codes, float* scales, void* stream);
+
+/* Size in bytes of the packed INT8 weight for an [n][k] layer (0 for invalid sizes). */
+size_t w8a16_packed_bytes(int64_t n, int64_t k);
+
+/*
+ * INT8 canonical codes [n][k] and scales [n][k/128] -> the packed INT8
+ * execution layout (w8a16_packed_bytes(n, k) bytes), and its exact inverse.
+ * codes and scales 4-byte aligned, packed 16-byte aligned, no overlaps.
+ * Returns W4A16_OK, W4A16_EINVAL or W4A16_EHIP.
+ */
+w4a16_status_t pack_weights_int8(const int8_t* codes, const float* scales, int64_t n, int64_t k, void* packed,
+                                 void* stream);
+w4a16_status_t unpack_weights_int8(const void* packed, int64_t n, int64_t k, int8_t* codes, float* scales,
+                                   void* stream);
+
+/* Workspace bytes w8a16_linear needs (0 if none; 0 for an unknown act); header rules as above. */
+size_t w8a16_linear_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k);
+
+/*
+ * y[m][n] = act(x)[m][k] . dequant(packed)^T + bias[n] for a packed INT8
+ * weight (from pack_weights_int8): the arithmetic, arguments, activations,
+ * no-op cases, overlap rules and status codes of w4a16_linear_act.  Paths:
+ * W4A16_PATH_AUTO, W4A16_PATH_GEMV (row blocks of 4) and W4A16_PATH_SKINNY
+ * (any m); W4A16_PATH_MGEMV and W4A16_PATH_GEMM give W4A16_EUNSUPPORTED.
+ * workspace >= w8a16_linear_workspace_bytes(act, m, n, k) bytes.
+ */
+w4a16_status_t w8a16_linear(w4a16_act_t act, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                            int64_t m, int64_t k, int64_t ldx, const void* packed, int64_t n, const void* bias,
+                            void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The path w8a16_linear takes for these sizes with W4A16_PATH_AUTO. */
+w4a16_path_t w8a16_linear_choose_path(int64_t m, int64_t n, int64_t k);
+
 /* Static, human-readable text for a status code. */
 const char* w4a16_status_string(w4a16_status_t status);
 

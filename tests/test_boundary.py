@@ -36,7 +36,9 @@ def test_exports_every_declared_function(lib):
     assert {"quantize_rtn_int4_g128", "pack_weights", "w4a16_linear", "unpack_weights",
             "w4a16_packed_bytes", "w4a16_linear_workspace_bytes", "w4a16_status_string",
             "w4a16_linear_with_path", "w4a16_linear_choose_path", "w4a16_linear_act",
-            "w4a16_linear_act_workspace_bytes", "shard_packed_weights", "w4a16_update_packed"} <= set(names)
+            "w4a16_linear_act_workspace_bytes", "shard_packed_weights", "w4a16_update_packed",
+            "quantize_rtn_int8_g128", "w8a16_packed_bytes", "pack_weights_int8", "unpack_weights_int8",
+            "w8a16_linear_workspace_bytes", "w8a16_linear", "w8a16_linear_choose_path"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -213,6 +215,60 @@ def test_shard_rejects(lib):
     assert sh(None, 100, 640, 0, 0, 10, A * 4, None) == B.EINVAL
     assert sh(A, 100, 640, 0, 0, 10, A + 8, None) == B.EINVAL        # misaligned / overlapping out
     assert sh(A, 100, 640, 0, 0, 10, A + 4096, None) == B.EINVAL     # out inside the packed weight
+
+
+def test_int8_packed_bytes_and_paths(lib):
+    # 16-row tiles x 128-column groups, 2048 code bytes + 64 scale bytes each
+    assert w4.packed_bytes(16, 128, bits=8) == 2112
+    assert w4.packed_bytes(17, 256, bits=8) == 2 * 2 * 2112
+    assert w4.packed_bytes(0, 128, bits=8) == 0
+    assert w4.packed_bytes(16, 100, bits=8) == 0
+    with pytest.raises(ValueError):
+        w4.packed_bytes(16, 128, bits=2)
+    assert w4.choose_path(1, 2048, 2048, bits=8) == w4.Path.GEMV
+    assert w4.choose_path(4, 2048, 2048, bits=8) == w4.Path.GEMV
+    for m in (5, 16, 50, 256, 4096):
+        assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.SKINNY
+    assert w4.workspace_bytes(1, 2048, 100, bits=8) == 0
+    assert w4.workspace_bytes(1, 2048, 16384, bits=8) > 0
+    assert lib.w8a16_linear_workspace_bytes(5, 16, 16, 128) == 0       # unknown activation
+
+
+def test_int8_quantize_and_pack_reject(lib):
+    q8 = lib.quantize_rtn_int8_g128
+    assert q8(A, B.F32, 4, 100, 100, A * 2, A * 3, None) == B.EINVAL      # k % 128
+    assert q8(A, 7, 4, 128, 128, A * 2, A * 3, None) == B.EUNSUPPORTED    # dtype
+    assert q8(A, B.F32, 4, 128, 128, A * 2 + 4, A * 3, None) == B.EINVAL  # codes not 8-byte aligned
+    assert q8(A, B.F32, 4, 128, 128, A, A * 3, None) == B.EINVAL          # codes overlap w
+    assert q8(A, B.F32, 4, 128, 128, A * 2, A * 2 + 256, None) == B.EINVAL  # scales inside the codes
+    assert q8(A, B.F32, 0, 128, 128, None, None, None) == B.OK            # empty: no-op
+    assert lib.pack_weights_int8(A, A * 2, 4, 100, A * 3, None) == B.EINVAL
+    assert lib.pack_weights_int8(A, A * 2, 4, 128, A * 3 + 8, None) == B.EINVAL
+    assert lib.pack_weights_int8(A, A * 2, 4, 128, A + 256, None) == B.EINVAL  # packed overlaps codes
+    assert lib.pack_weights_int8(A, A * 2, 0, 128, A * 3, None) == B.OK
+    assert lib.unpack_weights_int8(A * 3, 4, 128, A, A + 256, None) == B.EINVAL  # codes overlap scales
+    assert lib.unpack_weights_int8(A * 3, 0, 128, A, A * 2, None) == B.OK
+
+
+def lin8(lib, fn=0, path=0, x=A, act=B.BF16, m=1, k=128, ldx=128, packed=A * 4, n=16, bias=None, y=A * 8,
+         ldy=16, ws=None, ws_bytes=0):
+    return lib.w8a16_linear(fn, path, x, act, m, k, ldx, packed, n, bias, y, ldy, ws, ws_bytes, None)
+
+
+def test_int8_linear_rejects(lib):
+    assert lin8(lib, 3) == B.EINVAL                                         # unknown activation
+    assert lin8(lib, path=int(w4.Path.MGEMV)) == B.EUNSUPPORTED             # INT8: GEMV and SKINNY only
+    assert lin8(lib, path=int(w4.Path.GEMM), m=256) == B.EUNSUPPORTED
+    assert lin8(lib, path=9) == B.EINVAL
+    assert lin8(lib, act=B.F32) == B.EUNSUPPORTED
+    assert lin8(lib, k=100, ldx=104) == B.EINVAL
+    assert lin8(lib, fn=int(w4.Act.SWIGLU), ldx=128) == B.EINVAL             # [up | gate] needs 2k
+    assert lin8(lib, y=A * 4 + 2048) == B.EINVAL                            # y inside the INT8 packed weight
+    assert lin8(lib, y=A * 4 + 1200) == B.EINVAL                            # (an INT4 weight would end at 1088)
+    assert lin8(lib, m=0) == B.OK
+    need = w4.workspace_bytes(1, 2048, 32768, bits=8)
+    assert need > 0
+    assert lin8(lib, m=1, k=32768, ldx=32768, n=2048, ldy=2048, y=A * 1024, path=int(w4.Path.GEMV)) == B.EWORKSPACE
 
 
 def test_binding_rejects_cpu_tensors():

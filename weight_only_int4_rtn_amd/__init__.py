@@ -9,6 +9,12 @@ behind the C ABI of ``include/w4a16.h``.
     packed = pack(codes, scales)         # load time
     y = linear(x, packed, n, bias)       # every forward step
     y = linear(up_gate, packed_down, n, act=Act.SWIGLU)   # activation fused into the input
+
+INT8 weights (W8A16) take the same calls with the 8-bit quantizer:
+
+    codes8, scales8 = quantize_int8(w)
+    packed8 = pack_int8(codes8, scales8)
+    y = linear(x, packed8, n, bias, bits=8)
 """
 import torch  # noqa: F401  (load torch's HIP runtime before the library)
 
@@ -21,11 +27,14 @@ from ._binding import (  # noqa: F401
     lib,
     linear,
     pack,
+    pack_int8,
     packed_bytes,
     quantize,
+    quantize_int8,
     shard,
     status_string,
     unpack,
+    unpack_int8,
     update_,
     workspace_bytes,
 )

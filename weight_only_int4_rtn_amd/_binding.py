@@ -73,6 +73,20 @@ def _declare(lib):
     lib.w4a16_linear_act.restype = i32
     lib.w4a16_linear_choose_path.argtypes = [i64, i64, i64]
     lib.w4a16_linear_choose_path.restype = i32
+    lib.quantize_rtn_int8_g128.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.quantize_rtn_int8_g128.restype = i32
+    lib.w8a16_packed_bytes.argtypes = [i64, i64]
+    lib.w8a16_packed_bytes.restype = sz
+    lib.pack_weights_int8.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.pack_weights_int8.restype = i32
+    lib.unpack_weights_int8.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.unpack_weights_int8.restype = i32
+    lib.w8a16_linear_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.w8a16_linear_workspace_bytes.restype = sz
+    lib.w8a16_linear.argtypes = [i32, i32, vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, sz, vp]
+    lib.w8a16_linear.restype = i32
+    lib.w8a16_linear_choose_path.argtypes = [i64, i64, i64]
+    lib.w8a16_linear_choose_path.restype = i32
     lib.w4a16_status_string.argtypes = [i32]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     return lib
@@ -132,17 +146,29 @@ def _require_cuda(*ts):
 # ---------------------------------------------------------------------------
 
 
-def packed_bytes(n: int, k: int) -> int:
+def _bits(bits: int) -> int:
+    if bits not in (4, 8):
+        raise ValueError(f"weights are INT4 or INT8 (bits 4 or 8), got {bits}")
+    return bits
+
+
+def packed_bytes(n: int, k: int, bits: int = 4) -> int:
+    if _bits(bits) == 8:
+        return int(lib().w8a16_packed_bytes(n, k))
     return int(lib().w4a16_packed_bytes(n, k))
 
 
-def workspace_bytes(m: int, n: int, k: int, act: Act = Act.NONE) -> int:
+def workspace_bytes(m: int, n: int, k: int, act: Act = Act.NONE, bits: int = 4) -> int:
+    if _bits(bits) == 8:
+        return int(lib().w8a16_linear_workspace_bytes(int(act), m, n, k))
     if act == Act.NONE:
         return int(lib().w4a16_linear_workspace_bytes(m, n, k))
     return int(lib().w4a16_linear_act_workspace_bytes(int(act), m, n, k))
 
 
-def choose_path(m: int, n: int, k: int) -> Path:
+def choose_path(m: int, n: int, k: int, bits: int = 4) -> Path:
+    if _bits(bits) == 8:
+        return Path(lib().w8a16_linear_choose_path(m, n, k))
     return Path(lib().w4a16_linear_choose_path(m, n, k))
 
 
@@ -182,6 +208,46 @@ def unpack(packed: torch.Tensor, n: int, k: int):
     scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=packed.device)
     st = lib().unpack_weights(_ptr(packed), n, k, _ptr(codes), _ptr(scales), _stream(packed.device))
     _check(st, "unpack_weights")
+    return codes, scales
+
+
+def quantize_int8(w: torch.Tensor):
+    """RTN INT8 g128: w [n, k] (f32/bf16/f16, rows contiguous) -> (codes [n, k] int8, scales [n, k/128] f32)."""
+    _require_cuda(w)
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D tensor with contiguous rows")
+    n, k = w.shape
+    codes = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=w.device)
+    st = lib().quantize_rtn_int8_g128(_ptr(w), _w_tag(w.dtype), n, k, w.stride(0), _ptr(codes),
+                                      _ptr(scales), _stream(w.device))
+    _check(st, "quantize_rtn_int8_g128")
+    return codes, scales
+
+
+def pack_int8(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """INT8 codes [n, k] + scales [n, k/128] -> packed INT8 execution layout (uint8, 1-D)."""
+    _require_cuda(codes, scales)
+    if codes.dtype != torch.int8:
+        raise ValueError("INT8 codes must be torch.int8")
+    n, k = codes.shape
+    codes = codes.contiguous()
+    scales = scales.contiguous()
+    nbytes = packed_bytes(n, k, 8)
+    if nbytes == 0 and n > 0:
+        raise ValueError(f"invalid layer shape n={n}, k={k}")
+    packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    st = lib().pack_weights_int8(_ptr(codes), _ptr(scales), n, k, _ptr(packed), _stream(codes.device))
+    _check(st, "pack_weights_int8")
+    return packed
+
+
+def unpack_int8(packed: torch.Tensor, n: int, k: int):
+    _require_cuda(packed)
+    codes = torch.empty((n, k), dtype=torch.int8, device=packed.device)
+    scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=packed.device)
+    st = lib().unpack_weights_int8(_ptr(packed), n, k, _ptr(codes), _ptr(scales), _stream(packed.device))
+    _check(st, "unpack_weights_int8")
     return codes, scales
 
 
@@ -244,9 +310,11 @@ def workspace_for(device, stream_handle: int, nbytes: int) -> torch.Tensor | Non
 
 def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | None = None,
            out: torch.Tensor | None = None, path: Path = Path.AUTO,
-           workspace: torch.Tensor | None = None, act: Act = Act.NONE) -> torch.Tensor:
+           workspace: torch.Tensor | None = None, act: Act = Act.NONE, bits: int = 4) -> torch.Tensor:
     """y = act(x) . dequant(packed)^T + bias for x [..., k] (bf16/f16) -> y [..., n]
-    (x's dtype).  With ``act=Act.SWIGLU`` the rows of x are [up | gate], 2k values."""
+    (x's dtype).  With ``act=Act.SWIGLU`` the rows of x are [up | gate], 2k values.
+    ``bits=8``: ``packed`` is a packed INT8 weight (``pack_int8``)."""
+    bits = _bits(bits)
     _require_cuda(x, packed, bias, out)
     if x.requires_grad or (bias is not None and bias.requires_grad):
         raise ValueError("inference only: autograd inputs are not supported")
@@ -273,10 +341,15 @@ def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | N
     if y2 is None:
         raise ValueError("out must be contiguous")
     stream = _stream(x.device)
-    need = workspace_bytes(m, n, k, act)
+    need = workspace_bytes(m, n, k, act, bits)
     if workspace is None:
         workspace = workspace_for(x.device, stream.value, need)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if bits == 8:
+        st = lib().w8a16_linear(int(act), int(path), _ptr(x2), dt, m, k, x2.stride(0), _ptr(packed), n,
+                                _ptr(bias), _ptr(y2), n, _ptr(workspace), ws_bytes, stream)
+        _check(st, "w8a16_linear")
+        return out
     if act == Act.NONE:
         st = lib().w4a16_linear_with_path(int(path), _ptr(x2), dt, m, k, x2.stride(0), _ptr(packed), n,
                                           _ptr(bias), _ptr(y2), n, _ptr(workspace), ws_bytes, stream)

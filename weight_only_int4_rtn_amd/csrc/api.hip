@@ -39,14 +39,45 @@ bool valid_nk(int64_t n, int64_t k) {
 
 w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_EHIP; }
 
-size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k) {
+size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bits) {
     switch (path) {
-        case W4A16_PATH_GEMV: return plan_gemv(m < 4 ? m : 4, n, k).workspace;
-        case W4A16_PATH_MGEMV: return plan_mgemv(m < 16 ? m : 16, n, k).workspace;
-        case W4A16_PATH_SKINNY: return plan_skinny(m, n, k).workspace;
-        case W4A16_PATH_GEMM: return plan_gemm(m, n, k).workspace;
+        case W4A16_PATH_GEMV: return plan_gemv(m < 4 ? m : 4, n, k, bits).workspace;
+        case W4A16_PATH_MGEMV: return bits == 4 ? plan_mgemv(m < 16 ? m : 16, n, k).workspace : 0;
+        case W4A16_PATH_SKINNY: return plan_skinny(m, n, k, bits).workspace;
+        case W4A16_PATH_GEMM: return bits == 4 ? plan_gemm(m, n, k).workspace : 0;
         default: return 0;
     }
+}
+
+// Shared argument checks of quantize (either code width).
+w4a16_status_t check_quantize(const void* w, w4a16_dtype_t w_dtype, int64_t n, int64_t k, int64_t ldw,
+                              const void* codes, size_t cbytes, uintptr_t calign, const float* scales) {
+    if (w_dtype != W4A16_F32 && w_dtype != W4A16_BF16 && w_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
+    if (!valid_nk(n, k) || ldw < k || ldw > kMaxDim) return W4A16_EINVAL;
+    if (n == 0) return W4A16_OK;
+    const size_t elem = w_dtype == W4A16_F32 ? 4 : 2;
+    if (!w || !codes || !scales) return W4A16_EINVAL;
+    if (!aligned(w, 16) || (size_t(ldw) * elem) % 16 != 0) return W4A16_EINVAL;
+    if (!aligned(codes, calign) || !aligned(scales, 4)) return W4A16_EINVAL;
+    const size_t wbytes = span_bytes(n, k, ldw, elem), sbytes = size_t(n) * size_t(k / kGroup) * 4;
+    if (overlap(w, wbytes, codes, cbytes) || overlap(w, wbytes, scales, sbytes) ||
+        overlap(codes, cbytes, scales, sbytes))
+        return W4A16_EINVAL;
+    return W4A16_OK;
+}
+
+// Shared argument checks of pack / unpack (either code width).
+w4a16_status_t check_pack(const void* codes, size_t cbytes, const float* scales, int64_t n, int64_t k,
+                          const void* packed, size_t pbytes, bool codes_out) {
+    if (!valid_nk(n, k)) return W4A16_EINVAL;
+    if (n == 0) return W4A16_OK;
+    if (!codes || !scales || !packed) return W4A16_EINVAL;
+    if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(packed, 16)) return W4A16_EINVAL;
+    const size_t sbytes = size_t(n) * size_t(k / kGroup) * 4;
+    if (overlap(packed, pbytes, codes, cbytes) || overlap(packed, pbytes, scales, sbytes) ||
+        (codes_out && overlap(codes, cbytes, scales, sbytes)))
+        return W4A16_EINVAL;
+    return W4A16_OK;
 }
 
 }  // namespace
@@ -69,48 +100,61 @@ size_t w4a16_packed_bytes(int64_t n, int64_t k) {
     return size_t(Layout(n, k).bytes());
 }
 
+size_t w8a16_packed_bytes(int64_t n, int64_t k) {
+    if (!valid_nk(n, k)) return 0;
+    return size_t(Layout(n, k, 8).bytes());
+}
+
 w4a16_status_t quantize_rtn_int4_g128(const void* w, w4a16_dtype_t w_dtype, int64_t n, int64_t k,
                                       int64_t ldw, uint8_t* codes, float* scales, void* stream) {
-    if (w_dtype != W4A16_F32 && w_dtype != W4A16_BF16 && w_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
-    if (!valid_nk(n, k) || ldw < k || ldw > kMaxDim) return W4A16_EINVAL;
-    if (n == 0) return W4A16_OK;
-    const size_t elem = w_dtype == W4A16_F32 ? 4 : 2;
-    if (!w || !codes || !scales) return W4A16_EINVAL;
-    if (!aligned(w, 16) || (size_t(ldw) * elem) % 16 != 0) return W4A16_EINVAL;
-    if (!aligned(codes, 4) || !aligned(scales, 4)) return W4A16_EINVAL;
-    const size_t wbytes = span_bytes(n, k, ldw, elem), cbytes = size_t(n) * size_t(k) / 2,
-                 sbytes = size_t(n) * size_t(k / kGroup) * 4;
-    if (overlap(w, wbytes, codes, cbytes) || overlap(w, wbytes, scales, sbytes) ||
-        overlap(codes, cbytes, scales, sbytes))
-        return W4A16_EINVAL;
+    const w4a16_status_t st =
+        check_quantize(w, w_dtype, n, k, ldw, codes, size_t(n > 0 ? n : 0) * size_t(k > 0 ? k : 0) / 2, 4, scales);
+    if (st != W4A16_OK || n == 0) return st;
     return from_hip(launch_quantize(w, int(w_dtype), n, k, ldw, codes, scales,
                                     static_cast<hipStream_t>(stream)));
 }
 
+w4a16_status_t quantize_rtn_int8_g128(const void* w, w4a16_dtype_t w_dtype, int64_t n, int64_t k,
+                                      int64_t ldw, int8_t* codes, float* scales, void* stream) {
+    const w4a16_status_t st =
+        check_quantize(w, w_dtype, n, k, ldw, codes, size_t(n > 0 ? n : 0) * size_t(k > 0 ? k : 0), 8, scales);
+    if (st != W4A16_OK || n == 0) return st;
+    return from_hip(launch_quantize8(w, int(w_dtype), n, k, ldw, codes, scales,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 w4a16_status_t pack_weights(const uint8_t* codes, const float* scales, int64_t n, int64_t k,
                             void* packed, void* stream) {
-    if (!valid_nk(n, k)) return W4A16_EINVAL;
-    if (n == 0) return W4A16_OK;
-    if (!codes || !scales || !packed) return W4A16_EINVAL;
-    if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(packed, 16)) return W4A16_EINVAL;
-    const size_t cbytes = size_t(n) * size_t(k) / 2, sbytes = size_t(n) * size_t(k / kGroup) * 4,
-                 pbytes = w4a16_packed_bytes(n, k);
-    if (overlap(packed, pbytes, codes, cbytes) || overlap(packed, pbytes, scales, sbytes)) return W4A16_EINVAL;
+    const w4a16_status_t st =
+        check_pack(codes, size_t(n > 0 ? n : 0) * size_t(k > 0 ? k : 0) / 2, scales, n, k, packed,
+                   w4a16_packed_bytes(n, k), false);
+    if (st != W4A16_OK || n == 0) return st;
     return from_hip(launch_pack(codes, scales, n, k, packed, static_cast<hipStream_t>(stream)));
 }
 
 w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t* codes, float* scales,
                               void* stream) {
-    if (!valid_nk(n, k)) return W4A16_EINVAL;
-    if (n == 0) return W4A16_OK;
-    if (!codes || !scales || !packed) return W4A16_EINVAL;
-    if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(packed, 16)) return W4A16_EINVAL;
-    const size_t cbytes = size_t(n) * size_t(k) / 2, sbytes = size_t(n) * size_t(k / kGroup) * 4,
-                 pbytes = w4a16_packed_bytes(n, k);
-    if (overlap(packed, pbytes, codes, cbytes) || overlap(packed, pbytes, scales, sbytes) ||
-        overlap(codes, cbytes, scales, sbytes))
-        return W4A16_EINVAL;
+    const w4a16_status_t st =
+        check_pack(codes, size_t(n > 0 ? n : 0) * size_t(k > 0 ? k : 0) / 2, scales, n, k, packed,
+                   w4a16_packed_bytes(n, k), true);
+    if (st != W4A16_OK || n == 0) return st;
     return from_hip(launch_unpack(packed, n, k, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status_t pack_weights_int8(const int8_t* codes, const float* scales, int64_t n, int64_t k, void* packed,
+                                 void* stream) {
+    const w4a16_status_t st = check_pack(codes, size_t(n > 0 ? n : 0) * size_t(k > 0 ? k : 0), scales, n, k,
+                                         packed, w8a16_packed_bytes(n, k), false);
+    if (st != W4A16_OK || n == 0) return st;
+    return from_hip(launch_pack8(codes, scales, n, k, packed, static_cast<hipStream_t>(stream)));
+}
+
+w4a16_status_t unpack_weights_int8(const void* packed, int64_t n, int64_t k, int8_t* codes, float* scales,
+                                   void* stream) {
+    const w4a16_status_t st = check_pack(codes, size_t(n > 0 ? n : 0) * size_t(k > 0 ? k : 0), scales, n, k,
+                                         packed, w8a16_packed_bytes(n, k), true);
+    if (st != W4A16_OK || n == 0) return st;
+    return from_hip(launch_unpack8(packed, n, k, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
 w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
@@ -162,6 +206,12 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     return W4A16_PATH_GEMM;
 }
 
+w4a16_path_t w8a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
+    (void)n;
+    (void)k;
+    return m <= 4 ? W4A16_PATH_GEMV : W4A16_PATH_SKINNY;
+}
+
 }  // extern "C"
 
 namespace {
@@ -170,27 +220,28 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace of one path with an activation: the large-M path materialises
 // the activated input [m][k] after its own workspace.
-size_t act_path_workspace(int act_fn, w4a16_path_t path, int64_t m, int64_t n, int64_t k) {
-    const size_t base = path_workspace(path, m, n, k);
+size_t act_path_workspace(int act_fn, w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bits) {
+    const size_t base = path_workspace(path, m, n, k, bits);
     if (act_fn == kActFnNone || path != W4A16_PATH_GEMM) return base;
     return round_up(base, 256) + size_t(m) * size_t(k) * 2;
 }
 
-size_t act_workspace_bytes(int act_fn, int64_t m, int64_t n, int64_t k) {
+size_t act_workspace_bytes(int act_fn, int64_t m, int64_t n, int64_t k, int bits) {
     if (m <= 0 || !valid_nk(n, k) || n == 0 || m > kMaxDim) return 0;
     size_t best = 0;
     const w4a16_path_t paths[4] = {W4A16_PATH_GEMV, W4A16_PATH_MGEMV, W4A16_PATH_SKINNY, W4A16_PATH_GEMM};
     for (w4a16_path_t p : paths) {
-        const size_t b = act_path_workspace(act_fn, p, m, n, k);
+        const size_t b = act_path_workspace(act_fn, p, m, n, k, bits);
         best = b > best ? b : best;
     }
     return best;
 }
 
-// y = act(x) . dequant(packed)^T + bias on one kernel path (act_fn: ActFn).
-w4a16_status_t linear_impl(int act_fn, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype, int64_t m,
-                           int64_t k, int64_t ldx, const void* packed, int64_t n, const void* bias, void* y,
-                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+// y = act(x) . dequant(packed)^T + bias on one kernel path (act_fn: ActFn;
+// bits: 4 or 8, the packed weight's code width).
+w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                           int64_t m, int64_t k, int64_t ldx, const void* packed, int64_t n, const void* bias,
+                           void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
     if (act_dtype != W4A16_BF16 && act_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
     if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MGEMV &&
         path != W4A16_PATH_SKINNY && path != W4A16_PATH_GEMM)
@@ -206,14 +257,17 @@ w4a16_status_t linear_impl(int act_fn, w4a16_path_t path, const void* x, w4a16_d
     // is ldx, or k for the materialised activation
     const int64_t gemm_ld = act_fn == kActFnNone ? ldx : k;
     if (path == W4A16_PATH_AUTO) {
-        path = w4a16_linear_choose_path(m, n, k);
+        path = bits == 8 ? w8a16_linear_choose_path(m, n, k) : w4a16_linear_choose_path(m, n, k);
         if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) path = W4A16_PATH_SKINNY;
     }
     if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) return W4A16_EUNSUPPORTED;
+    // INT8 weights run on the GEMV and SKINNY kernels
+    if (bits == 8 && (path == W4A16_PATH_MGEMV || path == W4A16_PATH_GEMM)) return W4A16_EUNSUPPORTED;
 
     const size_t xbytes = span_bytes(m, xcols, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
-                 pbytes = w4a16_packed_bytes(n, k), bbytes = bias ? size_t(n) * 2 : 0;
-    const size_t need = act_path_workspace(act_fn, path, m, n, k);
+                 pbytes = bits == 8 ? w8a16_packed_bytes(n, k) : w4a16_packed_bytes(n, k),
+                 bbytes = bias ? size_t(n) * 2 : 0;
+    const size_t need = act_path_workspace(act_fn, path, m, n, k, bits);
     if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, packed, pbytes) ||
         overlap(y, ybytes, bias, bbytes) || overlap(y, ybytes, workspace, need))
         return W4A16_EINVAL;
@@ -232,7 +286,7 @@ w4a16_status_t linear_impl(int act_fn, w4a16_path_t path, const void* x, w4a16_d
         // row blocks of at most 4; launches on one stream share the workspace
         for (int64_t r0 = 0; r0 < m; r0 += 4) {
             const int64_t mm = m - r0 < 4 ? m - r0 : 4;
-            const hipError_t e = launch_gemv(xp + r0 * ldx, act, act_fn, mm, k, ldx, packed, n, bias,
+            const hipError_t e = launch_gemv(xp + r0 * ldx, act, act_fn, bits, mm, k, ldx, packed, n, bias,
                                              yp + r0 * ldy, ldy, workspace, s);
             if (e != hipSuccess) return W4A16_EHIP;
         }
@@ -250,12 +304,12 @@ w4a16_status_t linear_impl(int act_fn, w4a16_path_t path, const void* x, w4a16_d
     if (path == W4A16_PATH_GEMM) {
         if (act_fn == kActFnNone)
             return from_hip(launch_gemm(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
-        void* xa = static_cast<uint8_t*>(workspace) + round_up(path_workspace(path, m, n, k), 256);
+        void* xa = static_cast<uint8_t*>(workspace) + round_up(path_workspace(path, m, n, k, bits), 256);
         const hipError_t e = launch_activate(x, act, act_fn, m, k, ldx, xa, s);
         if (e != hipSuccess) return W4A16_EHIP;
         return from_hip(launch_gemm(xa, act, m, k, k, packed, n, bias, y, ldy, workspace, s));
     }
-    return from_hip(launch_skinny(x, act, act_fn, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
+    return from_hip(launch_skinny(x, act, act_fn, bits, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
 }
 
 }  // namespace
@@ -263,26 +317,39 @@ w4a16_status_t linear_impl(int act_fn, w4a16_path_t path, const void* x, w4a16_d
 extern "C" {
 
 size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-    return act_workspace_bytes(kActFnNone, m, n, k);
+    return act_workspace_bytes(kActFnNone, m, n, k, 4);
 }
 
 size_t w4a16_linear_act_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k) {
     if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return 0;
-    return act_workspace_bytes(int(act), m, n, k);
+    return act_workspace_bytes(int(act), m, n, k, 4);
+}
+
+size_t w8a16_linear_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k) {
+    if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return 0;
+    return act_workspace_bytes(int(act), m, n, k, 8);
+}
+
+w4a16_status_t w8a16_linear(w4a16_act_t act, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
+                            int64_t m, int64_t k, int64_t ldx, const void* packed, int64_t n, const void* bias,
+                            void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return W4A16_EINVAL;
+    return linear_impl(8, int(act), path, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
+                       workspace_bytes, stream);
 }
 
 w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
                                       int64_t m, int64_t k, int64_t ldx, const void* packed,
                                       int64_t n, const void* bias, void* y, int64_t ldy,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-    return linear_impl(kActFnNone, path, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
+    return linear_impl(4, kActFnNone, path, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
                        workspace_bytes, stream);
 }
 
 w4a16_status_t w4a16_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, int64_t k, int64_t ldx,
                             const void* packed, int64_t n, const void* bias, void* y, int64_t ldy,
                             void* workspace, size_t workspace_bytes, void* stream) {
-    return linear_impl(kActFnNone, W4A16_PATH_AUTO, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy,
+    return linear_impl(4, kActFnNone, W4A16_PATH_AUTO, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy,
                        workspace, workspace_bytes, stream);
 }
 
@@ -291,7 +358,7 @@ w4a16_status_t w4a16_linear_act(w4a16_act_t act, w4a16_path_t path, const void* 
                                 const void* bias, void* y, int64_t ldy, void* workspace,
                                 size_t workspace_bytes, void* stream) {
     if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return W4A16_EINVAL;
-    return linear_impl(int(act), path, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
+    return linear_impl(4, int(act), path, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
                        workspace_bytes, stream);
 }
 

@@ -29,21 +29,36 @@ namespace w4a16 {
 // B-operand layout of v_mfma_f32_16x16x32_{bf16,f16} for k-step s (lane L:
 // column n = L % 16, k = 8*(L/16) + j).  Rows n >= N of the last tile hold
 // code 0 (u = 8) and scale 0.
+//
+// INT8 weights use the same tiles, chunks and scale region with 2048-byte
+// chunks of one byte per code, u = q + 128.  A chunk is two 1 KB halves:
+// half h holds k-steps 2h and 2h + 1, and lane L owns bytes
+// [1024h + 16L, 1024h + 16L + 16) of it, four words w[j] = the 4 codes of
+// columns
+//     k = 128g + 32(2h + j/2) + 8kq + 4(j%2) + b,   byte b = 0..3,
+// so a wave reads each half with one contiguous 1 KB load and words 2j', 2j'+1
+// of a half form the same MFMA B operand (k-step, lane) as above.  Rows
+// n >= N of the last tile hold code 0 (u = 128) and scale 0.
 // ---------------------------------------------------------------------------
 constexpr int kGroup = 128;
 constexpr int kTileRows = 16;
 constexpr int kChunkBytes = 1024;
+constexpr int kChunkBytes8 = 2048;
 constexpr int kChunkScaleBytes = 64;
+
+template <int BITS>
+__host__ __device__ inline constexpr int chunk_bytes() { return BITS == 8 ? kChunkBytes8 : kChunkBytes; }
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-    int64_t n, k, tiles, groups;
-    __host__ __device__ Layout(int64_t n_, int64_t k_)
-        : n(n_), k(k_), tiles(ceil_div(n_, kTileRows)), groups(k_ / kGroup) {}
+    int64_t n, k, tiles, groups, cb;  // cb: code bytes of one chunk
+    __host__ __device__ Layout(int64_t n_, int64_t k_, int bits = 4)
+        : n(n_), k(k_), tiles(ceil_div(n_, kTileRows)), groups(k_ / kGroup),
+          cb(bits == 8 ? kChunkBytes8 : kChunkBytes) {}
     __host__ __device__ int64_t chunks() const { return tiles * groups; }
-    __host__ __device__ int64_t scale_offset() const { return chunks() * kChunkBytes; }
-    __host__ __device__ int64_t bytes() const { return chunks() * (kChunkBytes + kChunkScaleBytes); }
+    __host__ __device__ int64_t scale_offset() const { return chunks() * cb; }
+    __host__ __device__ int64_t bytes() const { return chunks() * (cb + kChunkScaleBytes); }
 };
 
 // Offset-binary nibble value of the packed-pair magic numbers.
@@ -170,8 +185,39 @@ __device__ inline void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Packed pair of the two codes in bytes (2h, 2h + 1) of an INT8 word (h = 0,
+// 1) as two 16-bit floats holding off + q exactly:
+//  f16: 0x6400 | u = 1024 + u = 1152 + q (one v_perm placing the bytes, one or);
+//  bf16: u itself (8 significant bits fit bf16's 8): each byte converted to
+//        FP32 (v_cvt_f32_ubyte), whose upper halves are the exact bf16 values.
 template <int ACT>
+__device__ inline uint32_t byte_pair(uint32_t word, int h) {
+    if constexpr (ACT == kActF16) {
+        return __builtin_amdgcn_perm(0u, word, h == 0 ? 0x0c010c00u : 0x0c030c02u) | kMagicF16x2;
+    } else {
+        const float lo = float((word >> (16 * h)) & 0xFFu);
+        const float hi = float((word >> (16 * h + 8)) & 0xFFu);
+        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    }
+}
+
+// The four packed pairs (columns 8kq + 0..7 of k-step s) of a lane's chunk
+// data: w holds the lane's 4 words (INT4) or 8 words (INT8, both halves).
+template <int BITS, int ACT>
+__device__ inline uint4 bpairs(const uint32_t* w, int s) {
+    if constexpr (BITS == 8) {
+        const uint32_t a = w[2 * s], b = w[2 * s + 1];
+        return make_uint4(byte_pair<ACT>(a, 0), byte_pair<ACT>(a, 1), byte_pair<ACT>(b, 0), byte_pair<ACT>(b, 1));
+    } else {
+        return make_uint4(magic_pair<ACT>(w[s], 0), magic_pair<ACT>(w[s], 1), magic_pair<ACT>(w[s], 2),
+                          magic_pair<ACT>(w[s], 3));
+    }
+}
+
+// The offset each packed pair value carries: off + q.
+template <int ACT, int BITS = 4>
 __device__ inline constexpr float code_offset() {
+    if constexpr (BITS == 8) return ACT == kActBf16 ? 128.0f : 1152.0f;
     return ACT == kActBf16 ? kOffsetBf16 : kOffsetF16;
 }
 

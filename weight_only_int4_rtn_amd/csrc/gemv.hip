@@ -54,14 +54,16 @@ constexpr int kGemvChunks = 8;  // chunks per wave, all loaded up front
 
 // AF: activation fused into the x staging (ActFn); for SwiGLU the x rows
 // hold [up | gate] and the gate values sit k columns after the up values.
-template <int M, int ACT, int WAVES, int CPW, int AF>
+// BITS: 4 (INT4 chunks) or 8 (INT8 chunks, two 1 KB halves per chunk).
+template <int M, int ACT, int WAVES, int CPW, int AF, int BITS>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     constexpr int THREADS = 64 * WAVES;
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
     // 16-byte x loads per thread while staging: the slice is M rows of at
     // most WAVES * CPW groups of 128 columns, M * CPW / 4 loads per thread.
     constexpr int kXRegs = (M * CPW + 3) / 4;
     extern __shared__ __align__(16) unsigned char smem[];
-    const Layout L(a.n, a.k);
+    const Layout L(a.n, a.k, BITS);
     const int split = int(blockIdx.x % unsigned(a.splits));
     const int64_t t = int64_t(blockIdx.x / unsigned(a.splits));
     const int64_t g0 = int64_t(split) * a.gps;
@@ -76,13 +78,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     const int wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
 
-    const uint8_t* cbase = a.packed + (t * L.groups + g0) * kChunkBytes + lane * 16;
+    const uint8_t* cbase = a.packed + (t * L.groups + g0) * CB + lane * 16;
     const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (t * L.groups + g0) * kTileRows + r;
 
     // Every chunk of the wave (CPW of them) is loaded before any is used.
     // The loads are unconditional straight-line code (clamped addresses), so
     // the compiler's wait counts stay exact: each use waits for its own load.
-    uint4 cw[CPW];
+    uint4 cw[CPW][H];
     float sc[CPW];
 
     // x slice first (loads complete in issue order, so the weight loads
@@ -108,7 +110,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * WAVES;
         const int gc = gl < ng ? gl : ng - 1;  // a valid chunk; unused when gl >= ng
-        cw[u] = load_stream16(cbase + int64_t(gc) * kChunkBytes);
+#pragma unroll
+        for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
         sc[u] = sbase[int64_t(gc) * kTileRows];
     }
 
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     }
     lds_barrier();
 
-    constexpr float off = code_offset<ACT>();
+    constexpr float off = code_offset<ACT, BITS>();
     float tot[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) tot[m] = 0.0f;
@@ -146,7 +149,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * WAVES;
         if (gl < ng) {
-            const uint32_t words[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+            uint32_t words[4 * H];
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                words[4 * h] = cw[u][h].x;
+                words[4 * h + 1] = cw[u][h].y;
+                words[4 * h + 2] = cw[u][h].z;
+                words[4 * h + 3] = cw[u][h].w;
+            }
             const float scale = sc[u];
 #pragma unroll
             for (int m = 0; m < M; ++m) {
@@ -155,10 +165,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const uint4 xq = *reinterpret_cast<const uint4*>(xp + 32 * s);
-                    acc = dot2<ACT>(magic_pair<ACT>(words[s], 0), xq.x, acc);
-                    acc = dot2<ACT>(magic_pair<ACT>(words[s], 1), xq.y, acc);
-                    acc = dot2<ACT>(magic_pair<ACT>(words[s], 2), xq.z, acc);
-                    acc = dot2<ACT>(magic_pair<ACT>(words[s], 3), xq.w, acc);
+                    const uint4 bp = bpairs<BITS, ACT>(words, s);
+                    acc = dot2<ACT>(bp.x, xq.x, acc);
+                    acc = dot2<ACT>(bp.y, xq.y, acc);
+                    acc = dot2<ACT>(bp.z, xq.z, acc);
+                    acc = dot2<ACT>(bp.w, xq.w, acc);
                 }
                 acc = fmaf(-off, xsum[(m * ng + gl) * 4 + kq], acc);
                 tot[m] = fmaf(scale, acc, tot[m]);
@@ -230,13 +241,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 // workspace's zero header; a launch whose tree does not fit there stores
 // partial sums for the split-K reduce kernel instead.
 
-GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
+GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits) {
     GemvPlan p{};
-    const Layout L(n, k);
+    const Layout L(n, k, bits);
     const int64_t G = L.groups;
     const int mm = int(m);
     p.waves = 4;
-    const int64_t gps = G < kGemvChunks * p.waves ? G : kGemvChunks * p.waves;
+    // the same bytes in flight per wave for INT8 (2 KB chunks)
+    const int64_t cap = (bits == 8 ? kGemvChunks / 2 : kGemvChunks) * p.waves;
+    const int64_t gps = G < cap ? G : cap;
     p.gps = int(gps);
     p.splits = int(ceil_div(G, gps));
     const int64_t per_wave = ceil_div(gps, p.waves);
@@ -250,15 +263,18 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-template <int M, int ACT, int AF>
+template <int M, int ACT, int AF, int BITS>
 static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
-    const Layout L(a.n, a.k);
+    const Layout L(a.n, a.k, BITS);
     const dim3 grid(unsigned(L.tiles * p.splits)), block(256);
     switch (p.cpw) {
-        case 1: gemv_kernel<M, ACT, 4, 1, AF><<<grid, block, p.lds, stream>>>(a); break;
-        case 2: gemv_kernel<M, ACT, 4, 2, AF><<<grid, block, p.lds, stream>>>(a); break;
-        case 4: gemv_kernel<M, ACT, 4, 4, AF><<<grid, block, p.lds, stream>>>(a); break;
-        default: gemv_kernel<M, ACT, 4, 8, AF><<<grid, block, p.lds, stream>>>(a); break;
+        case 1: gemv_kernel<M, ACT, 4, 1, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        case 2: gemv_kernel<M, ACT, 4, 2, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        case 4: gemv_kernel<M, ACT, 4, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        default:
+            if constexpr (BITS == 4) gemv_kernel<M, ACT, 4, 8, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+            else return hipErrorInvalidValue;  // the plan keeps INT8 to 4 chunks per wave
+            break;
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.exchange) return e;
@@ -266,19 +282,28 @@ static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s
                                 stream);
 }
 
-template <int M, int ACT>
+template <int M, int ACT, int BITS>
 static hipError_t launch_af(const GemvArgs& a, const GemvPlan& p, int act_fn, hipStream_t stream) {
     switch (act_fn) {
-        case kActFnSwiglu: return launch_one<M, ACT, kActFnSwiglu>(a, p, stream);
-        case kActFnGeluTanh: return launch_one<M, ACT, kActFnGeluTanh>(a, p, stream);
-        default: return launch_one<M, ACT, kActFnNone>(a, p, stream);
+        case kActFnSwiglu: return launch_one<M, ACT, kActFnSwiglu, BITS>(a, p, stream);
+        case kActFnGeluTanh: return launch_one<M, ACT, kActFnGeluTanh, BITS>(a, p, stream);
+        default: return launch_one<M, ACT, kActFnNone, BITS>(a, p, stream);
     }
 }
 
-hipError_t launch_gemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+template <int M>
+static hipError_t launch_m(const GemvArgs& a, const GemvPlan& p, int act, int act_fn, int bits,
+                           hipStream_t stream) {
+    const bool bf = act == kActBf16;
+    if (bits == 8)
+        return bf ? launch_af<M, kActBf16, 8>(a, p, act_fn, stream) : launch_af<M, kActF16, 8>(a, p, act_fn, stream);
+    return bf ? launch_af<M, kActBf16, 4>(a, p, act_fn, stream) : launch_af<M, kActF16, 4>(a, p, act_fn, stream);
+}
+
+hipError_t launch_gemv(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                        const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream) {
-    const GemvPlan p = plan_gemv(m, n, k);
+    const GemvPlan p = plan_gemv(m, n, k, bits);
     GemvArgs a;
     a.x = static_cast<const uint16_t*>(x);
     a.ldx = ldx;
@@ -293,12 +318,11 @@ hipError_t launch_gemv(const void* x, int act, int act_fn, int64_t m, int64_t k,
     a.splits = p.splits;
     a.gps = p.gps;
     a.exchange = p.exchange;
-    const bool bf = act == kActBf16;
     switch (m) {
-        case 1: return bf ? launch_af<1, kActBf16>(a, p, act_fn, stream) : launch_af<1, kActF16>(a, p, act_fn, stream);
-        case 2: return bf ? launch_af<2, kActBf16>(a, p, act_fn, stream) : launch_af<2, kActF16>(a, p, act_fn, stream);
-        case 3: return bf ? launch_af<3, kActBf16>(a, p, act_fn, stream) : launch_af<3, kActF16>(a, p, act_fn, stream);
-        default: return bf ? launch_af<4, kActBf16>(a, p, act_fn, stream) : launch_af<4, kActF16>(a, p, act_fn, stream);
+        case 1: return launch_m<1>(a, p, act, act_fn, bits, stream);
+        case 2: return launch_m<2>(a, p, act, act_fn, bits, stream);
+        case 3: return launch_m<3>(a, p, act, act_fn, bits, stream);
+        default: return launch_m<4>(a, p, act, act_fn, bits, stream);
     }
 }
 

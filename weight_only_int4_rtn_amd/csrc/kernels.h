@@ -21,7 +21,8 @@ struct GemvPlan {
     bool exchange;                // split finished through the header's exchange slots
     size_t lds, workspace;
 };
-GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k);
+// bits: 4 (INT4 packed weights) or 8 (INT8)
+GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 struct MgemvPlan {
     int mmax, gps, splits, cpw;
@@ -37,7 +38,7 @@ struct SkinnyPlan {
     int64_t tile_groups, mblocks;
     size_t workspace;
 };
-SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k);
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 struct GemmPlan {
     int64_t mtiles, ntiles;
@@ -53,6 +54,13 @@ hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t n, int
                        void* packed, hipStream_t stream);
 hipError_t launch_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, float* scales,
                          hipStream_t stream);
+// INT8: codes [n][k] one signed code per byte.
+hipError_t launch_quantize8(const void* w, int dtype, int64_t n, int64_t k, int64_t ldw, int8_t* codes,
+                            float* scales, hipStream_t stream);
+hipError_t launch_pack8(const int8_t* codes, const float* scales, int64_t n, int64_t k, void* packed,
+                        hipStream_t stream);
+hipError_t launch_unpack8(const void* packed, int64_t n, int64_t k, int8_t* codes, float* scales,
+                          hipStream_t stream);
 // In place: packed <- requantize(beta * dequant(packed) + alpha * U), U the
 // dense update [n][ldu] (rank 0) or mat1 [n][rank] @ mat2 [rank][k]; dtype
 // 0 (FP32), kActBf16 or kActF16; stochastic rounding with `seed` when set.
@@ -71,15 +79,16 @@ hipError_t launch_splitk_reduce(const float* partials, int splits, int64_t m, in
 
 // act_fn (ActFn, common.h): activation fused into the x staging; SwiGLU x
 // rows hold [up | gate], 2k values.
+// bits: 4 or 8 (packed INT4 or INT8 weights).
 // m <= 4 per launch (the caller splits larger m into row blocks).
-hipError_t launch_gemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+hipError_t launch_gemv(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                        const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream);
 // m <= 16 per launch (the caller splits larger m into row blocks).
 hipError_t launch_mgemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
                         const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                         hipStream_t stream);
-hipError_t launch_skinny(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+hipError_t launch_skinny(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                          const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                          hipStream_t stream);
 // The activated input [m][k] (row stride k) of x for the GEMM path.

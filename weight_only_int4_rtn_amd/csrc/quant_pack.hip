@@ -96,6 +96,57 @@ hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int64
     return hipGetLastError();
 }
 
+// INT8 (the same method with the 8-bit code range): s = amax / 127,
+// q = clamp(rint(w / s), -128, 127), q = 0 when s == 0; one signed code per
+// byte, 8 bytes per thread.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize8_kernel(const void* __restrict__ w, int64_t n, int64_t k,
+                                                        int64_t ldw, int8_t* __restrict__ codes,
+                                                        float* __restrict__ scales) {
+    const int64_t per_row = k / 8;
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = n * per_row;
+    const bool active = tid < total;  // whole 16-lane groups, as above
+    const int64_t row = active ? tid / per_row : 0;
+    const int64_t k0 = active ? (tid - row * per_row) * 8 : 0;
+
+    float v[8];
+    if (active) {
+        load_weights8<DT>(w, row * ldw + k0, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+    if (!active) return;
+
+    const float s = amax / 127.0f;
+    uint32_t word[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int q = 0;
+        if (s != 0.0f) q = int(fminf(fmaxf(rintf(v[i] / s), -128.0f), 127.0f));
+        word[i >> 2] |= (uint32_t(q) & 0xFFu) << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2*>(codes + row * k + k0) = make_uint2(word[0], word[1]);
+    if ((k0 & (kGroup - 1)) == 0) scales[row * (k / kGroup) + k0 / kGroup] = s;
+}
+
+hipError_t launch_quantize8(const void* w, int dtype, int64_t n, int64_t k, int64_t ldw, int8_t* codes,
+                            float* scales, hipStream_t stream) {
+    const int64_t blocks = ceil_div(n * (k / 8), 256);
+    switch (dtype) {
+        case 0: quantize8_kernel<0><<<dim3(blocks), dim3(256), 0, stream>>>(w, n, k, ldw, codes, scales); break;
+        case 1: quantize8_kernel<1><<<dim3(blocks), dim3(256), 0, stream>>>(w, n, k, ldw, codes, scales); break;
+        default: quantize8_kernel<2><<<dim3(blocks), dim3(256), 0, stream>>>(w, n, k, ldw, codes, scales); break;
+    }
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Canonical <-> packed.  One thread per (chunk, lane): four words.
 // Canonical word for 8 consecutive columns k0..k0+7 of a row: byte b holds
@@ -174,6 +225,76 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
         const float* sp = reinterpret_cast<const float*>(packed + L.scale_offset());
         scales[row * L.groups + g] = sp[chunk * kTileRows + r];
     }
+}
+
+// INT8 canonical <-> packed.  One thread per (chunk, lane, half): four words,
+// each the 4 consecutive columns 128g + 32(2h + j/2) + 8kq + 4(j%2) .. +3 of
+// the lane's row; u = q + 128 is the two's-complement byte with its top bit
+// flipped, so a word converts with one xor.
+__global__ __launch_bounds__(256) void pack8_kernel(const int8_t* __restrict__ codes,
+                                                    const float* __restrict__ scales, int64_t n, int64_t k,
+                                                    uint8_t* __restrict__ packed) {
+    const Layout L(n, k, 8);
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (tid >= L.chunks() * 128) return;
+    const int64_t chunk = tid >> 7;
+    const int h = int((tid >> 6) & 1), lane = int(tid & 63);
+    const int64_t t = chunk / L.groups, g = chunk - t * L.groups;
+    const int r = lane & 15, kq = lane >> 4;
+    const int64_t row = t * kTileRows + r;
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t k0 = g * kGroup + 32 * (2 * h + j / 2) + 8 * kq + 4 * (j % 2);
+        out[j] = row < n ? *reinterpret_cast<const uint32_t*>(codes + row * k + k0) ^ 0x80808080u : 0x80808080u;
+    }
+    *reinterpret_cast<uint4*>(packed + chunk * kChunkBytes8 + h * kChunkBytes + lane * 16) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+    if (h == 0 && kq == 0) {
+        float* sp = reinterpret_cast<float*>(packed + L.scale_offset());
+        sp[chunk * kTileRows + r] = row < n ? scales[row * L.groups + g] : 0.0f;
+    }
+}
+
+__global__ __launch_bounds__(256) void unpack8_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k,
+                                                      int8_t* __restrict__ codes, float* __restrict__ scales) {
+    const Layout L(n, k, 8);
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (tid >= L.chunks() * 128) return;
+    const int64_t chunk = tid >> 7;
+    const int h = int((tid >> 6) & 1), lane = int(tid & 63);
+    const int64_t t = chunk / L.groups, g = chunk - t * L.groups;
+    const int r = lane & 15, kq = lane >> 4;
+    const int64_t row = t * kTileRows + r;
+    if (row >= n) return;
+    const uint4 in = *reinterpret_cast<const uint4*>(packed + chunk * kChunkBytes8 + h * kChunkBytes + lane * 16);
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t k0 = g * kGroup + 32 * (2 * h + j / 2) + 8 * kq + 4 * (j % 2);
+        *reinterpret_cast<uint32_t*>(codes + row * k + k0) = w[j] ^ 0x80808080u;
+    }
+    if (h == 0 && kq == 0) {
+        const float* sp = reinterpret_cast<const float*>(packed + L.scale_offset());
+        scales[row * L.groups + g] = sp[chunk * kTileRows + r];
+    }
+}
+
+hipError_t launch_pack8(const int8_t* codes, const float* scales, int64_t n, int64_t k, void* packed,
+                        hipStream_t stream) {
+    const Layout L(n, k, 8);
+    const int64_t blocks = ceil_div(L.chunks() * 128, 256);
+    pack8_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(codes, scales, n, k, static_cast<uint8_t*>(packed));
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack8(const void* packed, int64_t n, int64_t k, int8_t* codes, float* scales,
+                          hipStream_t stream) {
+    const Layout L(n, k, 8);
+    const int64_t blocks = ceil_div(L.chunks() * 128, 256);
+    unpack8_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(static_cast<const uint8_t*>(packed), n, k, codes,
+                                                           scales);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

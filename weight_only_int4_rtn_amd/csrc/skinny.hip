@@ -55,14 +55,16 @@ __device__ inline f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 
 // AF: activation fused into the x staging (ActFn; SwiGLU gate values sit k
 // columns after the up values).  GMAX: most groups one workgroup covers (all
-// of its chunks are held in registers).
-template <int MB, int ACT, int AF, int GMAX>
+// of its chunks are held in registers).  BITS: 4 (INT4 chunks) or 8 (INT8
+// chunks, two 1 KB halves each).
+template <int MB, int ACT, int AF, int GMAX, int BITS>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     constexpr int BM = 16 * MB;
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
     __shared__ __align__(16) uint16_t xa[2][BM * kAStride];
     __shared__ __align__(16) float xrow[2][BM];
 
-    const Layout L(a.n, a.k);
+    const Layout L(a.n, a.k, BITS);
     const int split = int(blockIdx.x % unsigned(a.splits));
     const int64_t tg = int64_t(blockIdx.x / unsigned(a.splits));
     const int64_t mblk = blockIdx.y;
@@ -76,18 +78,19 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     const int64_t t = tg * kSkWaves + wave;
     const bool tile_ok = t < L.tiles;
     const int64_t tt = tile_ok ? t : L.tiles - 1;  // loads stay in bounds; results unused
-    const uint8_t* cbase = a.packed + (tt * L.groups + g0) * kChunkBytes + lane * 16;
+    const uint8_t* cbase = a.packed + (tt * L.groups + g0) * CB + lane * 16;
     const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (tt * L.groups + g0) * kTileRows + r;
-    constexpr float off = code_offset<ACT>();
+    constexpr float off = code_offset<ACT, BITS>();
 
     // Every chunk and scale of the wave's groups, loaded before anything
     // else, so the weight stream is in flight during all of the x staging.
-    uint4 cw[GMAX];
+    uint4 cw[GMAX][H];
     float sc[GMAX];
 #pragma unroll
     for (int u = 0; u < GMAX; ++u) {
         const int gc = u < ng ? u : ng - 1;  // a valid chunk; unused when u >= ng
-        cw[u] = load_stream16(cbase + int64_t(gc) * kChunkBytes);
+#pragma unroll
+        for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
         sc[u] = sbase[int64_t(gc) * kTileRows];
     }
 
@@ -143,12 +146,17 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
         // group gl + 2 into the register set group gl was staged from
         if (gl + 2 < ng) load_x(gl & 1, gl + 2);
 
-        const uint32_t words[4] = {cw[gl].x, cw[gl].y, cw[gl].z, cw[gl].w};
+        uint32_t words[4 * H];
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            words[4 * h] = cw[gl][h].x;
+            words[4 * h + 1] = cw[gl][h].y;
+            words[4 * h + 2] = cw[gl][h].z;
+            words[4 * h + 3] = cw[gl][h].w;
+        }
         uint4 b[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            b[s] = make_uint4(magic_pair<ACT>(words[s], 0), magic_pair<ACT>(words[s], 1),
-                              magic_pair<ACT>(words[s], 2), magic_pair<ACT>(words[s], 3));
+        for (int s = 0; s < 4; ++s) b[s] = bpairs<BITS, ACT>(words, s);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -196,9 +204,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
         }
 }
 
-SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits) {
     SkinnyPlan p{};
-    const Layout L(n, k);
+    const Layout L(n, k, bits);
     p.mb = m <= 16 ? 1 : m <= 32 ? 2 : m <= 48 ? 3 : 4;
     const int64_t bm = 16 * p.mb;
     p.mblocks = ceil_div(m, bm);
@@ -209,7 +217,8 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
     // workgroups would run (measured: that beats the cost of the reduce
     // launch a split adds).
     const int64_t minwg = 128;
-    const int64_t cap = p.mb <= 2 ? 16 : 8;
+    // (INT8 chunks take twice the registers: half the groups)
+    const int64_t cap = (p.mb <= 2 ? 16 : 8) / (bits == 8 ? 2 : 1);
     const int64_t base = p.tile_groups * p.mblocks;
     int64_t gps = L.groups < cap ? L.groups : cap;
     while (gps > 2 && base * ceil_div(L.groups, gps) < minwg) gps = ceil_div(gps, 2);
@@ -220,16 +229,21 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-template <int MB, int ACT, int AF>
+template <int MB, int ACT, int AF, int BITS>
 static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
     dim3 grid(unsigned(p.tile_groups * p.splits), unsigned(p.mblocks));
+    // the plan keeps the register footprint GMAX * BITS / 4 chunks <= 16, and
+    // <= 8 for MB > 2
+    constexpr int kMaxRegChunks = MB <= 2 ? 16 : 8;
     if (p.gmax == 4) {
-        skinny_kernel<MB, ACT, AF, 4><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+        if constexpr (4 * BITS / 4 <= kMaxRegChunks) skinny_kernel<MB, ACT, AF, 4, BITS><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+        else return hipErrorInvalidValue;
     } else if (p.gmax == 8) {
-        skinny_kernel<MB, ACT, AF, 8><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+        if constexpr (8 * BITS / 4 <= kMaxRegChunks) skinny_kernel<MB, ACT, AF, 8, BITS><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+        else return hipErrorInvalidValue;
     } else {
-        if constexpr (MB <= 2) skinny_kernel<MB, ACT, AF, 16><<<grid, dim3(kSkThreads), 0, stream>>>(a);
-        else return hipErrorInvalidValue;  // the plan keeps 16-group splits to MB <= 2
+        if constexpr (16 * BITS / 4 <= kMaxRegChunks) skinny_kernel<MB, ACT, AF, 16, BITS><<<grid, dim3(kSkThreads), 0, stream>>>(a);
+        else return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
@@ -237,19 +251,28 @@ static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream
                                 ACT, stream);
 }
 
-template <int MB, int ACT>
+template <int MB, int ACT, int BITS>
 static hipError_t launch_af(const SkinnyArgs& a, const SkinnyPlan& p, int act_fn, hipStream_t stream) {
     switch (act_fn) {
-        case kActFnSwiglu: return launch_one<MB, ACT, kActFnSwiglu>(a, p, stream);
-        case kActFnGeluTanh: return launch_one<MB, ACT, kActFnGeluTanh>(a, p, stream);
-        default: return launch_one<MB, ACT, kActFnNone>(a, p, stream);
+        case kActFnSwiglu: return launch_one<MB, ACT, kActFnSwiglu, BITS>(a, p, stream);
+        case kActFnGeluTanh: return launch_one<MB, ACT, kActFnGeluTanh, BITS>(a, p, stream);
+        default: return launch_one<MB, ACT, kActFnNone, BITS>(a, p, stream);
     }
 }
 
-hipError_t launch_skinny(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+template <int MB>
+static hipError_t launch_mb(const SkinnyArgs& a, const SkinnyPlan& p, int act, int act_fn, int bits,
+                            hipStream_t stream) {
+    const bool bf = act == kActBf16;
+    if (bits == 8)
+        return bf ? launch_af<MB, kActBf16, 8>(a, p, act_fn, stream) : launch_af<MB, kActF16, 8>(a, p, act_fn, stream);
+    return bf ? launch_af<MB, kActBf16, 4>(a, p, act_fn, stream) : launch_af<MB, kActF16, 4>(a, p, act_fn, stream);
+}
+
+hipError_t launch_skinny(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                          const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                          hipStream_t stream) {
-    const SkinnyPlan p = plan_skinny(m, n, k);
+    const SkinnyPlan p = plan_skinny(m, n, k, bits);
     SkinnyArgs a;
     a.x = static_cast<const uint16_t*>(x);
     a.ldx = ldx;
@@ -264,12 +287,11 @@ hipError_t launch_skinny(const void* x, int act, int act_fn, int64_t m, int64_t 
     a.splits = p.splits;
     a.gps = p.gps;
     a.tile_groups = p.tile_groups;
-    const bool bf = act == kActBf16;
     switch (p.mb) {
-        case 1: return bf ? launch_af<1, kActBf16>(a, p, act_fn, stream) : launch_af<1, kActF16>(a, p, act_fn, stream);
-        case 2: return bf ? launch_af<2, kActBf16>(a, p, act_fn, stream) : launch_af<2, kActF16>(a, p, act_fn, stream);
-        case 3: return bf ? launch_af<3, kActBf16>(a, p, act_fn, stream) : launch_af<3, kActF16>(a, p, act_fn, stream);
-        default: return bf ? launch_af<4, kActBf16>(a, p, act_fn, stream) : launch_af<4, kActF16>(a, p, act_fn, stream);
+        case 1: return launch_mb<1>(a, p, act, act_fn, bits, stream);
+        case 2: return launch_mb<2>(a, p, act, act_fn, bits, stream);
+        case 3: return launch_mb<3>(a, p, act, act_fn, bits, stream);
+        default: return launch_mb<4>(a, p, act, act_fn, bits, stream);
     }
 }
 
