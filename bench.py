@@ -52,9 +52,10 @@ def prefill_cases():
     return [c for c in synth.all_cases() if c.config == 4]
 
 
-def build_pool(cases, dev):
-    """Quantize + pack each case's weight once, then copy it until the pool
-    of layers exceeds POOL_BYTES.  Returns (layers, load_stats)."""
+def build_pool(cases, dev, bits=4):
+    """Quantize + pack each case's weight once (INT4, or INT8 for bits=8),
+    then copy it until the pool of layers exceeds POOL_BYTES.  Returns
+    (layers, load_stats)."""
     import torch
 
     import synth
@@ -66,12 +67,16 @@ def build_pool(cases, dev):
         w = synth.make_weight(c).to(dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        codes, scales = w4.quantize(w)
-        p = w4.pack(codes, scales)
+        if bits == 8:
+            codes, scales = w4.quantize_int8(w)
+            p = w4.pack_int8(codes, scales)
+        else:
+            codes, scales = w4.quantize(w)
+            p = w4.pack(codes, scales)
         torch.cuda.synchronize()
         load_time += time.perf_counter() - t0
         # quantize reads W (4 B) and writes codes + scales; pack reads those and writes packed
-        load_bytes += c.n * c.k * 4 + 2 * (c.n * c.k // 2 + c.n * (c.k // 128) * 4) + p.numel()
+        load_bytes += c.n * c.k * 4 + 2 * (c.n * c.k * bits // 8 + c.n * (c.k // 128) * 4) + p.numel()
         packed0.append(p)
         del w, codes, scales
     per_layer = sum(p.numel() for p in packed0)
@@ -92,12 +97,12 @@ def capture(fn):
     return g
 
 
-def make_step(cases, layer, xs, biases, ys, workspace):
+def make_step(cases, layer, xs, biases, ys, workspace, bits=4):
     import weight_only_int4_rtn_amd as w4
 
     def step():
         for j, c in enumerate(cases):
-            w4.linear(xs[j], layer[j], c.n, biases[j], out=ys[j], workspace=workspace)
+            w4.linear(xs[j], layer[j], c.n, biases[j], out=ys[j], workspace=workspace, bits=bits)
     return step
 
 
@@ -125,7 +130,7 @@ def time_graphs(graphs, per_graph, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_kernel(case, layers, j, x, bias, y, workspace, launches=24, replays=10):
+def time_kernel(case, layers, j, x, bias, y, workspace, launches=24, replays=10, bits=4):
     """Average duration of one projection's launch, from HIP events on its
     stream around replays of a graph of back-to-back launches (weights rotate
     over distinct copies)."""
@@ -135,7 +140,7 @@ def time_kernel(case, layers, j, x, bias, y, workspace, launches=24, replays=10)
 
     def many():
         for i in range(launches):
-            w4.linear(x, layers[i % len(layers)][j], case.n, bias, out=y, workspace=workspace)
+            w4.linear(x, layers[i % len(layers)][j], case.n, bias, out=y, workspace=workspace, bits=bits)
     g = capture(many)
     g.replay()
     stream = torch.cuda.current_stream()
@@ -161,26 +166,35 @@ def eager_ms(cases, layers, xs, biases, ys, workspace, steps=20):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def run_workload(cases, dev, steps, warmup, dominant):
+def alg_bytes(c, bits=4):
+    """Algorithmic HBM bytes of one projection: packed codes + FP32 scales +
+    x + y (+ bias), each read or written once."""
+    if bits == 4:
+        return c.alg_bytes()
+    return c.n * c.k + c.n * (c.k // 128) * 4 + 2 * c.m * c.k + 2 * c.m * c.n + (2 * c.n if c.bias else 0)
+
+
+def run_workload(cases, dev, steps, warmup, dominant, bits=4, eager=True):
     """Pool, graphs, timings for one workload.  Returns a dict of figures."""
     import torch
 
     import synth
     import weight_only_int4_rtn_amd as w4
-    layers, load = build_pool(cases, dev)
+    layers, load = build_pool(cases, dev, bits)
     xs = [synth.make_x(c).to(dev) for c in cases]
     biases = [synth.make_bias(c).to(dev) if c.bias else None for c in cases]
     ys = [torch.empty((c.m, c.n), dtype=c.torch_dtype, device=dev) for c in cases]
-    ws_bytes = max(w4.workspace_bytes(c.m, c.n, c.k) for c in cases)
+    ws_bytes = max(w4.workspace_bytes(c.m, c.n, c.k, bits=bits) for c in cases)
     workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     log(f"pool: {len(layers)} layers of {sum(p.numel() for p in layers[0]) / 1e6:.1f} MB; "
-        f"paths {[w4.choose_path(c.m, c.n, c.k).name for c in cases]}")
+        f"paths {[w4.choose_path(c.m, c.n, c.k, bits).name for c in cases]}")
     # Each graph runs `per` consecutive layers of the pool, as a decode loop
     # runs a model's layers back to back; the graphs together cover the pool.
     per = steps_per_graph(steps)
 
     def layer_run(first):
-        fns = [make_step(cases, layers[(first + i) % len(layers)], xs, biases, ys, workspace) for i in range(per)]
+        fns = [make_step(cases, layers[(first + i) % len(layers)], xs, biases, ys, workspace, bits)
+               for i in range(per)]
 
         def run():
             for f in fns:
@@ -189,8 +203,9 @@ def run_workload(cases, dev, steps, warmup, dominant):
     graphs = [capture(layer_run(first)) for first in range(0, len(layers), per)]
     ms = time_graphs(graphs, per, steps, warmup)
     dom = cases[dominant]
-    dom_ms = time_kernel(dom, layers, dominant, xs[dominant], biases[dominant], ys[dominant], workspace)
-    eager = eager_ms(cases, layers, xs, biases, ys, workspace)
+    dom_ms = time_kernel(dom, layers, dominant, xs[dominant], biases[dominant], ys[dominant], workspace,
+                         bits=bits)
+    eager = eager_ms(cases, layers, xs, biases, ys, workspace) if eager else None
     out = {"ms": ms, "dom_ms": dom_ms, "eager_ms": eager, "load": load, "steps_per_graph": per}
     del graphs, layers
     torch.cuda.synchronize()
@@ -565,6 +580,21 @@ def main():
     }
     log(f"ffn: {ffn}")
 
+    # --- the same decode step with INT8 weights (W8A16) ----------------------
+    log("w8a16 decode workload")
+    w8 = run_workload(cases, dev, args.steps, args.warmup, dominant, bits=8, eager=False)
+    w8_bytes = sum(alg_bytes(c, 8) for c in cases)
+    w8_gbs = w8_bytes / (w8["ms"] * 1e-3) / 1e9
+    w8_dom_gbs = alg_bytes(dom, 8) / (w8["dom_ms"] * 1e-3) / 1e9
+    w8a16 = {"workload": "decode layer M=1 as above with int8 g128 weights (amax/127)",
+             "GBps": round(w8_gbs, 2), "ms_per_step": round(w8["ms"], 5), "bytes_per_step": w8_bytes,
+             "pct_hbm_peak": round(100 * w8_gbs / HBM_PEAK_GBS, 2),
+             "roofline": {"bound": "hbm", "achieved": round(w8_dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(w8_dom_gbs / HBM_PEAK_GBS, 4),
+                          "kernel": f"{w4.choose_path(1, dom.n, dom.k, 8).name} int8 {dom.name}",
+                          "avg_launch_us": round(w8["dom_ms"] * 1e3, 3), "bytes_per_launch": alg_bytes(dom, 8)}}
+    log(f"w8a16: {w8a16}")
+
     out = {
         "metric": "W4A16 GEMM: HBM GB/s & %peak at M=1; TFLOP/s & %MFMA peak at M=1024",
         "value": round(value, 2),
@@ -596,6 +626,7 @@ def main():
                                "kernel": f"{w4.choose_path(pd.m, pd.n, pd.k).name} {pd.name}",
                                "avg_launch_us": round(pdom_ms * 1e3, 3)}},
         "ffn": ffn,
+        "w8a16": w8a16,
         "load": {"rows": "quantize + pack, decode layer weights",
                  "GBps": round(load["bytes"] / load["seconds"] / 1e9, 2) if load["seconds"] else None,
                  "shard_GBps": shard_rate(dev),
