@@ -83,11 +83,12 @@ def test_exact_arithmetic_bit_exact(dev, path, dtype, m, n, k):
 # GEMM tilings the planner picks by shape: 256 x 256 tiles with ragged M and
 # N, a K split whose parts hold odd and even group counts, a single group
 # (LDS-staged epilogue), a row stride that is not a multiple of 8 (direct
-# epilogue); and 128 x 256 tiles, one group deep and split.  Exact
-# arithmetic, checked bit for bit on whole rows and columns (first, last,
-# either side of a tile edge).
+# epilogue); and 128 x 256 tiles, one group deep and split; 256 x 256
+# tiles over a long K split in six parts of 17 groups and one of 11.
+# Exact arithmetic, checked bit for bit on whole rows and columns (first,
+# last, either side of a tile edge).
 GEMM_TILE_SHAPES = [(513, 16424, 1152), (769, 12296, 128), (300, 4104, 640), (1000, 2056, 2176),
-                    (512, 32772, 256)]
+                    (512, 32772, 256), (1000, 2056, 14464)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])

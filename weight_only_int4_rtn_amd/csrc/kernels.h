@@ -12,8 +12,9 @@ namespace w4a16 {
 // then FP32 partial sums [splits][m][npad] for the split-K reduce kernel.
 // The header must be zero before a call and every call leaves it zero (the
 // thread that empties a slot clears it); the partial sums need no
-// initialisation (every element read is written first).  Every path places
-// its partial sums after the header.
+// initialisation (every element that reaches an output is written first;
+// the reduce kernel also reads, and drops, the padding columns past n of a
+// 4-column group).  Every path places its partial sums after the header.
 constexpr size_t kSyncBytes = size_t(1) << 20;
 
 struct GemvPlan {
