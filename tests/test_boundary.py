@@ -227,8 +227,11 @@ def test_int8_packed_bytes_and_paths(lib):
         w4.packed_bytes(16, 128, bits=2)
     assert w4.choose_path(1, 2048, 2048, bits=8) == w4.Path.GEMV
     assert w4.choose_path(4, 2048, 2048, bits=8) == w4.Path.GEMV
-    for m in (5, 16, 50, 256, 4096):
+    for m in (5, 16, 50, 127):
         assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.SKINNY
+    for m in (128, 256, 4096):
+        assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.GEMM
+    assert w4.choose_path(256, 16, (1 << 22) + 128, bits=8) == w4.Path.SKINNY
     assert w4.workspace_bytes(1, 2048, 100, bits=8) == 0
     assert w4.workspace_bytes(1, 2048, 16384, bits=8) > 0
     assert lib.w8a16_linear_workspace_bytes(5, 16, 16, 128) == 0       # unknown activation
@@ -257,8 +260,9 @@ def lin8(lib, fn=0, path=0, x=A, act=B.BF16, m=1, k=128, ldx=128, packed=A * 4, 
 
 def test_int8_linear_rejects(lib):
     assert lin8(lib, 3) == B.EINVAL                                         # unknown activation
-    assert lin8(lib, path=int(w4.Path.MGEMV)) == B.EUNSUPPORTED             # INT8: GEMV and SKINNY only
-    assert lin8(lib, path=int(w4.Path.GEMM), m=256) == B.EUNSUPPORTED
+    assert lin8(lib, path=int(w4.Path.MGEMV)) == B.EUNSUPPORTED             # INT8: GEMV, SKINNY, GEMM
+    big = (1 << 22) + 8
+    assert lin8(lib, path=int(w4.Path.GEMM), m=256, ldx=big, y=A * 4096) == B.EUNSUPPORTED  # 32-bit x offsets
     assert lin8(lib, path=9) == B.EINVAL
     assert lin8(lib, act=B.F32) == B.EUNSUPPORTED
     assert lin8(lib, k=100, ldx=104) == B.EINVAL

@@ -6,8 +6,8 @@
   * packing: round trip on arbitrary bytes (code -128 included), and the
     packed bytes equal the layout documented in the library's headers,
     built here from that description;
-  * the linear layer on both INT8 kernel paths (GEMV, SKINNY) and the
-    automatic choice: exact-arithmetic cases bit for bit (integer codes with
+  * the linear layer on the three INT8 kernel paths (GEMV, SKINNY, and the
+    256 x 256 GEMM) and the automatic choice: exact-arithmetic cases bit for bit (integer codes with
     scale 2^-3 and small integer activations make every partial sum exact),
     random ragged cases within the tolerance of tests/gpu_util.py, fused
     activations, K splits through the exchange slots and through partial
@@ -23,7 +23,7 @@ from tests.gpu_util import bits, check_close, require_gpu, row_max_dequant, say,
 
 pytestmark = pytest.mark.gpu
 
-PATHS8 = ["GEMV", "SKINNY", "AUTO"]
+PATHS8 = ["GEMV", "SKINNY", "GEMM", "AUTO"]
 
 
 @pytest.fixture(scope="module")
@@ -222,6 +222,32 @@ def test_int8_exact_arithmetic_bit_exact(dev, path, dtype, m, n, k):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
 
 
+# The eight-wave GEMM on INT8 weights: ragged M and N over 256 x 256 tiles,
+# no split (one LDS-staged epilogue), an uneven long-K split (six parts of
+# 17 groups and one of 11), a single group, and a K split with odd group
+# counts.  Exact arithmetic, bit for bit on whole rows and columns at tile
+# edges.
+GEMM8_TILE_SHAPES = [(513, 16424, 1152), (1000, 2056, 14464), (769, 12296, 128), (300, 4104, 640)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", GEMM8_TILE_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k in GEMM8_TILE_SHAPES])
+def test_int8_gemm_tilings_bit_exact(dev, dtype, m, n, k):
+    w, x, b = exact_case8(m, n, k, seed=m + n + k + 1, dtype=dtype, with_bias=True)
+    say(f"int8 gemm tiling case dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare8(w, dev)
+    y = run8(x.to(dev), packed, n, b.to(dev), "GEMM").cpu().to(torch.float64).numpy()
+    edge_rows = sorted({0, 127, 128, 255, 256, m - 2, m - 1} & set(range(m)))
+    edge_cols = sorted({0, 15, 16, 255, 256, n - 17, n - 1} & set(range(n)))
+    rows = np.concatenate([np.repeat(edge_rows, n), np.tile(np.arange(m), len(edge_cols))])
+    cols = np.concatenate([np.tile(np.arange(n), len(edge_rows)), np.repeat(edge_cols, m)])
+    want = to_rne16(oracle.linear_entries(bits(x), tag(dtype), q, s, bits(b), rows, cols), dtype)
+    got = y[rows, cols]
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (f"{bad.size} mismatches, first at row {rows[bad[0]]} col {cols[bad[0]]}: "
+                           f"got {got[bad[0]]} want {want[bad[0]]}")
+
+
 def random_case8(m, n, k, seed, dtype, with_bias, xcols=None):
     g = torch.Generator().manual_seed(seed)
     w = torch.randn(n, k, generator=g) * 0.02
@@ -304,7 +330,8 @@ def test_int8_shared_workspace_and_determinism(dev):
 
 
 W8_WORKLOADS = ["c1_m1_k1024_n1024", "c2_down_m50_k4096_n1024", "c3_gate_up_m1_k2048_n32768",
-                "c3_down_m1_k16384_n2048", "c5_m1_k16384_n2048", "c4_m1024_k2048_n2560"]
+                "c3_down_m1_k16384_n2048", "c5_m1_k16384_n2048", "c4_m1024_k2048_n2560",
+                "c4_m1024_k2048_n32768", "c4_m1024_k16384_n2048"]
 
 
 @pytest.mark.parametrize("name", W8_WORKLOADS)

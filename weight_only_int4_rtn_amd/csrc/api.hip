@@ -44,7 +44,7 @@ size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bi
         case W4A16_PATH_GEMV: return plan_gemv(m < 4 ? m : 4, n, k, bits).workspace;
         case W4A16_PATH_MGEMV: return bits == 4 ? plan_mgemv(m < 16 ? m : 16, n, k).workspace : 0;
         case W4A16_PATH_SKINNY: return plan_skinny(m, n, k, bits).workspace;
-        case W4A16_PATH_GEMM: return bits == 4 ? plan_gemm(m, n, k).workspace : 0;
+        case W4A16_PATH_GEMM: return plan_gemm(m, n, k, bits).workspace;
         default: return 0;
     }
 }
@@ -200,7 +200,9 @@ w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, in
 
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     (void)n;
-    if (m <= 3) return W4A16_PATH_GEMV;
+    // measured (MI355X): from M = 3 the MFMA contraction beats v_dot2
+    // (3-15 % on 2048-32768-column layers; at M = 2 the two are within a few %)
+    if (m <= 2) return W4A16_PATH_GEMV;
     if (m <= 8) return W4A16_PATH_MGEMV;
     if (m < 128 || k > kGemmMaxLd) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
@@ -208,8 +210,9 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
 
 w4a16_path_t w8a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     (void)n;
-    (void)k;
-    return m <= 4 ? W4A16_PATH_GEMV : W4A16_PATH_SKINNY;
+    if (m <= 4) return W4A16_PATH_GEMV;
+    if (m < 128 || k > kGemmMaxLd) return W4A16_PATH_SKINNY;
+    return W4A16_PATH_GEMM;
 }
 
 }  // extern "C"
@@ -261,8 +264,8 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
         if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) path = W4A16_PATH_SKINNY;
     }
     if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) return W4A16_EUNSUPPORTED;
-    // INT8 weights run on the GEMV and SKINNY kernels
-    if (bits == 8 && (path == W4A16_PATH_MGEMV || path == W4A16_PATH_GEMM)) return W4A16_EUNSUPPORTED;
+    // INT8 weights run on the GEMV, SKINNY and (eight-wave) GEMM kernels
+    if (bits == 8 && path == W4A16_PATH_MGEMV) return W4A16_EUNSUPPORTED;
 
     const size_t xbytes = span_bytes(m, xcols, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
                  pbytes = bits == 8 ? w8a16_packed_bytes(n, k) : w4a16_packed_bytes(n, k),
@@ -303,11 +306,11 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
     }
     if (path == W4A16_PATH_GEMM) {
         if (act_fn == kActFnNone)
-            return from_hip(launch_gemm(x, act, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
+            return from_hip(launch_gemm(x, act, bits, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
         void* xa = static_cast<uint8_t*>(workspace) + round_up(path_workspace(path, m, n, k, bits), 256);
         const hipError_t e = launch_activate(x, act, act_fn, m, k, ldx, xa, s);
         if (e != hipSuccess) return W4A16_EHIP;
-        return from_hip(launch_gemm(xa, act, m, k, k, packed, n, bias, y, ldy, workspace, s));
+        return from_hip(launch_gemm(xa, act, bits, m, k, k, packed, n, bias, y, ldy, workspace, s));
     }
     return from_hip(launch_skinny(x, act, act_fn, bits, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
 }

@@ -24,6 +24,10 @@
 // the MFMAs of the current one.  Accumulators live in AGPRs (inline-asm
 // MFMA with an "a" constraint).
 //
+// INT8 weights (W8A16) run on gemm8_kernel only: the same stages with a
+// 16-byte run of each 1 KB chunk half per stage (byte codes, u = q + 128,
+// fma(u, s, -128 s)).
+//
 // The epilogue adds the bias in FP32 and rounds once to the output dtype, or,
 // for a K split, stores FP32 partial sums for the split-K reduce kernel.
 #include "common.h"
@@ -117,6 +121,17 @@ __device__ inline uint4 dequant_word(uint32_t w, float s, float neg8s) {
     const float c3 = fmaf(byte_f32<2>(hi), s, neg8s);
     const float c7 = fmaf(byte_f32<3>(hi), s, neg8s);
     return make_uint4(pack2<ACT>(c0, c1), pack2<ACT>(c2, c3), pack2<ACT>(c4, c5), pack2<ACT>(c6, c7));
+}
+
+// Two INT8 words (columns 0-3 and 4-7, byte b = column b, u = q + 128) ->
+// 8 dequantized 16-bit values in column order: fma(u, s, -128 s), -128 s
+// exact.
+template <int ACT>
+__device__ inline uint4 dequant_word8(uint32_t w0, uint32_t w1, float s, float neg128s) {
+    return make_uint4(pack2<ACT>(fmaf(byte_f32<0>(w0), s, neg128s), fmaf(byte_f32<1>(w0), s, neg128s)),
+                      pack2<ACT>(fmaf(byte_f32<2>(w0), s, neg128s), fmaf(byte_f32<3>(w0), s, neg128s)),
+                      pack2<ACT>(fmaf(byte_f32<0>(w1), s, neg128s), fmaf(byte_f32<1>(w1), s, neg128s)),
+                      pack2<ACT>(fmaf(byte_f32<2>(w1), s, neg128s), fmaf(byte_f32<3>(w1), s, neg128s)));
 }
 
 // LDS layout of an x tile: row r of BM rows holds its 128 columns as 16
@@ -401,14 +416,17 @@ constexpr int kG8WStage = 16 * 2 * 64 * 16;        // bytes per B stage
 // (16 consecutive rows, one segment) cover all 64 banks once.
 __device__ inline int swz8(int row, int seg) { return row * kG8K + ((seg ^ ((row >> 1) & 7)) << 3); }
 
-template <int ACT, bool STAGED>
+// BITS 8: INT8 chunks (two 1 KB halves, half h = stage 2g + h): a lane's
+// k-step is two words of four byte codes, u = q + 128.
+template <int ACT, bool STAGED, int BITS>
 __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
     __shared__ __align__(16) uint16_t X0[kG8XStage];
     __shared__ __align__(16) uint16_t X1[kG8XStage];
     __shared__ __align__(16) uint8_t W0[kG8WStage];
     __shared__ __align__(16) uint8_t W1[kG8WStage];
 
-    const Layout L(a.n, a.k);
+    const Layout L(a.n, a.k, BITS);
     const int split = int(blockIdx.x % unsigned(a.splits));
     const int64_t tile = int64_t(blockIdx.x / unsigned(a.splits));
     const int64_t mt = tile % a.mtiles, nt = tile / a.mtiles;  // consecutive workgroups share weights
@@ -449,18 +467,18 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
     const int validw = int(min<int64_t>(2, max<int64_t>(0, L.tiles - tw)));
     const int64_t twfirst = min<int64_t>(tw, L.tiles - 1);
     const __amdgpu_buffer_rsrc_t wres =
-        buffer_rsrc(a.packed + twfirst * L.groups * kChunkBytes, 2 * L.groups * kChunkBytes);
+        buffer_rsrc(a.packed + twfirst * L.groups * CB, 2 * L.groups * CB);
     const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
         a.packed + L.scale_offset() + twfirst * L.groups * kChunkScaleBytes, 2 * L.groups * kChunkScaleBytes);
     uint32_t woff[2], soff[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int cc = c < validw ? c : (validw > 0 ? validw - 1 : 0);
-        woff[c] = uint32_t(cc * L.groups * kChunkBytes + lane * 16);
+        woff[c] = uint32_t(cc * L.groups * CB + lane * 16);
         soff[c] = uint32_t(cc * L.groups * kChunkScaleBytes + r * 4);
     }
     struct Words {
-        uint32_t w[2][4];
+        uint32_t w[2][4 * H];  // INT8: half h in words 4h .. 4h + 3
         float s[2];
     };
     // one group's words and scales (groups past the split's end reload its
@@ -469,11 +487,15 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
         const int64_t g = g0 + min(gl, ng - 1);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[c], uniform(int(g * kChunkBytes)), 0);
-            d.w[c][0] = v[0];
-            d.w[c][1] = v[1];
-            d.w[c][2] = v[2];
-            d.w[c][3] = v[3];
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[c] + h * kChunkBytes,
+                                                                     uniform(int(g * CB)), 0);
+                d.w[c][4 * h] = v[0];
+                d.w[c][4 * h + 1] = v[1];
+                d.w[c][4 * h + 2] = v[2];
+                d.w[c][4 * h + 3] = v[3];
+            }
             d.s[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                    sres, soff[c], uniform(int(g * kChunkScaleBytes)), 0));
         }
@@ -499,9 +521,12 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
     // buffers nobody reads any more), which keeps the loop free of branches.
     auto stage = [&](const uint16_t* Xp, const uint8_t* Wp, uint16_t* Xq, uint8_t* Wq, int s, auto odd_c) {
         constexpr bool odd = decltype(odd_c)::value;
-        // an even stage issued its successor's x pieces and then four word
-        // loads; an odd stage only x pieces
-        if constexpr (odd)
+        // an even stage issued its successor's x pieces and then the word
+        // loads (two 16-byte runs and two scales; INT8: four runs); an odd
+        // stage only x pieces
+        if constexpr (odd && BITS == 8)
+            asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory");
+        else if constexpr (odd)
             asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
         else
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -540,8 +565,24 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
                 // word (c, ks') of stage s + 1: c = f / 8, ks' = (f / 4) % 2,
                 // quarter f % 4
                 const int c = f >> 3, kn = (f >> 2) & 1, q = f & 3;
-                const uint32_t w = src.w[c][2 * h1 + kn];
                 const float sj = c < validw ? src.s[c] : 0.0f;
+                if constexpr (BITS == 8) {
+                    // words 4 h1 + 2 kn (columns 0-3) and + 1 (columns 4-7):
+                    // quarter q converts columns 2q, 2q + 1
+                    const uint32_t w = src.w[c][4 * h1 + 2 * kn + (q >> 1)];
+                    const float oj = -128.0f * sj;
+                    const float va = fmaf((q & 1) ? byte_f32<2>(w) : byte_f32<0>(w), sj, oj);
+                    const float vb = fmaf((q & 1) ? byte_f32<3>(w) : byte_f32<1>(w), sj, oj);
+                    const uint32_t pr = pack2<ACT>(va, vb);
+                    if (q == 0) out.x = pr;
+                    else if (q == 1) out.y = pr;
+                    else if (q == 2) out.z = pr;
+                    else {
+                        out.w = pr;
+                        *reinterpret_cast<uint4*>(Wq + wslot(2 * wave + c, kn)) = out;
+                    }
+                } else {
+                const uint32_t w = src.w[c][2 * h1 + kn];
                 const float oj = -8.0f * sj;
                 if (q == 0) {
                     lo = w & 0x0F0F0F0Fu;  // bytes: columns 0, 4, 1, 5
@@ -563,6 +604,7 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
                     out.w = pack2<ACT>(c6, c7);
                     *reinterpret_cast<uint4*>(Wq + wslot(2 * wave + c, kn)) = out;
                 }
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -582,7 +624,9 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
         const float sj = c < validw ? wcur.s[c] : 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            *reinterpret_cast<uint4*>(W0 + wslot(2 * wave + c, ks)) = dequant_word<ACT>(wcur.w[c][ks], sj, -8.0f * sj);
+            *reinterpret_cast<uint4*>(W0 + wslot(2 * wave + c, ks)) =
+                BITS == 8 ? dequant_word8<ACT>(wcur.w[c][2 * ks], wcur.w[c][2 * ks + 1], sj, -128.0f * sj)
+                          : dequant_word<ACT>(wcur.w[c][ks], sj, -8.0f * sj);
     }
 
     for (int s = 0; s < nstages; s += 2) {
@@ -684,9 +728,9 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
     }
 }
 
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits) {
     GemmPlan p{};
-    const Layout L(n, k);
+    const Layout L(n, k, bits);
     // 256 x 256 tiles (eight waves, each weight dequantized once per 256
     // rows) where they alone give every CU work; else 128 x 256 tiles of
     // four waves, two workgroups per CU.
@@ -696,6 +740,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
     const int64_t tiles8 = ceil_div(m, kG8Rows) * ceil_div(n, kGmBN);
     const int64_t splits8 = tiles8 >= 256 ? 1 : 256 / tiles8;
     p.waves = tiles8 >= 128 || L.groups >= 16 * splits8 ? 8 : 4;
+    if (bits == 8) p.waves = 8;  // INT8 weights: the eight-wave kernel only
     p.mb = p.waves == 8 ? 16 : 8;
     p.mtiles = ceil_div(m, 16 * p.mb);
     p.ntiles = ceil_div(n, kGmBN);
@@ -712,10 +757,22 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-hipError_t launch_gemm(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
+template <int BITS>
+static void launch_g8(const GemmArgs& a, bool bf, bool staged, dim3 grid, hipStream_t stream) {
+    const dim3 b8(kG8Threads);
+    if (staged) {
+        if (bf) gemm8_kernel<kActBf16, true, BITS><<<grid, b8, 0, stream>>>(a);
+        else gemm8_kernel<kActF16, true, BITS><<<grid, b8, 0, stream>>>(a);
+    } else {
+        if (bf) gemm8_kernel<kActBf16, false, BITS><<<grid, b8, 0, stream>>>(a);
+        else gemm8_kernel<kActF16, false, BITS><<<grid, b8, 0, stream>>>(a);
+    }
+}
+
+hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, int64_t ldx, const void* packed,
                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream) {
-    const GemmPlan p = plan_gemm(m, n, k);
+    const GemmPlan p = plan_gemm(m, n, k, bits);
     // the x tile's buffer resource takes 32-bit byte offsets
     if (int64_t(16 * p.mb) * ldx * 2 > int64_t(0xFFFFFFFF)) return hipErrorInvalidValue;
     GemmArgs a;
@@ -738,14 +795,8 @@ hipError_t launch_gemm(const void* x, int act, int64_t m, int64_t k, int64_t ldx
     const dim3 grid(unsigned(p.mtiles * p.ntiles * p.splits)), block(kGmThreads);
     const bool bf = act == kActBf16;
     if (p.waves == 8) {
-        const dim3 b8(kG8Threads);
-        if (p.splits == 1 && a.vec16) {
-            if (bf) gemm8_kernel<kActBf16, true><<<grid, b8, 0, stream>>>(a);
-            else gemm8_kernel<kActF16, true><<<grid, b8, 0, stream>>>(a);
-        } else {
-            if (bf) gemm8_kernel<kActBf16, false><<<grid, b8, 0, stream>>>(a);
-            else gemm8_kernel<kActF16, false><<<grid, b8, 0, stream>>>(a);
-        }
+        if (bits == 8) launch_g8<8>(a, bf, p.splits == 1 && a.vec16, grid, stream);
+        else launch_g8<4>(a, bf, p.splits == 1 && a.vec16, grid, stream);
     } else {
         if (bf) gemm_kernel<kActBf16, 8><<<grid, block, 0, stream>>>(a);
         else gemm_kernel<kActF16, 8><<<grid, block, 0, stream>>>(a);

@@ -47,7 +47,7 @@ struct GemmPlan {
     int mb, gps, splits;  // mb: 16-row blocks per workgroup (128 or 256 rows)
     size_t workspace;
 };
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k);
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int64_t ldw,
                            uint8_t* codes, float* scales, hipStream_t stream);
@@ -95,7 +95,7 @@ hipError_t launch_skinny(const void* x, int act, int act_fn, int bits, int64_t m
 // The activated input [m][k] (row stride k) of x for the GEMM path.
 hipError_t launch_activate(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx, void* out,
                            hipStream_t stream);
-hipError_t launch_gemm(const void* x, int act, int64_t m, int64_t k, int64_t ldx, const void* packed,
+hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, int64_t ldx, const void* packed,
                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream);
 
