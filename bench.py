@@ -593,6 +593,16 @@ def main():
                           "frac": round(w8_dom_gbs / HBM_PEAK_GBS, 4),
                           "kernel": f"{w4.choose_path(1, dom.n, dom.k, 8).name} int8 {dom.name}",
                           "avg_launch_us": round(w8["dom_ms"] * 1e3, 3), "bytes_per_launch": alg_bytes(dom, 8)}}
+    pre8 = run_workload(pcases, dev, 20, 3, pdom, bits=8, eager=False)
+    p8tf = pflops / (pre8["ms"] * 1e-3) / 1e12
+    p8d_tf = pd.flops() / (pre8["dom_ms"] * 1e-3) / 1e12
+    w8a16["m1024"] = {"workload": "prefill M=1024 fp16 with bias as above, int8 g128 weights",
+                      "tflops": round(p8tf, 2), "ms_per_step": round(pre8["ms"], 4),
+                      "pct_mfma_peak": round(100 * p8tf / MFMA_PEAK_TFLOPS, 2),
+                      "roofline": {"bound": "mfma", "achieved": round(p8d_tf, 2), "peak": MFMA_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(p8d_tf / MFMA_PEAK_TFLOPS, 4),
+                                   "kernel": f"{w4.choose_path(pd.m, pd.n, pd.k, 8).name} int8 {pd.name}",
+                                   "avg_launch_us": round(pre8["dom_ms"] * 1e3, 3)}}
     log(f"w8a16: {w8a16}")
 
     out = {
