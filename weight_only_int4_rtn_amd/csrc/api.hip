@@ -199,11 +199,15 @@ w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, in
 }
 
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
-    (void)n;
-    // measured (MI355X): from M = 3 the MFMA contraction beats v_dot2
-    // (3-15 % on 2048-32768-column layers; at M = 2 the two are within a few %)
+    // Measured (MI355X, graph replay): from M = 3 the MFMA contraction beats
+    // v_dot2 (3-15 %; at M = 2 the two are within a few %).  The small-M MFMA
+    // kernel finishes its K splits in-kernel and wins over the mid-M kernel
+    // (split + reduce launch) up to M = 16 on layers of <= 8 M weights (by
+    // 15-50 %), up to M = 8 on layers of <= 4096 outputs and up to M = 4 on
+    // wider ones (32768 x 2048: 13.2 vs 15.2 us at M = 4, 18.8 vs 15.2 at 8).
     if (m <= 2) return W4A16_PATH_GEMV;
-    if (m <= 8) return W4A16_PATH_MGEMV;
+    const bool small = n * k <= (int64_t(8) << 20);
+    if (m <= 4 || (m <= 8 && n <= 4096) || (m <= 16 && small)) return W4A16_PATH_MGEMV;
     if (m < 128 || k > kGemmMaxLd) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
 }
