@@ -11,13 +11,15 @@ from tests.gpu_util import require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-# (m, n, k, act, bits): GEMV with a K split finished through the exchange
-# slots, MGEMV split, SKINNY split + reduce kernel, GEMM, a fused SwiGLU
-# input, the GEMM path with a materialised GELU input; INT8 weights on the
-# GEMV (eight-part split), SKINNY and 256 x 256 GEMM paths
-CALLS = [(1, 2048, 16384, "NONE", 4), (6, 520, 8192, "NONE", 4), (50, 1000, 4096, "NONE", 4),
-         (300, 2056, 1152, "NONE", 4), (1, 1024, 4096, "SWIGLU", 4), (256, 512, 1024, "GELU_TANH", 4),
-         (1, 2048, 16384, "NONE", 8), (50, 1000, 4096, "SWIGLU", 8), (300, 2056, 1152, "GELU_TANH", 8)]
+# (m, n, k, act, bits, path): GEMV with a K split finished through the
+# exchange slots, MGEMV split, SKINNY split + reduce kernel, GEMM, a fused
+# SwiGLU input, the GEMM path with a materialised GELU input; INT8 weights on
+# the GEMV (eight-part split), SKINNY and 256 x 256 GEMM paths
+CALLS = [(1, 2048, 16384, "NONE", 4, "AUTO"), (6, 520, 8192, "NONE", 4, "AUTO"),
+         (50, 1000, 4096, "NONE", 4, "AUTO"), (300, 2056, 1152, "NONE", 4, "GEMM"),
+         (1, 1024, 4096, "SWIGLU", 4, "AUTO"), (256, 512, 1024, "GELU_TANH", 4, "GEMM"),
+         (1, 2048, 16384, "NONE", 8, "AUTO"), (50, 1000, 4096, "SWIGLU", 8, "AUTO"),
+         (300, 2056, 1152, "GELU_TANH", 8, "GEMM")]
 
 
 def test_graph_replays_equal_eager(dev=None):
@@ -26,7 +28,7 @@ def test_graph_replays_equal_eager(dev=None):
     g = torch.Generator().manual_seed(11)
     setups = []
     ws_bytes = 16
-    for m, n, k, act, nbits in CALLS:
+    for m, n, k, act, nbits, path in CALLS:
         w = torch.randn(n, k, generator=g) * 0.02
         width = 2 * k if act == "SWIGLU" else k
         x = torch.randn(m, width, generator=g).to(torch.bfloat16).to(dev)
@@ -38,13 +40,13 @@ def test_graph_replays_equal_eager(dev=None):
             c, s = w4.quantize(w.to(dev))
             p = w4.pack(c, s)
         y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-        setups.append((m, n, k, w4.Act[act], nbits, x, p, b, y))
+        setups.append((m, n, k, w4.Act[act], nbits, w4.Path[path], x, p, b, y))
         ws_bytes = max(ws_bytes, w4.workspace_bytes(m, n, k, w4.Act[act], nbits))
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
 
     def run():
-        for m, n, k, act, nbits, x, p, b, y in setups:
-            w4.linear(x, p, n, b, out=y, workspace=ws, act=act, bits=nbits)
+        for m, n, k, act, nbits, path, x, p, b, y in setups:
+            w4.linear(x, p, n, b, out=y, workspace=ws, act=act, bits=nbits, path=path)
 
     run()
     torch.cuda.synchronize()
@@ -66,5 +68,5 @@ def test_graph_replays_equal_eager(dev=None):
             assert torch.equal(s[-1], eager[i]), f"replay {rep}, call {i} {CALLS[i]}"
         assert int(ws[:1 << 20].count_nonzero()) == 0, f"replay {rep}: exchange slots not left zero"
         # eager work between replays (same workspace, other shapes)
-        w4.linear(setups[2][5], setups[2][6], setups[2][1], workspace=ws)
+        w4.linear(setups[2][6], setups[2][7], setups[2][1], workspace=ws)
         torch.cuda.synchronize()
