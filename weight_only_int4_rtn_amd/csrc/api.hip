@@ -205,14 +205,15 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     // (split + reduce launch) up to M = 16 on layers of <= 8 M weights (by
     // 15-50 %), up to M = 8 on layers of <= 4096 outputs and up to M = 4 on
     // wider ones (32768 x 2048: 13.2 vs 15.2 us at M = 4, 18.8 vs 15.2 at 8).
-    // The mid-M kernel also beats the GEMM (whose few tiles need a K split
-    // and a reduce launch) on small layers up to M = 512 (256 x 4096 x 1024:
-    // 10.6 vs 26.5 us; 512 x 2560 x 2048: 23.3 vs 26.4 us); on larger
-    // layers the GEMM wins from M = 128 (128 x 2048 x 16384: 30.7 vs 41.3 us).
+    // The mid-M kernel beats the GEMM (whose few tiles need a K split and a
+    // reduce launch) on small layers up to M = 512 (256 x 4096 x 1024: 10.6
+    // vs 26.5 us; 512 x 2560 x 2048: 23.3 vs 26.4 us); on larger layers only
+    // up to M = 64 (two 32-row blocks: 64 x 2048 x 16384 25.5 vs 30.6 us;
+    // 100 x 2048 x 16384 40.2 vs 30.4 us).
     if (m <= 2) return W4A16_PATH_GEMV;
     const bool small = n * k <= (int64_t(8) << 20);
     if (m <= 4 || (m <= 8 && n <= 4096) || (m <= 16 && small)) return W4A16_PATH_MGEMV;
-    if (m < 128 || k > kGemmMaxLd || (small && m <= 512)) return W4A16_PATH_SKINNY;
+    if (k > kGemmMaxLd || m <= 64 || (small && m <= 512)) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
 }
 
