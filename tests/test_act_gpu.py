@@ -103,6 +103,45 @@ def test_row_stride_and_deterministic(dev):
                     f"strided {path}")
 
 
+def test_gemm_activation_leaves_slot_header_zero(dev):
+    """A GEMM-path call with a materialised activation whose GEMM needs no
+    K split (so no workspace of its own) keeps the activated input out of the
+    exchange-slot header: the header stays zero, and a small-M call that
+    finishes its K split through the slots, sharing the workspace, stays
+    exact."""
+    from tests.gpu_util import to_rne16
+    lib = w4()
+    g = torch.Generator().manual_seed(99)
+    m, n, k = 300, 4104, 640
+    w = torch.randn(n, k, generator=g) * 0.02
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    codes, scales = lib.quantize(w.to(dev))
+    packed = lib.pack(codes, scales)
+    ws = torch.zeros(max(lib.workspace_bytes(m, n, k, lib.Act.GELU_TANH), lib.workspace_bytes(1, 2048, 16384)),
+                     dtype=torch.uint8, device=dev)
+    say(f"gemm activation workspace: m={m} n={n} k={k}")
+    y = lib.linear(x.to(dev), packed, n, path=lib.Path.GEMM, act=lib.Act.GELU_TANH, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:1 << 20].count_nonzero()) == 0, "activated input written into the slot header"
+    q, s = oracle.quantize(w.numpy())
+    y_ref, anorm = reference(x, torch.bfloat16, "gelu", q, s, None)
+    check_close(y.cpu().to(torch.float64).numpy(), y_ref, anorm[:, None], row_max_dequant(q, s)[None, :],
+                "gemm gelu unsplit")
+    # exact-arithmetic GEMV with a four-part split through the slots
+    rng = np.random.default_rng(5)
+    qi = rng.integers(-7, 8, size=(2048, 16384), dtype=np.int8)
+    qi[:, ::128] = 7
+    w2 = torch.from_numpy((qi * 2.0 ** -3).astype(np.float32))
+    x2 = torch.from_numpy(rng.integers(-4, 5, size=(1, 16384)).astype(np.float32)).to(torch.bfloat16)
+    c2, s2 = lib.quantize(w2.to(dev))
+    y2 = lib.linear(x2.to(dev), lib.pack(c2, s2), 2048, path=lib.Path.GEMV, workspace=ws)
+    torch.cuda.synchronize()
+    q2, s2o = oracle.quantize(w2.numpy())
+    want = to_rne16(oracle.linear(bits(x2), tag(torch.bfloat16), q2, s2o), torch.bfloat16)
+    assert np.array_equal(y2.cpu().to(torch.float64).numpy(), want)
+    assert int(ws[:1 << 20].count_nonzero()) == 0
+
+
 FFN_CASES = [("swiglu", 1, 2048, 2048, torch.bfloat16), ("swiglu", 4, 1024, 1536, torch.bfloat16),
              ("gelu", 50, 1024, 4096, torch.bfloat16), ("gelu", 256, 512, 1024, torch.float16)]
 

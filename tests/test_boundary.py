@@ -177,6 +177,10 @@ def test_linear_act_rejects(lib):
     assert lin_act(lib, ge, path=gemm, m=256, k=(1 << 22) + 128, ldx=(1 << 22) + 128, n=16,
                    y=A * 8192) == B.EUNSUPPORTED
     assert lin_act(lib, ge, path=gemm, m=256, k=128, ldx=big, y=A * 8192, ws=None) == B.EWORKSPACE
+    # an unsplit GEMM keeps the activated input after the 1 MiB header of
+    # exchange slots, never inside it
+    assert w4.workspace_bytes(300, 4104, 640) == 0
+    assert w4.workspace_bytes(300, 4104, 640, w4.Act.GELU_TANH) >= (1 << 20) + 300 * 640 * 2
     assert lib.w4a16_linear_act_workspace_bytes(5, 16, 16, 128) == 0
     assert lib.w4a16_linear_act_workspace_bytes(int(w4.Act.NONE), 1, 2048, 16384) == w4.workspace_bytes(1, 2048, 16384)
 

@@ -84,11 +84,12 @@ def test_exact_arithmetic_bit_exact(dev, path, dtype, m, n, k):
 # N, a K split whose parts hold odd and even group counts, a single group
 # (LDS-staged epilogue), a row stride that is not a multiple of 8 (direct
 # epilogue); and 128 x 256 tiles, one group deep and split; 256 x 256
-# tiles over a long K split in six parts of 17 groups and one of 11.
+# tiles over a long K split in six parts of 17 groups and one of 11; 64 x 256
+# tiles over a short K, split in two (5 + 4 groups) and unsplit.
 # Exact arithmetic, checked bit for bit on whole rows and columns (first,
 # last, either side of a tile edge).
 GEMM_TILE_SHAPES = [(513, 16424, 1152), (769, 12296, 128), (300, 4104, 640), (1000, 2056, 2176),
-                    (512, 32772, 256), (1000, 2056, 14464)]
+                    (512, 32772, 256), (1000, 2056, 14464), (100, 16136, 1152), (1000, 4104, 1024)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
@@ -98,7 +99,7 @@ def test_gemm_tilings_bit_exact(dev, dtype, m, n, k):
     say(f"gemm tiling case dtype={dtype} m={m} n={n} k={k}")
     packed, q, s = prepare(w, dev)
     y = run(x.to(dev), packed, n, b.to(dev), "GEMM").cpu().to(torch.float64).numpy()
-    edge_rows = sorted({0, 127, 128, 255, 256, m - 2, m - 1} & set(range(m)))
+    edge_rows = sorted({0, 63, 64, 127, 128, 255, 256, m - 2, m - 1} & set(range(m)))
     edge_cols = sorted({0, 15, 16, 255, 256, n - 17, n - 1} & set(range(n)))
     rows = np.concatenate([np.repeat(edge_rows, n), np.tile(np.arange(m), len(edge_cols))])
     cols = np.concatenate([np.tile(np.arange(n), len(edge_rows)), np.repeat(edge_cols, m)])

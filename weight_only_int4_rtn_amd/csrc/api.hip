@@ -230,12 +230,20 @@ namespace {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Byte offset of the materialised activated input in a GEMM + activation
+// workspace: after the path's own workspace and never inside the zero
+// header of exchange slots (an unsplit GEMM needs no workspace of its own).
+size_t act_input_offset(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bits) {
+    const size_t base = path_workspace(path, m, n, k, bits);
+    return round_up(base > kSyncBytes ? base : kSyncBytes, 256);
+}
+
 // Workspace of one path with an activation: the large-M path materialises
 // the activated input [m][k] after its own workspace.
 size_t act_path_workspace(int act_fn, w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bits) {
     const size_t base = path_workspace(path, m, n, k, bits);
     if (act_fn == kActFnNone || path != W4A16_PATH_GEMM) return base;
-    return round_up(base, 256) + size_t(m) * size_t(k) * 2;
+    return act_input_offset(path, m, n, k, bits) + size_t(m) * size_t(k) * 2;
 }
 
 size_t act_workspace_bytes(int act_fn, int64_t m, int64_t n, int64_t k, int bits) {
@@ -316,7 +324,7 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
     if (path == W4A16_PATH_GEMM) {
         if (act_fn == kActFnNone)
             return from_hip(launch_gemm(x, act, bits, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
-        void* xa = static_cast<uint8_t*>(workspace) + round_up(path_workspace(path, m, n, k, bits), 256);
+        void* xa = static_cast<uint8_t*>(workspace) + act_input_offset(path, m, n, k, bits);
         const hipError_t e = launch_activate(x, act, act_fn, m, k, ldx, xa, s);
         if (e != hipSuccess) return W4A16_EHIP;
         return from_hip(launch_gemm(xa, act, bits, m, k, k, packed, n, bias, y, ldy, workspace, s));

@@ -12,9 +12,10 @@
 // the epilogue stores together.
 //
 // Two kernels, chosen by tile count:
-//   gemm_kernel<ACT, 8>: 128 x 256 tiles, four waves (two workgroups per
-//     CU); wave w owns 64 columns and all 128 rows, and dequantizes its own
-//     chunks in registers between its MFMAs.
+//   gemm_kernel<ACT, MB>: 16 MB x 256 tiles (MB = 8: 128 rows; MB = 4: 64
+//     rows for short K), four waves (two workgroups per CU); wave w owns 64
+//     columns and all the rows, and dequantizes its own chunks in registers
+//     between its MFMAs.
 //   gemm8_kernel: 256 x 256 tiles, eight waves (two per SIMD); the
 //     workgroup dequantizes each weight once into an LDS operand tile that
 //     all waves read, so each weight is decoded once per 256 rows.
@@ -742,6 +743,14 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits) {
     p.waves = tiles8 >= 128 || L.groups >= 16 * splits8 ? 8 : 4;
     if (bits == 8) p.waves = 8;  // INT8 weights: the eight-wave kernel only
     p.mb = p.waves == 8 ? 16 : 8;
+    // A short K (<= 16 groups) whose 128-row tiles would need a K split takes
+    // 64-row tiles: twice the workgroups, and no partial sums to write and
+    // reduce (1024 x 4096 x 1024: 31.5 -> 19.7 us; 256 x 16384 x 2048: 37.2
+    // -> 33.9 us).  Up to 8 groups it never splits; with more, tiles filling
+    // half the chip split in two (100 x 16384 x 2048: 25.7 us against 31.4
+    // unsplit).
+    const bool rows64 = p.waves == 4 && L.groups <= 16 && ceil_div(m, 128) * ceil_div(n, kGmBN) < 256;
+    if (rows64) p.mb = 4;
     p.mtiles = ceil_div(m, 16 * p.mb);
     p.ntiles = ceil_div(n, kGmBN);
     const int64_t tiles = p.mtiles * p.ntiles;
@@ -749,6 +758,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits) {
     // still fit one round of 256 workgroups (a second, partial round would
     // cost a whole round's time)
     int64_t splits = tiles >= 256 ? 1 : 256 / tiles;
+    if (rows64 && L.groups <= 8) splits = 1;
     if (splits > L.groups) splits = L.groups;
     int64_t gps = ceil_div(L.groups, splits);
     p.gps = int(gps);
@@ -798,8 +808,13 @@ hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, i
         if (bits == 8) launch_g8<8>(a, bf, p.splits == 1 && a.vec16, grid, stream);
         else launch_g8<4>(a, bf, p.splits == 1 && a.vec16, grid, stream);
     } else {
-        if (bf) gemm_kernel<kActBf16, 8><<<grid, block, 0, stream>>>(a);
-        else gemm_kernel<kActF16, 8><<<grid, block, 0, stream>>>(a);
+        if (p.mb == 4) {
+            if (bf) gemm_kernel<kActBf16, 4><<<grid, block, 0, stream>>>(a);
+            else gemm_kernel<kActF16, 4><<<grid, block, 0, stream>>>(a);
+        } else {
+            if (bf) gemm_kernel<kActBf16, 8><<<grid, block, 0, stream>>>(a);
+            else gemm_kernel<kActF16, 8><<<grid, block, 0, stream>>>(a);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;

@@ -44,7 +44,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits = 4);
 struct GemmPlan {
     int64_t mtiles, ntiles;
     int waves;            // 8: 256 x 256 tiles, eight waves; 4: 16 mb x 256 tiles, four waves
-    int mb, gps, splits;  // mb: 16-row blocks per workgroup (128 or 256 rows)
+    int mb, gps, splits;  // mb: 16-row blocks per workgroup (64, 128 or 256 rows)
     size_t workspace;
 };
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits = 4);
