@@ -239,7 +239,8 @@ w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dt
 /*
  * Workspace bytes w4a16_linear_act needs (0 if none; 0 for an unknown act).
  * Same header rules as w4a16_linear_workspace_bytes; with an activation the
- * large-M path also keeps the activated input, m * k 16-bit values, there.
+ * large-M path also keeps the activated input, m * k 16-bit values, there
+ * (after the header and the GEMM's own partial sums).
  */
 size_t w4a16_linear_act_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k);
 
