@@ -231,10 +231,12 @@ def test_int8_packed_bytes_and_paths(lib):
         w4.packed_bytes(16, 128, bits=2)
     assert w4.choose_path(1, 2048, 2048, bits=8) == w4.Path.GEMV
     assert w4.choose_path(4, 2048, 2048, bits=8) == w4.Path.GEMV
-    for m in (5, 16, 50, 127):
+    for m in (5, 16, 50, 127, 512):
         assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.SKINNY
-    for m in (128, 256, 4096):
+    for m in (513, 4096):
         assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.GEMM
+    assert w4.choose_path(64, 2048, 16384, bits=8) == w4.Path.SKINNY
+    assert w4.choose_path(65, 2048, 16384, bits=8) == w4.Path.GEMM
     assert w4.choose_path(256, 16, (1 << 22) + 128, bits=8) == w4.Path.SKINNY
     assert w4.workspace_bytes(1, 2048, 100, bits=8) == 0
     assert w4.workspace_bytes(1, 2048, 16384, bits=8) > 0

@@ -218,9 +218,14 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
 }
 
 w4a16_path_t w8a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
-    (void)n;
+    // Measured on INT8 weights (MI355X): the v_dot2 GEMV up to M = 4 (even
+    // with SKINNY at M = 4 on 32768 x 2048), the mid-M kernel above, the
+    // GEMM from M = 65 on layers above 8 M weights (100 x 16384 x 2048: 31.7
+    // vs 43.9 us) and from M = 513 on smaller ones (256 x 4096 x 1024: 13.3
+    // vs 29.3 us; 1024 x 4096 x 1024: even).
     if (m <= 4) return W4A16_PATH_GEMV;
-    if (m < 128 || k > kGemmMaxLd) return W4A16_PATH_SKINNY;
+    const bool small = n * k <= (int64_t(8) << 20);
+    if (k > kGemmMaxLd || m <= 64 || (small && m <= 512)) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
 }
 
