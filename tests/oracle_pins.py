@@ -29,12 +29,23 @@ import os
 from fractions import Fraction
 
 import numpy as np
-import torch
 
 import oracle
 from tests import exact
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+class _LazyTorch:
+    """torch, imported on first use: the quantizer pins do not need it, and
+    the mutation test runs the pins in many short child processes."""
+
+    def __getattr__(self, name):
+        import torch as _t
+        return getattr(_t, name)
+
+
+torch = _LazyTorch()
 
 
 def _read_lines(name):

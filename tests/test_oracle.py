@@ -153,6 +153,8 @@ for pin in oracle_pins.ALL_PINS:
         pin(lib)
     except Exception as e:  # a pin caught the mutant (or the mutant broke)
         failed.append(pin.__name__)
+        if {stop_first!r}:
+            break
 print("FAILED:" + ",".join(failed))
 """
 
@@ -172,7 +174,7 @@ def test_pins_catch_planted_mistake(desc, old, new):
         with open(src_path, "w") as f:
             f.write(mutated)
         oracle.build(src=src_path, out=so_path, extra_flags=["-w"])
-        proc = subprocess.run([sys.executable, "-c", _RUNNER.format(root=ROOT, path=so_path)],
+        proc = subprocess.run([sys.executable, "-c", _RUNNER.format(root=ROOT, path=so_path, stop_first=True)],
                               capture_output=True, text=True, timeout=300)
     line = [ln for ln in proc.stdout.splitlines() if ln.startswith("FAILED:")]
     if proc.returncode != 0 and not line:
@@ -189,7 +191,7 @@ def test_pins_pass_under_ubsan():
     with tempfile.TemporaryDirectory() as d:
         so_path = os.path.join(d, "libubsan_oracle.so")
         oracle.build(out=so_path, extra_flags=["-fsanitize=undefined", "-fno-sanitize-recover=all", "-g"])
-        proc = subprocess.run([sys.executable, "-c", _RUNNER.format(root=ROOT, path=so_path)],
+        proc = subprocess.run([sys.executable, "-c", _RUNNER.format(root=ROOT, path=so_path, stop_first=False)],
                               capture_output=True, text=True, timeout=600)
     line = [ln for ln in proc.stdout.splitlines() if ln.startswith("FAILED:")]
     assert proc.returncode == 0 and line == ["FAILED:"], proc.stdout[-2000:] + proc.stderr[-2000:]
