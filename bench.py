@@ -531,8 +531,8 @@ def main():
         print(text)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the layer is benchmarked on one MI355X "
-              "(multi-GPU sharding is a design note, not part of this build)", file=sys.stderr)
+        print("bench.py measures one GPU only: the layer runs on one MI355X per process, and "
+              "sharding it across GPUs is described in the design notes, not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch

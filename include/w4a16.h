@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     W4A16_OK = 0,
     W4A16_EINVAL = 1,        /* bad shape, stride, pointer, alignment or overlap */
-    W4A16_EUNSUPPORTED = 2,  /* valid request this build does not implement (e.g. dtype) */
+    W4A16_EUNSUPPORTED = 2,  /* valid request the library does not implement (e.g. dtype) */
     W4A16_EWORKSPACE = 3,    /* workspace missing or smaller than required */
     W4A16_EHIP = 4           /* the HIP runtime reported an error at launch */
 } w4a16_status_t;
