@@ -305,6 +305,14 @@ w4a16_status_t pack_weights_int8(const int8_t* codes, const float* scales, int64
 w4a16_status_t unpack_weights_int8(const void* packed, int64_t n, int64_t k, int8_t* codes, float* scales,
                                    void* stream);
 
+/*
+ * A shard of an already packed INT8 [n][k] weight: the rules, arguments and
+ * status codes of shard_packed_weights, with w8a16_packed_bytes sizes; the
+ * shard equals pack_weights_int8 of the same canonical rows / columns.
+ */
+w4a16_status_t shard_packed_weights_int8(const void* packed, int64_t n, int64_t k, int dim, int64_t start,
+                                         int64_t length, void* out, void* stream);
+
 /* Workspace bytes w8a16_linear needs (0 if none; 0 for an unknown act); header rules as above. */
 size_t w8a16_linear_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k);
 

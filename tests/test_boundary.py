@@ -38,7 +38,8 @@ def test_exports_every_declared_function(lib):
             "w4a16_linear_with_path", "w4a16_linear_choose_path", "w4a16_linear_act",
             "w4a16_linear_act_workspace_bytes", "shard_packed_weights", "w4a16_update_packed",
             "quantize_rtn_int8_g128", "w8a16_packed_bytes", "pack_weights_int8", "unpack_weights_int8",
-            "w8a16_linear_workspace_bytes", "w8a16_linear", "w8a16_linear_choose_path"} <= set(names)
+            "w8a16_linear_workspace_bytes", "w8a16_linear", "w8a16_linear_choose_path",
+            "shard_packed_weights_int8"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -279,6 +280,18 @@ def test_int8_linear_rejects(lib):
     need = w4.workspace_bytes(1, 2048, 32768, bits=8)
     assert need > 0
     assert lin8(lib, m=1, k=32768, ldx=32768, n=2048, ldy=2048, y=A * 1024, path=int(w4.Path.GEMV)) == B.EWORKSPACE
+
+
+def test_int8_shard_rejects(lib):
+    sh = lib.shard_packed_weights_int8
+    assert sh(A, 100, 640, 2, 0, 10, A * 4, None) == B.EINVAL        # dim
+    assert sh(A, 100, 640, 0, 95, 10, A * 4, None) == B.EINVAL       # past n
+    assert sh(A, 100, 640, 1, 64, 128, A * 4, None) == B.EINVAL      # start not on a group
+    assert sh(A, 0, 640, 0, 0, 1, A * 4, None) == B.EINVAL           # empty weight
+    # an INT8 weight of 100 x 640 spans 7 tiles x 5 groups x 2112 bytes: an
+    # output 40 KB in overlaps it (an INT4 weight ends at 38080 bytes)
+    assert w4.packed_bytes(100, 640, bits=8) == 7 * 5 * 2112
+    assert sh(A, 100, 640, 0, 0, 10, A + 40960, None) == B.EINVAL
 
 
 def test_binding_rejects_cpu_tensors():

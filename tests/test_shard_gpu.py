@@ -121,3 +121,54 @@ def test_input_feature_shards_sum(dev):
     y_ref = oracle.linear(bits(x), tag(torch.bfloat16), q, s, bits(b))
     xnorm = np.linalg.norm(x.to(torch.float64).numpy(), axis=1)[:, None]
     check_close(y.cpu().to(torch.float64).numpy(), y_ref, xnorm, row_max_dequant(q, s)[None, :], "K shards summed")
+
+
+# --- INT8 weights --------------------------------------------------------------
+
+
+def weights8(n, k, seed):
+    rng = np.random.default_rng(seed)
+    qi = rng.integers(-127, 128, size=(n, k)).astype(np.int16)
+    qi[:, ::128] = 127 * np.where(rng.random((n, k // 128)) < 0.5, 1, -1)
+    return torch.from_numpy((qi * 2.0 ** -3).astype(np.float32))
+
+
+def padding8_ok(packed_bytes: np.ndarray, rows: int, k: int) -> bool:
+    """INT8: rows past `rows` in the last tile: both halves' lane runs 0x80.., scale 0."""
+    tiles, groups = -(-rows // 16), k // 128
+    pad = range(rows - (tiles - 1) * 16, 16)
+    codes = packed_bytes[:tiles * groups * 2048].reshape(tiles, groups, 2, 64, 16)
+    scales = packed_bytes[tiles * groups * 2048:].view(np.float32).reshape(tiles, groups, 16)
+    for r in pad:
+        lanes = [r + 16 * q for q in range(4)]
+        if not np.all(codes[tiles - 1][:, :, lanes, :] == 0x80) or not np.all(scales[tiles - 1][:, r] == 0):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("n,k,dim,start,length", CASES, ids=[f"n{a}_k{b}_d{c}_s{d}_l{e}" for a, b, c, d, e in CASES])
+def test_int8_shard_matches_oracle_slice(dev, n, k, dim, start, length):
+    lib = w4()
+    say(f"int8 shard n={n} k={k} dim={dim} start={start} length={length}")
+    w = weights8(n, k, seed=n + k + start + 1)
+    codes, scales = lib.quantize_int8(w.to(dev))
+    packed = lib.pack_int8(codes, scales)
+    part = lib.shard(packed, n, k, dim, start, length, bits=8)
+    torch.cuda.synchronize()
+    q, s = oracle.quantize_int8(w.numpy())
+    if dim == 0:
+        qs, ss, rows, cols = q[start:start + length], s[start:start + length], length, k
+    else:
+        qs, ss, rows, cols = q[:, start:start + length], s[:, start // 128:(start + length) // 128], n, length
+    assert part.numel() == lib.packed_bytes(rows, cols, bits=8)
+    c2, s2 = lib.unpack_int8(part, rows, cols)
+    assert np.array_equal(c2.cpu().numpy(), qs)
+    assert np.array_equal(s2.cpu().numpy().view(np.uint32), np.ascontiguousarray(ss).view(np.uint32))
+    assert padding8_ok(part.cpu().numpy(), rows, cols)
+    rng = np.random.default_rng(2)
+    x = torch.from_numpy(rng.integers(-4, 5, size=(3, cols)).astype(np.float32)).to(torch.bfloat16)
+    y = lib.linear(x.to(dev), part, rows, bits=8)
+    torch.cuda.synchronize()
+    want = to_rne16(oracle.linear(bits(x), tag(torch.bfloat16), np.ascontiguousarray(qs), np.ascontiguousarray(ss)),
+                    torch.bfloat16)
+    assert np.array_equal(y.cpu().to(torch.float64).numpy(), want)

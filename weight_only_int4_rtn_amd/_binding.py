@@ -87,6 +87,8 @@ def _declare(lib):
     lib.w8a16_linear.restype = i32
     lib.w8a16_linear_choose_path.argtypes = [i64, i64, i64]
     lib.w8a16_linear_choose_path.restype = i32
+    lib.shard_packed_weights_int8.argtypes = [vp, i64, i64, i32, i64, i64, vp, vp]
+    lib.shard_packed_weights_int8.restype = i32
     lib.w4a16_status_string.argtypes = [i32]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     return lib
@@ -281,15 +283,19 @@ def update_(packed: torch.Tensor, n: int, k: int, update: torch.Tensor | None = 
     return packed
 
 
-def shard(packed: torch.Tensor, n: int, k: int, dim: int, start: int, length: int) -> torch.Tensor:
+def shard(packed: torch.Tensor, n: int, k: int, dim: int, start: int, length: int, bits: int = 4) -> torch.Tensor:
     """Rows [start, start+length) (dim 0) or group-aligned columns (dim 1) of a
-    packed [n, k] weight as a new packed weight (no requantization)."""
+    packed [n, k] weight (INT4, or INT8 with bits=8) as a new packed weight
+    (no requantization)."""
     _require_cuda(packed)
+    bits = _bits(bits)
     rows, cols = (length, k) if dim == 0 else (n, length)
-    out = torch.empty(max(packed_bytes(rows, cols), 16), dtype=torch.uint8, device=packed.device)
-    st = lib().shard_packed_weights(_ptr(packed), n, k, dim, start, length, _ptr(out), _stream(packed.device))
-    _check(st, "shard_packed_weights")
-    return out[:packed_bytes(rows, cols)]
+    size = packed_bytes(rows, cols, bits)
+    out = torch.empty(max(size, 16), dtype=torch.uint8, device=packed.device)
+    fn = lib().shard_packed_weights_int8 if bits == 8 else lib().shard_packed_weights
+    st = fn(_ptr(packed), n, k, dim, start, length, _ptr(out), _stream(packed.device))
+    _check(st, "shard_packed_weights_int8" if bits == 8 else "shard_packed_weights")
+    return out[:size]
 
 
 _workspaces: dict = {}

@@ -184,18 +184,39 @@ w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const voi
                                   static_cast<hipStream_t>(stream)));
 }
 
-w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, int dim, int64_t start,
-                                    int64_t length, void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+w4a16_status_t shard_impl(int bits, const void* packed, int64_t n, int64_t k, int dim, int64_t start,
+                          int64_t length, void* out, void* stream) {
     // a shard is a nonempty contiguous interval; input-feature shards hold
     // whole quantization groups
     if (!valid_nk(n, k) || n == 0 || (dim != 0 && dim != 1) || start < 0 || length <= 0) return W4A16_EINVAL;
     if (dim == 0 && start + length > n) return W4A16_EINVAL;
     if (dim == 1 && (start % kGroup != 0 || length % kGroup != 0 || start + length > k)) return W4A16_EINVAL;
     if (!packed || !out || !aligned(packed, 16) || !aligned(out, 16)) return W4A16_EINVAL;
-    const size_t in_bytes = w4a16_packed_bytes(n, k);
-    const size_t out_bytes = dim == 0 ? w4a16_packed_bytes(length, k) : w4a16_packed_bytes(n, length);
+    auto bytes = [bits](int64_t rows, int64_t cols) {
+        return bits == 8 ? w8a16_packed_bytes(rows, cols) : w4a16_packed_bytes(rows, cols);
+    };
+    const size_t in_bytes = bytes(n, k);
+    const size_t out_bytes = dim == 0 ? bytes(length, k) : bytes(n, length);
     if (overlap(packed, in_bytes, out, out_bytes)) return W4A16_EINVAL;
-    return from_hip(launch_shard(packed, n, k, dim, start, length, out, static_cast<hipStream_t>(stream)));
+    return from_hip(launch_shard(packed, n, k, dim, start, length, out, bits, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, int dim, int64_t start,
+                                    int64_t length, void* out, void* stream) {
+    return shard_impl(4, packed, n, k, dim, start, length, out, stream);
+}
+
+w4a16_status_t shard_packed_weights_int8(const void* packed, int64_t n, int64_t k, int dim, int64_t start,
+                                         int64_t length, void* out, void* stream) {
+    return shard_impl(8, packed, n, k, dim, start, length, out, stream);
 }
 
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {

@@ -69,9 +69,9 @@ hipError_t launch_update(void* packed, int64_t n, int64_t k, const void* upd, in
                          const void* mat2, int64_t rank, int dtype, float alpha, float beta, int stochastic,
                          uint64_t seed, hipStream_t stream);
 // Rows [start, start + len) (dim 0) or group-aligned columns (dim 1) of a
-// packed [n][k] weight into a new packed weight.
+// packed [n][k] weight (bits 4 or 8) into a new packed weight.
 hipError_t launch_shard(const void* packed, int64_t n, int64_t k, int dim, int64_t start, int64_t len,
-                        void* out, hipStream_t stream);
+                        void* out, int bits, hipStream_t stream);
 
 // y[m][n] = round(sum over splits of partials[s][m][npad] + bias): finishes K-split launches.
 hipError_t launch_splitk_reduce(const float* partials, int splits, int64_t m, int64_t n, int64_t npad,

@@ -309,11 +309,16 @@ hipError_t launch_unpack8(const void* packed, int64_t n, int64_t k, int8_t* code
 //   dim 1: output groups are source groups start/128 + g': whole chunks and
 //          their scale blocks are copied.
 // ---------------------------------------------------------------------------
+// BITS 8: INT8 chunks, whose lane runs sit in two 1 KB halves (each moved
+// alike); padding rows get code 0 as u = 0x80.
+template <int BITS>
 __global__ __launch_bounds__(256) void shard_kernel(const uint8_t* __restrict__ src, int64_t n, int64_t k,
                                                     int dim, int64_t start, int64_t len,
                                                     uint8_t* __restrict__ dst) {
-    const Layout S(n, k);
-    const Layout D(dim == 0 ? len : n, dim == 0 ? k : len);
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
+    constexpr uint32_t kZero = BITS == 8 ? 0x80808080u : 0x88888888u;
+    const Layout S(n, k, BITS);
+    const Layout D(dim == 0 ? len : n, dim == 0 ? k : len, BITS);
     const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (tid >= D.chunks() * 64) return;
     const int64_t chunk = tid >> 6;
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(256) void shard_kernel(const uint8_t* __restrict__ 
     const int r = lane & 15, kq = lane >> 4;
     const float* ss = reinterpret_cast<const float*>(src + S.scale_offset());
     float* ds = reinterpret_cast<float*>(dst + D.scale_offset());
-    uint4 v;
+    uint4 v[H];
     float sc;
     if (dim == 0) {
         const int64_t orow = t * kTileRows + r;
@@ -330,27 +335,37 @@ __global__ __launch_bounds__(256) void shard_kernel(const uint8_t* __restrict__ 
             const int64_t srow = start + orow;
             const int64_t schunk = (srow / kTileRows) * S.groups + g;
             const int slane = int(srow % kTileRows) + 16 * kq;
-            v = *reinterpret_cast<const uint4*>(src + schunk * kChunkBytes + slane * 16);
+#pragma unroll
+            for (int h = 0; h < H; ++h)
+                v[h] = *reinterpret_cast<const uint4*>(src + schunk * CB + h * kChunkBytes + slane * 16);
             sc = ss[schunk * kTileRows + srow % kTileRows];
         } else {
-            v = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+#pragma unroll
+            for (int h = 0; h < H; ++h) v[h] = make_uint4(kZero, kZero, kZero, kZero);
             sc = 0.0f;
         }
     } else {
         const int64_t schunk = t * S.groups + start / kGroup + g;
-        v = *reinterpret_cast<const uint4*>(src + schunk * kChunkBytes + lane * 16);
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+            v[h] = *reinterpret_cast<const uint4*>(src + schunk * CB + h * kChunkBytes + lane * 16);
         sc = ss[schunk * kTileRows + r];
     }
-    *reinterpret_cast<uint4*>(dst + chunk * kChunkBytes + lane * 16) = v;
+#pragma unroll
+    for (int h = 0; h < H; ++h) *reinterpret_cast<uint4*>(dst + chunk * CB + h * kChunkBytes + lane * 16) = v[h];
     if (kq == 0) ds[chunk * kTileRows + r] = sc;
 }
 
 hipError_t launch_shard(const void* packed, int64_t n, int64_t k, int dim, int64_t start, int64_t len,
-                        void* out, hipStream_t stream) {
-    const Layout D(dim == 0 ? len : n, dim == 0 ? k : len);
+                        void* out, int bits, hipStream_t stream) {
+    const Layout D(dim == 0 ? len : n, dim == 0 ? k : len, bits);
     const int64_t blocks = ceil_div(D.chunks() * 64, 256);
-    shard_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(static_cast<const uint8_t*>(packed), n, k, dim, start,
-                                                         len, static_cast<uint8_t*>(out));
+    const uint8_t* src = static_cast<const uint8_t*>(packed);
+    uint8_t* dst = static_cast<uint8_t*>(out);
+    if (bits == 8)
+        shard_kernel<8><<<dim3(blocks), dim3(256), 0, stream>>>(src, n, k, dim, start, len, dst);
+    else
+        shard_kernel<4><<<dim3(blocks), dim3(256), 0, stream>>>(src, n, k, dim, start, len, dst);
     return hipGetLastError();
 }
 
