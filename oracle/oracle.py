@@ -67,7 +67,7 @@ def _declare(lib):
     lib.oracle_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
     lib.oracle_uniform.restype = ctypes.c_float
     lib.oracle_update.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, i32, ctypes.c_float, ctypes.c_float,
-                                  i32, ctypes.c_uint64]
+                                  i32, ctypes.c_uint64, i32]
     lib.oracle_update.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
@@ -233,10 +233,11 @@ def _upd_array(a: np.ndarray, tag):
 
 
 def update(q: np.ndarray, s: np.ndarray, upd=None, mat1=None, mat2=None, alpha=1.0, beta=1.0,
-           seed=None, dtype_tag=None, lib=None):
+           seed=None, dtype_tag=None, lib=None, bits=4):
     """Requantized codes and scales of beta * dequant(q, s) + alpha * U, U a
     dense [n, k] update or mat1 [n, r] @ mat2 [r, k] (float32, or uint16 bits
-    with a dtype tag); stochastic rounding when ``seed`` is given.
+    with a dtype tag); stochastic rounding when ``seed`` is given; ``bits``
+    4 (INT4 codes, amax/7) or 8 (INT8 codes, amax/127).
     Returns new (q, s); the inputs are not modified."""
     lib = lib or load()
     q = np.array(q, dtype=np.int8, order="C", copy=True)
@@ -250,7 +251,7 @@ def update(q: np.ndarray, s: np.ndarray, upd=None, mat1=None, mat2=None, alpha=1
         b, _ = _upd_array(mat2, dtype_tag)
         args = (None, 0, _p(a), _p(b), a.shape[1], tag)
     rc = lib.oracle_update(_p(q), _p(s), n, k, *args, float(alpha), float(beta), int(seed is not None),
-                           int(seed or 0))
+                           int(seed or 0), int(bits))
     if rc != 0:
         raise ValueError("oracle_update rejected its arguments")
     return q, s

@@ -69,7 +69,9 @@
  *   element e of the weight (row-major offset n * K + k) draws the (e+1)-th
  *   output of SplitMix64 seeded with the 64-bit seed; its top 24 bits give a
  *   uniform u in [0, 1) (u = bits * 2^-24), and the code rounds up exactly
- *   when u < v - floor(v), v = fl32(w' / s').
+ *   when u < v - floor(v), v = fl32(w' / s').  The same update applies to
+ *   INT8 weights with the INT8 quantizer and code range (bits = 8), as the
+ *   pages describe it for their 8-bit codes.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared
  * The quantizer relies on IEEE binary32 division and on nearbyintf under the
@@ -433,10 +435,15 @@ static float update_value(const void *u, int u_dtype, int64_t idx)
  */
 int oracle_update(int8_t *q, float *s, int64_t n, int64_t k, const void *upd, int64_t ldu,
                   const void *mat1, const void *mat2, int64_t rank, int u_dtype,
-                  float alpha, float beta, int has_seed, uint64_t seed)
+                  float alpha, float beta, int has_seed, uint64_t seed, int bits)
 {
     if (k <= 0 || k % ORACLE_GROUP != 0 || n < 0 || rank < 0)
         return -1;
+    if (bits != 4 && bits != 8)
+        return -1;
+    /* the code range of the weight's format: [-8, 7] or [-128, 127] */
+    const int qmax = bits == 8 ? 127 : 7;
+    const int qmin = -qmax - 1;
     if (u_dtype != ORACLE_F32 && u_dtype != ORACLE_BF16 && u_dtype != ORACLE_F16)
         return -1;
     if (rank == 0 && (!upd || ldu < k))
@@ -471,7 +478,7 @@ int oracle_update(int8_t *q, float *s, int64_t n, int64_t k, const void *upd, in
             for (int j = 0; j < ORACLE_GROUP; ++j)
                 if (fabsf(w[j]) > amax)
                     amax = fabsf(w[j]);
-            const float scale = amax / 7.0f;
+            const float scale = amax / (float)qmax;
             s[row * groups + g] = scale;
             for (int64_t j = 0; j < ORACLE_GROUP; ++j) {
                 const int64_t kk = g * ORACLE_GROUP + j;
@@ -479,17 +486,17 @@ int oracle_update(int8_t *q, float *s, int64_t n, int64_t k, const void *upd, in
                 if (scale != 0.0f) {
                     const float v = w[j] / scale;
                     const float lo = floorf(v);
-                    if (has_seed && lo >= -8.0f && lo + 1.0f <= 7.0f) {
+                    if (has_seed && lo >= (float)qmin && lo + 1.0f <= (float)qmax) {
                         /* interior: one of the two adjacent codes */
                         const float frac = v - lo;
                         const float u = oracle_uniform(seed, (uint64_t)(row * k + kk));
                         code = (int)lo + (u < frac ? 1 : 0);
                     } else {
                         float r = nearbyintf(v);
-                        if (r < -8.0f)
-                            r = -8.0f;
-                        if (r > 7.0f)
-                            r = 7.0f;
+                        if (r < (float)qmin)
+                            r = (float)qmin;
+                        if (r > (float)qmax)
+                            r = (float)qmax;
                         code = (int)r;
                     }
                 }

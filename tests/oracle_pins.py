@@ -459,26 +459,33 @@ def _exact_update(q, s, upd=None, m1=None, m2=None, alpha=1.0, beta=1.0):
     return out
 
 
-def pin_update_matches_exact_steps(lib, seed=31):
+def _quantizer(bits):
+    return oracle.quantize_int8 if bits == 8 else oracle.quantize
+
+
+def pin_update_matches_exact_steps(lib, seed=31, bits=4):
     """Round-to-nearest updates (dense and low-rank, several alpha/beta) equal
     the quantizer applied to the exactly emulated FP32 steps."""
     rng = np.random.default_rng(seed)
     n, k = 4, 256
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
-    q, s = oracle.quantize(w, lib=lib)
+    quant = _quantizer(bits)
+    q, s = quant(w, lib=lib)
     upd = (rng.standard_normal((n, k)) * 0.01).astype(np.float32)
     m1 = (rng.standard_normal((n, 3)) * 0.1).astype(np.float32)
     m2 = (rng.standard_normal((3, k)) * 0.1).astype(np.float32)
     for kind in ("dense", "lowrank"):
         for alpha, beta in ((1.0, 1.0), (0.375, 1.0), (-2.0, 0.5)):
             if kind == "dense":
-                got = oracle.update(q, s, upd=upd, alpha=alpha, beta=beta, lib=lib)
+                got = oracle.update(q, s, upd=upd, alpha=alpha, beta=beta, lib=lib, bits=bits)
                 wn = _exact_update(q, s, upd=upd, alpha=alpha, beta=beta)
             else:
-                got = oracle.update(q, s, mat1=m1, mat2=m2, alpha=alpha, beta=beta, lib=lib)
+                got = oracle.update(q, s, mat1=m1, mat2=m2, alpha=alpha, beta=beta, lib=lib, bits=bits)
                 wn = _exact_update(q, s, m1=m1, m2=m2, alpha=alpha, beta=beta)
-            want = oracle.quantize(wn, lib=lib)
+            want = quant(wn, lib=lib)
             assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), (kind, alpha, beta)
+    if bits == 8:
+        return
     # a dense update with a row stride wider than the row (the C entry point)
     wide = np.zeros((n, k + 8), dtype=np.float32)
     wide[:, :k] = upd
@@ -486,7 +493,7 @@ def pin_update_matches_exact_steps(lib, seed=31):
     q2, s2 = q.copy(), s.copy()
     rc = lib.oracle_update(q2.ctypes.data_as(ctypes.c_void_p), s2.ctypes.data_as(ctypes.c_void_p), n, k,
                            wide.ctypes.data_as(ctypes.c_void_p), k + 8, None, None, 0, oracle.F32,
-                           ctypes.c_float(1.0), ctypes.c_float(1.0), 0, 0)
+                           ctypes.c_float(1.0), ctypes.c_float(1.0), 0, 0, 4)
     assert rc == 0
     want = oracle.update(q, s, upd=upd, lib=lib)
     assert np.array_equal(q2, want[0]) and np.array_equal(s2, want[1])
@@ -523,7 +530,19 @@ def pin_update_identities(lib, seed=32):
         assert np.array_equal(q4, q) and np.array_equal(s4, 2 * s)
 
 
-def pin_stochastic_rounding(lib, seed=33):
+def pin_update_int8_matches_exact_steps(lib):
+    """The INT8 update: the pinned INT8 quantizer on the exactly emulated FP32
+    steps (dense and low-rank, several alpha/beta)."""
+    pin_update_matches_exact_steps(lib, seed=41, bits=8)
+
+
+def pin_stochastic_rounding_int8(lib):
+    """Stochastic INT8 codes: adjacency, draw offsets, reproducibility,
+    unbiasedness and the crafted cases, with the INT8 code range."""
+    pin_stochastic_rounding(lib, seed=43, bits=8)
+
+
+def pin_stochastic_rounding(lib, seed=33, bits=4):
     """Stochastic codes: each is floor(v) or floor(v) + 1 of the exactly
     emulated quotient v (codes outside the interior keep the nearest code),
     element (i, j) rounds up exactly when draw i*K + j of the seed falls below
@@ -531,26 +550,28 @@ def pin_stochastic_rounding(lib, seed=33):
     code approaches v (unbiased)."""
     rng = np.random.default_rng(seed)
     n, k = 3, 256
+    quant = _quantizer(bits)
+    qmax = 127 if bits == 8 else 7
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
-    q, s = oracle.quantize(w, lib=lib)
-    upd = (rng.standard_normal((n, k)) * 0.005).astype(np.float32)
+    q, s = quant(w, lib=lib)
+    upd = (rng.standard_normal((n, k)) * (0.005 if bits == 4 else 0.0005)).astype(np.float32)
     wn = _exact_update(q, s, upd=upd)
-    qn, sn = oracle.quantize(wn, lib=lib)
+    qn, sn = quant(wn, lib=lib)
     v = np.empty((n, k))
     for i in range(n):
         for j in range(k):
             v[i, j] = exact.round_to_f32(Fraction(float(wn[i, j])) / Fraction(float(sn[i, j // 128])))
     lo = np.floor(v)
-    interior = (lo >= -8) & (lo + 1 <= 7)
+    interior = (lo >= -qmax - 1) & (lo + 1 <= qmax)
     trials = []
     for sd in range(300):
-        q2, s2 = oracle.update(q, s, upd=upd, seed=sd, lib=lib)
+        q2, s2 = oracle.update(q, s, upd=upd, seed=sd, lib=lib, bits=bits)
         assert np.array_equal(s2, sn)  # the deterministic scales
         assert np.all(((q2 == lo) | (q2 == lo + 1))[interior])
         assert np.array_equal(q2[~interior], qn[~interior])
         trials.append(q2.astype(np.float64))
-    q_a, _ = oracle.update(q, s, upd=upd, seed=12345, lib=lib)
-    q_b, _ = oracle.update(q, s, upd=upd, seed=12345, lib=lib)
+    q_a, _ = oracle.update(q, s, upd=upd, seed=12345, lib=lib, bits=bits)
+    q_b, _ = oracle.update(q, s, upd=upd, seed=12345, lib=lib, bits=bits)
     assert np.array_equal(q_a, q_b)
     for i in range(n):
         for j in range(k):
@@ -558,22 +579,24 @@ def pin_stochastic_rounding(lib, seed=33):
                 up = lib.oracle_uniform(12345, i * k + j) < v[i, j] - lo[i, j]
                 assert q_a[i, j] == lo[i, j] + up, (i, j)
     # a quotient equal to its own draw does not round up (u < frac is strict):
-    # from an all-zero weight, the dense update itself is w'; 7 fixes s' = 1
+    # from an all-zero weight, the dense update itself is w'; qmax fixes s' = 1
     u0 = lib.oracle_uniform(77, 0)
     z = np.zeros((1, 128), dtype=np.float32)
     craft = np.zeros((1, 128), dtype=np.float32)
-    craft[0, 0], craft[0, 1] = u0, 7.0
-    qc, sc = oracle.update(z.astype(np.int8), np.zeros((1, 1), np.float32), upd=craft, seed=77, lib=lib)
-    assert sc[0, 0] == 1.0 and qc[0, 0] == 0 and qc[0, 1] == 7, (qc[0, :2], sc)
+    craft[0, 0], craft[0, 1] = u0, float(qmax)
+    qc, sc = oracle.update(z.astype(np.int8), np.zeros((1, 1), np.float32), upd=craft, seed=77, lib=lib, bits=bits)
+    assert sc[0, 0] == 1.0 and qc[0, 0] == 0 and qc[0, 1] == qmax, (qc[0, :2], sc)
     # outside the interior the nearest code stands: a = 1.0000007 gives
     # s' = fl32(a/7) = 0.14285724 and v = 7.0000005 (floor 7, no code 8);
-    # seed 1127518 draws 2 * 2^-24 first, below v - 7, so a rounding that
-    # ignored the code range would produce 8 here
+    # for INT8, a = 2.7708886 gives s' = fl32(a/127) and v = 127.00001
+    # (floor 127, no code 128); seed 1127518 draws 2 * 2^-24 first, below
+    # v - qmax, so a rounding that ignored the code range would step past it
     craft = np.zeros((1, 128), dtype=np.float32)
-    craft[0, 0] = np.float32(1.0000007)
-    qc, sc = oracle.update(z.astype(np.int8), np.zeros((1, 1), np.float32), upd=craft, seed=1127518, lib=lib)
+    craft[0, 0] = np.float32(2.7708886 if bits == 8 else 1.0000007)
+    qc, sc = oracle.update(z.astype(np.int8), np.zeros((1, 1), np.float32), upd=craft, seed=1127518, lib=lib,
+                           bits=bits)
     assert lib.oracle_uniform(1127518, 0) == 2 * 2.0 ** -24
-    assert np.float32(craft[0, 0]) / sc[0, 0] > np.float32(7.0) and qc[0, 0] == 7, (qc[0, 0], sc[0, 0])
+    assert np.float32(craft[0, 0]) / sc[0, 0] > np.float32(qmax) and qc[0, 0] == qmax, (qc[0, 0], sc[0, 0])
     mean = np.mean(trials, axis=0)
     frac = v - lo
     sd_err = np.sqrt(frac * (1 - frac) / len(trials)) + 1e-6
@@ -603,4 +626,6 @@ ALL_PINS = [
     pin_update_matches_exact_steps,
     pin_update_identities,
     pin_stochastic_rounding,
+    pin_update_int8_matches_exact_steps,
+    pin_stochastic_rounding_int8,
 ]

@@ -123,7 +123,11 @@ MUTANTS = [
      "for (int64_t r = rank - 1; r >= 0; --r)\n                        p = fmaf("),
     ("dense update row stride ignored", "p = update_value(upd, u_dtype, row * ldu + kk);",
      "p = update_value(upd, u_dtype, row * k + kk);"),
-    ("stochastic outside the interior", "if (has_seed && lo >= -8.0f && lo + 1.0f <= 7.0f) {", "if (has_seed) {"),
+    ("stochastic outside the interior", "if (has_seed && lo >= (float)qmin && lo + 1.0f <= (float)qmax) {",
+     "if (has_seed) {"),
+    ("stochastic up to the top code", "lo + 1.0f <= (float)qmax) {", "lo <= (float)qmax) {"),
+    ("update int8 range taken as int4", "const int qmax = bits == 8 ? 127 : 7;", "const int qmax = 7;"),
+    ("update int8 divisor 128", "const int qmax = bits == 8 ? 127 : 7;", "const int qmax = bits == 8 ? 128 : 7;"),
     ("int8 divisor 128", "onto code 127 */\n            float scale8 = amax / 127.0f;",
      "onto code 127 */\n            float scale8 = amax / 128.0f;"),
     ("int8 divisor 255", "onto code 127 */\n            float scale8 = amax / 127.0f;",
@@ -137,8 +141,8 @@ MUTANTS = [
     ("int8 absmax over the first group", "float mag = fabsf(weight_as_float(w, w_dtype, row * ldw + g * ORACLE_GROUP + j));",
      "float mag = fabsf(weight_as_float(w, w_dtype, row * ldw + j));"),
     ("int8 codes written to the group start", "q[row * k + kk] = (int8_t)code8;", "q[row * k + g * ORACLE_GROUP] = (int8_t)code8;"),
-    ("update scale divisor 8", "const float scale = amax / 7.0f;\n            s[row * groups + g] = scale;",
-     "const float scale = amax / 8.0f;\n            s[row * groups + g] = scale;"),
+    ("update scale divisor qmax + 1", "const float scale = amax / (float)qmax;",
+     "const float scale = amax / (float)(qmax + 1);"),
 ]
 
 _RUNNER = r"""
