@@ -313,6 +313,18 @@ w4a16_status_t unpack_weights_int8(const void* packed, int64_t n, int64_t k, int
 w4a16_status_t shard_packed_weights_int8(const void* packed, int64_t n, int64_t k, int dim, int64_t start,
                                          int64_t length, void* out, void* stream);
 
+/*
+ * In-place update of a packed INT8 [n][k] weight (from pack_weights_int8):
+ * the arithmetic, arguments and status codes of w4a16_update_packed, with
+ * the INT8 quantizer (scale amax / 127, codes [-128, 127]) and, with a seed,
+ * stochastic rounding where -128 <= floor(v) <= 126 ("Piper Kernels",
+ * section "ConvRot INT8": one of the two adjacent INT8 codes).
+ */
+w4a16_status_t w8a16_update_packed(void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
+                                   const void* mat1, const void* mat2, int64_t rank,
+                                   w4a16_dtype_t update_dtype, float alpha, float beta,
+                                   const uint64_t* rounding_seed, void* stream);
+
 /* Workspace bytes w8a16_linear needs (0 if none; 0 for an unknown act); header rules as above. */
 size_t w8a16_linear_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k);
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
             "w4a16_linear_act_workspace_bytes", "shard_packed_weights", "w4a16_update_packed",
             "quantize_rtn_int8_g128", "w8a16_packed_bytes", "pack_weights_int8", "unpack_weights_int8",
             "w8a16_linear_workspace_bytes", "w8a16_linear", "w8a16_linear_choose_path",
-            "shard_packed_weights_int8"} <= set(names)
+            "shard_packed_weights_int8", "w8a16_update_packed"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -280,6 +280,18 @@ def test_int8_linear_rejects(lib):
     need = w4.workspace_bytes(1, 2048, 32768, bits=8)
     assert need > 0
     assert lin8(lib, m=1, k=32768, ldx=32768, n=2048, ldy=2048, y=A * 1024, path=int(w4.Path.GEMV)) == B.EWORKSPACE
+
+
+def test_int8_update_rejects(lib):
+    import ctypes
+    up = lib.w8a16_update_packed
+    f1 = ctypes.c_float(1.0)
+    assert up(A, 16, 128, A * 4, 128, None, None, 0, 7, f1, f1, None, None) == B.EUNSUPPORTED   # dtype
+    assert up(A, 16, 128, None, 0, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL        # no update
+    assert up(A, 16, 128, A * 4, 120, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL     # ldu < k
+    # the update inside the INT8 packed weight (2112 bytes; an INT4 one ends at 1088)
+    assert up(A, 16, 128, A + 1536, 128, None, None, 0, B.F32, f1, f1, None, None) == B.EINVAL
+    assert up(A, 0, 128, A * 4, 128, None, None, 0, B.F32, f1, f1, None, None) == B.OK          # empty: no-op
 
 
 def test_int8_shard_rejects(lib):

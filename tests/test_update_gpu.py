@@ -111,3 +111,51 @@ def test_strided_update_and_repeatability(dev):
     q, s = oracle.quantize(w.numpy())
     q2, s2 = oracle.update(q, s, upd=np.ascontiguousarray(u.numpy()[:, :k]), seed=31337)
     check(lib, p1, n, k, q2, s2, "strided")
+
+
+# --- INT8 weights --------------------------------------------------------------
+
+
+def check8(lib, packed, n, k, q_want, s_want, what):
+    codes, scales = lib.unpack_int8(packed, n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), q_want), f"{what}: codes differ"
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), s_want.view(np.uint32)), f"{what}: scales differ"
+
+
+@pytest.mark.parametrize("seed", [None, 2024, (1 << 64) - 3], ids=["nearest", "seed2024", "seedbig"])
+@pytest.mark.parametrize("n,k,dt,alpha,beta", DENSE, ids=[f"n{a}_k{b}_{str(c)[6:]}_a{d}_b{e}" for a, b, c, d, e in DENSE])
+def test_int8_dense_update(dev, n, k, dt, alpha, beta, seed):
+    lib = w4()
+    say(f"int8 dense update n={n} k={k} dtype={dt} alpha={alpha} beta={beta} seed={seed}")
+    g = torch.Generator().manual_seed(n + k + 1)
+    w = torch.randn(n, k, generator=g) * 0.02
+    u = (torch.randn(n, k, generator=g) * 0.001).to(dt)
+    codes, scales = lib.quantize_int8(w.to(dev))
+    packed = lib.pack_int8(codes, scales)
+    lib.update_(packed, n, k, update=u.to(dev), alpha=alpha, beta=beta, seed=seed, bits=8)
+    q, s = oracle.quantize_int8(w.numpy())
+    ua, tag = oracle_arrays(u)
+    q2, s2 = oracle.update(q, s, upd=ua, alpha=alpha, beta=beta, seed=seed, dtype_tag=tag, bits=8)
+    check8(lib, packed, n, k, q2, s2, f"int8 dense n={n} seed={seed}")
+    if seed is not None:
+        assert not np.array_equal(q2, oracle.update(q, s, upd=ua, alpha=alpha, beta=beta, dtype_tag=tag, bits=8)[0])
+
+
+@pytest.mark.parametrize("seed", [None, 99], ids=["nearest", "seed99"])
+@pytest.mark.parametrize("n,k,rank,dt", LOWRANK, ids=[f"n{a}_k{b}_r{c}_{str(d)[6:]}" for a, b, c, d in LOWRANK])
+def test_int8_lowrank_update(dev, n, k, rank, dt, seed):
+    lib = w4()
+    say(f"int8 low-rank update n={n} k={k} rank={rank} dtype={dt} seed={seed}")
+    g = torch.Generator().manual_seed(n * 3 + k + rank + 1)
+    w = torch.randn(n, k, generator=g) * 0.02
+    m1 = (torch.randn(n, rank, generator=g) * 0.02).to(dt)
+    m2 = (torch.randn(rank, k, generator=g) * 0.02).to(dt)
+    codes, scales = lib.quantize_int8(w.to(dev))
+    packed = lib.pack_int8(codes, scales)
+    lib.update_(packed, n, k, mat1=m1.to(dev), mat2=m2.to(dev), alpha=0.8, beta=1.0, seed=seed, bits=8)
+    q, s = oracle.quantize_int8(w.numpy())
+    a1, tag = oracle_arrays(m1)
+    a2, _ = oracle_arrays(m2)
+    q2, s2 = oracle.update(q, s, mat1=a1, mat2=a2, alpha=0.8, beta=1.0, seed=seed, dtype_tag=tag, bits=8)
+    check8(lib, packed, n, k, q2, s2, f"int8 low-rank n={n} rank={rank} seed={seed}")

@@ -87,6 +87,9 @@ def _declare(lib):
     lib.w8a16_linear.restype = i32
     lib.w8a16_linear_choose_path.argtypes = [i64, i64, i64]
     lib.w8a16_linear_choose_path.restype = i32
+    lib.w8a16_update_packed.argtypes = [vp, i64, i64, vp, i64, vp, vp, i64, i32, ctypes.c_float, ctypes.c_float,
+                                        ctypes.POINTER(ctypes.c_uint64), vp]
+    lib.w8a16_update_packed.restype = i32
     lib.shard_packed_weights_int8.argtypes = [vp, i64, i64, i32, i64, i64, vp, vp]
     lib.shard_packed_weights_int8.restype = i32
     lib.w4a16_status_string.argtypes = [i32]
@@ -255,10 +258,12 @@ def unpack_int8(packed: torch.Tensor, n: int, k: int):
 
 def update_(packed: torch.Tensor, n: int, k: int, update: torch.Tensor | None = None,
             mat1: torch.Tensor | None = None, mat2: torch.Tensor | None = None,
-            alpha: float = 1.0, beta: float = 1.0, seed: int | None = None) -> torch.Tensor:
+            alpha: float = 1.0, beta: float = 1.0, seed: int | None = None, bits: int = 4) -> torch.Tensor:
     """In place: packed <- requantize(beta * dequant(packed) + alpha * U), U the
     dense ``update`` [n, k] or ``mat1`` [n, r] @ ``mat2`` [r, k]; stochastic
-    rounding when ``seed`` (unsigned 64-bit) is given."""
+    rounding when ``seed`` (unsigned 64-bit) is given; ``bits=8`` for a
+    packed INT8 weight."""
+    bits = _bits(bits)
     _require_cuda(packed, update, mat1, mat2)
     src = update if update is not None else mat1
     dt = _w_tag(src.dtype)
@@ -277,9 +282,10 @@ def update_(packed: torch.Tensor, n: int, k: int, update: torch.Tensor | None = 
     sp = None
     if seed is not None:
         sp = ctypes.pointer(ctypes.c_uint64(int(seed) & ((1 << 64) - 1)))
-    st = lib().w4a16_update_packed(_ptr(packed), n, k, _ptr(update), ldu, _ptr(mat1), _ptr(mat2), rank, dt,
-                                   float(alpha), float(beta), sp, _stream(packed.device))
-    _check(st, "w4a16_update_packed")
+    fn = lib().w8a16_update_packed if bits == 8 else lib().w4a16_update_packed
+    st = fn(_ptr(packed), n, k, _ptr(update), ldu, _ptr(mat1), _ptr(mat2), rank, dt,
+            float(alpha), float(beta), sp, _stream(packed.device))
+    _check(st, "w8a16_update_packed" if bits == 8 else "w4a16_update_packed")
     return packed
 
 

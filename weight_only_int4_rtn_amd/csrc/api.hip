@@ -157,9 +157,13 @@ w4a16_status_t unpack_weights_int8(const void* packed, int64_t n, int64_t k, int
     return from_hip(launch_unpack8(packed, n, k, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
-w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
-                                   const void* mat1, const void* mat2, int64_t rank, w4a16_dtype_t update_dtype,
-                                   float alpha, float beta, const uint64_t* rounding_seed, void* stream) {
+}  // extern "C"
+
+namespace {
+
+w4a16_status_t update_impl(int bits, void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
+                           const void* mat1, const void* mat2, int64_t rank, w4a16_dtype_t update_dtype,
+                           float alpha, float beta, const uint64_t* rounding_seed, void* stream) {
     if (update_dtype != W4A16_F32 && update_dtype != W4A16_BF16 && update_dtype != W4A16_F16)
         return W4A16_EUNSUPPORTED;
     if (!valid_nk(n, k) || rank < 0 || rank > kMaxRank) return W4A16_EINVAL;
@@ -168,7 +172,7 @@ w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const voi
     if (n == 0) return W4A16_OK;
     if (!packed || !aligned(packed, 16)) return W4A16_EINVAL;
     const size_t elem = update_dtype == W4A16_F32 ? 4 : 2;
-    const size_t pbytes = w4a16_packed_bytes(n, k);
+    const size_t pbytes = bits == 8 ? w8a16_packed_bytes(n, k) : w4a16_packed_bytes(n, k);
     if (dense) {
         if (ldu < k || ldu > kMaxDim || !aligned(update, 16) || (size_t(ldu) * elem) % 16 != 0) return W4A16_EINVAL;
         if (overlap(packed, pbytes, update, span_bytes(n, k, ldu, elem))) return W4A16_EINVAL;
@@ -180,8 +184,26 @@ w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const voi
     }
     const int dt = update_dtype == W4A16_F32 ? 0 : update_dtype == W4A16_BF16 ? kActBf16 : kActF16;
     return from_hip(launch_update(packed, n, k, update, ldu, mat1, mat2, rank, dt, alpha, beta,
-                                  rounding_seed != nullptr, rounding_seed ? *rounding_seed : 0,
+                                  rounding_seed != nullptr, rounding_seed ? *rounding_seed : 0, bits,
                                   static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status_t w4a16_update_packed(void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
+                                   const void* mat1, const void* mat2, int64_t rank, w4a16_dtype_t update_dtype,
+                                   float alpha, float beta, const uint64_t* rounding_seed, void* stream) {
+    return update_impl(4, packed, n, k, update, ldu, mat1, mat2, rank, update_dtype, alpha, beta, rounding_seed,
+                       stream);
+}
+
+w4a16_status_t w8a16_update_packed(void* packed, int64_t n, int64_t k, const void* update, int64_t ldu,
+                                   const void* mat1, const void* mat2, int64_t rank, w4a16_dtype_t update_dtype,
+                                   float alpha, float beta, const uint64_t* rounding_seed, void* stream) {
+    return update_impl(8, packed, n, k, update, ldu, mat1, mat2, rank, update_dtype, alpha, beta, rounding_seed,
+                       stream);
 }
 
 }  // extern "C"

@@ -67,7 +67,7 @@ hipError_t launch_unpack8(const void* packed, int64_t n, int64_t k, int8_t* code
 // 0 (FP32), kActBf16 or kActF16; stochastic rounding with `seed` when set.
 hipError_t launch_update(void* packed, int64_t n, int64_t k, const void* upd, int64_t ldu, const void* mat1,
                          const void* mat2, int64_t rank, int dtype, float alpha, float beta, int stochastic,
-                         uint64_t seed, hipStream_t stream);
+                         uint64_t seed, int bits, hipStream_t stream);
 // Rows [start, start + len) (dim 0) or group-aligned columns (dim 1) of a
 // packed [n][k] weight (bits 4 or 8) into a new packed weight.
 hipError_t launch_shard(const void* packed, int64_t n, int64_t k, int dim, int64_t start, int64_t len,

@@ -16,7 +16,9 @@
 // and Flood, OOPSLA 2014) seeded with the 64-bit seed.
 //
 // One thread per (chunk, lane) of the packed layout: the lane's 32 weights
-// (16 bytes) of one row and group quarter.  The four lanes of a row (L,
+// (16 bytes, INT8: two 16-byte runs) of one row and group quarter.  INT8
+// weights (BITS 8) take the INT8 quantizer: scale amax / 127, codes
+// [-128, 127], stochastic rounding where -128 <= floor(v) <= 126.  The four lanes of a row (L,
 // L+16, L+32, L+48 of the same wave) combine their magnitudes with two
 // cross-lane exchanges; every lane reads its words and the row's scale
 // before any lane writes (one wave), so the update is in place.
@@ -72,9 +74,11 @@ __device__ inline void load8_f32(const void* p, int64_t idx, float* out) {
     }
 }
 
-template <int DT, bool LOWRANK>
+template <int DT, bool LOWRANK, int BITS>
 __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
-    const Layout L(a.n, a.k);
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
+    constexpr float kQmax = BITS == 8 ? 127.0f : 7.0f, kQmin = -kQmax - 1.0f;
+    const Layout L(a.n, a.k, BITS);
     const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t chunk = tid >> 6;
     // whole waves stay together (the grid covers whole chunks) so the row's
@@ -85,15 +89,24 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
     const int r = lane & 15, kq = lane >> 4;
     const int64_t row = t * kTileRows + r;
     const bool live = row < a.n;
-    uint8_t* cp = a.packed + chunk * kChunkBytes + lane * 16;
+    uint8_t* cp = a.packed + chunk * CB + lane * 16;
     float* sp = reinterpret_cast<float*>(a.packed + L.scale_offset()) + chunk * kTileRows + r;
 
-    const uint4 in = *reinterpret_cast<const uint4*>(cp);
+    uint32_t words[4 * H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        const uint4 in = *reinterpret_cast<const uint4*>(cp + h * kChunkBytes);
+        words[4 * h] = in.x;
+        words[4 * h + 1] = in.y;
+        words[4 * h + 2] = in.z;
+        words[4 * h + 3] = in.w;
+    }
     const float s_old = *sp;
-    const uint32_t words[4] = {in.x, in.y, in.z, in.w};
 
-    // word s holds columns 128g + 32s + 8kq + j: nibble i = column 2i,
-    // nibble i + 4 = column 2i + 1, offset-binary u = q + 8
+    // INT4: word s holds columns 128g + 32s + 8kq + j: nibble i = column 2i,
+    // nibble i + 4 = column 2i + 1, offset-binary u = q + 8.  INT8: words
+    // 2s and 2s + 1 hold columns 8kq + 0..3 and 4..7 of k-step s, one byte
+    // each, u = q + 128.
     float w[32];
     float amax = 0.0f;
 #pragma unroll
@@ -120,8 +133,13 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t nib = (words[s] >> (j % 2 == 0 ? 2 * j : 16 + 2 * (j - 1))) & 0xFu;
-            const float d = float(int(nib) - 8) * s_old;
+            int qc;
+            if constexpr (BITS == 8) {
+                qc = int((words[2 * s + j / 4] >> (8 * (j % 4))) & 0xFFu) - 128;
+            } else {
+                qc = int((words[s] >> (j % 2 == 0 ? 2 * j : 16 + 2 * (j - 1))) & 0xFu) - 8;
+            }
+            const float d = float(qc) * s_old;
             const float bd = a.beta * d;
             const float v = fmaf(a.alpha, p[j], bd);
             w[8 * s + j] = v;
@@ -130,41 +148,66 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
     }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float scale = amax / 7.0f;
+    const float scale = amax / kQmax;
 
-    uint32_t out[4];
+    uint32_t out[4 * H];
+#pragma unroll
+    for (int i = 0; i < 4 * H; ++i) out[i] = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             int code = 0;
             if (scale != 0.0f) {
                 const float v = w[8 * s + j] / scale;
                 const float lo = floorf(v);
-                if (a.stochastic && lo >= -8.0f && lo + 1.0f <= 7.0f) {
+                if (a.stochastic && lo >= kQmin && lo + 1.0f <= kQmax) {
                     const int64_t col = g * kGroup + 32 * s + 8 * kq + j;
                     const uint64_t e = uint64_t(row * a.k + col);
                     const float u = float(splitmix64(a.seed, e) >> 40) * 0x1p-24f;
                     code = int(lo) + (u < v - lo ? 1 : 0);
                 } else {
-                    code = int(fminf(fmaxf(__builtin_rintf(v), -8.0f), 7.0f));
+                    code = int(fminf(fmaxf(__builtin_rintf(v), kQmin), kQmax));
                 }
             }
-            const uint32_t u4 = uint32_t(code + 8) & 0xFu;
-            word |= u4 << (j % 2 == 0 ? 2 * j : 16 + 2 * (j - 1));
+            if constexpr (BITS == 8) {
+                out[2 * s + j / 4] |= (uint32_t(code + 128) & 0xFFu) << (8 * (j % 4));
+            } else {
+                out[s] |= (uint32_t(code + 8) & 0xFu) << (j % 2 == 0 ? 2 * j : 16 + 2 * (j - 1));
+            }
         }
-        out[s] = word;
     }
     if (!live) return;
-    *reinterpret_cast<uint4*>(cp) = make_uint4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+        *reinterpret_cast<uint4*>(cp + h * kChunkBytes) =
+            make_uint4(out[4 * h], out[4 * h + 1], out[4 * h + 2], out[4 * h + 3]);
     if (kq == 0) *sp = scale;
+}
+
+template <int BITS>
+static void launch_update_bits(const UpdateArgs& a, int dtype, dim3 grid, dim3 block, hipStream_t stream) {
+    const bool lr = a.rank > 0;
+    switch (dtype) {
+        case 0:
+            if (lr) update_kernel<0, true, BITS><<<grid, block, 0, stream>>>(a);
+            else update_kernel<0, false, BITS><<<grid, block, 0, stream>>>(a);
+            break;
+        case kActBf16:
+            if (lr) update_kernel<kActBf16, true, BITS><<<grid, block, 0, stream>>>(a);
+            else update_kernel<kActBf16, false, BITS><<<grid, block, 0, stream>>>(a);
+            break;
+        default:
+            if (lr) update_kernel<kActF16, true, BITS><<<grid, block, 0, stream>>>(a);
+            else update_kernel<kActF16, false, BITS><<<grid, block, 0, stream>>>(a);
+            break;
+    }
 }
 
 hipError_t launch_update(void* packed, int64_t n, int64_t k, const void* upd, int64_t ldu, const void* mat1,
                          const void* mat2, int64_t rank, int dtype, float alpha, float beta, int stochastic,
-                         uint64_t seed, hipStream_t stream) {
-    const Layout L(n, k);
+                         uint64_t seed, int bits, hipStream_t stream) {
+    const Layout L(n, k, bits);
     UpdateArgs a;
     a.packed = static_cast<uint8_t*>(packed);
     a.n = n;
@@ -179,21 +222,8 @@ hipError_t launch_update(void* packed, int64_t n, int64_t k, const void* upd, in
     a.stochastic = stochastic;
     a.seed = seed;
     const dim3 grid(unsigned(ceil_div(L.chunks() * 64, 256))), block(256);
-    const bool lr = rank > 0;
-    switch (dtype) {
-        case 0:
-            if (lr) update_kernel<0, true><<<grid, block, 0, stream>>>(a);
-            else update_kernel<0, false><<<grid, block, 0, stream>>>(a);
-            break;
-        case kActBf16:
-            if (lr) update_kernel<kActBf16, true><<<grid, block, 0, stream>>>(a);
-            else update_kernel<kActBf16, false><<<grid, block, 0, stream>>>(a);
-            break;
-        default:
-            if (lr) update_kernel<kActF16, true><<<grid, block, 0, stream>>>(a);
-            else update_kernel<kActF16, false><<<grid, block, 0, stream>>>(a);
-            break;
-    }
+    if (bits == 8) launch_update_bits<8>(a, dtype, grid, block, stream);
+    else launch_update_bits<4>(a, dtype, grid, block, stream);
     return hipGetLastError();
 }
 
