@@ -275,3 +275,31 @@ def test_workload_case(dev, name):
         cols = np.concatenate([rng.integers(0, c.n, 4096), [0, c.n - 1, 0, c.n - 1]])
         y_ref = oracle.linear_entries(xb, tag(c.torch_dtype), q, s, bb, rows, cols)
         check_close(y[rows, cols], y_ref, xnorm[rows], wmax[cols], name)
+
+
+def test_concurrent_streams_separate_workspaces(dev):
+    """Calls with K splits finished through the exchange slots, issued on two
+    streams at once, each with the binding's own workspace for its stream,
+    equal the same calls made one after the other, bit for bit."""
+    lib = w4()
+    g = torch.Generator().manual_seed(77)
+    layers = []
+    for n, k in ((2048, 16384), (1040, 16384)):
+        w = torch.randn(n, k, generator=g) * 0.02
+        c, s = lib.quantize(w.to(dev))
+        layers.append((lib.pack(c, s), n, k))
+    xs = [torch.randn(m, k, generator=g).to(torch.bfloat16).to(dev) for m, (_, _, k) in zip((1, 6), layers)]
+    want = [lib.linear(x, p, n) for x, (p, n, _) in zip(xs, layers)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    say("two streams, 8 rounds of split-K calls each")
+    outs = [[], []]
+    for _ in range(8):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                p, n, _ = layers[i]
+                outs[i].append(lib.linear(xs[i], p, n))
+    torch.cuda.synchronize()
+    for i in range(2):
+        for y in outs[i]:
+            assert torch.equal(y, want[i]), f"stream {i}"
