@@ -400,6 +400,84 @@ def traffic_probe(dev):
         f"4 elementwise launches of {src.numel() * 4} bytes read + written; sources {kernel_source_hash()}")
 
 
+GEMM_PROBE_CASE = "c4_m1024_k2048_n32768"
+
+
+def gemm_probe(dev):
+    """Launches for the stall-counter runs: the M = 1024 prefill GEMM (K 2048,
+    N 32768, fp16 with bias) 8 times over distinct weight copies."""
+    import torch
+
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    c = synth.case_by_name(GEMM_PROBE_CASE)
+    layers, _ = build_pool([c], dev)
+    x = synth.make_x(c).to(dev)
+    bias = synth.make_bias(c).to(dev) if c.bias else None
+    y = torch.empty((c.m, c.n), dtype=c.torch_dtype, device=dev)
+    ws = torch.zeros(max(w4.workspace_bytes(c.m, c.n, c.k), 16), dtype=torch.uint8, device=dev)
+    for i in range(8):
+        w4.linear(x, layers[i % len(layers)][0], c.n, bias, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"gemm probe: 8 launches of {c.name} on the {w4.choose_path(c.m, c.n, c.k).name} path")
+
+
+# Stall counters of the GEMM (two rocprofv3 --pmc passes of --gemm-probe):
+# SQ_*_CYCLES wave counters count quad-cycles (4 clocks); the MFMA busy
+# counter counts clocks summed over the 1024 SIMDs.
+SQ_PASSES = (
+    ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+     "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"),
+    ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+     "SQ_ACTIVE_INST_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"),
+)
+
+
+def summarize_sq(dbs):
+    """Markdown summary of the GEMM's SQ counters from the counter databases
+    of --gemm-probe: mean per dispatch (first dispatch dropped), per-wave
+    counts, and the shares of a wave's lifetime spent issuing, waiting on
+    its counters or a barrier, and waiting to issue."""
+    vals = {}
+    name = None
+    for db in dbs:
+        rows = _rocpd_rows(db, "select dispatch_id, kernel_name, counter_name, value from counters_collection")
+        per = {}
+        for d, kname, cname, v in rows:
+            if "gemm" not in kname:
+                continue
+            name = kname.split("(")[0]
+            per.setdefault(cname, {}).setdefault(d, 0.0)
+            per[cname][d] += v
+        for cname, byd in per.items():
+            v = [byd[d] for d in sorted(byd)]
+            v = v[1:] if len(v) > 1 else v
+            vals[cname] = sum(v) / len(v)
+    if not vals:
+        raise SystemExit("no GEMM dispatch in the counter databases")
+    lines = [f"Kernel `{name}`; mean per dispatch:", "", "| counter | value |", "|---|---:|"]
+    lines += [f"| {k} | {vals[k]:,.0f} |" for k in sorted(vals)]
+    waves = vals.get("SQ_WAVES")
+    if waves:
+        lines += ["", "Per wave:"]
+        for k, what in (("SQ_INSTS_MFMA", "MFMA instructions"), ("SQ_INSTS_VALU", "VALU instructions (MFMA included)"),
+                        ("SQ_INSTS_LDS", "LDS instructions"), ("SQ_INSTS_VMEM", "vector memory instructions"),
+                        ("SQ_INSTS_SALU", "scalar ALU instructions")):
+            if k in vals:
+                lines.append(f"- {what}: {vals[k] / waves:,.1f}")
+    life = vals.get("SQ_WAVE_CYCLES")
+    if life:
+        lines += ["", "Share of the waves' lifetime (quad-cycles over SQ_WAVE_CYCLES):"]
+        for k, what in (("SQ_ACTIVE_INST_ANY", "issuing"), ("SQ_WAIT_ANY", "waiting on s_waitcnt or a barrier"),
+                        ("SQ_WAIT_INST_ANY", "ready but waiting to issue (dependency or a busy unit)"),
+                        ("SQ_WAIT_INST_LDS", "waiting to issue an LDS instruction")):
+            if k in vals:
+                lines.append(f"- {what}: {100 * vals[k] / life:.1f} %")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+        lines += ["", f"MFMA busy clocks per SIMD (over 1024 SIMDs): {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:,.0f}"]
+    return "\n".join(lines)
+
+
 def _rocpd_rows(db, sql):
     import sqlite3
     con = sqlite3.connect(db)
@@ -492,6 +570,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the launches the HBM counter runs measure (see TRAFFIC_FILE)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only the launches the GEMM stall-counter runs measure (8 launches of the M = 1024 GEMM)")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DB",
+                    help="print the SQ counter summary of --gemm-probe counter databases and exit")
     ap.add_argument("--summarize-trace", metavar="DB",
                     help="print the per-kernel table of a rocprofv3 --kernel-trace database and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -499,6 +581,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_sq:
+        print(summarize_sq(args.summarize_sq))
         return
     if args.summarize_traffic:
         parts, traffic = summarize_traffic(*args.summarize_traffic)
@@ -542,6 +627,9 @@ def main():
     w4.lib()
     if args.traffic_probe:
         traffic_probe(dev)
+        return
+    if args.gemm_probe:
+        gemm_probe(dev)
         return
 
     # --- decode step (M = 1) --------------------------------------------------
