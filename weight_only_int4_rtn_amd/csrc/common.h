@@ -177,6 +177,23 @@ __device__ inline uint4 load_stream16(const uint8_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A value the same in every lane, kept in a scalar register (buffer
+// resources and offsets must be; per-wave indices computed from it stay on
+// the scalar unit instead of costing vector instructions in every lane).
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Buffer resource over `bytes` bytes from `base` (bytes < 2^31); loads past
+// the end return zero.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = uint32_t(uniform(int(uint32_t(b)))), hi = uint32_t(uniform(int(uint32_t(b >> 32))));
+    void* p = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, uniform(int(uint32_t(bytes))), 0x00020000);
+}
+
+// Cache-policy operand of a buffer load: nontemporal (data read once).
+constexpr int kBufNontemporal = 2;
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, then s_barrier.  __syncthreads() also waits for every
 // outstanding global load (vmcnt(0)), which would serialise the weight

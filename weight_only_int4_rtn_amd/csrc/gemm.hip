@@ -144,16 +144,6 @@ __device__ inline int swz(int row, int seg) { return row * 128 + ((seg ^ (row & 
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// A value the same in every lane, kept in a scalar register (buffer
-// resources and offsets must be).
-__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = uint32_t(uniform(int(uint32_t(b)))), hi = uint32_t(uniform(int(uint32_t(b >> 32))));
-    void* p = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(p, 0, uniform(int(uint32_t(bytes))), 0x00020000);
-}
-
 // A wave's four 1 KB weight chunks of one group and their dequantization
 // into MFMA B operands, one k-step (one word per lane per chunk) at a time.
 template <int ACT>

@@ -75,11 +75,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     float* red = xsum + M * a.gps * 4;                                             // [WAVES][M][16]
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
 
     const uint8_t* cbase = a.packed + (t * L.groups + g0) * CB + lane * 16;
     const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (t * L.groups + g0) * kTileRows + r;
+    // M = 1: the split's chunks and scales through buffer resources, so a
+    // chunk's address is a scalar offset plus the lane's 16 bytes (measured
+    // faster at M = 1 only; larger M keep the flat loads)
+    const __amdgpu_buffer_rsrc_t cres = buffer_rsrc(a.packed + (t * L.groups + g0) * CB, int64_t(ng) * CB);
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
+        a.packed + L.scale_offset() + (t * L.groups + g0) * kChunkScaleBytes, int64_t(ng) * kChunkScaleBytes);
 
     // Every chunk of the wave (CPW of them) is loaded before any is used.
     // The loads are unconditional straight-line code (clamped addresses), so
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         if (j * THREADS >= total) break;
         const int i = j * THREADS + tid;
         const int ic = i < total ? i : total - 1;
-        const int m = ic / per_row, c = ic - m * per_row;
+        const int m = M == 1 ? 0 : ic / per_row, c = ic - m * per_row;
         const uint16_t* src = a.x + m * a.ldx + g0 * kGroup + c * 8;
         xv[j] = *reinterpret_cast<const uint4*>(src);
         if constexpr (AF == kActFnSwiglu) xgate[j] = *reinterpret_cast<const uint4*>(src + a.k);
@@ -110,9 +116,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * WAVES;
         const int gc = gl < ng ? gl : ng - 1;  // a valid chunk; unused when gl >= ng
+        if constexpr (M == 1) {
 #pragma unroll
-        for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
-        sc[u] = sbase[int64_t(gc) * kTileRows];
+            for (int h = 0; h < H; ++h) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(cres, lane * 16 + h * kChunkBytes, uniform(gc * CB),
+                                                                     kBufNontemporal);
+                cw[u][h] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+            sc[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   sres, r * 4, uniform(gc * kChunkScaleBytes), kBufNontemporal));
+        } else {
+#pragma unroll
+            for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
+            sc[u] = sbase[int64_t(gc) * kTileRows];
+        }
     }
 
     // Stage x into LDS and sum each lane-quarter's 32 activations of every
@@ -124,7 +141,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         if (j * THREADS >= total) break;
         const int i = j * THREADS + tid;
         const bool on = i < total;
-        const int m = on ? i / per_row : 0, c = on ? i - m * per_row : 0;
+        const int m = (M == 1 || !on) ? 0 : i / per_row, c = on ? i - m * per_row : 0;
         if constexpr (AF != kActFnNone) xv[j] = activate8<ACT, AF>(xv[j], xgate[AF == kActFnSwiglu ? j : 0]);
         if (on) *reinterpret_cast<uint4*>(xs + m * klen + c * 8) = xv[j];
         if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
