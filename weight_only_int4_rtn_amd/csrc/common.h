@@ -112,6 +112,24 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float acc) {
     }
 }
 
+// Sum of the eight 16-bit values of a 16-byte x load in FP32: four v_dot2
+// against (1, 1) (exact products, FP32 accumulation) instead of eight
+// conversions and seven additions.
+template <int ACT>
+__device__ inline float sum8(uint4 v) {
+    constexpr uint32_t ones = ACT == kActBf16 ? 0x3F803F80u : 0x3C003C00u;
+    float s = dot2<ACT>(v.x, ones, 0.0f);
+    s = dot2<ACT>(v.y, ones, s);
+    s = dot2<ACT>(v.z, ones, s);
+    return dot2<ACT>(v.w, ones, s);
+}
+
+// i / d for 0 <= i < 2^13 and d >= 1 without an integer division sequence
+// (inv_d = 1.0f / d): (i + 1/2) / d lies at least 1/(2d) from an integer,
+// and its FP32 evaluation errs by less than (i + 1/2) / d * 2^-23 < 2^-10 / d,
+// so the truncation is exact.
+__device__ inline int div_small(int i, float inv_d) { return int((float(i) + 0.5f) * inv_d); }
+
 // (a & mask) | bits in one v_and_or_b32.  gfx9 VOP3 encodings take no
 // literal constants, so the compiler would otherwise emit a separate and + or
 // pair; the operands here are registers (constants hoisted out of loops).

@@ -97,7 +97,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     // issued next never delay the staging), then the first weight batch.
     // The plan keeps M * klen / 8 <= kXRegs * THREADS.
     const int per_row = klen / 8;  // multiple of 16
-    const int total = M * per_row;
+    const int total = M * per_row;  // <= 2048: M <= 4 rows of <= 4096 columns
+    const float inv_row = 1.0f / float(per_row);
     uint4 xv[kXRegs];
     uint4 xgate[AF == kActFnSwiglu ? kXRegs : 1];
 #pragma unroll
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         if (j * THREADS >= total) break;
         const int i = j * THREADS + tid;
         const int ic = i < total ? i : total - 1;
-        const int m = M == 1 ? 0 : ic / per_row, c = ic - m * per_row;
+        const int m = M == 1 ? 0 : div_small(ic, inv_row), c = ic - m * per_row;
         const uint16_t* src = a.x + m * a.ldx + g0 * kGroup + c * 8;
         xv[j] = *reinterpret_cast<const uint4*>(src);
         if constexpr (AF == kActFnSwiglu) xgate[j] = *reinterpret_cast<const uint4*>(src + a.k);
@@ -141,15 +142,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         if (j * THREADS >= total) break;
         const int i = j * THREADS + tid;
         const bool on = i < total;
-        const int m = (M == 1 || !on) ? 0 : i / per_row, c = on ? i - m * per_row : 0;
+        const int m = (M == 1 || !on) ? 0 : div_small(i, inv_row), c = on ? i - m * per_row : 0;
         if constexpr (AF != kActFnNone) xv[j] = activate8<ACT, AF>(xv[j], xgate[AF == kActFnSwiglu ? j : 0]);
         if (on) *reinterpret_cast<uint4*>(xs + m * klen + c * 8) = xv[j];
         if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            s += to_f32<ACT>(uint16_t(w[q] & 0xFFFFu)) + to_f32<ACT>(uint16_t(w[q] >> 16));
+        float s = sum8<ACT>(xv[j]);
         s += __shfl_xor(s, 4, 16);
         s += __shfl_xor(s, 8, 16);
         const int wb = c & 15;

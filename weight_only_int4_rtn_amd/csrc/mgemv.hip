@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     float* red = xg + a.gps * 16;                                                          // [waves][16][16]
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
 
     const uint8_t* cbase = a.packed + (t * L.groups + g0) * kChunkBytes + lane * 16;
@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     // order: staging waits for x only).  The plan keeps m * klen / 8 <=
     // kXRegs * threads.
     const int per_row = klen / 8;
-    const int total = m * per_row;
+    const int total = m * per_row;  // <= 2048: the plan keeps m * gps <= 128 groups
+    const float inv_row = 1.0f / float(per_row);
     uint4 xv[kXRegs];
     uint4 xgate[AF == kActFnSwiglu ? kXRegs : 1];
 #pragma unroll
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
         if (j * kMgThreads >= total) break;
         const int i = j * kMgThreads + tid;
         const int ic = i < total ? i : total - 1;
-        const int row = ic / per_row, c = ic - row * per_row;
+        const int row = div_small(ic, inv_row), c = ic - row * per_row;
         const uint16_t* src = a.x + row * a.ldx + g0 * kGroup + c * 8;
         xv[j] = *reinterpret_cast<const uint4*>(src);
         if constexpr (AF == kActFnSwiglu) xgate[j] = *reinterpret_cast<const uint4*>(src + a.k);
@@ -122,15 +123,11 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
         if (j * kMgThreads >= total) break;
         const int i = j * kMgThreads + tid;
         const bool on = i < total;
-        const int row = on ? i / per_row : 0, c = on ? i - row * per_row : 0;
+        const int row = on ? div_small(i, inv_row) : 0, c = on ? i - row * per_row : 0;
         if constexpr (AF != kActFnNone) xv[j] = activate8<ACT, AF>(xv[j], xgate[AF == kActFnSwiglu ? j : 0]);
         if (on) *reinterpret_cast<uint4*>(xs + row * xstride + c * 8) = xv[j];
         if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            s += to_f32<ACT>(uint16_t(w[q] & 0xFFFFu)) + to_f32<ACT>(uint16_t(w[q] >> 16));
+        float s = sum8<ACT>(xv[j]);
 #pragma unroll
         for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 16);
         if (on && (c & 15) == 0) xg[(c >> 4) * 16 + row] = s;
