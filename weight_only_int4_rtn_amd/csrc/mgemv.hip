@@ -2,16 +2,19 @@
 // the v_dot2 kernel (gemv.hip), with the contraction done by MFMA.
 //
 // A workgroup of 4 waves owns one 16-row weight tile and a K split.  The
-// workgroup stages its slice of x (M rows) in LDS once, with each row's sum
-// over every 128-column group.  Per chunk, a wave turns its four words into
+// workgroup stages its slice of x (M rows) in LDS once.  Per chunk, a wave
+// turns its four words into
 // four B operands of v_mfma_f32_16x16x32_{bf16,f16} (the chunk layout is that
 // operand layout: lane L holds column L % 16 of the tile, columns
 // 8*(L/16) + j of each 32-wide k-step), reads the matching A operands (row
 // L % 16 of x, zero for rows >= M) from LDS, and runs four MFMAs into a fresh
 // accumulator.  The packed pairs hold off + q exactly (off = 136 for bf16,
-// 1032 for f16), so per group
-//     sum_k x_k q_k = mfma result - off * sum_k x_k,
-// and the group's FP32 scale multiplies that into the FP32 totals.  The
+// 1032 for f16); four more MFMAs with the same A operands and a B operand of
+// -off in every element (exact in both types) leave
+//     sum_k x_k q_k
+// in the accumulator, and the group's FP32 scale multiplies that into the
+// FP32 totals.  (The extra MFMAs replace per-row sums of x and their
+// cross-lane reductions: measured 2-25 % faster for M 3-16.)  The
 // accumulator layout of the MFMA gives lane L the rows 4*(L/16) + i, i = 0..3,
 // of column L % 16.  Per weight element this costs 7/8 of a VALU instruction
 // for the nibble conversion, against 11/8 for the v_dot2 kernel at M = 1.
@@ -72,8 +75,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     // fall in different LDS banks.
     const int xstride = klen + 8;
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                                      // [MMAX][xstride]
-    float* xg = reinterpret_cast<float*>(smem + size_t(MMAX) * (a.gps * kGroup + 8) * 2);    // [ng][16]
-    float* red = xg + a.gps * 16;                                                          // [waves][16][16]
+    float* red = reinterpret_cast<float*>(smem + size_t(MMAX) * (a.gps * kGroup + 8) * 2);   // [waves][16][16]
 
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6), lane = tid & 63;
@@ -116,8 +118,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
         sc[u] = sbase[int64_t(gc) * kTileRows];
     }
 
-    // Stage rows [0, m); group sums over the 16 threads that cover one row's
-    // 128 columns of a group (lanes 1, 2, 4, 8 apart).
+    // Stage rows [0, m).
 #pragma unroll
     for (int j = 0; j < kXRegs; ++j) {
         if (j * kMgThreads >= total) break;
@@ -126,18 +127,12 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
         const int row = on ? div_small(i, inv_row) : 0, c = on ? i - row * per_row : 0;
         if constexpr (AF != kActFnNone) xv[j] = activate8<ACT, AF>(xv[j], xgate[AF == kActFnSwiglu ? j : 0]);
         if (on) *reinterpret_cast<uint4*>(xs + row * xstride + c * 8) = xv[j];
-        if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
-        float s = sum8<ACT>(xv[j]);
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 16);
-        if (on && (c & 15) == 0) xg[(c >> 4) * 16 + row] = s;
     }
-    // rows m..15 of the group sums are zero (their A operands are zero)
-    for (int i = tid; i < ng * 16; i += kMgThreads)
-        if ((i & 15) >= m) xg[i] = 0.0f;
     lds_barrier();
 
     constexpr float off = code_offset<ACT>();
+    const uint32_t noff2 = uint32_t(from_f32<ACT>(-off)) * 0x00010001u;
+    const uint4 bneg = make_uint4(noff2, noff2, noff2, noff2);  // -off in every element
     const bool row_on = r < m;
     const uint16_t* xrow = xs + (row_on ? r : 0) * xstride + 8 * kq;
     f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
@@ -156,12 +151,12 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
                 const uint4 bv = make_uint4(magic_pair<ACT>(words[s], 0), magic_pair<ACT>(words[s], 1),
                                             magic_pair<ACT>(words[s], 2), magic_pair<ACT>(words[s], 3));
                 acc = mfma_16x16x32<ACT>(av, bv, acc);
+                acc = mfma_16x16x32<ACT>(av, bneg, acc);
             }
-            const float4 xsum = *reinterpret_cast<const float4*>(xg + gl * 16 + 4 * kq);
-            tot[0] = fmaf(scale, fmaf(-off, xsum.x, acc[0]), tot[0]);
-            tot[1] = fmaf(scale, fmaf(-off, xsum.y, acc[1]), tot[1]);
-            tot[2] = fmaf(scale, fmaf(-off, xsum.z, acc[2]), tot[2]);
-            tot[3] = fmaf(scale, fmaf(-off, xsum.w, acc[3]), tot[3]);
+            tot[0] = fmaf(scale, acc[0], tot[0]);
+            tot[1] = fmaf(scale, acc[1], tot[1]);
+            tot[2] = fmaf(scale, acc[2], tot[2]);
+            tot[3] = fmaf(scale, acc[3], tot[3]);
         }
     }
 
@@ -224,7 +219,7 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k) {
     p.splits = int(ceil_div(L.groups, gps));
     const int64_t per_wave = ceil_div(gps, kMgWaves);
     p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
-    p.lds = size_t(p.mmax) * (gps * kGroup + 8) * 2 + size_t(gps) * 16 * 4 + size_t(kMgWaves) * 256 * 4;
+    p.lds = size_t(p.mmax) * (gps * kGroup + 8) * 2 + size_t(kMgWaves) * 256 * 4;
     const int64_t slots = L.tiles * (p.splits - 1) * m * kTileRows;
     p.exchange = p.splits > 1 && slots * 8 <= int64_t(kSyncBytes);
     p.workspace = p.splits == 1 ? 0

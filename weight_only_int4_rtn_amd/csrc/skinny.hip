@@ -8,15 +8,19 @@
 // whole weight stream is in flight at once.  Then per 128-column group:
 //   1. the activation block's 128 columns, loaded into registers two groups
 //      ahead, are staged in one of two LDS buffers (with a fused input
-//      activation applied on the way) and each row is summed (for the offset
-//      correction below);
+//      activation applied on the way);
 //   2. each wave turns every word of its chunk into one MFMA B operand: the
 //      chunk layout is the B-operand layout of v_mfma_f32_16x16x32_{bf16,f16}
 //      (common.h), and each nibble pair becomes a packed pair of 16-bit
 //      floats holding off + q exactly (off = 136 for bf16, 1032 for f16);
-//   3. four MFMAs (k-steps of 32) per 16-row m-subtile give the group's
-//      sum_k x (off + q); the wave subtracts off * sum_k x, multiplies by the
-//      column's FP32 scale and adds into its FP32 totals.
+//   3. per 16-row m-subtile and k-step of 32, one MFMA adds x (off + q) and
+//      a second one, with the same x fragment and a B operand of -off in
+//      every element (exact in both 16-bit types), adds -off x: the
+//      accumulator ends with the group's sum_k x q, which the wave multiplies
+//      by the column's FP32 scale and adds into its FP32 totals.  The extra
+//      MFMAs replace a per-row sum of x with its cross-lane reduction, whose
+//      latency the few waves of this kernel could not hide (measured 15-31 %
+//      faster for M 16-256).
 // The weights never pass through LDS; x tiles are shared by the 4 waves.
 // K splits store FP32 partial sums that the split-K reduce kernel adds in
 // split order (reduce.hip), adding the bias in FP32 and rounding once.
@@ -63,7 +67,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     constexpr int BM = 16 * MB;
     constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
     __shared__ __align__(16) uint16_t xa[2][BM * kAStride];
-    __shared__ __align__(16) float xrow[2][BM];
 
     const Layout L(a.n, a.k, BITS);
     const int split = int(blockIdx.x % unsigned(a.splits));
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     const int ng = int(min<int64_t>(a.gps, L.groups - g0));
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
     const int64_t t = tg * kSkWaves + wave;
     const bool tile_ok = t < L.tiles;
@@ -82,6 +85,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     const uint8_t* cbase = a.packed + (tt * L.groups + g0) * CB + lane * 16;
     const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (tt * L.groups + g0) * kTileRows + r;
     constexpr float off = code_offset<ACT, BITS>();
+    // B operand of -off in every element (step 3 above)
+    const uint32_t noff2 = uint32_t(from_f32<ACT>(-off)) * 0x00010001u;
+    const uint4 bneg = make_uint4(noff2, noff2, noff2, noff2);
 
     // Every chunk and scale of the wave's groups, loaded before anything
     // else, so the weight stream is in flight during all of the x staging.
@@ -98,8 +104,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     // x of one group: rows m0 .. m0 + BM - 1, columns of the group; 16
     // threads per row, 8 columns each, MB passes (rows past M read row 0 and
     // are zeroed when staged).  Loaded into one of two register sets two
-    // groups ahead, then activated, staged in one of two LDS buffers and
-    // summed per row (for the offset correction below).
+    // groups ahead, then activated and staged in one of two LDS buffers.
     uint4 xr[2][MB];
     uint4 xgate[AF == kActFnSwiglu ? 2 : 1][AF == kActFnSwiglu ? MB : 1];
     auto load_x = [&](int set, int gl) {
@@ -121,14 +126,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
                 v = activate8<ACT, AF>(v, xgate[AF == kActFnSwiglu ? set : 0][AF == kActFnSwiglu ? pass : 0]);
             if (m0 + row >= a.m) v = make_uint4(0u, 0u, 0u, 0u);
             *reinterpret_cast<uint4*>(&xa[buf][row * kAStride + piece * 8]) = v;
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            float s = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s += to_f32<ACT>(uint16_t(w[i] & 0xFFFFu)) + to_f32<ACT>(uint16_t(w[i] >> 16));
-#pragma unroll
-            for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 16);
-            if (piece == 0) xrow[buf][row] = s;
         }
     };
 
@@ -163,12 +160,15 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
             const uint16_t* ap = &xa[buf][(mb * 16 + r) * kAStride + 8 * kq];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma16<ACT>(*reinterpret_cast<const uint4*>(ap + 32 * s), b[s], acc);
-            const float4 xs4 = *reinterpret_cast<const float4*>(&xrow[buf][mb * 16 + 4 * kq]);
-            tot[mb][0] = fmaf(sc[gl], fmaf(-off, xs4.x, acc[0]), tot[mb][0]);
-            tot[mb][1] = fmaf(sc[gl], fmaf(-off, xs4.y, acc[1]), tot[mb][1]);
-            tot[mb][2] = fmaf(sc[gl], fmaf(-off, xs4.z, acc[2]), tot[mb][2]);
-            tot[mb][3] = fmaf(sc[gl], fmaf(-off, xs4.w, acc[3]), tot[mb][3]);
+            for (int s = 0; s < 4; ++s) {
+                const uint4 av = *reinterpret_cast<const uint4*>(ap + 32 * s);
+                acc = mfma16<ACT>(av, b[s], acc);
+                acc = mfma16<ACT>(av, bneg, acc);
+            }
+            tot[mb][0] = fmaf(sc[gl], acc[0], tot[mb][0]);
+            tot[mb][1] = fmaf(sc[gl], acc[1], tot[mb][1]);
+            tot[mb][2] = fmaf(sc[gl], acc[2], tot[mb][2]);
+            tot[mb][3] = fmaf(sc[gl], acc[3], tot[mb][3]);
         }
         // group gl + 1 into the other LDS buffer, last read in the previous
         // group, which ended with a barrier
