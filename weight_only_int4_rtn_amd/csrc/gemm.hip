@@ -82,6 +82,28 @@ __device__ inline f32x4_t gm_mfma(uint4 a, uint4 b, f32x4_t c) {
     }
 }
 
+// Bias of the four output columns c0 .. c0 + 3 of each of a lane's four
+// 16-column tiles (t0 .. t0 + 3), in FP32, zero past n or without a bias.
+// The sixteen loads use clamped indices and no branches, so all of them are
+// in flight together (element-wise conditional loads were each waited for
+// before the next was issued).
+template <int ACT>
+__device__ inline void bias16(const uint16_t* bias, int64_t t0, int kq, int64_t n, float (&bv)[4][4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[j][e] = 0.0f;
+    if (!bias) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t c = (t0 + j) * 16 + 4 * kq + e;
+            const float v = to_f32<ACT>(bias[c < n ? c : n - 1]);
+            bv[j][e] = c < n ? v : 0.0f;
+        }
+}
+
 // Two FP32 values -> packed pair of the 16-bit type, round to nearest even
 // (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
 template <int ACT>
@@ -353,17 +375,14 @@ __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmA
     // outputs 4kq .. 4kq + 3 of tile t0 + j for x row r of row block i, four
     // consecutive columns (one 8-byte store, 16 bytes for FP32 partials).
     const int64_t npad = a.ntiles * kGmBN;
+    float ball[4][4];
+    bias16<ACT>(a.splits == 1 ? a.bias : nullptr, t0, kq, a.n, ball);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t c0 = (t0 + j) * 16 + 4 * kq;
         if (c0 >= a.n) continue;
         const bool full = c0 + 4 <= a.n;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (a.splits == 1 && a.bias) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (c0 + e < a.n) bv[e] = to_f32<ACT>(a.bias[c0 + e]);
-        }
+        const float* bv = ball[j];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             const int64_t row = m0 + i * 16 + r;
@@ -651,15 +670,11 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
                                            : W1;
             return q + (row & 63) * 512;
         };
+        float ball[4][4];
+        bias16<ACT>(a.bias, t0, kq, a.n, ball);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t c0 = (t0 + j) * 16 + 4 * kq;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (a.bias) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (c0 + e < a.n) bv[e] = to_f32<ACT>(a.bias[c0 + e]);
-            }
+            const float* bv = ball[j];
             const int u = (wn * 4 + j) * 2 + (kq >> 1);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -688,17 +703,14 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
             }
         }
     } else {
+    float ball[4][4];
+    bias16<ACT>(a.splits == 1 ? a.bias : nullptr, t0, kq, a.n, ball);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t c0 = (t0 + j) * 16 + 4 * kq;
         if (c0 >= a.n) continue;
         const bool full = c0 + 4 <= a.n;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (a.splits == 1 && a.bias) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (c0 + e < a.n) bv[e] = to_f32<ACT>(a.bias[c0 + e]);
-        }
+        const float* bv = ball[j];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t row = m0 + wm * 128 + i * 16 + r;

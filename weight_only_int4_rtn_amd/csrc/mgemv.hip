@@ -96,7 +96,12 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     const int per_row = klen / 8;
     const int total = m * per_row;  // <= 2048: the plan keeps m * gps <= 128 groups
     const float inv_row = 1.0f / float(per_row);
+    // zero-initialised so every register has a value on every path out of
+    // the load loop: the compiler then keeps all x loads in flight together
+    // (without it, it waited for each load before issuing the next)
     uint4 xv[kXRegs];
+#pragma unroll
+    for (int j = 0; j < kXRegs; ++j) xv[j] = make_uint4(0u, 0u, 0u, 0u);
     uint4 xgate[AF == kActFnSwiglu ? kXRegs : 1];
 #pragma unroll
     for (int j = 0; j < kXRegs; ++j) {
