@@ -72,6 +72,14 @@ def test_choose_path(lib):
     for m in (1, 2, 3, 4, 8, 16, 50, 64, 256, 1024, 4096):
         assert w4.choose_path(m, 2048, 2048) != w4.Path.AUTO
     assert w4.choose_path(4096, 2048, 2048) == w4.Path.GEMM
+    # measured crossovers: MFMA small-M kernel up to M = 8 on <= 16384 outputs,
+    # the mid-M kernel up to M = 96 on layers above 8 M weights
+    assert w4.choose_path(8, 16384, 2048) == w4.Path.MGEMV
+    assert w4.choose_path(8, 32768, 2048) == w4.Path.SKINNY
+    assert w4.choose_path(96, 32768, 2048) == w4.Path.SKINNY
+    assert w4.choose_path(97, 32768, 2048) == w4.Path.GEMM
+    assert w4.choose_path(512, 4096, 1024) == w4.Path.SKINNY
+    assert w4.choose_path(513, 4096, 1024) == w4.Path.GEMM
 
 
 def test_workspace_bytes(lib):
