@@ -74,6 +74,9 @@ def test_choose_path(lib):
     assert w4.choose_path(4096, 2048, 2048) == w4.Path.GEMM
     # measured crossovers: MFMA small-M kernel up to M = 8 on <= 16384 outputs,
     # the mid-M kernel up to M = 96 on layers above 8 M weights
+    assert w4.choose_path(2, 2560, 2048) == w4.Path.GEMV
+    assert w4.choose_path(2, 32768, 2048) == w4.Path.MGEMV
+    assert w4.choose_path(2, 1024, 4096) == w4.Path.MGEMV
     assert w4.choose_path(8, 16384, 2048) == w4.Path.MGEMV
     assert w4.choose_path(8, 32768, 2048) == w4.Path.SKINNY
     assert w4.choose_path(96, 32768, 2048) == w4.Path.SKINNY

@@ -243,8 +243,11 @@ w4a16_status_t shard_packed_weights_int8(const void* packed, int64_t n, int64_t 
 
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     // Measured (MI355X, graph replay, us): from M = 3 the MFMA contraction
-    // beats v_dot2 (3 x 2048 x 16384: 8.2 vs 10.1; at M = 2 the two are within
-    // a few %).  The small-M MFMA kernel finishes its K splits in-kernel and
+    // beats v_dot2 (3 x 2048 x 16384: 8.2 vs 10.1); at M = 2 it does so on
+    // layers above 8 M weights (2 x 32768 x 2048: 10.2 vs 10.5) and on narrow
+    // ones, whose few tiles it splits over more workgroups (2 x 1024 x 4096:
+    // 4.4 vs 5.1), while v_dot2 keeps the rest (2 x 2560 x 2048: 3.9 vs 4.3).
+    // The small-M MFMA kernel finishes its K splits in-kernel and
     // wins over the mid-M kernel up to M = 16 on layers of <= 8 M weights
     // (16 x 2560 x 2048: 5.3 vs 8.1), up to M = 8 on layers of <= 16384
     // outputs (8 x 16384 x 2048: 7.8 vs 9.1) and up to M = 4 on wider ones
@@ -253,8 +256,8 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     // to M = 512 (256 x 4096 x 1024: 9.3 vs 18.0); on larger layers up to
     // M = 96 (96 x 32768 x 2048: 38.8 vs 42.9; 96 x 2048 x 16384: 25.8 vs
     // 29.7; at M = 128 the GEMM leads, 46.3 vs 47.4 and 30.6 vs 32.4).
-    if (m <= 2) return W4A16_PATH_GEMV;
     const bool small = n * k <= (int64_t(8) << 20);
+    if (m <= 1 || (m == 2 && small && n >= 2048)) return W4A16_PATH_GEMV;
     if (m <= 4 || (m <= 8 && n <= 16384) || (m <= 16 && small)) return W4A16_PATH_MGEMV;
     if (k > kGemmMaxLd || m <= 96 || (small && m <= 512)) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
