@@ -99,7 +99,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     const int per_row = klen / 8;  // multiple of 16
     const int total = M * per_row;  // <= 2048: M <= 4 rows of <= 4096 columns
     const float inv_row = 1.0f / float(per_row);
+    // zero-initialised so every register has a value on every path out of
+    // the load loop (the compiler then keeps all x loads in flight together)
     uint4 xv[kXRegs];
+#pragma unroll
+    for (int j = 0; j < kXRegs; ++j) xv[j] = make_uint4(0u, 0u, 0u, 0u);
     uint4 xgate[AF == kActFnSwiglu ? kXRegs : 1];
 #pragma unroll
     for (int j = 0; j < kXRegs; ++j) {
