@@ -107,30 +107,37 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
     // nibble i + 4 = column 2i + 1, offset-binary u = q + 8.  INT8: words
     // 2s and 2s + 1 hold columns 8kq + 0..3 and 4..7 of k-step s, one byte
     // each, u = q + 128.
+    // The update U for the lane's 32 weights: dense, or the FMA chain over r
+    // ascending.  The rank loop is outermost: one mat1 value per r and the
+    // four k-steps' mat2 runs as independent loads (unrolled, so several
+    // r are in flight); each element's chain keeps the same order.
+    float pu[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) pu[i] = 0.0f;
+    if (live) {
+        if constexpr (LOWRANK) {
+            const int64_t colg = g * kGroup + 8 * kq;
+#pragma unroll 4
+            for (int64_t rr = 0; rr < a.rank; ++rr) {
+                const float m1 = elem_f32<DT>(a.mat1, row * a.rank + rr);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float m2[8];
+                    load8_f32<DT>(a.mat2, rr * a.k + colg + 32 * s, m2);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pu[8 * s + j] = fmaf(m1, m2[j], pu[8 * s + j]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) load8_f32<DT>(a.upd, row * a.ldu + g * kGroup + 32 * s + 8 * kq, pu + 8 * s);
+        }
+    }
     float w[32];
     float amax = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const int64_t col0 = g * kGroup + 32 * s + 8 * kq;
-        float p[8];
-        if (live) {
-            if constexpr (LOWRANK) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) p[j] = 0.0f;
-                for (int64_t rr = 0; rr < a.rank; ++rr) {
-                    const float m1 = elem_f32<DT>(a.mat1, row * a.rank + rr);
-                    float m2[8];
-                    load8_f32<DT>(a.mat2, rr * a.k + col0, m2);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) p[j] = fmaf(m1, m2[j], p[j]);
-                }
-            } else {
-                load8_f32<DT>(a.upd, row * a.ldu + col0, p);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = 0.0f;
-        }
+        const float* p = pu + 8 * s;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             int qc;
