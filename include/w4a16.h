@@ -332,9 +332,9 @@ size_t w8a16_linear_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64
  * y[m][n] = act(x)[m][k] . dequant(packed)^T + bias[n] for a packed INT8
  * weight (from pack_weights_int8): the arithmetic, arguments, activations,
  * no-op cases, overlap rules and status codes of w4a16_linear_act.  Paths:
- * W4A16_PATH_AUTO, W4A16_PATH_GEMV (row blocks of 4), W4A16_PATH_SKINNY and
- * W4A16_PATH_GEMM (any m; the GEMM with the row-stride limit of
- * w4a16_linear_with_path); W4A16_PATH_MGEMV gives W4A16_EUNSUPPORTED.
+ * W4A16_PATH_AUTO, W4A16_PATH_GEMV (row blocks of 4), W4A16_PATH_MGEMV (row
+ * blocks of 16), W4A16_PATH_SKINNY and W4A16_PATH_GEMM (any m; the GEMM with
+ * the row-stride limit of w4a16_linear_with_path).
  * workspace >= w8a16_linear_workspace_bytes(act, m, n, k) bytes.
  */
 w4a16_status_t w8a16_linear(w4a16_act_t act, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,

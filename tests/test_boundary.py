@@ -242,8 +242,13 @@ def test_int8_packed_bytes_and_paths(lib):
     with pytest.raises(ValueError):
         w4.packed_bytes(16, 128, bits=2)
     assert w4.choose_path(1, 2048, 2048, bits=8) == w4.Path.GEMV
-    assert w4.choose_path(4, 2048, 2048, bits=8) == w4.Path.GEMV
-    for m in (5, 16, 50, 127, 512):
+    assert w4.choose_path(2, 2048, 2048, bits=8) == w4.Path.GEMV
+    assert w4.choose_path(2, 32768, 2048, bits=8) == w4.Path.MGEMV
+    for m in (3, 4, 8, 16):
+        assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.MGEMV
+    assert w4.choose_path(8, 16384, 2048, bits=8) == w4.Path.MGEMV
+    assert w4.choose_path(9, 16384, 2048, bits=8) == w4.Path.SKINNY
+    for m in (17, 50, 127, 512):
         assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.SKINNY
     for m in (513, 4096):
         assert w4.choose_path(m, 2048, 2048, bits=8) == w4.Path.GEMM
@@ -278,7 +283,6 @@ def lin8(lib, fn=0, path=0, x=A, act=B.BF16, m=1, k=128, ldx=128, packed=A * 4, 
 
 def test_int8_linear_rejects(lib):
     assert lin8(lib, 3) == B.EINVAL                                         # unknown activation
-    assert lin8(lib, path=int(w4.Path.MGEMV)) == B.EUNSUPPORTED             # INT8: GEMV, SKINNY, GEMM
     big = (1 << 22) + 8
     assert lin8(lib, path=int(w4.Path.GEMM), m=256, ldx=big, y=A * 4096) == B.EUNSUPPORTED  # 32-bit x offsets
     assert lin8(lib, path=9) == B.EINVAL

@@ -42,7 +42,7 @@ w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A1
 size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bits) {
     switch (path) {
         case W4A16_PATH_GEMV: return plan_gemv(m < 4 ? m : 4, n, k, bits).workspace;
-        case W4A16_PATH_MGEMV: return bits == 4 ? plan_mgemv(m < 16 ? m : 16, n, k).workspace : 0;
+        case W4A16_PATH_MGEMV: return plan_mgemv(m < 16 ? m : 16, n, k, bits).workspace;
         case W4A16_PATH_SKINNY: return plan_skinny(m, n, k, bits).workspace;
         case W4A16_PATH_GEMM: return plan_gemm(m, n, k, bits).workspace;
         default: return 0;
@@ -264,13 +264,19 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
 }
 
 w4a16_path_t w8a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
-    // Measured on INT8 weights (MI355X): the v_dot2 GEMV up to M = 4 (even
-    // with SKINNY at M = 4 on 32768 x 2048), the mid-M kernel above, the
-    // GEMM from M = 65 on layers above 8 M weights (100 x 16384 x 2048: 31.7
-    // vs 43.9 us) and from M = 513 on smaller ones (256 x 4096 x 1024: 13.3
-    // vs 29.3 us; 1024 x 4096 x 1024: even).
-    if (m <= 4) return W4A16_PATH_GEMV;
+    // Measured on INT8 weights (MI355X, us): the v_dot2 GEMV at M = 1 and at
+    // M = 2 on layers of <= 8 M weights (2 x 2560 x 2048: 4.2 vs 4.6); the
+    // small-M MFMA kernel at M = 2 on larger layers (2 x 32768 x 2048: 14.8
+    // vs 15.1), at M = 3-8 (4 x 32768 x 2048: 15.1 vs 19.2; 8 x 2560 x 2048:
+    // 5.1 vs 8.4 on the mid-M kernel) and at M = 9-16 on layers of <= 8 M
+    // weights (16 x 4096 x 1024: 4.2 vs 6.8; on larger ones the mid-M kernel,
+    // 16 x 16384 x 2048: 12.9 vs 14.2); the mid-M kernel above, the GEMM
+    // from M = 65 on layers above 8 M weights (100 x 16384 x 2048: 31.7 vs
+    // 43.9) and from M = 513 on smaller ones (256 x 4096 x 1024: 13.3 vs
+    // 29.3; 1024 x 4096 x 1024: even).
     const bool small = n * k <= (int64_t(8) << 20);
+    if (m <= 1 || (m == 2 && small)) return W4A16_PATH_GEMV;
+    if (m <= 8 || (m <= 16 && small)) return W4A16_PATH_MGEMV;
     if (k > kGemmMaxLd || m <= 64 || (small && m <= 512)) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
 }
@@ -332,8 +338,6 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
         if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) path = W4A16_PATH_SKINNY;
     }
     if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) return W4A16_EUNSUPPORTED;
-    // INT8 weights run on the GEMV, SKINNY and (eight-wave) GEMM kernels
-    if (bits == 8 && path == W4A16_PATH_MGEMV) return W4A16_EUNSUPPORTED;
 
     const size_t xbytes = span_bytes(m, xcols, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
                  pbytes = bits == 8 ? w8a16_packed_bytes(n, k) : w4a16_packed_bytes(n, k),
@@ -366,7 +370,7 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
     if (path == W4A16_PATH_MGEMV) {
         for (int64_t r0 = 0; r0 < m; r0 += 16) {
             const int64_t mm = m - r0 < 16 ? m - r0 : 16;
-            const hipError_t e = launch_mgemv(xp + r0 * ldx, act, act_fn, mm, k, ldx, packed, n, bias,
+            const hipError_t e = launch_mgemv(xp + r0 * ldx, act, act_fn, bits, mm, k, ldx, packed, n, bias,
                                               yp + r0 * ldy, ldy, workspace, s);
             if (e != hipSuccess) return W4A16_EHIP;
         }

@@ -30,7 +30,7 @@ struct MgemvPlan {
     bool exchange;  // split finished through the header's exchange slots
     size_t lds, workspace;
 };
-MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k);
+MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 struct SkinnyPlan {
     int mb;             // 16-row m-subtiles per workgroup (1..4)
@@ -85,8 +85,8 @@ hipError_t launch_splitk_reduce(const float* partials, int splits, int64_t m, in
 hipError_t launch_gemv(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                        const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream);
-// m <= 16 per launch (the caller splits larger m into row blocks).
-hipError_t launch_mgemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+// m <= 16 per launch (the caller splits larger m into row blocks); bits 4 or 8.
+hipError_t launch_mgemv(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                         const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                         hipStream_t stream);
 hipError_t launch_skinny(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,

@@ -60,10 +60,13 @@ __device__ inline f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
 
 // MMAX: rows of x staged (>= m, <= 16).  AF: activation fused into the x
 // staging (ActFn; SwiGLU gate values sit k columns after the up values).
-template <int MMAX, int ACT, int CPW, int AF>
+// BITS: 4 (INT4 chunks) or 8 (INT8 chunks, two 1 KB halves; each k-step's
+// B operand is two words of byte codes, u = q + 128).
+template <int MMAX, int ACT, int CPW, int AF, int BITS>
 __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
     extern __shared__ __align__(16) unsigned char smem[];
-    const Layout L(a.n, a.k);
+    const Layout L(a.n, a.k, BITS);
     const int split = int(blockIdx.x % unsigned(a.splits));
     const int64_t t = int64_t(blockIdx.x / unsigned(a.splits));
     const int64_t g0 = int64_t(split) * a.gps;
@@ -81,13 +84,13 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     const int wave = uniform(tid >> 6), lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
 
-    const uint8_t* cbase = a.packed + (t * L.groups + g0) * kChunkBytes + lane * 16;
+    const uint8_t* cbase = a.packed + (t * L.groups + g0) * CB + lane * 16;
     const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (t * L.groups + g0) * kTileRows + r;
 
     // Every chunk of the wave (CPW of them) is loaded before any is used.
     // The loads are unconditional straight-line code (clamped addresses), so
     // the compiler's wait counts stay exact: each use waits for its own load.
-    uint4 cw[CPW];
+    uint4 cw[CPW][H];
     float sc[CPW];
 
     // x slice first, then the first weight batch (loads complete in issue
@@ -119,7 +122,8 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * kMgWaves;
         const int gc = gl < ng ? gl : ng - 1;  // a valid chunk; unused when gl >= ng
-        cw[u] = *reinterpret_cast<const uint4*>(cbase + int64_t(gc) * kChunkBytes);
+#pragma unroll
+        for (int h = 0; h < H; ++h) cw[u][h] = *reinterpret_cast<const uint4*>(cbase + int64_t(gc) * CB + h * kChunkBytes);
         sc[u] = sbase[int64_t(gc) * kTileRows];
     }
 
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     }
     lds_barrier();
 
-    constexpr float off = code_offset<ACT>();
+    constexpr float off = code_offset<ACT, BITS>();
     const uint32_t noff2 = uint32_t(from_f32<ACT>(-off)) * 0x00010001u;
     const uint4 bneg = make_uint4(noff2, noff2, noff2, noff2);  // -off in every element
     const bool row_on = r < m;
@@ -146,15 +150,21 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * kMgWaves;
         if (gl < ng) {
-            const uint32_t words[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+            uint32_t words[4 * H];
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                words[4 * h] = cw[u][h].x;
+                words[4 * h + 1] = cw[u][h].y;
+                words[4 * h + 2] = cw[u][h].z;
+                words[4 * h + 3] = cw[u][h].w;
+            }
             const float scale = sc[u];
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 uint4 av = make_uint4(0u, 0u, 0u, 0u);
                 if (row_on) av = *reinterpret_cast<const uint4*>(xrow + gl * kGroup + 32 * s);
-                const uint4 bv = make_uint4(magic_pair<ACT>(words[s], 0), magic_pair<ACT>(words[s], 1),
-                                            magic_pair<ACT>(words[s], 2), magic_pair<ACT>(words[s], 3));
+                const uint4 bv = bpairs<BITS, ACT>(words, s);
                 acc = mfma_16x16x32<ACT>(av, bv, acc);
                 acc = mfma_16x16x32<ACT>(av, bneg, acc);
             }
@@ -208,16 +218,18 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
 
 // Same plan shape as the v_dot2 kernel: split K only when the row tiles
 // cannot fill the chip; the x slice stays within 16 rows x 2048 columns.
-MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k) {
+MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits) {
     MgemvPlan p{};
-    const Layout L(n, k);
+    const Layout L(n, k, bits);
     p.mmax = m <= 4 ? 4 : m <= 8 ? 8 : 16;
     int64_t splits = 1;
     if (L.tiles < 512) splits = ceil_div(512, L.tiles);
     int64_t gps = ceil_div(L.groups, splits);
     if (gps < 2 * kMgWaves) gps = 2 * kMgWaves;
     int64_t max_gps = 128 / m;                       // x slice <= kXRegs loads per thread
-    if (max_gps > kMgChunks * kMgWaves) max_gps = kMgChunks * kMgWaves;  // chunks per wave
+    // chunks per wave held in registers (INT8 chunks take twice the registers)
+    const int64_t wave_chunks = bits == 8 ? kMgChunks / 2 : kMgChunks;
+    if (max_gps > wave_chunks * kMgWaves) max_gps = wave_chunks * kMgWaves;
     if (gps > max_gps) gps = max_gps;
     if (gps > L.groups) gps = L.groups;
     p.gps = int(gps);
@@ -233,15 +245,19 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-template <int MMAX, int ACT, int AF>
+template <int MMAX, int ACT, int AF, int BITS>
 static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t stream) {
-    const Layout L(a.n, a.k);
+    const Layout L(a.n, a.k, BITS);
     const dim3 grid(unsigned(L.tiles * p.splits)), block(kMgThreads);
     switch (p.cpw) {
-        case 1: mgemv_kernel<MMAX, ACT, 1, AF><<<grid, block, p.lds, stream>>>(a); break;
-        case 2: mgemv_kernel<MMAX, ACT, 2, AF><<<grid, block, p.lds, stream>>>(a); break;
-        case 4: mgemv_kernel<MMAX, ACT, 4, AF><<<grid, block, p.lds, stream>>>(a); break;
-        default: mgemv_kernel<MMAX, ACT, 8, AF><<<grid, block, p.lds, stream>>>(a); break;
+        case 1: mgemv_kernel<MMAX, ACT, 1, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        case 2: mgemv_kernel<MMAX, ACT, 2, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        case 4: mgemv_kernel<MMAX, ACT, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        default:
+            // the INT8 plan holds at most 4 chunks per wave
+            if constexpr (BITS == 4) mgemv_kernel<MMAX, ACT, 8, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+            else return hipErrorInvalidValue;
+            break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.exchange) return e;
@@ -249,19 +265,32 @@ static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t
                                 ACT, stream);
 }
 
-template <int MMAX, int ACT>
+template <int MMAX, int ACT, int BITS>
 static hipError_t launch_af(const MgemvArgs& a, const MgemvPlan& p, int act_fn, hipStream_t stream) {
     switch (act_fn) {
-        case kActFnSwiglu: return launch_one<MMAX, ACT, kActFnSwiglu>(a, p, stream);
-        case kActFnGeluTanh: return launch_one<MMAX, ACT, kActFnGeluTanh>(a, p, stream);
-        default: return launch_one<MMAX, ACT, kActFnNone>(a, p, stream);
+        case kActFnSwiglu: return launch_one<MMAX, ACT, kActFnSwiglu, BITS>(a, p, stream);
+        case kActFnGeluTanh: return launch_one<MMAX, ACT, kActFnGeluTanh, BITS>(a, p, stream);
+        default: return launch_one<MMAX, ACT, kActFnNone, BITS>(a, p, stream);
     }
 }
 
-hipError_t launch_mgemv(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx,
+template <int BITS>
+static hipError_t launch_bits(const MgemvArgs& a, const MgemvPlan& p, int act, int act_fn, hipStream_t stream) {
+    const bool bf = act == kActBf16;
+    switch (p.mmax) {
+        case 4: return bf ? launch_af<4, kActBf16, BITS>(a, p, act_fn, stream)
+                          : launch_af<4, kActF16, BITS>(a, p, act_fn, stream);
+        case 8: return bf ? launch_af<8, kActBf16, BITS>(a, p, act_fn, stream)
+                          : launch_af<8, kActF16, BITS>(a, p, act_fn, stream);
+        default: return bf ? launch_af<16, kActBf16, BITS>(a, p, act_fn, stream)
+                           : launch_af<16, kActF16, BITS>(a, p, act_fn, stream);
+    }
+}
+
+hipError_t launch_mgemv(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                         const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                         hipStream_t stream) {
-    const MgemvPlan p = plan_mgemv(m, n, k);
+    const MgemvPlan p = plan_mgemv(m, n, k, bits);
     MgemvArgs a;
     a.x = static_cast<const uint16_t*>(x);
     a.ldx = ldx;
@@ -277,12 +306,7 @@ hipError_t launch_mgemv(const void* x, int act, int act_fn, int64_t m, int64_t k
     a.splits = p.splits;
     a.gps = p.gps;
     a.exchange = p.exchange;
-    const bool bf = act == kActBf16;
-    switch (p.mmax) {
-        case 4: return bf ? launch_af<4, kActBf16>(a, p, act_fn, stream) : launch_af<4, kActF16>(a, p, act_fn, stream);
-        case 8: return bf ? launch_af<8, kActBf16>(a, p, act_fn, stream) : launch_af<8, kActF16>(a, p, act_fn, stream);
-        default: return bf ? launch_af<16, kActBf16>(a, p, act_fn, stream) : launch_af<16, kActF16>(a, p, act_fn, stream);
-    }
+    return bits == 8 ? launch_bits<8>(a, p, act, act_fn, stream) : launch_bits<4>(a, p, act, act_fn, stream);
 }
 
 }  // namespace w4a16
