@@ -14,12 +14,13 @@ pytestmark = pytest.mark.gpu
 # (m, n, k, act, bits, path): GEMV with a K split finished through the
 # exchange slots, MGEMV split, SKINNY split + reduce kernel, GEMM, a fused
 # SwiGLU input, the GEMM path with a materialised GELU input; INT8 weights on
-# the GEMV (eight-part split), SKINNY and 256 x 256 GEMM paths
+# the GEMV (eight-part split), MGEMV (split through the exchange slots),
+# SKINNY and 256 x 256 GEMM paths
 CALLS = [(1, 2048, 16384, "NONE", 4, "AUTO"), (6, 520, 8192, "NONE", 4, "AUTO"),
          (50, 1000, 4096, "NONE", 4, "AUTO"), (300, 2056, 1152, "NONE", 4, "GEMM"),
          (1, 1024, 4096, "SWIGLU", 4, "AUTO"), (256, 512, 1024, "GELU_TANH", 4, "GEMM"),
-         (1, 2048, 16384, "NONE", 8, "AUTO"), (50, 1000, 4096, "SWIGLU", 8, "AUTO"),
-         (300, 2056, 1152, "GELU_TANH", 8, "GEMM")]
+         (1, 2048, 16384, "NONE", 8, "AUTO"), (4, 2048, 16384, "NONE", 8, "MGEMV"),
+         (50, 1000, 4096, "SWIGLU", 8, "AUTO"), (300, 2056, 1152, "GELU_TANH", 8, "GEMM")]
 
 
 def test_graph_replays_equal_eager(dev=None):
