@@ -6,8 +6,8 @@
   * packing: round trip on arbitrary bytes (code -128 included), and the
     packed bytes equal the layout documented in the library's headers,
     built here from that description;
-  * the linear layer on the three INT8 kernel paths (GEMV, SKINNY, and the
-    256 x 256 GEMM) and the automatic choice: exact-arithmetic cases bit for bit (integer codes with
+  * the linear layer on the four INT8 kernel paths (GEMV, the MFMA small-M
+    kernel, SKINNY, and the 256 x 256 GEMM) and the automatic choice: exact-arithmetic cases bit for bit (integer codes with
     scale 2^-3 and small integer activations make every partial sum exact),
     random ragged cases within the tolerance of tests/gpu_util.py, fused
     activations, K splits through the exchange slots and through partial
