@@ -592,12 +592,12 @@ def main():
         text = "\n".join([
             "# HBM traffic of the gate_up GEMV at M = 1 (K 2048, N 32768, bf16)",
             "",
-            "Commands (MI355X, one GPU; R = repository root, databases under $R/gpurun_out):",
+            "Commands (MI355X, one GPU; R = repository root, OUT = an output directory):",
             "",
             "    cd /tmp && export TMPDIR=/tmp",
-            "    timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch -o run -- python3 $R/bench.py --traffic-probe",
-            "    timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write -o run -- python3 $R/bench.py --traffic-probe",
-            "    python3 $R/bench.py --summarize-traffic $R/gpurun_out/pmc_fetch/run_results.db $R/gpurun_out/pmc_write/run_results.db",
+            "    timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_fetch -o run -- python3 $R/bench.py --traffic-probe",
+            "    timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_write -o run -- python3 $R/bench.py --traffic-probe",
+            "    python3 $R/bench.py --summarize-traffic $OUT/pmc_fetch/run_results.db $OUT/pmc_write/run_results.db",
             "",
             "The probe launches the GEMV 16 times over distinct weight copies and an",
             "elementwise kernel that reads and writes exactly 256 MiB; each counter is",
