@@ -107,8 +107,12 @@ w4a16_status_t quantize_rtn_int4_g128(const void* w, w4a16_dtype_t w_dtype, int6
 /*
  * Size in bytes of the packed weight for an [n][k] layer (k % 128 == 0),
  * or 0 for invalid sizes.  The packed layout is the library's own execution
- * format (the "physical" form of the weight); it is not a storage format:
- * store codes and scales, and pack after loading.
+ * format: a quantized weight carries a layout of its own that a plain 16-bit
+ * GEMM cannot execute ("Kernel dispatch and Humming quantization in PhyAI",
+ * section "Humming makes the separation useful"), the physical form of a
+ * weight whose semantic form is its codes and scales ("量化概述", section
+ * "量化").  It is not a storage format: store codes and scales, and pack
+ * after loading.  Pure host arithmetic; no error status (0 marks bad sizes).
  */
 size_t w4a16_packed_bytes(int64_t n, int64_t k);
 
@@ -126,7 +130,14 @@ w4a16_status_t pack_weights(const uint8_t* codes, const float* scales, int64_t n
 
 /*
  * Inverse of pack_weights: packed layout -> canonical codes and scales,
- * bit-exact.  Same argument rules as pack_weights.
+ * bit-exact (the lowering from the semantic to the physical form loses
+ * nothing, "量化概述", section "量化"; nibble and packed-pair order are
+ * preserved, "Piper Kernels", section "NVFP4 construction").
+ *   packed  device, w4a16_packed_bytes(n, k) bytes from pack_weights; 16-byte aligned.
+ *   codes   device output, [n][k/2] canonical bytes; 4-byte aligned.
+ *   scales  device output, [n][k/128] FP32; 4-byte aligned; codes and scales
+ *           must not overlap each other or packed.
+ * n == 0 is a no-op.  Returns W4A16_OK, W4A16_EINVAL or W4A16_EHIP.
  */
 w4a16_status_t unpack_weights(const void* packed, int64_t n, int64_t k, uint8_t* codes,
                               float* scales, void* stream);
@@ -188,7 +199,12 @@ w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, in
 
 /*
  * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
- * kernel path (0 if none).  A K split needs it: a 1 MiB header of exchange
+ * kernel path (0 if none, also for invalid sizes).  The caller owns it: the
+ * library allocates nothing and reads nothing back ("Piper Kernels", section
+ * "Validation contract": no temporary device allocations, no
+ * synchronization, nothing that would stop graph capture; "Kernel dispatch
+ * and Humming quantization in PhyAI", section "A kernel choice belongs to a
+ * workload": a kernel used inside a graph must support capture).  A K split needs it: a 1 MiB header of exchange
  * slots through which the small-M kernels add the parts' sums inside one
  * launch, then FP32 partial sums that a second small kernel adds in split
  * order (no floating-point atomics either way).  The caller zero-fills a
@@ -203,6 +219,13 @@ size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
  * y[m][n] = x[m][k] . dequant(packed)^T + bias[n], with
  * dequant(q, s)[n][k] = q[n][k] * s[n][k / 128]; FP32 accumulation; the bias
  * is added in FP32 once; the result is rounded to act_dtype (nearest even).
+ * The W4A16 layer: INT4 weights with one scale per group of 128, BF16 or
+ * FP16 activations ("Kernel dispatch and Humming quantization in PhyAI",
+ * section "Humming makes the separation useful"); weight [out_features,
+ * in_features], input [..., in_features], output [..., out_features] in the
+ * input's dtype ("Piper Kernels", section "ConvRot INT8"); scales and bias
+ * in FP32 before the one final 16-bit conversion ("Piper Kernels", section
+ * "NVFP4 construction").
  *
  *   x         device, [m][ldx] of act_dtype (BF16 or F16), 16-byte aligned, ldx >= k,
  *             ldx % 8 == 0.
@@ -344,7 +367,14 @@ w4a16_status_t w8a16_linear(w4a16_act_t act, w4a16_path_t path, const void* x, w
 /* The path w8a16_linear takes for these sizes with W4A16_PATH_AUTO. */
 w4a16_path_t w8a16_linear_choose_path(int64_t m, int64_t n, int64_t k);
 
-/* Static, human-readable text for a status code. */
+/*
+ * Static, human-readable text for a status code ("unknown status" for values
+ * outside w4a16_status_t).  Errors cross the ABI as status codes only, and
+ * each names a concrete reason ("Kernel dispatch and Humming quantization in
+ * PhyAI", section "Put deployment choices in a policy": an unsupported
+ * layout or a capture restriction becomes a concrete diagnosis).  The
+ * returned string is owned by the library; never NULL.
+ */
 const char* w4a16_status_string(w4a16_status_t status);
 
 #ifdef __cplusplus

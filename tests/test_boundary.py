@@ -325,3 +325,86 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         w4.quantize(torch.zeros(16, 128))
+
+
+def test_status_maps_to_exception_type(lib):
+    # EINVAL, EUNSUPPORTED and EWORKSPACE reject a request from its
+    # arguments: ValueError; EHIP is a runtime failure: RuntimeError
+    for status in (B.EINVAL, B.EUNSUPPORTED, B.EWORKSPACE):
+        with pytest.raises(ValueError) as ei:
+            B._check(status, "call")
+        assert ei.value.status == status and not isinstance(ei.value, RuntimeError)
+        assert isinstance(ei.value, w4.W4A16Error)
+    with pytest.raises(RuntimeError) as ei:
+        B._check(B.EHIP, "call")
+    assert ei.value.status == B.EHIP and not isinstance(ei.value, ValueError)
+    B._check(B.OK, "call")  # no exception
+
+
+def test_binding_checks_tensor_sizes_before_any_launch(lib):
+    """Every size, dtype and shape mismatch between a tensor and the (n, k,
+    bits) passed with it is rejected on the host, before the device check and
+    before any launch (so these run without a GPU, on CPU tensors)."""
+    import torch
+    n, k = 40, 256
+    p4 = torch.zeros(w4.packed_bytes(n, k), dtype=torch.uint8)
+    x = torch.zeros(3, k, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.linear(x, p4[:-64], n)                            # packed too small for (n, k)
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.linear(x, p4, n + 16)                             # n larger than the packed weight
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.linear(x, p4, n, bits=8)                          # an INT4 weight passed as INT8
+    with pytest.raises(ValueError, match="packed must be torch.uint8"):
+        w4.linear(x, p4.view(torch.int8), n)
+    with pytest.raises(ValueError, match="bias"):
+        w4.linear(x, p4, n, torch.zeros(n, dtype=torch.float16))
+    with pytest.raises(ValueError, match="out must"):
+        w4.linear(x, p4, n, out=torch.zeros(3, n + 1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="contiguous"):
+        w4.linear(x, p4, n, out=torch.zeros(n, 3, dtype=torch.bfloat16).t())
+    with pytest.raises(ValueError, match="on a GPU"):
+        w4.linear(x, p4, n)                                  # everything matches: only the device is wrong
+    codes = torch.zeros(n, k // 2, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="scales must be torch.float32"):
+        w4.pack(codes, torch.zeros(n, k // 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="scales must have shape"):
+        w4.pack(codes, torch.zeros(n, k // 128 + 1, dtype=torch.float32))
+    with pytest.raises(ValueError, match="codes must be torch.uint8"):
+        w4.pack(codes.view(torch.int8), torch.zeros(n, k // 128, dtype=torch.float32))
+    with pytest.raises(ValueError, match="scales must have shape"):
+        w4.pack_int8(torch.zeros(n, k, dtype=torch.int8), torch.zeros(n + 1, k // 128, dtype=torch.float32))
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.unpack(p4[:100], n, k)
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.unpack_int8(p4, n, k)                             # INT4-sized buffer read as INT8
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.shard(p4[:1000], n, k, 0, 0, 16)
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.update_(p4[:1000], n, k, update=torch.zeros(n, k))
+    with pytest.raises(ValueError, match="update must be"):
+        w4.update_(p4, n, k, update=torch.zeros(n + 1, k))   # in place: a wrong n would write past packed
+    with pytest.raises(ValueError, match="mat1"):
+        w4.update_(p4, n, k, mat1=torch.zeros(n + 1, 4), mat2=torch.zeros(4, k))
+    with pytest.raises(ValueError, match="either update"):
+        w4.update_(p4, n, k)
+
+
+def test_captured_call_needs_an_explicit_workspace(lib, monkeypatch):
+    """Under graph capture a call whose plan needs a workspace must be given
+    one (allocated and zero-filled before the capture); calls that need none
+    are unaffected.  Checked from metadata before anything else."""
+    import torch
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    n, k = 2048, 16384          # M = 1, K split across workgroups: needs a workspace
+    assert w4.workspace_bytes(1, n, k) > 0
+    p = torch.zeros(w4.packed_bytes(n, k), dtype=torch.uint8)
+    x = torch.zeros(1, k, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="graph capture"):
+        w4.linear(x, p, n)
+    with pytest.raises(ValueError, match="on a GPU"):       # explicit workspace: past the capture rule
+        w4.linear(x, p, n, workspace=torch.zeros(w4.workspace_bytes(1, n, k), dtype=torch.uint8))
+    n2, k2 = 4096, 256          # two groups: no path splits K, no workspace needed
+    assert w4.workspace_bytes(1, n2, k2) == 0
+    with pytest.raises(ValueError, match="on a GPU"):
+        w4.linear(torch.zeros(1, k2, dtype=torch.bfloat16), torch.zeros(w4.packed_bytes(n2, k2), dtype=torch.uint8), n2)

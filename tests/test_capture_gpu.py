@@ -71,3 +71,48 @@ def test_graph_replays_equal_eager(dev=None):
         # eager work between replays (same workspace, other shapes)
         w4.linear(setups[2][6], setups[2][7], setups[2][1], workspace=ws)
         torch.cuda.synchronize()
+
+
+def test_two_graphs_without_workspace():
+    """Calls that need no workspace capture with workspace=None: two graphs
+    captured one after the other, each replayed several times between eager
+    work, equal the eager results bit for bit.  (A call that needs a
+    workspace is refused under capture without one: a host check, tested in
+    test_boundary.py.)"""
+    dev = require_gpu()
+    import weight_only_int4_rtn_amd as w4
+    g = torch.Generator().manual_seed(12)
+    # (m, n, k): GEMV and MGEMV at two groups, SKINNY, GEMM - no K split anywhere
+    shapes = [[(1, 4096, 256), (3, 1040, 128)], [(40, 2056, 256), (300, 512, 128)]]
+    setups = []
+    for group in shapes:
+        calls = []
+        for m, n, k in group:
+            assert w4.workspace_bytes(m, n, k) == 0
+            c, s = w4.quantize((torch.randn(n, k, generator=g) * 0.02).to(dev))
+            x = torch.randn(m, k, generator=g).to(torch.bfloat16).to(dev)
+            calls.append((x, w4.pack(c, s), n, torch.empty(m, n, dtype=torch.bfloat16, device=dev)))
+        setups.append(calls)
+    eager = []
+    for calls in setups:
+        eager.append([w4.linear(x, p, n).clone() for x, p, n, _ in calls])
+    torch.cuda.synchronize()
+    graphs = []
+    for calls in setups:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for x, p, n, y in calls:
+                w4.linear(x, p, n, out=y)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for gi, (gr, calls) in enumerate(zip(graphs, setups)):
+            say(f"graph {gi} replay {rep}")
+            for *_, y in calls:
+                y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            for ci, (*_, y) in enumerate(calls):
+                assert torch.equal(y, eager[gi][ci]), f"graph {gi} replay {rep} call {ci}"
+            w4.linear(setups[0][0][0], setups[0][0][1], setups[0][0][2])  # eager work between replays

@@ -22,7 +22,9 @@ from ._binding import (  # noqa: F401
     GROUP,
     Act,
     Path,
+    W4A16ArgumentError,
     W4A16Error,
+    W4A16LaunchError,
     choose_path,
     lib,
     linear,

@@ -36,10 +36,21 @@ class Act(enum.IntEnum):
     GELU_TANH = 2   # tanh-approximate GELU of the input
 
 
-class W4A16Error(RuntimeError):
+class W4A16Error(Exception):
+    """A status other than W4A16_OK from the C ABI; ``status`` holds it."""
+
     def __init__(self, status: int, what: str):
         self.status = status
         super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class W4A16ArgumentError(W4A16Error, ValueError):
+    """W4A16_EINVAL, W4A16_EUNSUPPORTED or W4A16_EWORKSPACE: the request was
+    rejected from its arguments before anything was launched."""
+
+
+class W4A16LaunchError(W4A16Error, RuntimeError):
+    """W4A16_EHIP: the HIP runtime reported an error at launch."""
 
 
 _lib = None
@@ -116,8 +127,26 @@ def status_string(status: int) -> str:
 
 
 def _check(status: int, what: str):
-    if status != OK:
-        raise W4A16Error(status, what)
+    if status == OK:
+        return
+    if status in (EINVAL, EUNSUPPORTED, EWORKSPACE):
+        raise W4A16ArgumentError(status, what)
+    raise W4A16LaunchError(status, what)
+
+
+def _need(t, dtype, what: str, nbytes: int | None = None, shape=None):
+    """Host-side checks of a tensor argument before any launch: dtype, shape,
+    and at least ``nbytes`` bytes of storage from its data pointer."""
+    if t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if nbytes is not None:
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise ValueError(f"{what} holds {have} bytes, the layer needs {nbytes}")
 
 
 def _ptr(t):
@@ -177,37 +206,58 @@ def choose_path(m: int, n: int, k: int, bits: int = 4) -> Path:
     return Path(lib().w4a16_linear_choose_path(m, n, k))
 
 
-def quantize(w: torch.Tensor):
-    """RTN INT4 g128: w [n, k] (f32/bf16/f16, rows contiguous) -> (codes [n, k/2] uint8, scales [n, k/128] f32)."""
-    _require_cuda(w)
+def quantize(w: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """RTN INT4 g128: w [n, k] (f32/bf16/f16, rows contiguous) -> (codes [n, k/2] uint8, scales [n, k/128] f32).
+    ``codes`` and ``scales`` may be given as preallocated outputs."""
     if w.dim() != 2 or w.stride(1) != 1:
         raise ValueError("w must be a 2-D tensor with contiguous rows")
     n, k = w.shape
-    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=w.device)
+    if codes is not None:
+        _need(codes, torch.uint8, "codes", shape=(n, k // 2))
+    if scales is not None:
+        _need(scales, torch.float32, "scales", shape=(n, k // GROUP))
+    _require_cuda(w, codes, scales)
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=w.device)
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes and scales must be contiguous")
     st = lib().quantize_rtn_int4_g128(_ptr(w), _w_tag(w.dtype), n, k, w.stride(0), _ptr(codes),
                                       _ptr(scales), _stream(w.device))
     _check(st, "quantize_rtn_int4_g128")
     return codes, scales
 
 
-def pack(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
-    """Canonical codes [n, k/2] + scales [n, k/128] -> packed execution layout (uint8, 1-D)."""
-    _require_cuda(codes, scales)
+def pack(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Canonical codes [n, k/2] + scales [n, k/128] -> packed execution layout (uint8, 1-D);
+    ``out`` may be a preallocated uint8 buffer of at least packed_bytes(n, k) bytes."""
+    if codes.dim() != 2:
+        raise ValueError("codes must be a 2-D [n, k/2] uint8 tensor")
     n, half = codes.shape
     k = 2 * half
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float32, "scales", shape=(n, k // GROUP))
+    _require_cuda(codes, scales)
     codes = codes.contiguous()
     scales = scales.contiguous()
     nbytes = packed_bytes(n, k)
     if nbytes == 0 and n > 0:
         raise ValueError(f"invalid layer shape n={n}, k={k}")
-    packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    if out is not None:
+        _need(out, torch.uint8, "out", nbytes)
+        _require_cuda(out)
+        packed = out
+    else:
+        packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
     st = lib().pack_weights(_ptr(codes), _ptr(scales), n, k, _ptr(packed), _stream(codes.device))
     _check(st, "pack_weights")
     return packed
 
 
 def unpack(packed: torch.Tensor, n: int, k: int):
+    """Packed INT4 weight -> canonical (codes [n, k/2] uint8, scales [n, k/128] f32)."""
+    _need(packed, torch.uint8, "packed", packed_bytes(n, k))
     _require_cuda(packed)
     codes = torch.empty((n, k // 2), dtype=torch.uint8, device=packed.device)
     scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=packed.device)
@@ -218,9 +268,9 @@ def unpack(packed: torch.Tensor, n: int, k: int):
 
 def quantize_int8(w: torch.Tensor):
     """RTN INT8 g128: w [n, k] (f32/bf16/f16, rows contiguous) -> (codes [n, k] int8, scales [n, k/128] f32)."""
-    _require_cuda(w)
     if w.dim() != 2 or w.stride(1) != 1:
         raise ValueError("w must be a 2-D tensor with contiguous rows")
+    _require_cuda(w)
     n, k = w.shape
     codes = torch.empty((n, k), dtype=torch.int8, device=w.device)
     scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=w.device)
@@ -232,10 +282,11 @@ def quantize_int8(w: torch.Tensor):
 
 def pack_int8(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
     """INT8 codes [n, k] + scales [n, k/128] -> packed INT8 execution layout (uint8, 1-D)."""
-    _require_cuda(codes, scales)
-    if codes.dtype != torch.int8:
-        raise ValueError("INT8 codes must be torch.int8")
+    if codes.dtype != torch.int8 or codes.dim() != 2:
+        raise ValueError("INT8 codes must be a 2-D [n, k] torch.int8 tensor")
     n, k = codes.shape
+    _need(scales, torch.float32, "scales", shape=(n, k // GROUP))
+    _require_cuda(codes, scales)
     codes = codes.contiguous()
     scales = scales.contiguous()
     nbytes = packed_bytes(n, k, 8)
@@ -248,6 +299,8 @@ def pack_int8(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
 
 
 def unpack_int8(packed: torch.Tensor, n: int, k: int):
+    """Packed INT8 weight -> canonical (codes [n, k] int8, scales [n, k/128] f32)."""
+    _need(packed, torch.uint8, "packed", packed_bytes(n, k, 8))
     _require_cuda(packed)
     codes = torch.empty((n, k), dtype=torch.int8, device=packed.device)
     scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=packed.device)
@@ -264,21 +317,26 @@ def update_(packed: torch.Tensor, n: int, k: int, update: torch.Tensor | None = 
     rounding when ``seed`` (unsigned 64-bit) is given; ``bits=8`` for a
     packed INT8 weight."""
     bits = _bits(bits)
-    _require_cuda(packed, update, mat1, mat2)
+    _need(packed, torch.uint8, "packed", packed_bytes(n, k, bits))
+    if (update is None) == (mat1 is None or mat2 is None):
+        raise ValueError("pass either update, or mat1 and mat2")
     src = update if update is not None else mat1
     dt = _w_tag(src.dtype)
     rank = 0
     ldu = 0
     if update is not None:
-        if update.shape[-1] != k or update.stride(-1) != 1:
+        if update.dim() != 2 or tuple(update.shape) != (n, k) or update.stride(-1) != 1:
             raise ValueError("update must be [n, k] with unit column stride")
         ldu = update.stride(0)
     else:
+        if mat1.dim() != 2 or mat2.dim() != 2:
+            raise ValueError("mat1 [n, r] and mat2 [r, k] must be 2-D")
         mat1 = mat1.contiguous()
         mat2 = mat2.contiguous()
         if mat2.dtype != mat1.dtype or mat1.shape[0] != n or mat2.shape != (mat1.shape[1], k):
             raise ValueError("mat1 [n, r] and mat2 [r, k] of one dtype")
         rank = mat1.shape[1]
+    _require_cuda(packed, update, mat1, mat2)
     sp = None
     if seed is not None:
         sp = ctypes.pointer(ctypes.c_uint64(int(seed) & ((1 << 64) - 1)))
@@ -293,8 +351,9 @@ def shard(packed: torch.Tensor, n: int, k: int, dim: int, start: int, length: in
     """Rows [start, start+length) (dim 0) or group-aligned columns (dim 1) of a
     packed [n, k] weight (INT4, or INT8 with bits=8) as a new packed weight
     (no requantization)."""
-    _require_cuda(packed)
     bits = _bits(bits)
+    _need(packed, torch.uint8, "packed", packed_bytes(n, k, bits))
+    _require_cuda(packed)
     rows, cols = (length, k) if dim == 0 else (n, length)
     size = packed_bytes(rows, cols, bits)
     out = torch.empty(max(size, 16), dtype=torch.uint8, device=packed.device)
@@ -327,7 +386,6 @@ def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | N
     (x's dtype).  With ``act=Act.SWIGLU`` the rows of x are [up | gate], 2k values.
     ``bits=8``: ``packed`` is a packed INT8 weight (``pack_int8``)."""
     bits = _bits(bits)
-    _require_cuda(x, packed, bias, out)
     if x.requires_grad or (bias is not None and bias.requires_grad):
         raise ValueError("inference only: autograd inputs are not supported")
     act = Act(act)
@@ -345,15 +403,26 @@ def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | N
         if bias.dtype != x.dtype or bias.shape != (n,):
             raise ValueError("bias must have shape [n] and x's dtype")
         bias = bias.contiguous()
+    if out is not None:
+        if out.shape != (*lead, n) or out.dtype != x.dtype:
+            raise ValueError("out must have shape [..., n] and x's dtype")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    _need(packed, torch.uint8, "packed", packed_bytes(n, k, bits))
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    need = workspace_bytes(m, n, k, act, bits)
+    if workspace is None and need > 0 and torch.cuda.is_current_stream_capturing():
+        # a workspace allocated here would belong to the graph's memory pool
+        # and its zero fill would only run at replay: a captured call needs
+        # its own workspace, zero-filled before the capture
+        raise ValueError(f"this call needs a {need}-byte workspace: under graph capture pass a "
+                         "zero-filled workspace= allocated before the capture")
+    _require_cuda(x, packed, bias, out, workspace)
     if out is None:
         out = torch.empty((*lead, n), dtype=x.dtype, device=x.device)
-    elif out.shape != (*lead, n) or out.dtype != x.dtype:
-        raise ValueError("out must have shape [..., n] and x's dtype")
-    y2 = out.view(-1, n) if out.is_contiguous() else None
-    if y2 is None:
-        raise ValueError("out must be contiguous")
+    y2 = out.view(-1, n)
     stream = _stream(x.device)
-    need = workspace_bytes(m, n, k, act, bits)
     if workspace is None:
         workspace = workspace_for(x.device, stream.value, need)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

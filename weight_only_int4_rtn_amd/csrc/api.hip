@@ -316,9 +316,12 @@ size_t act_workspace_bytes(int act_fn, int64_t m, int64_t n, int64_t k, int bits
 
 // y = act(x) . dequant(packed)^T + bias on one kernel path (act_fn: ActFn;
 // bits: 4 or 8, the packed weight's code width).
+// launch == false: only the argument checks (the status a launching call
+// would return before launching anything).
 w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
                            int64_t m, int64_t k, int64_t ldx, const void* packed, int64_t n, const void* bias,
-                           void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+                           void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream,
+                           bool launch = true) {
     if (act_dtype != W4A16_BF16 && act_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
     if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MGEMV &&
         path != W4A16_PATH_SKINNY && path != W4A16_PATH_GEMM)
@@ -353,6 +356,7 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
             overlap(workspace, need, bias, bbytes))
             return W4A16_EINVAL;
     }
+    if (!launch) return W4A16_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int act = act_dtype == W4A16_BF16 ? kActBf16 : kActF16;
     const uint16_t* xp = static_cast<const uint16_t*>(x);
@@ -388,6 +392,17 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
 }
 
 }  // namespace
+
+namespace w4a16 {
+
+w4a16_status_t check_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, int64_t k, int64_t ldx,
+                            const void* packed, int64_t n, const void* bias, void* y, int64_t ldy,
+                            void* workspace, size_t workspace_bytes) {
+    return linear_impl(4, kActFnNone, W4A16_PATH_AUTO, x, act_dtype, m, k, ldx, packed, n, bias, y, ldy, workspace,
+                       workspace_bytes, nullptr, false);
+}
+
+}  // namespace w4a16
 
 extern "C" {
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "w4a16.h"
+
 namespace w4a16 {
 
 // Workspace of a K-split launch: a header of kSyncBytes holding the 64-bit
@@ -98,5 +100,12 @@ hipError_t launch_activate(const void* x, int act, int act_fn, int64_t m, int64_
 hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, int64_t ldx, const void* packed,
                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                        hipStream_t stream);
+
+// The argument checks of w4a16_linear alone (its status before any launch;
+// OK means the call would launch or is a no-op).  Declared here so other
+// entry points of the library can validate before their own set-up.
+w4a16_status_t check_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, int64_t k, int64_t ldx,
+                            const void* packed, int64_t n, const void* bias, void* y, int64_t ldy,
+                            void* workspace, size_t workspace_bytes);
 
 }  // namespace w4a16
