@@ -290,6 +290,29 @@ w4a16_status_t w4a16_linear_act(w4a16_act_t act, w4a16_path_t path, const void* 
                                 const void* bias, void* y, int64_t ldy, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * w4a16_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (minus the workspace), checks, kernels and bit-identical
+ * results as w4a16_linear; the workspace is instead a fixed array of
+ * W4A16_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends.  The call allocates nothing.  Its first call on a
+ * device looks the array's address up (hipGetSymbolAddress) and launches one
+ * small kernel on `stream` that zeroes the array's header.
+ *   - A call whose plan needs more workspace than the array holds returns
+ *     W4A16_EWORKSPACE before launching anything (the limit is a property
+ *     of the shape: w4a16_linear with a caller workspace takes any size).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls that may overlap on one GPU (several streams,
+ *     several host threads) race and must be serialised by the caller.
+ * Returns the statuses of w4a16_linear (W4A16_EUNSUPPORTED also for a device
+ * index of 64 or more).
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+w4a16_status_t w4a16_linear_noalloc(const void* x, w4a16_dtype_t act_dtype, int64_t m, int64_t k, int64_t ldx,
+                                    const void* packed, int64_t n, const void* bias, void* y, int64_t ldy,
+                                    void* stream);
+
 /* The path w4a16_linear would take for these sizes (never W4A16_PATH_AUTO). */
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k);
 

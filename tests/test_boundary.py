@@ -408,3 +408,14 @@ def test_captured_call_needs_an_explicit_workspace(lib, monkeypatch):
     assert w4.workspace_bytes(1, n2, k2) == 0
     with pytest.raises(ValueError, match="on a GPU"):
         w4.linear(torch.zeros(1, k2, dtype=torch.bfloat16), torch.zeros(w4.packed_bytes(n2, k2), dtype=torch.uint8), n2)
+
+
+def test_noalloc_scratch_size_matches_header(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define W4A16_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "W4A16_NOALLOC_SCRATCH_BYTES not found"
+    assert B.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    # the no-alloc call's host checks come before any device work
+    import torch
+    with pytest.raises(ValueError, match="packed holds"):
+        w4.linear_noalloc(torch.zeros(1, 256, dtype=torch.bfloat16), torch.zeros(100, dtype=torch.uint8), 16)

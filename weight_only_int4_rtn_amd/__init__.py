@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     choose_path,
     lib,
     linear,
+    linear_noalloc,
     pack,
     pack_int8,
     packed_bytes,

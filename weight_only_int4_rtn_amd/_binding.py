@@ -16,6 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 GROUP = 128
+NOALLOC_SCRATCH_BYTES = 32 << 20  # W4A16_NOALLOC_SCRATCH_BYTES of include/w4a16.h
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 F32, BF16, F16 = 0, 1, 2
@@ -82,6 +83,8 @@ def _declare(lib):
     lib.w4a16_linear_act_workspace_bytes.restype = sz
     lib.w4a16_linear_act.argtypes = [i32, i32, vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, sz, vp]
     lib.w4a16_linear_act.restype = i32
+    lib.w4a16_linear_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp]
+    lib.w4a16_linear_noalloc.restype = i32
     lib.w4a16_linear_choose_path.argtypes = [i64, i64, i64]
     lib.w4a16_linear_choose_path.restype = i32
     lib.quantize_rtn_int8_g128.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
@@ -438,4 +441,31 @@ def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | N
         st = lib().w4a16_linear_act(int(act), int(path), _ptr(x2), dt, m, k, x2.stride(0), _ptr(packed), n,
                                     _ptr(bias), _ptr(y2), n, _ptr(workspace), ws_bytes, stream)
     _check(st, "w4a16_linear_act" if act != Act.NONE else "w4a16_linear")
+    return out
+
+
+def linear_noalloc(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x . dequant(packed)^T + bias through w4a16_linear_noalloc: the
+    library's fixed per-GPU scratch array stands in for the workspace, so the
+    call allocates nothing (pass ``out`` to allocate nothing here either).
+    Calls that may overlap on one GPU race on that array."""
+    dt = _act_tag(x.dtype)
+    k = x.shape[-1]
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, k)
+    if x2.stride(-1) != 1:
+        raise ValueError("x rows must be contiguous")
+    m = x2.shape[0]
+    if bias is not None and (bias.dtype != x.dtype or bias.shape != (n,) or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [n] tensor of x's dtype")
+    if out is not None and (out.shape != (*lead, n) or out.dtype != x.dtype or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous [..., n] tensor of x's dtype")
+    _need(packed, torch.uint8, "packed", packed_bytes(n, k))
+    _require_cuda(x, packed, bias, out)
+    if out is None:
+        out = torch.empty((*lead, n), dtype=x.dtype, device=x.device)
+    st = lib().w4a16_linear_noalloc(_ptr(x2), dt, m, k, x2.stride(0), _ptr(packed), n, _ptr(bias),
+                                    _ptr(out.view(-1, n)), n, _stream(x.device))
+    _check(st, "w4a16_linear_noalloc")
     return out
