@@ -313,6 +313,36 @@ w4a16_status_t w4a16_linear_noalloc(const void* x, w4a16_dtype_t act_dtype, int6
                                     const void* packed, int64_t n, const void* bias, void* y, int64_t ldy,
                                     void* stream);
 
+/*
+ * The plan of one linear call: which kernel family runs and how its work is
+ * cut.  The library plans from (bits, act, m, n, k) alone, with no tuning
+ * and no state, so the same sizes always take the same plan and results are
+ * reproducible.
+ */
+typedef struct {
+    int32_t path;              /* the w4a16_path_t the call takes (never W4A16_PATH_AUTO) */
+    int32_t waves;             /* waves of 64 lanes per workgroup of the main kernel */
+    int32_t tile_m, tile_n;    /* x rows and output columns one workgroup computes */
+    int32_t splits;            /* parts K is split into (1: none) */
+    int32_t groups_per_split;  /* 128-column groups per part */
+    int64_t workgroups;        /* workgroups of one launch of the main kernel */
+    int64_t launches;          /* kernel launches of the whole call */
+    uint64_t workspace_bytes;  /* workspace this plan needs (<= w4a16_linear_act_workspace_bytes) */
+} w4a16_plan_t;
+
+/*
+ * Explains the plan w4a16_linear_act / w8a16_linear (bits 4 / 8) would run
+ * for an [m][k] input with contiguous rows and an [n][k] weight on `path`
+ * (W4A16_PATH_AUTO: the library's choice).  Pure host computation, no
+ * launch; the dispatcher can explain its decision ("Kernel dispatch and
+ * Humming quantization in PhyAI", section "Put deployment choices in a
+ * policy").  m == 0 or n == 0 report the path with zero launches.
+ *   plan  host pointer, filled on W4A16_OK.
+ * Returns W4A16_OK or W4A16_EINVAL (bits, act, path, sizes, NULL plan).
+ */
+w4a16_status_t w4a16_linear_explain(int bits, w4a16_act_t act, w4a16_path_t path, int64_t m, int64_t n, int64_t k,
+                                    w4a16_plan_t* plan);
+
 /* The path w4a16_linear would take for these sizes (never W4A16_PATH_AUTO). */
 w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k);
 

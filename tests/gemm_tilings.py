@@ -1,0 +1,32 @@
+"""Shapes that reach every tiling of the large-M path: (bits, waves, tile
+rows, tile columns, K split?) -> (m, n, k) with ragged M, N and K.  The plan
+of each shape is checked on the host (test_boundary.py), the results on the
+GPU (test_gemm_tiles_gpu.py)."""
+
+TILINGS = [
+    # (bits, waves, tile_m, tile_n, split, (m, n, k))
+    (4, 4, 64, 256, False, (130, 32772, 128)),
+    (4, 4, 64, 256, True, (257, 8200, 4096)),
+    (4, 4, 128, 256, False, (257, 32772, 128)),
+    (4, 8, 128, 128, False, (97, 136, 128)),
+    (4, 8, 128, 128, True, (97, 136, 640)),
+    (4, 8, 128, 256, False, (257, 16424, 128)),
+    (4, 8, 128, 256, True, (513, 4104, 2176)),
+    (4, 8, 256, 128, False, (130, 16424, 128)),
+    (4, 8, 256, 128, True, (1030, 520, 2176)),
+    (4, 8, 256, 256, False, (1000, 8200, 128)),
+    (4, 8, 256, 256, True, (1030, 2600, 4096)),
+    (8, 8, 128, 128, False, (97, 136, 128)),
+    (8, 8, 128, 128, True, (97, 136, 640)),
+    (8, 8, 128, 256, False, (257, 16424, 128)),
+    (8, 8, 128, 256, True, (513, 4104, 2176)),
+    (8, 8, 256, 128, False, (130, 16424, 128)),
+    (8, 8, 256, 128, True, (1030, 520, 2176)),
+    (8, 8, 256, 256, False, (130, 32772, 128)),
+    (8, 8, 256, 256, True, (1030, 2600, 4096)),
+]
+
+
+def tiling_id(t):
+    bits, waves, tm, tn, split, (m, n, k) = t
+    return f"int{bits}_{waves}w_{tm}x{tn}_{'split' if split else 'unsplit'}_m{m}_n{n}_k{k}"

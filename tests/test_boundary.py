@@ -419,3 +419,35 @@ def test_noalloc_scratch_size_matches_header(lib):
     import torch
     with pytest.raises(ValueError, match="packed holds"):
         w4.linear_noalloc(torch.zeros(1, 256, dtype=torch.bfloat16), torch.zeros(100, dtype=torch.uint8), 16)
+
+
+def test_explain_reports_the_plan(lib):
+    p = w4.explain(1, 32768, 2048)
+    assert p["path"] == w4.Path.GEMV and p["tile_n"] == 16 and p["splits"] == 1 and p["launches"] == 1
+    assert p["workgroups"] == 2048 and p["workspace_bytes"] == 0
+    p = w4.explain(1, 2048, 16384)          # K split over workgroups: exchange slots in the workspace
+    assert p["splits"] > 1 and p["workspace_bytes"] > 0
+    assert p["workspace_bytes"] <= w4.workspace_bytes(1, 2048, 16384)
+    p = w4.explain(6, 1024, 2048)           # MGEMV: one launch per 16-row block
+    assert p["path"] == w4.Path.MGEMV and p["tile_m"] == 6
+    assert w4.explain(40, 1024, 2048, path=w4.Path.GEMV)["launches"] >= 10
+    p = w4.explain(300, 2056, 1152, act=w4.Act.GELU_TANH, path=w4.Path.GEMM)
+    assert p["launches"] == (3 if p["splits"] > 1 else 2)  # activation, GEMM (+ reduce)
+    assert p["workspace_bytes"] >= 300 * 1152 * 2
+    assert w4.explain(0, 2048, 2048)["launches"] == 0
+    for bad in (dict(bits=2), dict(act=7), dict(path=9)):
+        with pytest.raises(ValueError):
+            w4.explain(4, 2048, 2048, **bad)
+    with pytest.raises(ValueError):
+        w4.explain(4, 2048, 100)
+
+
+@pytest.mark.parametrize("t", __import__("tests.gemm_tilings", fromlist=["TILINGS"]).TILINGS,
+                         ids=__import__("tests.gemm_tilings", fromlist=["tiling_id"]).tiling_id)
+def test_gemm_tiling_shapes_take_their_tiling(lib, t):
+    """The GPU tiling tests reach every tiling the planner can pick: each
+    listed shape takes exactly its tiling, so a planner change that moves one
+    fails here instead of silently dropping coverage."""
+    bits, waves, tm, tn, split, (m, n, k) = t
+    p = w4.explain(m, n, k, path=w4.Path.GEMM, bits=bits)
+    assert (p["waves"], p["tile_m"], p["tile_n"], p["splits"] > 1) == (waves, tm, tn, split), p

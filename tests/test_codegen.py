@@ -22,7 +22,7 @@ sys.path.insert(0, ROOT)
 from weight_only_int4_rtn_amd import build as libbuild  # noqa: E402
 
 CSRC = os.path.join(ROOT, "weight_only_int4_rtn_amd", "csrc")
-SOURCES = ("gemv.hip", "mgemv.hip", "skinny.hip", "gemm.hip")
+SOURCES = ("gemv.hip", "mgemv.hip", "skinny.hip", "gemm.hip", "gemm8_rows256.hip", "gemm8_rows128.hip")
 
 
 def _assembly(src, tmp_path):

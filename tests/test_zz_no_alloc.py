@@ -46,9 +46,10 @@ def test_noalloc_equals_linear_call_after_call():
 def test_noalloc_refuses_plans_beyond_the_scratch():
     dev = require_gpu()
     import weight_only_int4_rtn_amd as w4
-    # M = 4096, K = 16384, N = 2048 takes the GEMM split in two: 64 MiB of
-    # partial sums, more than the scratch array holds
-    m, n, k = 4096, 2048, 16384
+    # M = 1024, K = 16384, N = 2048 takes the GEMM with a K split whose FP32
+    # partial sums need more than the scratch array holds
+    m, n, k = 1024, 2048, 16384
+    assert w4.explain(m, n, k)["workspace_bytes"] > w4._binding.NOALLOC_SCRATCH_BYTES
     x = torch.zeros(m, k, dtype=torch.bfloat16, device=dev)
     p = torch.zeros(w4.packed_bytes(n, k), dtype=torch.uint8, device=dev)
     y = torch.full((m, n), 7.0, dtype=torch.bfloat16, device=dev)

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     W4A16Error,
     W4A16LaunchError,
     choose_path,
+    explain,
     lib,
     linear,
     linear_noalloc,

@@ -54,6 +54,13 @@ class W4A16LaunchError(W4A16Error, RuntimeError):
     """W4A16_EHIP: the HIP runtime reported an error at launch."""
 
 
+class PlanT(ctypes.Structure):
+    """w4a16_plan_t"""
+    _fields_ = [("path", ctypes.c_int32), ("waves", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("splits", ctypes.c_int32), ("groups_per_split", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("launches", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -85,6 +92,8 @@ def _declare(lib):
     lib.w4a16_linear_act.restype = i32
     lib.w4a16_linear_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp]
     lib.w4a16_linear_noalloc.restype = i32
+    lib.w4a16_linear_explain.argtypes = [i32, i32, i32, i64, i64, i64, ctypes.POINTER(PlanT)]
+    lib.w4a16_linear_explain.restype = i32
     lib.w4a16_linear_choose_path.argtypes = [i64, i64, i64]
     lib.w4a16_linear_choose_path.restype = i32
     lib.quantize_rtn_int8_g128.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
@@ -207,6 +216,16 @@ def choose_path(m: int, n: int, k: int, bits: int = 4) -> Path:
     if _bits(bits) == 8:
         return Path(lib().w8a16_linear_choose_path(m, n, k))
     return Path(lib().w4a16_linear_choose_path(m, n, k))
+
+
+def explain(m: int, n: int, k: int, act: Act = Act.NONE, path: Path = Path.AUTO, bits: int = 4) -> dict:
+    """The plan a linear call of these sizes runs (w4a16_linear_explain)."""
+    plan = PlanT()
+    _check(lib().w4a16_linear_explain(_bits(bits), int(act), int(path), m, n, k, ctypes.byref(plan)),
+           "w4a16_linear_explain")
+    out = {f: getattr(plan, f) for f, _ in PlanT._fields_}
+    out["path"] = Path(out["path"])
+    return out
 
 
 def quantize(w: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):

@@ -410,6 +410,43 @@ size_t w4a16_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     return act_workspace_bytes(kActFnNone, m, n, k, 4);
 }
 
+w4a16_status_t w4a16_linear_explain(int bits, w4a16_act_t act, w4a16_path_t path, int64_t m, int64_t n, int64_t k,
+                                    w4a16_plan_t* plan) {
+    if (!plan || (bits != 4 && bits != 8)) return W4A16_EINVAL;
+    if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return W4A16_EINVAL;
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MGEMV &&
+        path != W4A16_PATH_SKINNY && path != W4A16_PATH_GEMM)
+        return W4A16_EINVAL;
+    if (!valid_nk(n, k) || m < 0 || m > kMaxDim) return W4A16_EINVAL;
+    *plan = w4a16_plan_t{};
+    // rows contiguous: the GEMM sees a row stride of k (also for an activation,
+    // which it materialises with stride k)
+    if (path == W4A16_PATH_AUTO) {
+        path = bits == 8 ? w8a16_linear_choose_path(m, n, k) : w4a16_linear_choose_path(m, n, k);
+        if (path == W4A16_PATH_GEMM && k > kGemmMaxLd) path = W4A16_PATH_SKINNY;
+    }
+    plan->path = path;
+    if (m == 0 || n == 0) return W4A16_OK;
+    const int fn = int(act);
+    PlanInfo info{};
+    int64_t launches = 1;
+    switch (path) {
+        case W4A16_PATH_GEMV: info = describe_gemv(m < 4 ? m : 4, n, k, bits); launches = ceil_div(m, 4); break;
+        case W4A16_PATH_MGEMV: info = describe_mgemv(m < 16 ? m : 16, n, k, bits); launches = ceil_div(m, 16); break;
+        case W4A16_PATH_SKINNY: info = describe_skinny(m, n, k, bits); break;
+        default: info = describe_gemm(m, n, k, bits); break;
+    }
+    plan->waves = info.waves;
+    plan->tile_m = info.tile_m;
+    plan->tile_n = info.tile_n;
+    plan->splits = info.splits;
+    plan->groups_per_split = info.gps;
+    plan->workgroups = info.workgroups;
+    plan->launches = launches * (info.reduce ? 2 : 1) + (path == W4A16_PATH_GEMM && fn != kActFnNone ? 1 : 0);
+    plan->workspace_bytes = uint64_t(act_path_workspace(fn, path, m, n, k, bits));
+    return W4A16_OK;
+}
+
 size_t w4a16_linear_act_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64_t k) {
     if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return 0;
     return act_workspace_bytes(int(act), m, n, k, 4);

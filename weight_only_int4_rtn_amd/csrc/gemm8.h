@@ -1,0 +1,443 @@
+// Eight-wave large-M kernel: a BM x BN output tile per workgroup (BM, BN in
+// {128, 256}), eight waves of 64 lanes, one workgroup per CU.
+//
+// The K loop runs in stages of 64 (half a quantization group).  Per stage
+// the workgroup stages in LDS the x tile (BM rows x 64, by direct
+// global-to-LDS loads) and the B tile: the stage's weights dequantized to
+// 16-bit MFMA operands, BN/16 tiles x 2 k-steps x 64 lanes x 16 bytes.  Each
+// wave dequantizes BN/128 of the weight tiles (one word per lane per k-step,
+// written where the reading lane finds it), so each weight is dequantized
+// once per BM rows of x.  The waves form a WM x WN grid over the tile; a
+// wave owns a (BM/WM) x (BN/WN) block of outputs as 16 x 16 MFMA blocks
+// (v_mfma_f32_16x16x32_{bf16,f16}, FP32 accumulators):
+//   256 x 256: 2 x 4 waves of 128 x 64     256 x 128: 4 x 2 waves of 64 x 64
+//   128 x 256: 2 x 4 waves of  64 x 64     128 x 128: 2 x 4 waves of 64 x 32
+// Each D = W . x^T block puts four consecutive outputs of one x row in a
+// lane, which the epilogue stores together.
+//
+// Every stage runs its MFMA blocks, each followed by a slice of the next
+// stage's dequantization (a finished word goes to the next B tile).  The
+// barrier that publishes the next stage sits two blocks before the end of
+// the stage: past it the x pieces of the stage after next are issued into
+// the buffer just freed and the next stage's first fragments are read, both
+// overlapping the last two blocks (see `stage` below).
+//
+// INT8 weights: the same stages with a 16-byte run of each 1 KB chunk half
+// per stage (byte codes, u = q + 128, fma(u, s, -128 s)).
+//
+// The epilogue adds the bias in FP32 and rounds once to the output dtype
+// (through LDS as whole 16-byte rows when unsplit and aligned), or, for a K
+// split, stores FP32 partial sums for the split-K reduce kernel.
+#pragma once
+
+#include "gemm_common.h"
+
+namespace w4a16 {
+
+constexpr int kG8Threads = 512, kG8K = 64;
+
+template <int BM, int BN>
+struct G8Shape {
+    static constexpr int WN = (BM == 256 && BN == 128) ? 2 : 4;  // waves along N
+    static constexpr int WM = 8 / WN;                            // waves along M
+    static constexpr int WTM = BM / WM, WTN = BN / WN;           // a wave's output block
+    static constexpr int RB = WTM / 16, CB = WTN / 16;           // its 16 x 16 MFMA blocks
+    static constexpr int NT = BN / 16;                           // 16-column weight tiles of the workgroup
+    static constexpr int TPW = NT / 8;                           // weight tiles each wave dequantizes
+    static constexpr int XP = BM / 64;                           // 1 KB x pieces each wave loads per stage
+    static constexpr int SPI = 4 * TPW / RB;                     // dequantization quarter-words per MFMA block
+    static constexpr int XSTAGE = BM * kG8K;                     // 16-bit elements of an x stage
+    static constexpr int WSTAGE = NT * 2 * 64 * 16;              // bytes of a B stage
+    static constexpr int RX = BM * 64 / BN;                      // output rows an x buffer holds (epilogue)
+    static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile");
+    static_assert(SPI * 2 * RB == 8 * TPW && SPI >= 1, "dequantization slices");
+};
+
+// x stage layout: row r holds its 64 columns as 8 segments of 16 bytes,
+// segment c at position c ^ ((r >> 1) & 7): the 16 lanes of an operand read
+// (16 consecutive rows, one segment) cover all 64 banks once.
+__device__ inline int swz8(int row, int seg) { return row * kG8K + ((seg ^ ((row >> 1) & 7)) << 3); }
+
+// Waits for all but N vector memory operations and for all LDS operations.
+template <int N>
+__device__ inline void wait_vm_lds() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
+    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory");
+    else static_assert(N == 0, "unsupported count");
+}
+
+// BITS 8: INT8 chunks (two 1 KB halves, half h = stage 2g + h): a lane's
+// k-step is two words of four byte codes, u = q + 128.
+template <int ACT, bool STAGED, int BITS, int BM, int BN>
+__global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
+    using S = G8Shape<BM, BN>;
+    // Arrays the lambdas below capture are sized by these fixed maxima, not
+    // by the shape's constants: a captured array whose bound depends on the
+    // template arguments makes the host pass drop the kernel's launch stub.
+    constexpr int kMaxXP = 4, kMaxTPW = 2, kMaxRB = 8, kMaxCB = 4;
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
+    constexpr int RB = S::RB, CBL = S::CB, TPW = S::TPW, XP = S::XP, SPI = S::SPI, WTM = S::WTM, WN = S::WN,
+                  NT = S::NT;
+    __shared__ __align__(16) uint16_t X0[S::XSTAGE];
+    __shared__ __align__(16) uint16_t X1[S::XSTAGE];
+    __shared__ __align__(16) uint8_t W0[S::WSTAGE];
+    __shared__ __align__(16) uint8_t W1[S::WSTAGE];
+
+    const Layout L(a.n, a.k, BITS);
+    const int split = int(blockIdx.x % unsigned(a.splits));
+    const int64_t tile = int64_t(blockIdx.x / unsigned(a.splits));
+    const int64_t mt = tile % a.mtiles, nt = tile / a.mtiles;  // consecutive workgroups share weights
+    const int64_t m0 = mt * BM;
+    const int64_t g0 = int64_t(split) * a.gps;
+    const int ng = int(min<int64_t>(a.gps, L.groups - g0));
+    const int nstages = 2 * ng;
+
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // x: rows m0 .. m0 + BM - 1 through a buffer resource ending at row M
+    // (loads of rows past M fetch nothing; those rows only feed outputs never
+    // stored).  Piece p of wave w fills stage rows 8 (XP w + p) .. +7; lane i
+    // lands at row + i / 8, position i % 8.
+    const int64_t rows_valid = min<int64_t>(BM, a.m - m0);
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(a.x + m0 * a.ldx, rows_valid * a.ldx * 2);
+    static_assert(XP <= kMaxXP && TPW <= kMaxTPW && RB <= kMaxRB && CBL <= kMaxCB, "array maxima");
+    uint32_t xoff[kMaxXP];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int row = 8 * (XP * wave + p) + (lane >> 3);
+        xoff[p] = uint32_t(row * a.ldx * 2 + (((lane & 7) ^ ((row >> 1) & 7)) << 4));
+    }
+    auto load_x = [&](uint16_t* dst, int s) {
+        const int soff = uniform(int((g0 + (s >> 1)) * kGroup * 2 + (s & 1) * kG8K * 2));
+#pragma unroll
+        for (int p = 0; p < XP; ++p)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_ptr_t)(dst + (XP * wave + p) * 512), 16, xoff[p],
+                                                     soff, 0, 0);
+    };
+
+    // Weights: this wave dequantizes the workgroup's tiles TPW w .. TPW w +
+    // TPW - 1.  Tiles past N read the last tile again (clamped) with their
+    // scales zeroed.
+    const int64_t tw = nt * NT + TPW * wave;
+    const int validw = int(min<int64_t>(TPW, max<int64_t>(0, L.tiles - tw)));
+    const int64_t twfirst = min<int64_t>(tw, L.tiles - 1);
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(a.packed + twfirst * L.groups * CB, TPW * L.groups * CB);
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
+        a.packed + L.scale_offset() + twfirst * L.groups * kChunkScaleBytes, TPW * L.groups * kChunkScaleBytes);
+    uint32_t woff[kMaxTPW], soff[kMaxTPW];
+#pragma unroll
+    for (int c = 0; c < TPW; ++c) {
+        const int cc = c < validw ? c : (validw > 0 ? validw - 1 : 0);
+        woff[c] = uint32_t(cc * L.groups * CB + lane * 16);
+        soff[c] = uint32_t(cc * L.groups * kChunkScaleBytes + r * 4);
+    }
+    struct Words {
+        uint32_t w[kMaxTPW][4 * H];  // INT8: half h in words 4h .. 4h + 3 (tiles c < TPW used)
+        float s[kMaxTPW];
+    };
+    // one group's words and scales (groups past the split's end reload its
+    // last group, keeping the count of loads in flight fixed)
+    auto load_words = [&](Words& d, int gl) {
+        const int64_t g = g0 + min(gl, ng - 1);
+#pragma unroll
+        for (int c = 0; c < TPW; ++c) {
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[c] + h * kChunkBytes,
+                                                                     uniform(int(g * CB)), 0);
+                d.w[c][4 * h] = v[0];
+                d.w[c][4 * h + 1] = v[1];
+                d.w[c][4 * h + 2] = v[2];
+                d.w[c][4 * h + 3] = v[3];
+            }
+            d.s[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   sres, soff[c], uniform(int(g * kChunkScaleBytes)), 0));
+        }
+    };
+
+    // FP32 accumulators of the wave's 16 x 16 blocks (i < RB, j < CBL used).
+    // The MFMAs go through the compiler's builtin, so its hazard recognizer
+    // pads only real hazards: the loop's operands come from LDS reads, and an
+    // unconditional s_nop before each MFMA (inline assembly) cost 128 issue
+    // slots per group.
+    f32x4_t acc[kMaxRB][kMaxCB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CBL; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    Words wcur, wnext, wfut;
+    // B-stage slot of (tile, k-step) for this lane
+    auto wslot = [&](int tt, int ks) { return ((tt * 2 + ks) * 64 + lane) * 16; };
+
+    // The first three x fragments and the k-step 0 weight fragments of a stage,
+    // read as soon as the barrier that publishes the stage has passed (inside
+    // the previous stage, overlapping its last MFMA blocks).
+    uint4 xa[3], wa[kMaxCB];
+    auto read_first = [&](const uint16_t* Xs, const uint8_t* Ws) {
+#pragma unroll
+        for (int f = 0; f < 3; ++f)
+            xa[f] = *reinterpret_cast<const uint4*>(Xs + swz8(wm * WTM + (f % RB) * 16 + r, 4 * (f / RB) + kq));
+#pragma unroll
+        for (int j = 0; j < CBL; ++j) wa[j] = *reinterpret_cast<const uint4*>(Ws + wslot(wn * CBL + j, 0));
+    };
+
+    // One stage: F = 2 RB blocks of CBL MFMAs on fragments of the stage's
+    // buffers (Xp, Wp), x fragments read three blocks ahead, the k-step 1
+    // weight fragments RB / 2 + 1 blocks before they are needed.  Blocks 0 .. A - 1
+    // (A = F - 2) also carry the dequantization slices of the next stage's
+    // B tile into Wq.  After block A - 1 the wave has issued every read of
+    // Xp / Wp and written its part of Wq: it waits for its own LDS traffic
+    // and for the next stage's x pieces, and the workgroup barrier follows
+    // there.  Past it nobody reads Xp any more, so the pieces of the stage
+    // after next go into Xp at once (with, at an even stage, the weight words
+    // two groups ahead), and the next stage's first fragments are read while
+    // blocks F - 2 and F - 1 run.  Fixed buffer roles per call let the
+    // compiler tell the direct loads and B writes from the reads.  The last
+    // stages load clamped copies into buffers nobody reads any more, which
+    // keeps the loop free of branches.
+    auto stage = [&](uint16_t* Xp, const uint8_t* Wp, uint16_t* Xq, uint8_t* Wq, int s, auto odd_c) {
+        constexpr bool odd = decltype(odd_c)::value;
+        constexpr int F = 2 * RB, A = F - 2, NS = 8 * TPW;
+        // words of stage s + 1: the second half of this group, or the first
+        // half of the next
+        const Words& src = odd ? wnext : wcur;
+        constexpr int h1 = odd ? 0 : 1;
+
+        uint4 xf[4];
+        xf[0] = xa[0];
+        xf[1] = xa[1];
+        xf[2] = xa[2];
+        uint4 wf[kMaxCB], wg[kMaxCB];
+#pragma unroll
+        for (int j = 0; j < CBL; ++j) wf[j] = wa[j];
+        auto read_x = [&](int f) {
+            const int ks = f / RB, i = f % RB;
+            return *reinterpret_cast<const uint4*>(Xp + swz8(wm * WTM + i * 16 + r, 4 * ks + kq));
+        };
+        uint32_t lo = 0, hi = 0;
+        float c0 = 0.f, c4 = 0.f, c2 = 0.f, c6 = 0.f;
+        uint4 out = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const int ks = f / RB, i = f % RB;
+            const uint4 xop = xf[f % 4];
+            if (f + 3 < F) xf[(f + 3) % 4] = read_x(f + 3);
+            if (f == RB / 2 - 1) {
+#pragma unroll
+                for (int j = 0; j < CBL; ++j) wg[j] = *reinterpret_cast<const uint4*>(Wp + wslot(wn * CBL + j, 1));
+            }
+#pragma unroll
+            for (int j = 0; j < CBL; ++j) acc[i][j] = gm_mfma<ACT>(ks == 0 ? wf[j] : wg[j], xop, acc[i][j]);
+#pragma unroll
+            for (int sl = f * NS / A; sl < (f + 1) * NS / A && f < A; ++sl) {
+                // quarter q of word (c, k-step kn) of stage s + 1
+                const int wi = sl >> 2;
+                const int c = wi >> 1, kn = wi & 1, q = sl & 3;
+                const float sj = c < validw ? src.s[c] : 0.0f;
+                if constexpr (BITS == 8) {
+                    // words 4 h1 + 2 kn (columns 0-3) and + 1 (columns 4-7):
+                    // quarter q converts columns 2q, 2q + 1
+                    const uint32_t w = src.w[c][4 * h1 + 2 * kn + (q >> 1)];
+                    const float oj = -128.0f * sj;
+                    const float va = fmaf((q & 1) ? byte_f32<2>(w) : byte_f32<0>(w), sj, oj);
+                    const float vb = fmaf((q & 1) ? byte_f32<3>(w) : byte_f32<1>(w), sj, oj);
+                    const uint32_t pr = pack2<ACT>(va, vb);
+                    if (q == 0) out.x = pr;
+                    else if (q == 1) out.y = pr;
+                    else if (q == 2) out.z = pr;
+                    else {
+                        out.w = pr;
+                        *reinterpret_cast<uint4*>(Wq + wslot(TPW * wave + c, kn)) = out;
+                    }
+                } else {
+                    const uint32_t w = src.w[c][2 * h1 + kn];
+                    const float oj = -8.0f * sj;
+                    if (q == 0) {
+                        lo = w & 0x0F0F0F0Fu;  // bytes: columns 0, 4, 1, 5
+                        c0 = fmaf(byte_f32<0>(lo), sj, oj);
+                        c4 = fmaf(byte_f32<1>(lo), sj, oj);
+                    } else if (q == 1) {
+                        const float c1 = fmaf(byte_f32<2>(lo), sj, oj);
+                        const float c5 = fmaf(byte_f32<3>(lo), sj, oj);
+                        out.x = pack2<ACT>(c0, c1);
+                        out.z = pack2<ACT>(c4, c5);
+                    } else if (q == 2) {
+                        hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: columns 2, 6, 3, 7
+                        c2 = fmaf(byte_f32<0>(hi), sj, oj);
+                        c6 = fmaf(byte_f32<1>(hi), sj, oj);
+                    } else {
+                        const float c3 = fmaf(byte_f32<2>(hi), sj, oj);
+                        const float c7 = fmaf(byte_f32<3>(hi), sj, oj);
+                        out.y = pack2<ACT>(c2, c3);
+                        out.w = pack2<ACT>(c6, c7);
+                        *reinterpret_cast<uint4*>(Wq + wslot(TPW * wave + c, kn)) = out;
+                    }
+                }
+            }
+            if (f == A - 1) {
+                // the next stage's x pieces were issued at the previous
+                // stage's barrier, followed there (when that stage was even,
+                // i.e. this one is odd) by the weight-word loads
+                if constexpr (odd)
+                    wait_vm_lds<TPW * (H + 1)>();
+                else
+                    wait_vm_lds<0>();
+                __builtin_amdgcn_s_barrier();
+                load_x(Xp, min(s + 2, nstages - 1));
+                if constexpr (!odd) load_words(wfut, (s >> 1) + 2);
+                read_first(Xq, Wq);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (odd) {
+            wcur = wnext;
+            wnext = wfut;
+        }
+    };
+
+    // prologue: stage 0's x and the first two groups' words, stage 0's B
+    // tile; then stage 1's x pieces and the words two groups ahead, the
+    // barrier that publishes stage 0, and its first fragments
+    load_x(X0, 0);
+    load_words(wcur, 0);
+    load_words(wnext, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < TPW; ++c) {
+        const float sj = c < validw ? wcur.s[c] : 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            *reinterpret_cast<uint4*>(W0 + wslot(TPW * wave + c, ks)) =
+                BITS == 8 ? dequant_word8<ACT>(wcur.w[c][2 * ks], wcur.w[c][2 * ks + 1], sj, -128.0f * sj)
+                          : dequant_word<ACT>(wcur.w[c][ks], sj, -8.0f * sj);
+    }
+    load_x(X1, min(1, nstages - 1));
+    load_words(wfut, 2);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    read_first(X0, W0);
+
+    for (int s = 0; s < nstages; s += 2) {
+        stage(X0, W0, X1, W1, s, BoolC<false>{});
+        stage(X1, W1, X0, W0, s + 1, BoolC<true>{});
+    }
+    // the last stages' clamped x pieces land in LDS asynchronously: wait for
+    // them before the epilogue reuses the buffers
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // --- epilogue: lane (r, kq) holds outputs 4kq .. 4kq + 3 of tile t0 + j
+    // for x row r of row block i
+    const int64_t npad = a.ntiles * BN;
+    const int64_t t0 = nt * NT + wn * CBL;
+    if constexpr (STAGED) {
+        // Through LDS (one K split, 16-byte aligned rows): the BM x BN tile of
+        // 16-bit outputs (2 BN bytes a row) fills the stage buffers (RX rows
+        // in each x buffer, 64 in each B buffer) and leaves as whole rows in
+        // 16-byte stores.  Within a row, 16-byte unit u sits at position
+        // u ^ (row & (U - 1)), so the sixteen rows one write touches and the
+        // units one row read touches spread over the banks.
+        constexpr int RBY = 2 * BN, U = BN / 8, RX = S::RX;
+        static_assert(2 * RX + 128 >= BM, "the output tile fits the stage buffers");
+        __builtin_amdgcn_s_barrier();  // every wave is done with the last stage
+        auto tile_row = [&](int row) -> uint8_t* {
+            return row < RX            ? reinterpret_cast<uint8_t*>(X0) + row * RBY
+                   : row < 2 * RX      ? reinterpret_cast<uint8_t*>(X1) + (row - RX) * RBY
+                   : row < 2 * RX + 64 ? W0 + (row - 2 * RX) * RBY
+                                       : W1 + (row - 2 * RX - 64) * RBY;
+        };
+        float ball[CBL][4];
+        bias_tiles<ACT, CBL>(a.bias, t0, kq, a.n, ball);
+#pragma unroll
+        for (int j = 0; j < CBL; ++j) {
+            const float* bv = ball[j];
+            const int u = (wn * CBL + j) * 2 + (kq >> 1);
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int row = wm * WTM + i * 16 + r;
+                const f32x4_t v = acc[i][j];
+                *reinterpret_cast<uint2*>(tile_row(row) + ((u ^ (row & (U - 1))) << 4) + (kq & 1) * 8) =
+                    make_uint2(pack2<ACT>(v[0] + bv[0], v[1] + bv[1]), pack2<ACT>(v[2] + bv[2], v[3] + bv[3]));
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        constexpr int RPI = kG8Threads / U;  // rows per pass
+        const int u = tid % U;
+        const int64_t col = nt * BN + u * 8;
+#pragma unroll
+        for (int it = 0; it < BM / RPI; ++it) {
+            const int row = it * RPI + tid / U;
+            const int64_t grow = m0 + row;
+            const uint4 v = *reinterpret_cast<const uint4*>(tile_row(row) + ((u ^ (row & (U - 1))) << 4));
+            if (grow >= a.m || col >= a.n) continue;
+            uint16_t* dst = a.y + grow * a.ldy + col;
+            if (col + 8 <= a.n) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                for (int e = 0; e < 8 && col + e < a.n; ++e) dst[e] = uint16_t(w4[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    } else {
+        float ball[CBL][4];
+        bias_tiles<ACT, CBL>(a.splits == 1 ? a.bias : nullptr, t0, kq, a.n, ball);
+#pragma unroll
+        for (int j = 0; j < CBL; ++j) {
+            const int64_t c0 = (t0 + j) * 16 + 4 * kq;
+            if (c0 >= a.n) continue;
+            const bool full = c0 + 4 <= a.n;
+            const float* bv = ball[j];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int64_t row = m0 + wm * WTM + i * 16 + r;
+                if (row >= a.m) continue;
+                const f32x4_t v = acc[i][j];
+                if (a.splits > 1) {
+                    *reinterpret_cast<f32x4_t*>(a.partials + (int64_t(split) * a.m + row) * npad + c0) = v;
+                } else if (full && a.vec_store) {
+                    *reinterpret_cast<uint2*>(a.y + row * a.ldy + c0) = make_uint2(
+                        pack2<ACT>(v[0] + bv[0], v[1] + bv[1]), pack2<ACT>(v[2] + bv[2], v[3] + bv[3]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (c0 + e < a.n) a.y[row * a.ldy + c0 + e] = from_f32<ACT>(v[e] + bv[e]);
+                }
+            }
+        }
+    }
+}
+
+// Launches the kernel variant of one tile (instantiated in the gemm8_*.hip
+// file that defines that tile's launcher).
+template <int BM, int BN>
+static hipError_t launch_gemm8(const GemmArgs& a, int bits, bool bf, bool staged, dim3 grid, hipStream_t stream) {
+    const dim3 b8(kG8Threads);
+#define W4A16_G8(ACT, ST, BITS) gemm8_kernel<ACT, ST, BITS, BM, BN><<<grid, b8, 0, stream>>>(a)
+    if (bits == 8) {
+        if (staged) {
+            if (bf) W4A16_G8(kActBf16, true, 8);
+            else W4A16_G8(kActF16, true, 8);
+        } else {
+            if (bf) W4A16_G8(kActBf16, false, 8);
+            else W4A16_G8(kActF16, false, 8);
+        }
+    } else {
+        if (staged) {
+            if (bf) W4A16_G8(kActBf16, true, 4);
+            else W4A16_G8(kActF16, true, 4);
+        } else {
+            if (bf) W4A16_G8(kActBf16, false, 4);
+            else W4A16_G8(kActF16, false, 4);
+        }
+    }
+#undef W4A16_G8
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -281,6 +281,12 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits) {
     return p;
 }
 
+PlanInfo describe_gemv(int64_t m, int64_t n, int64_t k, int bits) {
+    const GemvPlan p = plan_gemv(m, n, k, bits);
+    const Layout L(n, k, bits);
+    return {p.waves, int(m), kTileRows, p.splits, p.gps, L.tiles * p.splits, p.splits > 1 && !p.exchange};
+}
+
 template <int M, int ACT, int AF, int BITS>
 static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k, BITS);

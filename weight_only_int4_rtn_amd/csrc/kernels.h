@@ -45,11 +45,25 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 struct GemmPlan {
     int64_t mtiles, ntiles;
-    int waves;            // 8: 256 x 256 tiles, eight waves; 4: 16 mb x 256 tiles, four waves
-    int mb, gps, splits;  // mb: 16-row blocks per workgroup (64, 128 or 256 rows)
+    int waves;            // 8: the eight-wave kernel (bm x bn tiles); 4: the four-wave kernel (bm x 256)
+    int bm, bn;           // workgroup tile: rows of x, output columns
+    int mb, gps, splits;  // mb = bm / 16; gps: groups per K split
     size_t workspace;
 };
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits = 4);
+
+// One launch of a path's main kernel, as w4a16_linear_explain reports it.
+struct PlanInfo {
+    int waves;           // waves (64 lanes) per workgroup
+    int tile_m, tile_n;  // x rows and output columns one workgroup computes
+    int splits, gps;     // K parts, 128-column groups per part
+    int64_t workgroups;  // grid size
+    bool reduce;         // a split-K reduce launch follows
+};
+PlanInfo describe_gemv(int64_t m, int64_t n, int64_t k, int bits);    // m <= 4 (one row block)
+PlanInfo describe_mgemv(int64_t m, int64_t n, int64_t k, int bits);   // m <= 16 (one row block)
+PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits);
+PlanInfo describe_gemm(int64_t m, int64_t n, int64_t k, int bits);
 
 hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int64_t ldw,
                            uint8_t* codes, float* scales, hipStream_t stream);

@@ -245,6 +245,12 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits) {
     return p;
 }
 
+PlanInfo describe_mgemv(int64_t m, int64_t n, int64_t k, int bits) {
+    const MgemvPlan p = plan_mgemv(m, n, k, bits);
+    const Layout L(n, k, bits);
+    return {kMgWaves, int(m), kTileRows, p.splits, p.gps, L.tiles * p.splits, p.splits > 1 && !p.exchange};
+}
+
 template <int MMAX, int ACT, int AF, int BITS>
 static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k, BITS);

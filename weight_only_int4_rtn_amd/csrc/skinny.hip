@@ -242,6 +242,11 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits) {
     return p;
 }
 
+PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits) {
+    const SkinnyPlan p = plan_skinny(m, n, k, bits);
+    return {kSkWaves, 16 * p.mb, kSkCols, p.splits, p.gps, p.tile_groups * p.splits * p.mblocks, p.splits > 1};
+}
+
 template <int MB, int ACT, int AF, int BITS>
 static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
     dim3 grid(unsigned(p.tile_groups * p.splits), unsigned(p.mblocks));
