@@ -59,7 +59,13 @@ def exact_case(m, n, k, seed, dtype, with_bias):
     return w, x, b
 
 
+# (1, 48, 2176): a 17-group K, the shortest split on 8 waves (3 chunks for
+# some waves, 2 for others); (1, 40, 8192): two 8-wave splits; (1, 72,
+# 32896): nine splits, the last holding one group; (6, 2056, 16384): 8-wave
+# splits of 21 groups on the MFMA small-M path, and on the v_dot2 path a
+# 4-row and a 2-row block of 8-wave splits of 32, ragged last tile.
 EXACT_SHAPES = [(1, 16, 128), (2, 40, 384), (3, 1000, 2048), (4, 2056, 16384), (5, 72, 256),
+                (1, 48, 2176), (1, 40, 8192), (1, 72, 32896), (6, 2056, 16384),
                 (17, 130, 640), (33, 64, 1152), (63, 130, 512), (64, 2048, 8192), (65, 40, 256),
                 (130, 100, 1152), (255, 72, 384), (257, 136, 256)]
 

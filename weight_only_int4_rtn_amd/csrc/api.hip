@@ -41,7 +41,12 @@ w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A1
 
 size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bits) {
     switch (path) {
-        case W4A16_PATH_GEMV: return plan_gemv(m < 4 ? m : 4, n, k, bits).workspace;
+        case W4A16_PATH_GEMV: {
+            // row blocks of 4 and a last block of m % 4 rows, each with its own plan
+            const size_t full = plan_gemv(m < 4 ? m : 4, n, k, bits).workspace;
+            const size_t last = m > 4 && m % 4 ? plan_gemv(m % 4, n, k, bits).workspace : 0;
+            return full > last ? full : last;
+        }
         case W4A16_PATH_MGEMV: return plan_mgemv(m < 16 ? m : 16, n, k, bits).workspace;
         case W4A16_PATH_SKINNY: return plan_skinny(m, n, k, bits).workspace;
         case W4A16_PATH_GEMM: return plan_gemm(m, n, k, bits).workspace;

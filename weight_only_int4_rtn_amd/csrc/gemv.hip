@@ -50,8 +50,6 @@ struct GemvArgs {
     int exchange;               // splits > 1: finish through the slots (else through partials)
 };
 
-constexpr int kGemvChunks = 8;  // chunks per wave, all loaded up front
-
 // AF: activation fused into the x staging (ActFn); for SwiGLU the x rows
 // hold [up | gate] and the gate values sit k columns after the up values.
 // BITS: 4 (INT4 chunks) or 8 (INT8 chunks, two 1 KB halves per chunk).
@@ -135,6 +133,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
             for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
             sc[u] = sbase[int64_t(gc) * kTileRows];
         }
+        // Issue each chunk's scale right after its codes.  Left alone, the
+        // compiler issues all code loads, then all scale loads; loads
+        // complete in order, so the wait for chunk 0's scale then waits for
+        // every chunk and the products of the later chunks no longer overlap
+        // the stream.
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Stage x into LDS and sum each lane-quarter's 32 activations of every
@@ -251,27 +255,35 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 
 // --- planning ---------------------------------------------------------------
 //
-// Workgroups of 4 waves, one row tile each, at most 8 chunks per wave: a
-// workgroup covers up to 32 groups (K <= 4096) and a longer K is split into
-// equal parts.  Splitting only to fill the chip costs more than it gains:
-// the exchange adds a device round trip per tree level, while a tile's
-// chunks are all in flight at once anyway.  The exchange slots live in the
-// workspace's zero header; a launch whose tree does not fit there stores
-// partial sums for the split-K reduce kernel instead.
+// One row tile per workgroup and at most 4 chunks per wave: a split longer
+// than 16 groups takes workgroups of 8 waves, so a workgroup covers up to 32
+// groups (K <= 4096) and a longer K is split into equal parts.  Measured on
+// the K 16384 down projection: the same split over 8 waves of 4 chunks
+// streams its weight about 1.6 us faster than over 4 waves of 8 chunks (more
+// waves, each with fewer loads in flight).  INT8 chunks are twice as long: 4
+// waves of at most 4 of them.
+//
+// Splitting only to fill the chip costs more than it gains: the exchange
+// adds a device round trip per tree level (about 0.45 us each, measured),
+// while a tile's chunks are all in flight at once anyway.  Nor do two
+// workgroups per tile, one per 8-row half of every chunk, pay: measured
+// slower than a K split on every shape tried (the two halves of a chunk are
+// then read at different times from different XCDs).  The exchange slots
+// live in the workspace's zero header; a launch whose tree does not fit
+// there stores partial sums for the split-K reduce kernel instead.
 
 GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits) {
     GemvPlan p{};
     const Layout L(n, k, bits);
     const int64_t G = L.groups;
     const int mm = int(m);
-    p.waves = 4;
-    // the same bytes in flight per wave for INT8 (2 KB chunks)
-    const int64_t cap = (bits == 8 ? kGemvChunks / 2 : kGemvChunks) * p.waves;
+    const int64_t cap = bits == 8 ? 4 * 4 : 8 * 4;
     const int64_t gps = G < cap ? G : cap;
     p.gps = int(gps);
     p.splits = int(ceil_div(G, gps));
+    p.waves = (bits == 4 && gps > 16) ? 8 : 4;
     const int64_t per_wave = ceil_div(gps, p.waves);
-    p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+    p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : 4;
     p.lds = size_t(mm) * gps * kGroup * 2 + size_t(mm) * gps * 4 * 4 + size_t(p.waves) * mm * 16 * 4;
     const int64_t slots = L.tiles * (p.splits - 1) * mm * kTileRows;
     p.exchange = p.splits > 1 && slots * 8 <= int64_t(kSyncBytes);
@@ -290,15 +302,17 @@ PlanInfo describe_gemv(int64_t m, int64_t n, int64_t k, int bits) {
 template <int M, int ACT, int AF, int BITS>
 static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k, BITS);
-    const dim3 grid(unsigned(L.tiles * p.splits)), block(256);
-    switch (p.cpw) {
-        case 1: gemv_kernel<M, ACT, 4, 1, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
-        case 2: gemv_kernel<M, ACT, 4, 2, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
-        case 4: gemv_kernel<M, ACT, 4, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
-        default:
-            if constexpr (BITS == 4) gemv_kernel<M, ACT, 4, 8, AF, BITS><<<grid, block, p.lds, stream>>>(a);
-            else return hipErrorInvalidValue;  // the plan keeps INT8 to 4 chunks per wave
-            break;
+    const dim3 grid(unsigned(L.tiles * p.splits)), block(unsigned(64 * p.waves));
+    if (p.waves == 8) {
+        // 17..32 groups per split (INT4 only): 8 waves of 4 chunks
+        if constexpr (BITS == 4) gemv_kernel<M, ACT, 8, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+        else return hipErrorInvalidValue;
+    } else {
+        switch (p.cpw) {
+            case 1: gemv_kernel<M, ACT, 4, 1, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+            case 2: gemv_kernel<M, ACT, 4, 2, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+            default: gemv_kernel<M, ACT, 4, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        }
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.exchange) return e;

@@ -28,7 +28,7 @@ struct GemvPlan {
 GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 struct MgemvPlan {
-    int mmax, gps, splits, cpw;
+    int mmax, waves, gps, splits, cpw;
     bool exchange;  // split finished through the header's exchange slots
     size_t lds, workspace;
 };

@@ -1,7 +1,7 @@
 // Small-M forward on the matrix cores (M <= 16): the same weight stream as
 // the v_dot2 kernel (gemv.hip), with the contraction done by MFMA.
 //
-// A workgroup of 4 waves owns one 16-row weight tile and a K split.  The
+// A workgroup of 4 or 8 waves owns one 16-row weight tile and a K split.  The
 // workgroup stages its slice of x (M rows) in LDS once.  Per chunk, a wave
 // turns its four words into
 // four B operands of v_mfma_f32_16x16x32_{bf16,f16} (the chunk layout is that
@@ -42,10 +42,8 @@ struct MgemvArgs {
     int exchange;               // splits > 1: finish through the slots (else through partials)
 };
 
-constexpr int kMgWaves = 4;
-constexpr int kMgThreads = 64 * kMgWaves;
-constexpr int kMgChunks = 8;  // chunks per wave, all loaded up front
-constexpr int kXRegs = 8;  // 16-byte x loads per thread while staging
+constexpr int kMgChunks = 4;  // at most this many chunks per wave, all loaded up front
+constexpr int kXRegs = 8;     // 16-byte x loads per thread while staging (4 waves)
 
 template <int ACT>
 __device__ inline f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
@@ -62,9 +60,14 @@ __device__ inline f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
 // staging (ActFn; SwiGLU gate values sit k columns after the up values).
 // BITS: 4 (INT4 chunks) or 8 (INT8 chunks, two 1 KB halves; each k-step's
 // B operand is two words of byte codes, u = q + 128).
-template <int MMAX, int ACT, int CPW, int AF, int BITS>
-__global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
+// WAVES: 4 or 8 waves per workgroup.
+template <int MMAX, int ACT, int WAVES, int CPW, int AF, int BITS>
+__global__ __launch_bounds__(64 * WAVES) void mgemv_kernel(MgemvArgs a) {
     constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
+    constexpr int kMgWaves = WAVES, kMgThreads = 64 * WAVES;
+    // x staging: the slice is m <= 16 rows of at most 128 / m groups, i.e.
+    // at most 2048 16-byte loads, kXRegs * 256 of them
+    constexpr int XR = kXRegs * 4 / WAVES;
     extern __shared__ __align__(16) unsigned char smem[];
     const Layout L(a.n, a.k, BITS);
     const int split = int(blockIdx.x % unsigned(a.splits));
@@ -102,12 +105,12 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
     // zero-initialised so every register has a value on every path out of
     // the load loop: the compiler then keeps all x loads in flight together
     // (without it, it waited for each load before issuing the next)
-    uint4 xv[kXRegs];
+    uint4 xv[XR];
 #pragma unroll
-    for (int j = 0; j < kXRegs; ++j) xv[j] = make_uint4(0u, 0u, 0u, 0u);
-    uint4 xgate[AF == kActFnSwiglu ? kXRegs : 1];
+    for (int j = 0; j < XR; ++j) xv[j] = make_uint4(0u, 0u, 0u, 0u);
+    uint4 xgate[AF == kActFnSwiglu ? XR : 1];
 #pragma unroll
-    for (int j = 0; j < kXRegs; ++j) {
+    for (int j = 0; j < XR; ++j) {
         if (j * kMgThreads >= total) break;
         const int i = j * kMgThreads + tid;
         const int ic = i < total ? i : total - 1;
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
 
     // Stage rows [0, m).
 #pragma unroll
-    for (int j = 0; j < kXRegs; ++j) {
+    for (int j = 0; j < XR; ++j) {
         if (j * kMgThreads >= total) break;
         const int i = j * kMgThreads + tid;
         const bool on = i < total;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * kq + i) * 16 + r] = tot[i];
     __syncthreads();
-    const int orow = tid >> 4, ocol = tid & 15;  // 256 threads = 16 x 16 outputs
+    const int orow = tid >> 4, ocol = tid & 15;  // the first 256 threads: 16 x 16 outputs
     if (orow >= m) return;
     float v = 0.0f;
 #pragma unroll
@@ -217,7 +220,9 @@ __global__ __launch_bounds__(kMgThreads) void mgemv_kernel(MgemvArgs a) {
 }
 
 // Same plan shape as the v_dot2 kernel: split K only when the row tiles
-// cannot fill the chip; the x slice stays within 16 rows x 2048 columns.
+// cannot fill the chip; the x slice stays within 16 rows x 2048 columns; at
+// most 4 chunks per wave (a split of more than 16 INT4 groups takes 8 waves:
+// measured faster than 4 waves of 8 chunks, as for the v_dot2 kernel).
 MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits) {
     MgemvPlan p{};
     const Layout L(n, k, bits);
@@ -225,18 +230,19 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits) {
     int64_t splits = 1;
     if (L.tiles < 512) splits = ceil_div(512, L.tiles);
     int64_t gps = ceil_div(L.groups, splits);
-    if (gps < 2 * kMgWaves) gps = 2 * kMgWaves;
-    int64_t max_gps = 128 / m;                       // x slice <= kXRegs loads per thread
-    // chunks per wave held in registers (INT8 chunks take twice the registers)
-    const int64_t wave_chunks = bits == 8 ? kMgChunks / 2 : kMgChunks;
-    if (max_gps > wave_chunks * kMgWaves) max_gps = wave_chunks * kMgWaves;
+    if (gps < 8) gps = 8;
+    int64_t max_gps = 128 / m;  // x slice <= 2048 16-byte loads
+    // chunks per workgroup held in registers (INT8 chunks take twice the registers)
+    const int64_t wg_chunks = bits == 8 ? kMgChunks * 4 : kMgChunks * 8;
+    if (max_gps > wg_chunks) max_gps = wg_chunks;
     if (gps > max_gps) gps = max_gps;
     if (gps > L.groups) gps = L.groups;
     p.gps = int(gps);
     p.splits = int(ceil_div(L.groups, gps));
-    const int64_t per_wave = ceil_div(gps, kMgWaves);
-    p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
-    p.lds = size_t(p.mmax) * (gps * kGroup + 8) * 2 + size_t(kMgWaves) * 256 * 4;
+    p.waves = gps > 4 * kMgChunks ? 8 : 4;
+    const int64_t per_wave = ceil_div(gps, p.waves);
+    p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : 4;
+    p.lds = size_t(p.mmax) * (gps * kGroup + 8) * 2 + size_t(p.waves) * 256 * 4;
     const int64_t slots = L.tiles * (p.splits - 1) * m * kTileRows;
     p.exchange = p.splits > 1 && slots * 8 <= int64_t(kSyncBytes);
     p.workspace = p.splits == 1 ? 0
@@ -248,22 +254,23 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits) {
 PlanInfo describe_mgemv(int64_t m, int64_t n, int64_t k, int bits) {
     const MgemvPlan p = plan_mgemv(m, n, k, bits);
     const Layout L(n, k, bits);
-    return {kMgWaves, int(m), kTileRows, p.splits, p.gps, L.tiles * p.splits, p.splits > 1 && !p.exchange};
+    return {p.waves, int(m), kTileRows, p.splits, p.gps, L.tiles * p.splits, p.splits > 1 && !p.exchange};
 }
 
 template <int MMAX, int ACT, int AF, int BITS>
 static hipError_t launch_one(const MgemvArgs& a, const MgemvPlan& p, hipStream_t stream) {
     const Layout L(a.n, a.k, BITS);
-    const dim3 grid(unsigned(L.tiles * p.splits)), block(kMgThreads);
-    switch (p.cpw) {
-        case 1: mgemv_kernel<MMAX, ACT, 1, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
-        case 2: mgemv_kernel<MMAX, ACT, 2, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
-        case 4: mgemv_kernel<MMAX, ACT, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
-        default:
-            // the INT8 plan holds at most 4 chunks per wave
-            if constexpr (BITS == 4) mgemv_kernel<MMAX, ACT, 8, AF, BITS><<<grid, block, p.lds, stream>>>(a);
-            else return hipErrorInvalidValue;
-            break;
+    const dim3 grid(unsigned(L.tiles * p.splits)), block(unsigned(64 * p.waves));
+    if (p.waves == 8) {
+        // 17..32 groups per split (INT4 only): 8 waves of 4 chunks
+        if constexpr (BITS == 4) mgemv_kernel<MMAX, ACT, 8, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+        else return hipErrorInvalidValue;
+    } else {
+        switch (p.cpw) {
+            case 1: mgemv_kernel<MMAX, ACT, 4, 1, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+            case 2: mgemv_kernel<MMAX, ACT, 4, 2, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+            default: mgemv_kernel<MMAX, ACT, 4, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.exchange) return e;

@@ -146,8 +146,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     for (int gl = 0; gl < GMAX; ++gl) {
         if (gl >= ng) continue;  // (not break: the loop stays fully unrolled, arrays in registers)
         const int buf = gl & 1;
-        // group gl + 2 into the register set group gl was staged from
-        if (gl + 2 < ng) load_x(gl & 1, gl + 2);
 
         uint32_t words[4 * H];
 #pragma unroll
@@ -176,8 +174,13 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
             tot[mb][3] = fmaf(sc[gl], acc[3], tot[mb][3]);
         }
         // group gl + 1 into the other LDS buffer, last read in the previous
-        // group, which ended with a barrier
+        // group, which ended with a barrier; then group gl + 2 into the
+        // register set just staged from.  The loads go out after the staging:
+        // the compiler's wait before the staging covers every load issued
+        // before it, so loads issued earlier in this group would each cost a
+        // full memory round trip per group.
         if (gl + 1 < ng) stage_x((gl + 1) & 1, buf ^ 1);
+        if (gl + 2 < ng) load_x(gl & 1, gl + 2);
         __syncthreads();
     }
 
