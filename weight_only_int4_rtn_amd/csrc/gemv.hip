@@ -61,9 +61,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     // most WAVES * CPW groups of 128 columns, M * CPW / 4 loads per thread.
     constexpr int kXRegs = (M * CPW + 3) / 4;
     extern __shared__ __align__(16) unsigned char smem[];
+    // the x pointer in the first batch of kernel-argument loads (else the
+    // compiler fetches it separately, just before the x loads: one more
+    // scalar-memory round trip before any load is issued)
+    asm volatile("" ::"s"(a.x));
     const Layout L(a.n, a.k, BITS);
-    const int split = int(blockIdx.x % unsigned(a.splits));
-    const int64_t t = int64_t(blockIdx.x / unsigned(a.splits));
+    // no integer division before the first load when K is not split (the
+    // common decode case): it sits on every workgroup's path to its loads
+    int split = 0;
+    int64_t t = blockIdx.x;
+    if (a.splits > 1) {
+        split = int(blockIdx.x % unsigned(a.splits));
+        t = int64_t(blockIdx.x / unsigned(a.splits));
+    }
     const int64_t g0 = int64_t(split) * a.gps;
     const int ng = int(min<int64_t>(a.gps, L.groups - g0));
     const int klen = ng * kGroup;
@@ -75,15 +85,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6), lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-
-    const uint8_t* cbase = a.packed + (t * L.groups + g0) * CB + lane * 16;
-    const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (t * L.groups + g0) * kTileRows + r;
-    // M = 1: the split's chunks and scales through buffer resources, so a
-    // chunk's address is a scalar offset plus the lane's 16 bytes (measured
-    // faster at M = 1 only; larger M keep the flat loads)
-    const __amdgpu_buffer_rsrc_t cres = buffer_rsrc(a.packed + (t * L.groups + g0) * CB, int64_t(ng) * CB);
-    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
-        a.packed + L.scale_offset() + (t * L.groups + g0) * kChunkScaleBytes, int64_t(ng) * kChunkScaleBytes);
 
     // Every chunk of the wave (CPW of them) is loaded before any is used.
     // The loads are unconditional straight-line code (clamped addresses), so
@@ -113,8 +114,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         xv[j] = *reinterpret_cast<const uint4*>(src);
         if constexpr (AF == kActFnSwiglu) xgate[j] = *reinterpret_cast<const uint4*>(src + a.k);
     }
-    // keep the compiler from hoisting the weight loads above the x loads
+    // keep the compiler from hoisting the weight loads (and their address
+    // arithmetic) above the x loads
     __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* cbase = a.packed + (t * L.groups + g0) * CB + lane * 16;
+    const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (t * L.groups + g0) * kTileRows + r;
+    // M = 1: the split's chunks and scales through buffer resources, so a
+    // chunk's address is a scalar offset plus the lane's 16 bytes (measured
+    // faster at M = 1 only; larger M keep the flat loads)
+    const __amdgpu_buffer_rsrc_t cres = buffer_rsrc(a.packed + (t * L.groups + g0) * CB, int64_t(ng) * CB);
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
+        a.packed + L.scale_offset() + (t * L.groups + g0) * kChunkScaleBytes, int64_t(ng) * kChunkScaleBytes);
+
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * WAVES;
@@ -206,7 +217,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         tot[m] += __shfl_xor(tot[m], 32);
         if (lane < 16) red[(wave * M + m) * 16 + lane] = tot[m];
     }
-    __syncthreads();
+    lds_barrier();
     const bool out_thread = tid < M * 16;
     const int om = tid >> 4, orow = tid & 15;
     float v = 0.0f;
