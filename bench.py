@@ -280,9 +280,24 @@ def run_workload(cases, dev, steps, warmup, dominant, bits=4, eager=True, per_ke
 
 TRACE_M1 = os.path.join(ROOT, "profiles", "gemv_m1_decode_layer_kernel_trace.md")
 TRACE_M1024 = os.path.join(ROOT, "profiles", "gemm_m1024_prefill_kernel_trace.md")
-# (kernel name prefix, grid in threads) of each dominant kernel in its trace
-TRACE_M1_KERNEL = ("void w4a16::gemv_kernel<1, 1, 4, 8, 0, 4>", 524288)
-TRACE_M1024_KERNEL = ("void w4a16::gemm8_kernel<2, true, 4>", 262144)
+
+
+def trace_kernel(c):
+    """(name prefix, grid in threads) that identify the kernel a case's
+    automatic plan launches (its main kernel) in a kernel-trace summary."""
+    import weight_only_int4_rtn_amd as w4
+    e = w4.explain(c.m, c.n, c.k)
+    act = 1 if c.dtype == "bf16" else 2
+    grid = e["workgroups"] * e["waves"] * 64
+    if e["path"] == w4.Path.GEMV:
+        return f"void w4a16::gemv_kernel<{min(c.m, 4)}, {act}, {e['waves']}, ", grid
+    if e["path"] == w4.Path.MGEMV:
+        return f"void w4a16::mgemv_kernel<", grid
+    if e["path"] == w4.Path.SKINNY:
+        return f"void w4a16::skinny_kernel<", grid
+    if e["waves"] == 8:
+        return f"void w4a16::gemm8_kernel<{act}, ", grid
+    return f"void w4a16::gemm_kernel<{act}, ", grid
 
 
 def trace_row(path, kernel, grid):
@@ -1053,7 +1068,7 @@ def main():
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": f"{w4.choose_path(1, dom.n, dom.k).name} {dom.name}",
                      "avg_launch_us": round(dom_ms * 1e3, 3), "bytes_per_launch": dom.alg_bytes(),
-                     "trace": trace_view(TRACE_M1, *TRACE_M1_KERNEL, dom_ms * 1e3, dom.alg_bytes(),
+                     "trace": trace_view(TRACE_M1, *trace_kernel(dom), dom_ms * 1e3, dom.alg_bytes(),
                                          HBM_PEAK_GBS, 1e-3)},
         "m1024": {"workload": "prefill M=1024 fp16 with bias: K2048xN2560, K2048xN32768, K16384xN2048",
                   "tflops": round(ptf, 2), "ms_per_step": round(pms, 4),
@@ -1063,7 +1078,7 @@ def main():
                                "unit": "TFLOP/s", "frac": round(pd_tf / MFMA_PEAK_TFLOPS, 4),
                                "kernel": f"{w4.choose_path(pd.m, pd.n, pd.k).name} {pd.name}",
                                "avg_launch_us": round(pdom_ms * 1e3, 3), "flops_per_launch": pd.flops(),
-                               "trace": trace_view(TRACE_M1024, *TRACE_M1024_KERNEL, pdom_ms * 1e3, pd.flops(),
+                               "trace": trace_view(TRACE_M1024, *trace_kernel(pd), pdom_ms * 1e3, pd.flops(),
                                                    MFMA_PEAK_TFLOPS, 1e-6)}},
         "m4096": big[4096],
         "c5_m1024": big[1024],

@@ -91,3 +91,16 @@ def test_more_than_one_gpu_is_refused():
                           capture_output=True, text=True, timeout=120)
     assert proc.returncode == 2
     assert "one GPU only" in proc.stderr
+
+
+def test_trace_kernel_names_the_planned_kernel(tmp_path):
+    import synth
+    prefix, grid = bench.trace_kernel(synth.case_by_name("c3_gate_up_m1_k2048_n32768"))
+    assert prefix.startswith("void w4a16::gemv_kernel<1, 1, ") and grid == 2048 * 4 * 64
+    prefix, grid = bench.trace_kernel(synth.case_by_name("c4_m1024_k2048_n32768"))
+    assert prefix.startswith("void w4a16::gemm")
+    # a summary row of that kernel is found by prefix and grid
+    table = tmp_path / "t.md"
+    table.write_text("| kernel | grid | launches | mean us | total us | share |\n|---|---|---|---|---|---|\n"
+                     f"| `{prefix}16, 256, 256>` | {grid} | 10 | 12.5 | 125 | 50 |\n")
+    assert bench.trace_row(str(table), prefix, grid)[:2] == (12.5, 10)

@@ -18,9 +18,12 @@
 // Every stage runs its MFMA blocks, each followed by a slice of the next
 // stage's dequantization (a finished word goes to the next B tile).  The
 // barrier that publishes the next stage sits two blocks before the end of
-// the stage: past it the x pieces of the stage after next are issued into
-// the buffer just freed and the next stage's first fragments are read, both
-// overlapping the last two blocks (see `stage` below).
+// the stage: past it the x pieces of the stage three ahead are issued into
+// the buffer just freed (three x buffers, so an x tile has two stages to
+// arrive) and the next stage's first fragments are read, both overlapping
+// the last two blocks (see `stage` below).  Measured on the 128 x 128 tile
+// at M 1024, N 2560: with one stage of lead, x load latency set the stage
+// time (the MFMA work of a stage is 512 clocks per SIMD there).
 //
 // INT8 weights: the same stages with a 16-byte run of each 1 KB chunk half
 // per stage (byte codes, u = q + 128, fma(u, s, -128 s)).
@@ -61,12 +64,13 @@ __device__ inline int swz8(int row, int seg) { return row * kG8K + ((seg ^ ((row
 // Waits for all but N vector memory operations and for all LDS operations.
 template <int N>
 __device__ inline void wait_vm_lds() {
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
-    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory");
-    else static_assert(N == 0, "unsupported count");
+    static_assert(N >= 0 && N <= 15, "vmcnt range");
+#define W4A16_WAIT(n) \
+    if constexpr (N == n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)" ::: "memory");
+    W4A16_WAIT(0) W4A16_WAIT(1) W4A16_WAIT(2) W4A16_WAIT(3) W4A16_WAIT(4) W4A16_WAIT(5) W4A16_WAIT(6)
+    W4A16_WAIT(7) W4A16_WAIT(8) W4A16_WAIT(9) W4A16_WAIT(10) W4A16_WAIT(11) W4A16_WAIT(12) W4A16_WAIT(13)
+    W4A16_WAIT(14) W4A16_WAIT(15)
+#undef W4A16_WAIT
 }
 
 // BITS 8: INT8 chunks (two 1 KB halves, half h = stage 2g + h): a lane's
@@ -81,8 +85,13 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
     constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
     constexpr int RB = S::RB, CBL = S::CB, TPW = S::TPW, XP = S::XP, SPI = S::SPI, WTM = S::WTM, WN = S::WN,
                   NT = S::NT;
+    // x buffers: three (an x tile issued two stages ahead), or two for INT8
+    // at 256 x 256, whose register budget the third buffer's addresses
+    // would overrun (spills)
+    constexpr int XR = (BITS == 8 && BM == 256 && BN == 256) ? 2 : 3;
     __shared__ __align__(16) uint16_t X0[S::XSTAGE];
     __shared__ __align__(16) uint16_t X1[S::XSTAGE];
+    __shared__ __align__(16) uint16_t X2[XR == 3 ? S::XSTAGE : 8];
     __shared__ __align__(16) uint8_t W0[S::WSTAGE];
     __shared__ __align__(16) uint8_t W1[S::WSTAGE];
 
@@ -195,9 +204,9 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
     // B tile into Wq.  After block A - 1 the wave has issued every read of
     // Xp / Wp and written its part of Wq: it waits for its own LDS traffic
     // and for the next stage's x pieces, and the workgroup barrier follows
-    // there.  Past it nobody reads Xp any more, so the pieces of the stage
-    // after next go into Xp at once (with, at an even stage, the weight words
-    // two groups ahead), and the next stage's first fragments are read while
+    // there.  Past it nobody reads Xp any more, so the pieces of stage s + 3
+    // go into Xp at once (with, at an even stage, the weight words two
+    // groups ahead), and the next stage's first fragments are read while
     // blocks F - 2 and F - 1 run.  Fixed buffer roles per call let the
     // compiler tell the direct loads and B writes from the reads.  The last
     // stages load clamped copies into buffers nobody reads any more, which
@@ -282,15 +291,24 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
                 }
             }
             if (f == A - 1) {
-                // the next stage's x pieces were issued at the previous
-                // stage's barrier, followed there (when that stage was even,
-                // i.e. this one is odd) by the weight-word loads
+                // The next stage's x pieces were issued XR - 1 barriers ago.
+                // Since then (three buffers): at an even stage, the pieces of
+                // the stage after next (the previous, odd barrier); at an odd
+                // stage, the pieces of the stage after next and the words two
+                // groups ahead (the previous, even barrier).  Those may stay
+                // in flight; the words the next stage dequantizes (issued two
+                // barriers before an even stage) have landed with the rest.
+                // Two buffers: only the odd stage's words stay in flight.
                 if constexpr (odd)
-                    wait_vm_lds<TPW * (H + 1)>();
+                    wait_vm_lds<(XR - 2) * XP + TPW * (H + 1)>();
                 else
-                    wait_vm_lds<0>();
+                    wait_vm_lds<(XR - 2) * XP>();
                 __builtin_amdgcn_s_barrier();
-                load_x(Xp, min(s + 2, nstages - 1));
+                // keep the direct loads' M0 set-up below the barrier: hoisted
+                // above the last B write, it made the compiler wait there for
+                // every direct load in flight (x of the next stages)
+                __builtin_amdgcn_sched_barrier(0);
+                load_x(Xp, min(s + XR, nstages - 1));
                 if constexpr (!odd) load_words(wfut, (s >> 1) + 2);
                 read_first(Xq, Wq);
             }
@@ -303,8 +321,9 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
     };
 
     // prologue: stage 0's x and the first two groups' words, stage 0's B
-    // tile; then stage 1's x pieces and the words two groups ahead, the
-    // barrier that publishes stage 0, and its first fragments
+    // tile; then the x pieces of stages 1 and 2, the barrier that publishes
+    // stage 0, and its first fragments (stage 0's barrier issues the words
+    // two groups ahead)
     load_x(X0, 0);
     load_words(wcur, 0);
     load_words(wnext, 1);
@@ -319,14 +338,40 @@ __global__ __launch_bounds__(kG8Threads, 1) void gemm8_kernel(GemmArgs a) {
                           : dequant_word<ACT>(wcur.w[c][ks], sj, -8.0f * sj);
     }
     load_x(X1, min(1, nstages - 1));
-    load_words(wfut, 2);
+    if constexpr (XR == 3) load_x(X2, min(2, nstages - 1));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     read_first(X0, W0);
 
-    for (int s = 0; s < nstages; s += 2) {
-        stage(X0, W0, X1, W1, s, BoolC<false>{});
-        stage(X1, W1, X0, W0, s + 1, BoolC<true>{});
+    // B buffers and words alternate with the stage's parity (nstages is
+    // even); with three x buffers, stage s reads X[s % 3]: six stages per
+    // iteration, then the last two or four.  Each call names its buffers, so
+    // the compiler can tell the direct loads into one x buffer from the
+    // reads of another (through a pointer chosen at run time it would wait
+    // for every direct load before the next read).
+    if constexpr (XR == 3) {
+        const int nfull = nstages - nstages % 6;
+        for (int s = 0; s < nfull; s += 6) {
+            stage(X0, W0, X1, W1, s, BoolC<false>{});
+            stage(X1, W1, X2, W0, s + 1, BoolC<true>{});
+            stage(X2, W0, X0, W1, s + 2, BoolC<false>{});
+            stage(X0, W1, X1, W0, s + 3, BoolC<true>{});
+            stage(X1, W0, X2, W1, s + 4, BoolC<false>{});
+            stage(X2, W1, X0, W0, s + 5, BoolC<true>{});
+        }
+        if (nstages - nfull >= 2) {
+            stage(X0, W0, X1, W1, nfull, BoolC<false>{});
+            stage(X1, W1, X2, W0, nfull + 1, BoolC<true>{});
+        }
+        if (nstages - nfull >= 4) {
+            stage(X2, W0, X0, W1, nfull + 2, BoolC<false>{});
+            stage(X0, W1, X1, W0, nfull + 3, BoolC<true>{});
+        }
+    } else {
+        for (int s = 0; s < nstages; s += 2) {
+            stage(X0, W0, X1, W1, s, BoolC<false>{});
+            stage(X1, W1, X0, W0, s + 1, BoolC<true>{});
+        }
     }
     // the last stages' clamped x pieces land in LDS asynchronously: wait for
     // them before the epilogue reuses the buffers
