@@ -7,23 +7,22 @@ TILINGS = [
     # (bits, waves, tile_m, tile_n, split, (m, n, k))
     (4, 4, 64, 256, False, (130, 32772, 128)),
     (4, 4, 64, 256, True, (257, 8200, 4096)),
-    (4, 4, 128, 256, False, (257, 32772, 128)),
     (4, 8, 128, 128, False, (97, 136, 128)),
     (4, 8, 128, 128, True, (97, 136, 640)),
     (4, 8, 128, 256, False, (257, 16424, 128)),
-    (4, 8, 128, 256, True, (513, 4104, 2176)),
+    (4, 8, 128, 256, True, (97, 16424, 2176)),
     (4, 8, 256, 128, False, (130, 16424, 128)),
-    (4, 8, 256, 128, True, (1030, 520, 2176)),
+    (4, 8, 256, 128, True, (130, 2056, 4096)),
     (4, 8, 256, 256, False, (1000, 8200, 128)),
-    (4, 8, 256, 256, True, (1030, 2600, 4096)),
+    (4, 8, 256, 256, True, (130, 16424, 4096)),
     (8, 8, 128, 128, False, (97, 136, 128)),
     (8, 8, 128, 128, True, (97, 136, 640)),
     (8, 8, 128, 256, False, (257, 16424, 128)),
-    (8, 8, 128, 256, True, (513, 4104, 2176)),
+    (8, 8, 128, 256, True, (97, 16424, 2176)),
     (8, 8, 256, 128, False, (130, 16424, 128)),
-    (8, 8, 256, 128, True, (1030, 520, 2176)),
+    (8, 8, 256, 128, True, (130, 2056, 4096)),
     (8, 8, 256, 256, False, (130, 32772, 128)),
-    (8, 8, 256, 256, True, (1030, 2600, 4096)),
+    (8, 8, 256, 256, True, (257, 8200, 4096)),
 ]
 
 

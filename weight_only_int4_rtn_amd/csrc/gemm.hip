@@ -13,10 +13,11 @@
 //
 // Two kernel families; the planner below picks one, its tile and its K split
 // per shape:
-//   gemm_kernel<ACT, MB> (this file): 16 MB x 256 tiles (MB = 8: 128 rows;
-//     MB = 4: 64 rows), four waves (two workgroups per CU); wave w owns 64
-//     columns and all the rows, and dequantizes its own chunks in registers
-//     between its MFMAs.
+//   gemm_kernel<ACT, MB> (this file): 16 MB x 256 tiles (MB = 4: 64 rows),
+//     four waves (two workgroups per CU); wave w owns 64 columns and all the
+//     rows, and dequantizes its own chunks in registers between its MFMAs.
+//     (A 128-row variant measured slower than the eight-wave tiles on every
+//     large-M shape once those stage x three deep, and was dropped.)
 //   gemm8_kernel (gemm8.h): 256 x 256, 256 x 128, 128 x 256 or 128 x 128
 //     tiles, eight waves; the workgroup dequantizes each weight once into an
 //     LDS operand tile that all waves read.
@@ -24,8 +25,7 @@
 // outside the buffer and fetch nothing), double-buffered with one barrier
 // per stage, and spread the next stage's loads and dequantization between
 // the MFMAs of the current one.  The MFMAs go through the compiler builtin,
-// which pads only the hazards that are there (except the 128-row four-wave
-// tiles, whose accumulators stay in AGPRs through inline assembly).
+// which pads only the hazards that are there.
 //
 // INT8 weights (W8A16) run on gemm8_kernel only: the same stages with a
 // 16-byte run of each 1 KB chunk half per stage (byte codes, u = q + 128,
@@ -59,7 +59,8 @@ struct GroupWords {
 };
 
 template <int ACT, int MB>
-__global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGmThreads, 2) void gemm_kernel(GemmArgs a) {
+    static_assert(MB == 4, "64-row tiles");
     constexpr int BM = 16 * MB;
     constexpr int DMA = BM * kGroup * 2 / 1024 / 4;  // 1 KB x pieces per wave per group
     constexpr int NF = 4 * MB;                       // A fragments per wave per group
@@ -188,13 +189,7 @@ __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmA
                 if (sk == 0 && i < DMA && more) load_x_piece(Anext, gn, i);
                 if (sk == 1 && i < 4 && more) load_w_chunk(gn, i);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // MB = 8 keeps its 128 accumulators in AGPRs through inline
-                    // assembly (the builtin would spill at two workgroups per
-                    // CU); MB = 4 lets the compiler place them and pad hazards
-                    if constexpr (MB == 8) gm_mfma_acc<ACT>(bc[j], aop, acc[i][j]);
-                    else acc[i][j] = gm_mfma<ACT>(bc[j], aop, acc[i][j]);
-                }
+                for (int j = 0; j < 4; ++j) acc[i][j] = gm_mfma<ACT>(bc[j], aop, acc[i][j]);
                 // word j of the next k-step (k-step 3: the next group's
                 // k-step 0) in MB / 4 slices, quarters q0 .. q0 + 4 / PER - 1
                 constexpr int PER = MB / 4;
@@ -253,17 +248,6 @@ __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmA
     }
     if (gl < ng) group(As0, As1, gl);
 
-    if constexpr (MB == 8) {
-        // results of the last inline-assembly MFMAs are read by ordinary
-        // instructions below: wait out the pipeline first, then mark every
-        // accumulator as produced after the wait
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
-    }
-
     // --- epilogue.  Each 16 x 16 block is D = W . x^T: lane (r, kq) holds
     // outputs 4kq .. 4kq + 3 of tile t0 + j for x row r of row block i, four
     // consecutive columns (one 8-byte store, 16 bytes for FP32 partials).
@@ -300,7 +284,7 @@ __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmA
 // The plan is a pure function of (m, n, k, bits): no autotuning and no
 // runtime state, so the workspace size is fixed by the shape.  Candidates:
 // the eight-wave kernel with 256 x 256, 256 x 128, 128 x 256 or 128 x 128
-// tiles and the four-wave kernel with 128 x 256 or 64 x 256 tiles (two
+// tiles and the four-wave kernel with 64 x 256 tiles (two
 // workgroups per CU), each with every K split into equal parts.  A
 // candidate's time is modelled as
 //     rounds x (tile work / (w x per-CU peak) + fixed)  [+ partials / bw + reduce]
@@ -310,12 +294,10 @@ __global__ __launch_bounds__(kGmThreads, MB <= 8 ? 2 : 1) void gemm_kernel(GemmA
 // weights w and the three constants were fitted to the measured times of
 // every tiling and split on 14 large-M shapes (MI355X, launches over >= 1 GiB
 // of distinct weights); with them the model picks the fastest measured
-// candidate on 13 of the 14 and is 1.3 % off on the last.  Measured
-// examples (us): 1024 x 2560 x 2048 fp16, 128 x 128 tiles unsplit 27.9
-// against 32.0 for the 64 x 256 four-wave tiles planned before; 256 x 16384 x
-// 2048, 128 x 128 unsplit 29.0 against 33.3; 1024 x 4096 x 1024, 17.4 against
-// 19.3; 1024 x 2048 x 16384 takes 256 x 256 tiles split in eight (80.8;
-// 256 x 128 in four: 79.7).
+// candidate on all 14.  Measured examples (us): 1024 x 2560 x 2048 fp16,
+// 128 x 128 tiles unsplit 22.7 (256 x 128 in three: 30.3); 1024 x 2048 x
+// 16384, 256 x 128 tiles split in four 76.6 (256 x 256 in eight: 84.5);
+// 4096 x 2048 x 16384, 256 x 256 in two 233.7 (unsplit: 237.3).
 namespace {
 
 struct GemmTile {
@@ -325,12 +307,12 @@ struct GemmTile {
 };
 
 constexpr GemmTile kTiles[] = {
-    {8, 256, 256, 0.55, 1}, {8, 256, 128, 0.38, 1}, {8, 128, 256, 0.32, 1},
-    {8, 128, 128, 0.22, 1}, {4, 128, 256, 0.21, 2}, {4, 64, 256, 0.28, 2},
+    {8, 256, 256, 0.70, 1}, {8, 256, 128, 0.499, 1}, {8, 128, 256, 0.428, 1},
+    {8, 128, 128, 0.289, 1}, {4, 64, 256, 0.381, 2},
 };
 constexpr double kRoundFixed = 4.0e-6;     // s per round of workgroups
-constexpr double kPartialBw = 4.4e12;      // B/s for partial sums written + read back
-constexpr double kReduceLaunch = 3.7e-6;   // s
+constexpr double kPartialBw = 3.93e12;     // B/s for partial sums written + read back
+constexpr double kReduceLaunch = 3.48e-6;  // s
 
 double tile_cost(const GemmTile& t, int64_t m, int64_t n, int64_t groups, int64_t splits, int64_t* gps_out,
                  int64_t* splits_out) {
@@ -416,13 +398,8 @@ hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, i
         else e = launch_gemm8_128x128(a, bits, bf, staged, grid, stream);
         if (e != hipSuccess) return e;
     } else {
-        if (p.mb == 4) {
-            if (bf) gemm_kernel<kActBf16, 4><<<grid, block, 0, stream>>>(a);
-            else gemm_kernel<kActF16, 4><<<grid, block, 0, stream>>>(a);
-        } else {
-            if (bf) gemm_kernel<kActBf16, 8><<<grid, block, 0, stream>>>(a);
-            else gemm_kernel<kActF16, 8><<<grid, block, 0, stream>>>(a);
-        }
+        if (bf) gemm_kernel<kActBf16, 4><<<grid, block, 0, stream>>>(a);
+        else gemm_kernel<kActF16, 4><<<grid, block, 0, stream>>>(a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;

@@ -35,20 +35,6 @@ __device__ inline f32x4_t gm_mfma(uint4 a, uint4 b, f32x4_t c) {
                                                       0, 0, 0);
 }
 
-template <int ACT>
-__device__ inline void gm_mfma_acc(uint4 a, uint4 b, f32x4_t& c) {
-    // accumulator pinned to AGPRs; the two wait states cover a VALU write of
-    // an operand just before
-    if constexpr (ACT == kActBf16)
-        asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-            : "+a"(c)
-            : "v"(__builtin_bit_cast(bf16x8_t, a)), "v"(__builtin_bit_cast(bf16x8_t, b)));
-    else
-        asm("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
-            : "+a"(c)
-            : "v"(__builtin_bit_cast(f16x8_t, a)), "v"(__builtin_bit_cast(f16x8_t, b)));
-}
-
 // Bias of the four output columns c0 .. c0 + 3 of each of a lane's T
 // 16-column tiles (t0 .. t0 + T - 1), in FP32, zero past n or without a
 // bias.  The loads use clamped indices and no branches, so all of them are
