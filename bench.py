@@ -37,6 +37,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -282,26 +283,26 @@ TRACE_M1 = os.path.join(ROOT, "profiles", "gemv_m1_decode_layer_kernel_trace.md"
 TRACE_M1024 = os.path.join(ROOT, "profiles", "gemm_m1024_prefill_kernel_trace.md")
 
 
-def trace_kernel(c):
-    """(name prefix, grid in threads) that identify the kernel a case's
+def trace_kernel(c, bits=4):
+    """(name pattern, grid in threads) that identify the kernel a case's
     automatic plan launches (its main kernel) in a kernel-trace summary."""
     import weight_only_int4_rtn_amd as w4
-    e = w4.explain(c.m, c.n, c.k)
+    e = w4.explain(c.m, c.n, c.k, bits=bits)
     act = 1 if c.dtype == "bf16" else 2
     grid = e["workgroups"] * e["waves"] * 64
     if e["path"] == w4.Path.GEMV:
-        return f"void w4a16::gemv_kernel<{min(c.m, 4)}, {act}, {e['waves']}, ", grid
+        return rf"void w4a16::gemv_kernel<{min(c.m, 4)}, {act}, {e['waves']}, \d+, 0, {bits}>", grid
     if e["path"] == w4.Path.MGEMV:
-        return f"void w4a16::mgemv_kernel<", grid
+        return rf"void w4a16::mgemv_kernel<\d+, {act}, {e['waves']}, \d+, 0, {bits}>", grid
     if e["path"] == w4.Path.SKINNY:
-        return f"void w4a16::skinny_kernel<", grid
+        return rf"void w4a16::skinny_kernel<\d+, {act}, 0, \d+, {bits}>", grid
     if e["waves"] == 8:
-        return f"void w4a16::gemm8_kernel<{act}, ", grid
-    return f"void w4a16::gemm_kernel<{act}, ", grid
+        return rf"void w4a16::gemm8_kernel<{act}, (true|false), {bits}, {e['tile_m']}, {e['tile_n']}>", grid
+    return rf"void w4a16::gemm_kernel<{act}, 4>", grid
 
 
 def trace_row(path, kernel, grid):
-    """(mean us, launches, sources current?) of a kernel (name prefix, grid)
+    """(mean us, launches, sources current?) of a kernel (name pattern, grid)
     in a committed trace summary, or None."""
     try:
         text = open(path).read()
@@ -310,7 +311,7 @@ def trace_row(path, kernel, grid):
     current = f"- sources_sha256: `{sources_hash()}`" in text
     for ln in text.splitlines():
         cells = [c.strip() for c in ln.strip().strip("|").split("|")]
-        if len(cells) >= 6 and cells[0].strip("`").startswith(kernel) and cells[1] == str(grid):
+        if len(cells) >= 6 and re.match(kernel, cells[0].strip("`")) and cells[1] == str(grid):
             try:
                 return float(cells[3]), int(cells[2]), current
             except ValueError:

@@ -2,6 +2,7 @@
 databases built here with the tables and columns they query, and more than
 one GPU is refused with a message."""
 import os
+import re
 import sqlite3
 import subprocess
 import sys
@@ -95,12 +96,16 @@ def test_more_than_one_gpu_is_refused():
 
 def test_trace_kernel_names_the_planned_kernel(tmp_path):
     import synth
-    prefix, grid = bench.trace_kernel(synth.case_by_name("c3_gate_up_m1_k2048_n32768"))
-    assert prefix.startswith("void w4a16::gemv_kernel<1, 1, ") and grid == 2048 * 4 * 64
-    prefix, grid = bench.trace_kernel(synth.case_by_name("c4_m1024_k2048_n32768"))
-    assert prefix.startswith("void w4a16::gemm")
-    # a summary row of that kernel is found by prefix and grid
+    pat, grid = bench.trace_kernel(synth.case_by_name("c3_gate_up_m1_k2048_n32768"))
+    assert grid == 2048 * 4 * 64
+    assert re.match(pat, "void w4a16::gemv_kernel<1, 1, 4, 4, 0, 4>")
+    assert not re.match(pat, "void w4a16::gemv_kernel<1, 1, 4, 4, 0, 8>")  # INT8 codes
+    pat, grid = bench.trace_kernel(synth.case_by_name("c4_m1024_k2048_n32768"))
+    assert re.match(pat, "void w4a16::gemm8_kernel<2, true, 4, 256, 256>")
+    assert not re.match(pat, "void w4a16::gemm8_kernel<2, true, 8, 256, 256>")
+    # a summary row of that kernel is found by pattern and grid, INT8 rows skipped
     table = tmp_path / "t.md"
     table.write_text("| kernel | grid | launches | mean us | total us | share |\n|---|---|---|---|---|---|\n"
-                     f"| `{prefix}16, 256, 256>` | {grid} | 10 | 12.5 | 125 | 50 |\n")
-    assert bench.trace_row(str(table), prefix, grid)[:2] == (12.5, 10)
+                     f"| `void w4a16::gemm8_kernel<2, true, 8, 256, 256>` | {grid} | 7 | 99.0 | 693 | 50 |\n"
+                     f"| `void w4a16::gemm8_kernel<2, true, 4, 256, 256>` | {grid} | 10 | 12.5 | 125 | 50 |\n")
+    assert bench.trace_row(str(table), pat, grid)[:2] == (12.5, 10)
