@@ -64,7 +64,9 @@ typedef enum {
     W4A16_PATH_GEMV = 1,    /* small M: VALU v_dot2 products, split-K, cross-lane reductions */
     W4A16_PATH_MGEMV = 2,   /* small M: the same weight stream contracted on MFMA */
     W4A16_PATH_SKINNY = 3,  /* mid M: register-dequantized MFMA, x tiles through LDS */
-    W4A16_PATH_GEMM = 4     /* large M: LDS-staged dequantized tiles into MFMA */
+    W4A16_PATH_GEMM = 4,    /* large M: LDS-staged dequantized tiles into MFMA */
+    W4A16_PATH_GEMM_STREAMK = 5 /* the large-M kernel with a stream-K decomposition (explicit only:
+                                   slower than the planner's cut on the shapes measured) */
 } w4a16_path_t;
 
 /*
@@ -199,7 +201,8 @@ w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, in
 
 /*
  * Workspace bytes w4a16_linear needs for an [m][k] x [n][k] product, for every
- * kernel path (0 if none, also for invalid sizes).  The caller owns it: the
+ * kernel path but W4A16_PATH_GEMM_STREAMK, whose need w4a16_linear_explain
+ * reports (0 if none, also for invalid sizes).  The caller owns it: the
  * library allocates nothing and reads nothing back ("Piper Kernels", section
  * "Validation contract": no temporary device allocations, no
  * synchronization, nothing that would stop graph capture; "Kernel dispatch
@@ -207,7 +210,8 @@ w4a16_status_t shard_packed_weights(const void* packed, int64_t n, int64_t k, in
  * workload": a kernel used inside a graph must support capture).  A K split needs it: a 1 MiB header of exchange
  * slots through which the small-M kernels add the parts' sums inside one
  * launch, then FP32 partial sums that a second small kernel adds in split
- * order (no floating-point atomics either way).  The caller zero-fills a
+ * order (no floating-point atomics either way); a stream-K launch keeps one
+ * counter per output tile in the header and its FP32 tile sums after it.  The caller zero-fills a
  * workspace once, before its first use; every call leaves the header zero
  * again, so a workspace is reused without clearing (also by calls of other
  * shapes and paths).  Two calls that may run at the same time must not share
@@ -253,6 +257,17 @@ w4a16_status_t w4a16_linear(const void* x, w4a16_dtype_t act_dtype, int64_t m, i
  * is the fast one.  For tests and measurements of each kernel.  The GEMM path
  * addresses its x tiles with 32-bit offsets and returns W4A16_EUNSUPPORTED for
  * ldx > 4194304 (2^22); the automatic choice then takes the SKINNY path.
+ * W4A16_PATH_GEMM_STREAMK runs the GEMM kernel with a stream-K decomposition
+ * whatever the planner would choose ("Kernel dispatch and Humming
+ * quantization in PhyAI", introduction: a kernel cut that suits one workload
+ * can be a poor one for another): the tiles x 128-column groups of work are
+ * cut into runs of equal length, one workgroup each, and the runs that share
+ * a tile add their FP32 sums in K order through the workspace, the last one
+ * to finish a tile storing it (reproducible, no waiting between
+ * workgroups).  Same limits as the GEMM path; its workspace is the one
+ * w4a16_linear_explain reports for it.  The automatic choice never takes
+ * it: on MI355X it measured slower than the planner's equal K split on every
+ * shape tried (the fix-up's slot round trips fall on the launch's tail).
  */
 w4a16_status_t w4a16_linear_with_path(w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,
                                       int64_t m, int64_t k, int64_t ldx, const void* packed,
@@ -328,6 +343,10 @@ typedef struct {
     int64_t workgroups;        /* workgroups of one launch of the main kernel */
     int64_t launches;          /* kernel launches of the whole call */
     uint64_t workspace_bytes;  /* workspace this plan needs (<= w4a16_linear_act_workspace_bytes) */
+    int32_t stream_k;          /* 1: stream-K (workgroups = runs of equal length over tiles x groups;
+                                  splits = the most runs sharing a tile, groups_per_split = the
+                                  longest run) */
+    int32_t reserved;
 } w4a16_plan_t;
 
 /*
@@ -409,8 +428,8 @@ size_t w8a16_linear_workspace_bytes(w4a16_act_t act, int64_t m, int64_t n, int64
  * weight (from pack_weights_int8): the arithmetic, arguments, activations,
  * no-op cases, overlap rules and status codes of w4a16_linear_act.  Paths:
  * W4A16_PATH_AUTO, W4A16_PATH_GEMV (row blocks of 4), W4A16_PATH_MGEMV (row
- * blocks of 16), W4A16_PATH_SKINNY and W4A16_PATH_GEMM (any m; the GEMM with
- * the row-stride limit of w4a16_linear_with_path).
+ * blocks of 16), W4A16_PATH_SKINNY, W4A16_PATH_GEMM and W4A16_PATH_GEMM_STREAMK
+ * (any m; the GEMM with the row-stride limit of w4a16_linear_with_path).
  * workspace >= w8a16_linear_workspace_bytes(act, m, n, k) bytes.
  */
 w4a16_status_t w8a16_linear(w4a16_act_t act, w4a16_path_t path, const void* x, w4a16_dtype_t act_dtype,

@@ -437,11 +437,37 @@ def test_explain_reports_the_plan(lib):
     assert p["launches"] == (3 if p["splits"] > 1 else 2)  # activation, GEMM (+ reduce)
     assert p["workspace_bytes"] >= 300 * 1152 * 2
     assert w4.explain(0, 2048, 2048)["launches"] == 0
+    # the planner's K splits go through the reduce kernel
+    p = w4.explain(1024, 2048, 16384)
+    assert (p["stream_k"], p["splits"], p["launches"], p["workgroups"]) == (0, 4, 2, 256)
+    # the stream-K path: runs of equal length over tiles x groups, one per
+    # CU, its own workspace (not part of workspace_bytes' paths)
+    p = w4.explain(1024, 2560, 2048, path=w4.Path.GEMM_STREAMK)
+    assert p["path"] == w4.Path.GEMM_STREAMK and p["stream_k"] == 1 and p["workgroups"] == 256
+    assert p["launches"] == 1 and p["groups_per_split"] == 10 and p["splits"] == 3
+    assert w4.explain(1024, 2560, 2048)["stream_k"] == 0
+    assert w4.explain(64, 40, 128, path=w4.Path.GEMM_STREAMK)["workgroups"] == 1
     for bad in (dict(bits=2), dict(act=7), dict(path=9)):
         with pytest.raises(ValueError):
             w4.explain(4, 2048, 2048, **bad)
     with pytest.raises(ValueError):
         w4.explain(4, 2048, 100)
+
+
+@pytest.mark.parametrize("t", __import__("tests.gemm_tilings", fromlist=["STREAMK_TILINGS"]).STREAMK_TILINGS,
+                         ids=__import__("tests.gemm_tilings", fromlist=["streamk_id"]).streamk_id)
+def test_streamk_shapes_take_their_cut(lib, t):
+    """Each stream-K test shape takes its tile, one run per CU, and its kind
+    of cut: runs that each lie inside a tile (P slots) or runs that cross
+    tile ends (2 P slots), several runs sharing a tile."""
+    bits, tm, tn, inside, (m, n, k) = t
+    p = w4.explain(m, n, k, path=w4.Path.GEMM_STREAMK, bits=bits)
+    assert (p["stream_k"], p["tile_m"], p["tile_n"], p["launches"], p["workgroups"]) == (1, tm, tn, 1, 256), p
+    groups = k // 128
+    units = -(-m // tm) * -(-n // tn) * groups
+    assert (units % 256 == 0 and groups % (units // 256) == 0) == inside
+    assert p["splits"] >= (4 if inside else 3), p
+    assert p["workspace_bytes"] == (1 << 20) + (1 if inside else 2) * 256 * tm * tn * 4
 
 
 @pytest.mark.parametrize("t", __import__("tests.gemm_tilings", fromlist=["TILINGS"]).TILINGS,

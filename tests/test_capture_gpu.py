@@ -15,12 +15,15 @@ pytestmark = pytest.mark.gpu
 # exchange slots, MGEMV split, SKINNY split + reduce kernel, GEMM, a fused
 # SwiGLU input, the GEMM path with a materialised GELU input; INT8 weights on
 # the GEMV (eight-part split), MGEMV (split through the exchange slots),
-# SKINNY and 256 x 256 GEMM paths
+# SKINNY and 256 x 256 GEMM paths; stream-K GEMMs whose runs share tiles
+# (tile counters in the header, INT4 and INT8, one with a GELU input)
 CALLS = [(1, 2048, 16384, "NONE", 4, "AUTO"), (6, 520, 8192, "NONE", 4, "AUTO"),
          (50, 1000, 4096, "NONE", 4, "AUTO"), (300, 2056, 1152, "NONE", 4, "GEMM"),
          (1, 1024, 4096, "SWIGLU", 4, "AUTO"), (256, 512, 1024, "GELU_TANH", 4, "GEMM"),
          (1, 2048, 16384, "NONE", 8, "AUTO"), (4, 2048, 16384, "NONE", 8, "MGEMV"),
-         (50, 1000, 4096, "SWIGLU", 8, "AUTO"), (300, 2056, 1152, "GELU_TANH", 8, "GEMM")]
+         (50, 1000, 4096, "SWIGLU", 8, "AUTO"), (300, 2056, 1152, "GELU_TANH", 8, "GEMM"),
+         (130, 2056, 2176, "NONE", 4, "GEMM_STREAMK"), (97, 4104, 4096, "GELU_TANH", 4, "GEMM_STREAMK"),
+         (130, 2056, 2176, "NONE", 8, "GEMM_STREAMK")]
 
 
 def test_graph_replays_equal_eager(dev=None):
@@ -42,7 +45,8 @@ def test_graph_replays_equal_eager(dev=None):
             p = w4.pack(c, s)
         y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
         setups.append((m, n, k, w4.Act[act], nbits, w4.Path[path], x, p, b, y))
-        ws_bytes = max(ws_bytes, w4.workspace_bytes(m, n, k, w4.Act[act], nbits))
+        ws_bytes = max(ws_bytes, w4.workspace_bytes(m, n, k, w4.Act[act], nbits),
+                       w4.explain(m, n, k, w4.Act[act], w4.Path[path], nbits)["workspace_bytes"])
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
 
     def run():

@@ -20,7 +20,7 @@ from tests.gpu_util import bits, check_close, require_gpu, row_max_dequant, say,
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ["GEMV", "MGEMV", "SKINNY", "GEMM"]
+PATHS = ["GEMV", "MGEMV", "SKINNY", "GEMM", "GEMM_STREAMK"]
 
 
 @pytest.fixture(scope="module")
@@ -128,7 +128,7 @@ def test_strided_output_bit_exact(dev):
     w, x, b = exact_case(m, n, k, seed=5, dtype=torch.bfloat16, with_bias=True)
     packed, q, s = prepare(w, dev)
     xd, bd = x.to(dev), b.to(dev)
-    need = B.workspace_bytes(m, n, k)
+    need = max(B.workspace_bytes(m, n, k), B.explain(m, n, k, path=B.Path.GEMM_STREAMK)["workspace_bytes"])
     ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     rows = np.array(sorted({0, 1, 255, 256, 511, 1022, 1023}))
     cols = np.array(sorted({0, 7, 8, 255, 256, 16383, 16384, 16385, 16386, 16387}))
@@ -156,25 +156,30 @@ def test_strided_output_bit_exact(dev):
 # have been: every result bit-exact, and the 1 MiB exchange-slot header zero
 # again after every call.  Small-M splits: GEMV into 4, 3 (a tree with an odd
 # child), 8 (too many slots: partial sums and the reduce kernel) and 5 parts;
-# MGEMV into 8 (three tree levels), 16 (partial sums) and 2 parts.
+# MGEMV into 8 (three tree levels), 16 (partial sums) and 2 parts; stream-K
+# GEMMs whose runs share tiles (their tile counters sit in the same header).
 SYNC_HEADER = 1 << 20
 SHARED_WS_CALLS = [("GEMV", 1, 2048, 16384), ("SKINNY", 50, 1000, 4096), ("GEMV", 3, 40, 12288),
                    ("MGEMV", 8, 2048, 16384), ("GEMM", 300, 4104, 640), ("GEMV", 4, 4688, 32768),
-                   ("MGEMV", 16, 1040, 16384), ("GEMV", 2, 100, 20480), ("MGEMV", 6, 520, 2048),
-                   ("GEMV", 1, 2048, 16384)]
+                   ("MGEMV", 16, 1040, 16384), ("GEMM_STREAMK", 130, 2056, 2176), ("GEMV", 2, 100, 20480),
+                   ("MGEMV", 6, 520, 2048), ("GEMM_STREAMK", 97, 4104, 4096), ("GEMV", 1, 2048, 16384)]
 
 
 def test_shared_workspace_header_stays_clear(dev):
     from weight_only_int4_rtn_amd import _binding as B
     lib = w4()
-    need = max(B.workspace_bytes(m, n, k) for _, m, n, k in SHARED_WS_CALLS)
+    need = max(max(B.workspace_bytes(m, n, k), B.explain(m, n, k, path=B.Path[p])["workspace_bytes"])
+               for p, m, n, k in SHARED_WS_CALLS)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     splits_seen = 0
     for i, (path, m, n, k) in enumerate(SHARED_WS_CALLS):
         say(f"shared workspace call {i}: path={path} m={m} n={n} k={k}")
         w, x, b = exact_case(m, n, k, seed=40 + i, dtype=torch.bfloat16, with_bias=(i % 2 == 0))
         packed, q, s = prepare(w, dev)
-        splits_seen += B.workspace_bytes(m, n, k) > 0
+        plan = B.explain(m, n, k, path=B.Path[path])
+        splits_seen += plan["splits"] > 1
+        if path == "GEMM_STREAMK":
+            assert plan["stream_k"] == 1 and plan["splits"] > 1, plan
         y = lib.linear(x.to(dev), packed, n, b.to(dev) if b is not None else None, path=lib.Path[path],
                        workspace=ws)
         torch.cuda.synchronize()
@@ -184,7 +189,7 @@ def test_shared_workspace_header_stays_clear(dev):
         got = y.cpu().to(torch.float64).numpy()
         bad = np.argwhere(got != want)
         assert bad.size == 0, f"call {i} ({path} {m}x{n}x{k}): {len(bad)} mismatches, first {bad[:3].tolist()}"
-    assert splits_seen >= 9
+    assert splits_seen >= 10
 
 
 def random_case(m, n, k, seed, dtype, with_bias):

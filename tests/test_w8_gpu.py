@@ -23,7 +23,7 @@ from tests.gpu_util import bits, check_close, require_gpu, row_max_dequant, say,
 
 pytestmark = pytest.mark.gpu
 
-PATHS8 = ["GEMV", "MGEMV", "SKINNY", "GEMM", "AUTO"]
+PATHS8 = ["GEMV", "MGEMV", "SKINNY", "GEMM", "GEMM_STREAMK", "AUTO"]
 
 
 @pytest.fixture(scope="module")

@@ -28,6 +28,7 @@ class Path(enum.IntEnum):
     MGEMV = 2
     SKINNY = 3
     GEMM = 4
+    GEMM_STREAMK = 5
 
 
 class Act(enum.IntEnum):
@@ -58,7 +59,8 @@ class PlanT(ctypes.Structure):
     """w4a16_plan_t"""
     _fields_ = [("path", ctypes.c_int32), ("waves", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("splits", ctypes.c_int32), ("groups_per_split", ctypes.c_int32),
-                ("workgroups", ctypes.c_int64), ("launches", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
+                ("workgroups", ctypes.c_int64), ("launches", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
+                ("stream_k", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -223,7 +225,7 @@ def explain(m: int, n: int, k: int, act: Act = Act.NONE, path: Path = Path.AUTO,
     plan = PlanT()
     _check(lib().w4a16_linear_explain(_bits(bits), int(act), int(path), m, n, k, ctypes.byref(plan)),
            "w4a16_linear_explain")
-    out = {f: getattr(plan, f) for f, _ in PlanT._fields_}
+    out = {f: getattr(plan, f) for f, _ in PlanT._fields_ if f != "reserved"}
     out["path"] = Path(out["path"])
     return out
 
@@ -434,6 +436,8 @@ def linear(x: torch.Tensor, packed: torch.Tensor, n: int, bias: torch.Tensor | N
     if workspace is not None and not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     need = workspace_bytes(m, n, k, act, bits)
+    if Path(path) == Path.GEMM_STREAMK and m > 0 and n > 0:
+        need = max(need, explain(m, n, k, act, path, bits)["workspace_bytes"])
     if workspace is None and need > 0 and torch.cuda.is_current_stream_capturing():
         # a workspace allocated here would belong to the graph's memory pool
         # and its zero fill would only run at replay: a captured call needs

@@ -33,6 +33,14 @@ constexpr int64_t kGemmMaxLd = int64_t(1) << 22;
 // Largest rank of a low-rank update (mat1 [n][rank] @ mat2 [rank][k]).
 constexpr int64_t kMaxRank = int64_t(1) << 16;
 
+bool valid_path(w4a16_path_t p) {
+    return p == W4A16_PATH_AUTO || p == W4A16_PATH_GEMV || p == W4A16_PATH_MGEMV || p == W4A16_PATH_SKINNY ||
+           p == W4A16_PATH_GEMM || p == W4A16_PATH_GEMM_STREAMK;
+}
+
+// the large-M kernel, with the planner's decomposition or forced stream-K
+bool is_gemm(w4a16_path_t p) { return p == W4A16_PATH_GEMM || p == W4A16_PATH_GEMM_STREAMK; }
+
 bool valid_nk(int64_t n, int64_t k) {
     return n >= 0 && n <= kMaxDim && k > 0 && k <= kMaxDim && k % kGroup == 0;
 }
@@ -50,6 +58,7 @@ size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bi
         case W4A16_PATH_MGEMV: return plan_mgemv(m < 16 ? m : 16, n, k, bits).workspace;
         case W4A16_PATH_SKINNY: return plan_skinny(m, n, k, bits).workspace;
         case W4A16_PATH_GEMM: return plan_gemm(m, n, k, bits).workspace;
+        case W4A16_PATH_GEMM_STREAMK: return plan_gemm_streamk(m, n, k, bits).workspace;
         default: return 0;
     }
 }
@@ -304,7 +313,7 @@ size_t act_input_offset(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int 
 // the activated input [m][k] after its own workspace.
 size_t act_path_workspace(int act_fn, w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bits) {
     const size_t base = path_workspace(path, m, n, k, bits);
-    if (act_fn == kActFnNone || path != W4A16_PATH_GEMM) return base;
+    if (act_fn == kActFnNone || !is_gemm(path)) return base;
     return act_input_offset(path, m, n, k, bits) + size_t(m) * size_t(k) * 2;
 }
 
@@ -328,9 +337,7 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
                            void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream,
                            bool launch = true) {
     if (act_dtype != W4A16_BF16 && act_dtype != W4A16_F16) return W4A16_EUNSUPPORTED;
-    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MGEMV &&
-        path != W4A16_PATH_SKINNY && path != W4A16_PATH_GEMM)
-        return W4A16_EINVAL;
+    if (!valid_path(path)) return W4A16_EINVAL;
     if (!valid_nk(n, k) || m < 0 || m > kMaxDim) return W4A16_EINVAL;
     const int64_t xcols = act_fn == kActFnSwiglu ? 2 * k : k;  // SwiGLU rows hold [up | gate]
     if (ldx < xcols || ldx > kMaxDim || ldx % 8 != 0 || ldy < n || ldy > kMaxDim) return W4A16_EINVAL;
@@ -345,7 +352,7 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
         path = bits == 8 ? w8a16_linear_choose_path(m, n, k) : w4a16_linear_choose_path(m, n, k);
         if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) path = W4A16_PATH_SKINNY;
     }
-    if (path == W4A16_PATH_GEMM && gemm_ld > kGemmMaxLd) return W4A16_EUNSUPPORTED;
+    if (is_gemm(path) && gemm_ld > kGemmMaxLd) return W4A16_EUNSUPPORTED;
 
     const size_t xbytes = span_bytes(m, xcols, ldx, 2), ybytes = span_bytes(m, n, ldy, 2),
                  pbytes = bits == 8 ? w8a16_packed_bytes(n, k) : w4a16_packed_bytes(n, k),
@@ -385,13 +392,14 @@ w4a16_status_t linear_impl(int bits, int act_fn, w4a16_path_t path, const void* 
         }
         return W4A16_OK;
     }
-    if (path == W4A16_PATH_GEMM) {
+    if (is_gemm(path)) {
+        const bool sk = path == W4A16_PATH_GEMM_STREAMK;
         if (act_fn == kActFnNone)
-            return from_hip(launch_gemm(x, act, bits, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
+            return from_hip(launch_gemm(x, act, bits, m, k, ldx, packed, n, bias, y, ldy, workspace, sk, s));
         void* xa = static_cast<uint8_t*>(workspace) + act_input_offset(path, m, n, k, bits);
         const hipError_t e = launch_activate(x, act, act_fn, m, k, ldx, xa, s);
         if (e != hipSuccess) return W4A16_EHIP;
-        return from_hip(launch_gemm(xa, act, bits, m, k, k, packed, n, bias, y, ldy, workspace, s));
+        return from_hip(launch_gemm(xa, act, bits, m, k, k, packed, n, bias, y, ldy, workspace, sk, s));
     }
     return from_hip(launch_skinny(x, act, act_fn, bits, m, k, ldx, packed, n, bias, y, ldy, workspace, s));
 }
@@ -419,9 +427,7 @@ w4a16_status_t w4a16_linear_explain(int bits, w4a16_act_t act, w4a16_path_t path
                                     w4a16_plan_t* plan) {
     if (!plan || (bits != 4 && bits != 8)) return W4A16_EINVAL;
     if (act != W4A16_ACT_NONE && act != W4A16_ACT_SWIGLU && act != W4A16_ACT_GELU_TANH) return W4A16_EINVAL;
-    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MGEMV &&
-        path != W4A16_PATH_SKINNY && path != W4A16_PATH_GEMM)
-        return W4A16_EINVAL;
+    if (!valid_path(path)) return W4A16_EINVAL;
     if (!valid_nk(n, k) || m < 0 || m > kMaxDim) return W4A16_EINVAL;
     *plan = w4a16_plan_t{};
     // rows contiguous: the GEMM sees a row stride of k (also for an activation,
@@ -439,7 +445,7 @@ w4a16_status_t w4a16_linear_explain(int bits, w4a16_act_t act, w4a16_path_t path
         case W4A16_PATH_GEMV: info = describe_gemv(m < 4 ? m : 4, n, k, bits); launches = ceil_div(m, 4); break;
         case W4A16_PATH_MGEMV: info = describe_mgemv(m < 16 ? m : 16, n, k, bits); launches = ceil_div(m, 16); break;
         case W4A16_PATH_SKINNY: info = describe_skinny(m, n, k, bits); break;
-        default: info = describe_gemm(m, n, k, bits); break;
+        default: info = describe_gemm(m, n, k, bits, path == W4A16_PATH_GEMM_STREAMK); break;
     }
     plan->waves = info.waves;
     plan->tile_m = info.tile_m;
@@ -447,7 +453,8 @@ w4a16_status_t w4a16_linear_explain(int bits, w4a16_act_t act, w4a16_path_t path
     plan->splits = info.splits;
     plan->groups_per_split = info.gps;
     plan->workgroups = info.workgroups;
-    plan->launches = launches * (info.reduce ? 2 : 1) + (path == W4A16_PATH_GEMM && fn != kActFnNone ? 1 : 0);
+    plan->launches = launches * (info.reduce ? 2 : 1) + (is_gemm(path) && fn != kActFnNone ? 1 : 0);
+    plan->stream_k = info.stream_k ? 1 : 0;
     plan->workspace_bytes = uint64_t(act_path_workspace(fn, path, m, n, k, bits));
     return W4A16_OK;
 }

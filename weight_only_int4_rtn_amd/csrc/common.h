@@ -211,6 +211,10 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t b
 
 // Cache-policy operand of a buffer load: nontemporal (data read once).
 constexpr int kBufNontemporal = 2;
+// Cache-policy operand of a buffer access at device scope (SC1): stores write
+// through the L2 and loads read past it, so workgroups on different XCDs
+// see each other's data without L2 write-backs or invalidations.
+constexpr int kCoherent = 16;
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, then s_barrier.  __syncthreads() also waits for every

@@ -33,6 +33,14 @@
 //
 // The epilogue adds the bias in FP32 and rounds once to the output dtype, or,
 // for a K split, stores FP32 partial sums for the split-K reduce kernel.
+//
+// Stream-K (the explicit W4A16_PATH_GEMM_STREAMK path): gemm8_kernel on up
+// to 256 x 128 tiles with the launch's tiles x groups cut into one run of
+// equal length per CU; runs that share a tile add their sums in-kernel
+// (see gemm8.h).  The planner itself keeps to the equal splits, which
+// measured faster (plan_gemm below).
+#include <algorithm>
+
 #include "gemm_common.h"
 
 namespace w4a16 {
@@ -332,7 +340,41 @@ double tile_cost(const GemmTile& t, int64_t m, int64_t n, int64_t groups, int64_
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits) {
+// A stream-K plan of bm x bn tiles (eight waves): the tiles x groups units
+// cut into `runs` runs of equal length (+-1), one workgroup each.
+// Workspace: the header (one counter per tile) and an FP32 tile slot per
+// run, two when runs cross tile ends.  256 x 256 tiles are not offered (see
+// launch_gemm8).
+constexpr int64_t kSkMaxRuns = 256;  // one run per CU
+
+GemmPlan plan_gemm_sk(int64_t m, int64_t n, int64_t k, int bits, int bm, int bn, int64_t runs) {
+    GemmPlan p{};
+    const Layout L(n, k, bits);
+    p.waves = 8;
+    p.bm = bm;
+    p.bn = bn;
+    p.mb = bm / 16;
+    p.mtiles = ceil_div(m, bm);
+    p.ntiles = ceil_div(n, bn);
+    p.splits = 1;
+    p.sk = true;
+    const int64_t units = p.mtiles * p.ntiles * L.groups;
+    p.wgs = std::min(runs, units);
+    p.gps = int(ceil_div(units, p.wgs));
+    // runs that each lie inside one tile: units / runs whole and a divisor of the tile's groups
+    const bool inside = units % p.wgs == 0 && L.groups % (units / p.wgs) == 0;
+    p.workspace = kSyncBytes + size_t((inside ? 1 : 2) * p.wgs) * bm * bn * 4;
+    return p;
+}
+
+namespace {
+
+// The tile counters live in the workspace header.
+bool sk_fits(int64_t m, int64_t n, int bm, int bn) {
+    return ceil_div(m, bm) * ceil_div(n, bn) <= int64_t(kSyncBytes / 4);
+}
+
+GemmPlan plan_gemm_dp(int64_t m, int64_t n, int64_t k, int bits) {
     GemmPlan p{};
     const Layout L(n, k, bits);
     double best = 1e30;
@@ -355,19 +397,53 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits) {
     p.mb = p.bm / 16;
     p.mtiles = ceil_div(m, p.bm);
     p.ntiles = ceil_div(n, p.bn);
+    p.sk = false;
+    p.wgs = p.mtiles * p.ntiles * p.splits;
     p.workspace = p.splits > 1 ? kSyncBytes + size_t(p.splits) * m * p.ntiles * p.bn * 4 : 0;
     return p;
 }
 
-PlanInfo describe_gemm(int64_t m, int64_t n, int64_t k, int bits) {
-    const GemmPlan p = plan_gemm(m, n, k, bits);
-    return {p.waves, p.bm, p.bn, p.splits, p.gps, p.mtiles * p.ntiles * p.splits, p.splits > 1};
+}  // namespace
+
+// The forced stream-K path: the equal-split planner's tile where the
+// stream-K kernel takes it (256 x 256 -> 256 x 128, the four-wave 64 x 256
+// -> 128 x 256), one run per CU.
+GemmPlan plan_gemm_streamk(int64_t m, int64_t n, int64_t k, int bits) {
+    const GemmPlan d = plan_gemm_dp(m, n, k, bits);
+    const int bm = d.waves == 4 ? 128 : d.bm, bn = d.waves == 4 ? 256 : (d.bm == 256 ? 128 : d.bn);
+    return plan_gemm_sk(m, n, k, bits, bm, bn, kSkMaxRuns);
+}
+
+// The planner's choice: the equal-split candidates above.  Stream-K is not
+// among them: measured on MI355X it was slower than the equal split with
+// the reduce kernel on every shape tried.  A run's second segment restarts
+// the stage pipeline, and the fix-up puts the slot round trips of the last
+// run to finish each tile on the launch's tail, on the few workgroups that
+// finish tiles, where the reduce kernel spreads that pass over every CU
+// (1024 x 2560 x 2048: 23.7 us unsplit on 128 x 128 tiles, 28.1 us as
+// stream-K; 1024 x 16384 x 2048 on 256 x 128 tiles in four parts: 77 us
+// with the reduce kernel, 80 us with the parts added in-kernel).
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits) { return plan_gemm_dp(m, n, k, bits); }
+
+PlanInfo describe_gemm(int64_t m, int64_t n, int64_t k, int bits, bool streamk) {
+    const GemmPlan p = streamk ? plan_gemm_streamk(m, n, k, bits) : plan_gemm(m, n, k, bits);
+    if (!p.sk) return {p.waves, p.bm, p.bn, p.splits, p.gps, p.wgs, p.splits > 1, false};
+    // the most runs that share one tile
+    const int64_t G = Layout(n, k, bits).groups, U = p.mtiles * p.ntiles * G, P = p.wgs;
+    int64_t most = 1;
+    for (int64_t w = 0; w < P; ++w) {
+        const int64_t u0 = w * U / P;
+        if (u0 % G == 0) continue;  // only a run that begins inside a tile shares it with earlier runs
+        const int64_t t = u0 / G;
+        most = std::max(most, ((t * G + G) * P - 1) / U - ((t * G + 1) * P - 1) / U + 1);
+    }
+    return {p.waves, p.bm, p.bn, int(most), p.gps, p.wgs, false, true};
 }
 
 hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                       int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+                       int64_t n, const void* bias, void* y, int64_t ldy, void* workspace, bool streamk,
                        hipStream_t stream) {
-    const GemmPlan p = plan_gemm(m, n, k, bits);
+    const GemmPlan p = streamk ? plan_gemm_streamk(m, n, k, bits) : plan_gemm(m, n, k, bits);
     // the x tile's buffer resource takes 32-bit byte offsets
     if (int64_t(p.bm) * ldx * 2 > int64_t(0xFFFFFFFF)) return hipErrorInvalidValue;
     GemmArgs a;
@@ -387,15 +463,17 @@ hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, i
     a.gps = p.gps;
     a.mtiles = p.mtiles;
     a.ntiles = p.ntiles;
-    const dim3 grid(unsigned(p.mtiles * p.ntiles * p.splits)), block(kGmThreads);
+    a.counters = static_cast<unsigned*>(workspace);
+    a.sk_units = p.sk ? p.mtiles * p.ntiles * (k / kGroup) : 0;
+    const dim3 grid(unsigned(p.wgs)), block(kGmThreads);
     const bool bf = act == kActBf16;
     if (p.waves == 8) {
         const bool staged = p.splits == 1 && a.vec16;
         hipError_t e;
-        if (p.bm == 256 && p.bn == 256) e = launch_gemm8_256x256(a, bits, bf, staged, grid, stream);
-        else if (p.bm == 256) e = launch_gemm8_256x128(a, bits, bf, staged, grid, stream);
-        else if (p.bn == 256) e = launch_gemm8_128x256(a, bits, bf, staged, grid, stream);
-        else e = launch_gemm8_128x128(a, bits, bf, staged, grid, stream);
+        if (p.bm == 256 && p.bn == 256) e = launch_gemm8_256x256(a, bits, bf, staged, p.sk, grid, stream);
+        else if (p.bm == 256) e = launch_gemm8_256x128(a, bits, bf, staged, p.sk, grid, stream);
+        else if (p.bn == 256) e = launch_gemm8_128x256(a, bits, bf, staged, p.sk, grid, stream);
+        else e = launch_gemm8_128x128(a, bits, bf, staged, p.sk, grid, stream);
         if (e != hipSuccess) return e;
     } else {
         if (bf) gemm_kernel<kActBf16, 4><<<grid, block, 0, stream>>>(a);

@@ -16,11 +16,13 @@ struct GemmArgs {
     const uint16_t* bias;
     uint16_t* y;
     int64_t ldy;
-    float* partials;  // [splits][m][ntiles * tile columns] when splits > 1
+    float* partials;  // [splits][m][ntiles * tile columns] when splits > 1; stream-K: slots of FP32 tile sums
     int splits, gps;
     int vec_store;    // y 8-byte aligned and ldy % 4 == 0: 4 outputs per store
     int vec16;        // y 16-byte aligned and ldy % 8 == 0: 8 outputs per store
     int64_t mtiles, ntiles;
+    unsigned* counters;  // stream-K: a counter per tile in the workspace header (zero between calls)
+    int64_t sk_units;    // stream-K: tiles x 128-column groups (0: not stream-K)
 };
 
 // D = A . B + C on v_mfma_f32_16x16x32_{bf16,f16} through the compiler
@@ -119,9 +121,13 @@ struct BoolC {
 
 // The eight-wave kernel's launchers, one per workgroup tile (rows x
 // columns), defined in gemm8_rows256.hip and gemm8_rows128.hip.
-hipError_t launch_gemm8_256x256(const GemmArgs& a, int bits, bool bf, bool staged, dim3 grid, hipStream_t stream);
-hipError_t launch_gemm8_256x128(const GemmArgs& a, int bits, bool bf, bool staged, dim3 grid, hipStream_t stream);
-hipError_t launch_gemm8_128x256(const GemmArgs& a, int bits, bool bf, bool staged, dim3 grid, hipStream_t stream);
-hipError_t launch_gemm8_128x128(const GemmArgs& a, int bits, bool bf, bool staged, dim3 grid, hipStream_t stream);
+hipError_t launch_gemm8_256x256(const GemmArgs& a, int bits, bool bf, bool staged, bool sk, dim3 grid,
+                                hipStream_t stream);
+hipError_t launch_gemm8_256x128(const GemmArgs& a, int bits, bool bf, bool staged, bool sk, dim3 grid,
+                                hipStream_t stream);
+hipError_t launch_gemm8_128x256(const GemmArgs& a, int bits, bool bf, bool staged, bool sk, dim3 grid,
+                                hipStream_t stream);
+hipError_t launch_gemm8_128x128(const GemmArgs& a, int bits, bool bf, bool staged, bool sk, dim3 grid,
+                                hipStream_t stream);
 
 }  // namespace w4a16

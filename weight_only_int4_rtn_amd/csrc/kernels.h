@@ -48,9 +48,14 @@ struct GemmPlan {
     int waves;            // 8: the eight-wave kernel (bm x bn tiles); 4: the four-wave kernel (bm x 256)
     int bm, bn;           // workgroup tile: rows of x, output columns
     int mb, gps, splits;  // mb = bm / 16; gps: groups per K split
+    bool sk;              // stream-K: wgs workgroups, each a run of tiles x groups units (splits 1)
+    int64_t wgs;          // workgroups of the launch
     size_t workspace;
 };
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int bits = 4);
+// stream-K plans: a given tile, and the modelled fastest stream-K tile
+GemmPlan plan_gemm_sk(int64_t m, int64_t n, int64_t k, int bits, int bm, int bn, int64_t runs);
+GemmPlan plan_gemm_streamk(int64_t m, int64_t n, int64_t k, int bits);
 
 // One launch of a path's main kernel, as w4a16_linear_explain reports it.
 struct PlanInfo {
@@ -59,11 +64,12 @@ struct PlanInfo {
     int splits, gps;     // K parts, 128-column groups per part
     int64_t workgroups;  // grid size
     bool reduce;         // a split-K reduce launch follows
+    bool stream_k;       // stream-K: splits = the most runs sharing a tile, gps = the longest run
 };
 PlanInfo describe_gemv(int64_t m, int64_t n, int64_t k, int bits);    // m <= 4 (one row block)
 PlanInfo describe_mgemv(int64_t m, int64_t n, int64_t k, int bits);   // m <= 16 (one row block)
 PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits);
-PlanInfo describe_gemm(int64_t m, int64_t n, int64_t k, int bits);
+PlanInfo describe_gemm(int64_t m, int64_t n, int64_t k, int bits, bool streamk);
 
 hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int64_t ldw,
                            uint8_t* codes, float* scales, hipStream_t stream);
@@ -111,8 +117,10 @@ hipError_t launch_skinny(const void* x, int act, int act_fn, int bits, int64_t m
 // The activated input [m][k] (row stride k) of x for the GEMM path.
 hipError_t launch_activate(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx, void* out,
                            hipStream_t stream);
+// streamk: the stream-K decomposition (its modelled fastest tile) instead of
+// the planner's choice
 hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, int64_t ldx, const void* packed,
-                       int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
+                       int64_t n, const void* bias, void* y, int64_t ldy, void* workspace, bool streamk,
                        hipStream_t stream);
 
 // The argument checks of w4a16_linear alone (its status before any launch;
