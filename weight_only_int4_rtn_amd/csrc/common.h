@@ -253,6 +253,38 @@ __device__ inline uint4 bpairs(const uint32_t* w, int s) {
     }
 }
 
+// v >> N as one v_lshrrev_b64 (the compiler would split it into a funnel
+// shift and a 32-bit shift).
+template <int N>
+__device__ inline uint64_t shr64(uint64_t v) {
+    uint64_t d;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(d) : "i"(N), "v"(v));
+    return d;
+}
+
+// The packed pairs of k-steps s and s + 1 (s even) of a lane's chunk data,
+// b[h] = bpairs(w, s + h).  INT4 words go two at a time through 64-bit
+// shifts: one shift serves both words (the bits it carries from the upper
+// word into the lower fall outside the 0x000F000F mask), 1.5 shifts per word
+// instead of 3.
+template <int BITS, int ACT>
+__device__ inline void bpairs2(const uint32_t* w, int s, uint4 (&b)[2]) {
+    if constexpr (BITS == 8) {
+        b[0] = bpairs<BITS, ACT>(w, s);
+        b[1] = bpairs<BITS, ACT>(w, s + 1);
+    } else {
+        constexpr uint32_t magic = ACT == kActBf16 ? kMagicBf16x2 : kMagicF16x2;
+        const uint64_t v = uint64_t(w[s]) | (uint64_t(w[s + 1]) << 32);
+        const uint64_t sh[4] = {v, shr64<4>(v), shr64<8>(v), shr64<12>(v)};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            b[h] = make_uint4(and_or(uint32_t(sh[0] >> (32 * h)), 0x000F000Fu, magic),
+                              and_or(uint32_t(sh[1] >> (32 * h)), 0x000F000Fu, magic),
+                              and_or(uint32_t(sh[2] >> (32 * h)), 0x000F000Fu, magic),
+                              and_or(uint32_t(sh[3] >> (32 * h)), 0x000F000Fu, magic));
+    }
+}
+
 // The offset each packed pair value carries: off + q.
 template <int ACT, int BITS = 4>
 __device__ inline constexpr float code_offset() {

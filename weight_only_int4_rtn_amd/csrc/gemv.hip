@@ -196,13 +196,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
                 const uint16_t* xp = xs + m * klen + gl * kGroup + 8 * kq;
                 float acc = 0.0f;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint4 xq = *reinterpret_cast<const uint4*>(xp + 32 * s);
-                    const uint4 bp = bpairs<BITS, ACT>(words, s);
-                    acc = dot2<ACT>(bp.x, xq.x, acc);
-                    acc = dot2<ACT>(bp.y, xq.y, acc);
-                    acc = dot2<ACT>(bp.z, xq.z, acc);
-                    acc = dot2<ACT>(bp.w, xq.w, acc);
+                for (int s = 0; s < 4; s += 2) {
+                    uint4 bp[2];
+                    bpairs2<BITS, ACT>(words, s, bp);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint4 xq = *reinterpret_cast<const uint4*>(xp + 32 * (s + h));
+                        acc = dot2<ACT>(bp[h].x, xq.x, acc);
+                        acc = dot2<ACT>(bp[h].y, xq.y, acc);
+                        acc = dot2<ACT>(bp[h].z, xq.z, acc);
+                        acc = dot2<ACT>(bp[h].w, xq.w, acc);
+                    }
                 }
                 acc = fmaf(-off, xsum[(m * ng + gl) * 4 + kq], acc);
                 tot[m] = fmaf(scale, acc, tot[m]);

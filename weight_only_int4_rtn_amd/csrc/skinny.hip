@@ -155,9 +155,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
             words[4 * h + 2] = cw[gl][h].z;
             words[4 * h + 3] = cw[gl][h].w;
         }
-        uint4 b[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) b[s] = bpairs<BITS, ACT>(words, s);
+        uint4 b01[2], b23[2];
+        bpairs2<BITS, ACT>(words, 0, b01);
+        bpairs2<BITS, ACT>(words, 2, b23);
+        const uint4 b[4] = {b01[0], b01[1], b23[0], b23[1]};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
