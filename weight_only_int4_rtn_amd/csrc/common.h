@@ -216,6 +216,27 @@ constexpr int kBufNontemporal = 2;
 // see each other's data without L2 write-backs or invalidations.
 constexpr int kCoherent = 16;
 
+// v of lane (lane ^ M), M a power of two below 32: one ds_swizzle in bitmask
+// mode (__shfl_xor spends several vector instructions per call on the lane
+// index and its bounds).
+template <int M>
+__device__ inline float lane_xor(float v) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16, "swizzle mask");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+}
+
+// v(lane) + v(lane ^ 32), and the same with max: one v_permlane32_swap gives
+// each lane the pair {v(lane), v(lane ^ 32)} (in either order; both
+// operations are commutative, so every lane gets the same bits).
+__device__ inline float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, then s_barrier.  __syncthreads() also waits for every
 // outstanding global load (vmcnt(0)), which would serialise the weight

@@ -166,8 +166,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         if (on) *reinterpret_cast<uint4*>(xs + m * klen + c * 8) = xv[j];
         if (!on) xv[j] = make_uint4(0u, 0u, 0u, 0u);
         float s = sum8<ACT>(xv[j]);
-        s += __shfl_xor(s, 4, 16);
-        s += __shfl_xor(s, 8, 16);
+        s += lane_xor<4>(s);
+        s += lane_xor<8>(s);
         const int wb = c & 15;
         if (on && wb < 4) xsum[(m * ng + (c >> 4)) * 4 + wb] = s;
     }
@@ -217,8 +217,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     // Rows: sum the 4 lane-quarters, then the waves.
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        tot[m] += __shfl_xor(tot[m], 16);
-        tot[m] += __shfl_xor(tot[m], 32);
+        tot[m] += lane_xor<16>(tot[m]);
+        tot[m] = sum_xor32(tot[m]);
         if (lane < 16) red[(wave * M + m) * 16 + lane] = tot[m];
     }
     lds_barrier();

@@ -64,8 +64,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     // reduce over the 16 threads of the group (lanes differing in bits 0..3)
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+    amax = fmaxf(amax, lane_xor<1>(amax));
+    amax = fmaxf(amax, lane_xor<2>(amax));
+    amax = fmaxf(amax, lane_xor<4>(amax));
+    amax = fmaxf(amax, lane_xor<8>(amax));
     if (!active) return;
 
     const float s = amax / 7.0f;
@@ -120,8 +122,10 @@ __global__ __launch_bounds__(256) void quantize8_kernel(const void* __restrict__
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+    amax = fmaxf(amax, lane_xor<1>(amax));
+    amax = fmaxf(amax, lane_xor<2>(amax));
+    amax = fmaxf(amax, lane_xor<4>(amax));
+    amax = fmaxf(amax, lane_xor<8>(amax));
     if (!active) return;
 
     const float s = amax / 127.0f;

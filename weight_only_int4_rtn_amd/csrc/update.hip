@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
             amax = fmaxf(amax, fabsf(v));
         }
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = fmaxf(amax, lane_xor<16>(amax));
+    amax = max_xor32(amax);
     const float scale = amax / kQmax;
 
     uint32_t out[4 * H];
