@@ -297,7 +297,8 @@ def trace_kernel(c, bits=4):
     if e["path"] == w4.Path.SKINNY:
         return rf"void w4a16::skinny_kernel<\d+, {act}, 0, \d+, {bits}>", grid
     if e["waves"] == 8:
-        return rf"void w4a16::gemm8_kernel<{act}, (true|false), {bits}, {e['tile_m']}, {e['tile_n']}>", grid
+        sk = "true" if e["stream_k"] else "false"
+        return rf"void w4a16::gemm8_kernel<{act}, (true|false), {bits}, {e['tile_m']}, {e['tile_n']}, {sk}>", grid
     return rf"void w4a16::gemm_kernel<{act}, 4>", grid
 
 

@@ -101,11 +101,12 @@ def test_trace_kernel_names_the_planned_kernel(tmp_path):
     assert re.match(pat, "void w4a16::gemv_kernel<1, 1, 4, 4, 0, 4>")
     assert not re.match(pat, "void w4a16::gemv_kernel<1, 1, 4, 4, 0, 8>")  # INT8 codes
     pat, grid = bench.trace_kernel(synth.case_by_name("c4_m1024_k2048_n32768"))
-    assert re.match(pat, "void w4a16::gemm8_kernel<2, true, 4, 256, 256>")
-    assert not re.match(pat, "void w4a16::gemm8_kernel<2, true, 8, 256, 256>")
+    assert re.match(pat, "void w4a16::gemm8_kernel<2, true, 4, 256, 256, false>")
+    assert not re.match(pat, "void w4a16::gemm8_kernel<2, true, 8, 256, 256, false>")
+    assert not re.match(pat, "void w4a16::gemm8_kernel<2, true, 4, 256, 256, true>")  # stream-K
     # a summary row of that kernel is found by pattern and grid, INT8 rows skipped
     table = tmp_path / "t.md"
     table.write_text("| kernel | grid | launches | mean us | total us | share |\n|---|---|---|---|---|---|\n"
-                     f"| `void w4a16::gemm8_kernel<2, true, 8, 256, 256>` | {grid} | 7 | 99.0 | 693 | 50 |\n"
-                     f"| `void w4a16::gemm8_kernel<2, true, 4, 256, 256>` | {grid} | 10 | 12.5 | 125 | 50 |\n")
+                     f"| `void w4a16::gemm8_kernel<2, true, 8, 256, 256, false>` | {grid} | 7 | 99.0 | 693 | 50 |\n"
+                     f"| `void w4a16::gemm8_kernel<2, true, 4, 256, 256, false>` | {grid} | 10 | 12.5 | 125 | 50 |\n")
     assert bench.trace_row(str(table), pat, grid)[:2] == (12.5, 10)
