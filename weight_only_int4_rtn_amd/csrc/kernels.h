@@ -10,13 +10,15 @@
 namespace w4a16 {
 
 // Workspace of a K-split launch: a header of kSyncBytes holding the 64-bit
-// exchange slots through which small-M launches finish their split in-kernel,
-// then FP32 partial sums [splits][m][npad] for the split-K reduce kernel.
-// The header must be zero before a call and every call leaves it zero (the
-// thread that empties a slot clears it); the partial sums need no
-// initialisation (every element that reaches an output is written first;
-// the reduce kernel also reads, and drops, the padding columns past n of a
-// 4-column group).  Every path places its partial sums after the header.
+// exchange slots through which small-M launches finish their split in-kernel
+// (or the 32-bit tile counters of the mid-M and stream-K launches), then
+// FP32 partial sums [splits][m][npad] for the split-K reduce kernel (or the
+// tile slots those launches add in-kernel).  The header must be zero before
+// a call and every call leaves it zero (the thread that empties a slot, or
+// completes a count, clears it); the partial sums need no initialisation
+// (every element that reaches an output is written first; the reduce kernel
+// also reads, and drops, the padding columns past n of a 4-column group).
+// Every path places its partial sums after the header.
 constexpr size_t kSyncBytes = size_t(1) << 20;
 
 struct GemvPlan {
@@ -39,6 +41,7 @@ struct SkinnyPlan {
     int gps, splits;
     int gmax;           // register capacity for chunks (4, 8, 16 groups)
     int64_t tile_groups, mblocks;
+    bool in_kernel;     // a K split finished inside the launch (else by the reduce kernel)
     size_t workspace;
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits = 4);
@@ -117,8 +120,8 @@ hipError_t launch_skinny(const void* x, int act, int act_fn, int bits, int64_t m
 // The activated input [m][k] (row stride k) of x for the GEMM path.
 hipError_t launch_activate(const void* x, int act, int act_fn, int64_t m, int64_t k, int64_t ldx, void* out,
                            hipStream_t stream);
-// streamk: the stream-K decomposition (its modelled fastest tile) instead of
-// the planner's choice
+// streamk: the stream-K decomposition (on the planner's tile, or the nearest
+// one it offers) instead of the planner's choice
 hipError_t launch_gemm(const void* x, int act, int bits, int64_t m, int64_t k, int64_t ldx, const void* packed,
                        int64_t n, const void* bias, void* y, int64_t ldy, void* workspace, bool streamk,
                        hipStream_t stream);
