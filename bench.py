@@ -295,7 +295,9 @@ def trace_kernel(c, bits=4):
     if e["path"] == w4.Path.MGEMV:
         return rf"void w4a16::mgemv_kernel<\d+, {act}, {e['waves']}, \d+, 0, {bits}>", grid
     if e["path"] == w4.Path.SKINNY:
-        return rf"void w4a16::skinny_kernel<\d+, {act}, 0, \d+, {bits}>", grid
+        # staged x (skinny_kernel) or x whole in LDS (skinny_direct_kernel)
+        return (rf"void w4a16::skinny_(kernel<\d+, {act}, 0, \d+, {bits}>|direct_kernel<\d+, {act}, \d+, {bits}>)",
+                grid)
     if e["waves"] == 8:
         sk = "true" if e["stream_k"] else "false"
         return rf"void w4a16::gemm8_kernel<{act}, (true|false), {bits}, {e['tile_m']}, {e['tile_n']}, {sk}>", grid

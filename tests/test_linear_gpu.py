@@ -117,6 +117,36 @@ def test_gemm_tilings_bit_exact(dev, dtype, m, n, k):
                            f"got {got[bad[0]]} want {want[bad[0]]}")
 
 
+# Mid-M plans without a fused activation (x slice whole in LDS): 32-row
+# blocks on 8 waves (128 columns per workgroup), unsplit, ragged last tile and
+# rows past M; 16-row blocks with a K split finished in the launch whose last
+# part is one group short; a small layer in 16-row blocks, M not a multiple of
+# 16, split in four.  Exact arithmetic, whole rows and columns at the edges.
+SKINNY_SHAPES = [(37, 16376, 2048, 8, 1), (13, 2056, 16256, 4, 8), (61, 1000, 4096, 4, 4)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k,waves,splits", SKINNY_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k, _, _ in SKINNY_SHAPES])
+def test_skinny_plans_bit_exact(dev, dtype, m, n, k, waves, splits):
+    lib = w4()
+    plan = lib.explain(m, n, k, path=lib.Path.SKINNY)
+    assert (plan["waves"], plan["splits"]) == (waves, splits), plan
+    w, x, b = exact_case(m, n, k, seed=m + 3 * n + k, dtype=dtype, with_bias=True)
+    say(f"skinny plan case dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare(w, dev)
+    y = run(x.to(dev), packed, n, b.to(dev), "SKINNY").cpu().to(torch.float64).numpy()
+    edge_rows = sorted({0, 15, 16, 31, 32, m - 2, m - 1} & set(range(m)))
+    edge_cols = sorted({0, 15, 16, 63, 64, 127, 128, n - 17, n - 9, n - 1} & set(range(n)))
+    rows = np.concatenate([np.repeat(edge_rows, n), np.tile(np.arange(m), len(edge_cols))])
+    cols = np.concatenate([np.tile(np.arange(n), len(edge_rows)), np.repeat(edge_cols, m)])
+    y_ref = oracle.linear_entries(bits(x), tag(dtype), q, s, bits(b), rows, cols)
+    want = to_rne16(y_ref, dtype)
+    got = y[rows, cols]
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (f"{bad.size} mismatches, first at row {rows[bad[0]]} col {cols[bad[0]]}: "
+                           f"got {got[bad[0]]} want {want[bad[0]]}")
+
+
 def test_strided_output_bit_exact(dev):
     """Row stride ldy > n through the C-ABI: every path writes exactly the
     n outputs of each row (the padding keeps its sentinel), bit-exact.

@@ -56,7 +56,13 @@ size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bi
             return full > last ? full : last;
         }
         case W4A16_PATH_MGEMV: return plan_mgemv(m < 16 ? m : 16, n, k, bits).workspace;
-        case W4A16_PATH_SKINNY: return plan_skinny(m, n, k, bits).workspace;
+        case W4A16_PATH_SKINNY: {
+            // the plans with and without a fused activation (different
+            // workgroup widths): room for either
+            const size_t direct = plan_skinny(m, n, k, bits, kActFnNone).workspace;
+            const size_t staged = plan_skinny(m, n, k, bits, kActFnSwiglu).workspace;
+            return direct > staged ? direct : staged;
+        }
         case W4A16_PATH_GEMM: return plan_gemm(m, n, k, bits).workspace;
         case W4A16_PATH_GEMM_STREAMK: return plan_gemm_streamk(m, n, k, bits).workspace;
         default: return 0;
@@ -444,7 +450,7 @@ w4a16_status_t w4a16_linear_explain(int bits, w4a16_act_t act, w4a16_path_t path
     switch (path) {
         case W4A16_PATH_GEMV: info = describe_gemv(m < 4 ? m : 4, n, k, bits); launches = ceil_div(m, 4); break;
         case W4A16_PATH_MGEMV: info = describe_mgemv(m < 16 ? m : 16, n, k, bits); launches = ceil_div(m, 16); break;
-        case W4A16_PATH_SKINNY: info = describe_skinny(m, n, k, bits); break;
+        case W4A16_PATH_SKINNY: info = describe_skinny(m, n, k, bits, fn); break;
         default: info = describe_gemm(m, n, k, bits, path == W4A16_PATH_GEMM_STREAMK); break;
     }
     plan->waves = info.waves;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace w4a16 {
 
 // ---------------------------------------------------------------------------
@@ -235,6 +237,32 @@ __device__ inline float sum_xor32(float v) {
 __device__ inline float max_xor32(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// f(std::integral_constant<int, I>) for I = B .. E - 1 in order (a loop whose
+// index is a constant expression in the body).
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// LDS address operand of the direct global-to-LDS buffer loads.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Waits until at most N vector memory operations of this wave are in flight
+// (they complete in issue order).  For loads the compiler cannot track, such
+// as direct global-to-LDS loads, which write no register.  s_waitcnt's
+// immediate on gfx9: vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8
+// (those two left at their maxima: no wait).
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
 }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS

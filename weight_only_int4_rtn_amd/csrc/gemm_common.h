@@ -112,8 +112,6 @@ __device__ inline uint4 dequant_word8(uint32_t w0, uint32_t w1, float s, float n
                       pack2<ACT>(fmaf(byte_f32<2>(w1), s, neg128s), fmaf(byte_f32<3>(w1), s, neg128s)));
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 template <bool B>
 struct BoolC {
     static constexpr bool value = B;

@@ -38,13 +38,16 @@ MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 struct SkinnyPlan {
     int mb;             // 16-row m-subtiles per workgroup (1..4)
+    int waves;          // waves per workgroup, one 16-row weight tile each
+    bool direct;        // x slice whole in LDS (no fused activation), else staged per group
     int gps, splits;
     int gmax;           // register capacity for chunks (4, 8, 16 groups)
     int64_t tile_groups, mblocks;
     bool in_kernel;     // a K split finished inside the launch (else by the reduce kernel)
     size_t workspace;
 };
-SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits = 4);
+// act_fn: ActFn (common.h) fused into the input
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits, int act_fn);
 
 struct GemmPlan {
     int64_t mtiles, ntiles;
@@ -71,7 +74,7 @@ struct PlanInfo {
 };
 PlanInfo describe_gemv(int64_t m, int64_t n, int64_t k, int bits);    // m <= 4 (one row block)
 PlanInfo describe_mgemv(int64_t m, int64_t n, int64_t k, int bits);   // m <= 16 (one row block)
-PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits);
+PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits, int act_fn);
 PlanInfo describe_gemm(int64_t m, int64_t n, int64_t k, int bits, bool streamk);
 
 hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int64_t ldw,

@@ -54,7 +54,6 @@ struct SkinnyArgs {
 
 constexpr int kSkWaves = 4;
 constexpr int kSkThreads = 64 * kSkWaves;
-constexpr int kSkCols = 16 * kSkWaves;     // output columns per workgroup
 constexpr int kAStride = kGroup + 8;       // LDS row stride of the x tile (elements): 16 B pad
 
 template <int ACT>
@@ -66,6 +65,113 @@ __device__ inline f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
     }
+}
+
+// The end of a SKINNY launch for one workgroup: its FP32 sums (lane: rows
+// 16 mb + 4 kq + i, i = 0..3, of column r of the wave's tile) stored with the
+// bias, or a K split finished in the launch or through the reduce kernel.
+// flag: one int of LDS that no wave reads or writes any more.
+template <int MB, int ACT, int WAVES>
+__device__ inline void skinny_finish(const SkinnyArgs& a, const f32x4_t (&tot)[MB], const int64_t tg,
+                                     const int64_t mblk, const int split, int* const flag) {
+    constexpr int BM = 16 * MB, COLS = 16 * WAVES;
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int64_t m0 = mblk * BM;
+    const int64_t t = tg * WAVES + wave;
+    const bool tile_ok = t < ceil_div(a.n, int64_t(kTileRows));
+    const int64_t col = t * kTileRows + r;
+    if (a.splits == 1) {
+        if (tile_ok && col < a.n) {
+            const float bv = a.bias ? to_f32<ACT>(a.bias[col]) : 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t row = m0 + mb * 16 + 4 * kq + i;
+                    if (row < a.m) a.y[row * a.ldy + col] = from_f32<ACT>(tot[mb][i] + bv);
+                }
+        }
+        return;
+    }
+
+    if (a.in_kernel) {
+        // K split finished in this launch: every split stores its FP32 sums in
+        // its slot, lane by lane as the registers hold them, written through
+        // to the device's coherence point (SC1: the XCDs' L2s are not
+        // coherent), and counts itself in the tile's counter; the split that
+        // completes the count adds the slots in split order, 0 + s_0 + s_1 +
+        // ... (its own sums from registers at their place: the reduce
+        // kernel's order, so the same bits), clears the counter for the next
+        // call and stores the outputs with the bias.  Nobody waits.
+        const int64_t blocks = a.tile_groups * gridDim.y, tile = tg * gridDim.y + mblk;
+        const int64_t slot_bytes = int64_t(BM) * COLS * 4;
+        const __amdgpu_buffer_rsrc_t sl = buffer_rsrc(a.slots, int64_t(a.splits) * blocks * slot_bytes);
+        const uint32_t lane_off = uint32_t((wave * MB * 64 + lane) * 16);
+        auto slot_of = [&](int sp) { return uint32_t((int64_t(sp) * blocks + tile) * slot_bytes) + lane_off; };
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, tot[mb]), sl, slot_of(split) + mb * 1024,
+                                                   0, kCoherent);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        int* const last = flag;
+        if (tid == 0) {
+            const unsigned before =
+                __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *last = before == unsigned(a.splits - 1);
+            if (*last) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!*last) return;
+        f32x4_t sum[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) sum[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // eight splits' sums in flight at a time
+        for (int s0 = 0; s0 < a.splits; s0 += 8) {
+            f32x4_t part[8][MB];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int sp = min(s0 + j, a.splits - 1);
+                    part[j][mb] = sp == split ? tot[mb]
+                                              : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                                sl, slot_of(sp) + mb * 1024, 0,
+                                                                                kCoherent));
+                }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    if (s0 + j < a.splits) sum[mb] += part[j][mb];
+        }
+        if (tile_ok && col < a.n) {
+            const float bv = a.bias ? to_f32<ACT>(a.bias[col]) : 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t row = m0 + mb * 16 + 4 * kq + i;
+                    if (row < a.m) a.y[row * a.ldy + col] = from_f32<ACT>(sum[mb][i] + bv);
+                }
+        }
+        return;
+    }
+
+    // K split: store the FP32 partial sums; the split-K reduce kernel adds
+    // them in split order, adds the bias and rounds (reduce.hip).
+    if (!tile_ok) return;
+    const int64_t npad = a.tile_groups * COLS;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + mb * 16 + 4 * kq + i;
+            if (row < a.m) a.partials[(int64_t(split) * a.m + row) * npad + col] = tot[mb][i];
+        }
 }
 
 // AF: activation fused into the x staging (ActFn; SwiGLU gate values sit k
@@ -192,114 +298,133 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
         __syncthreads();
     }
 
-    // Lane holds output rows 16mb + 4kq + i (i = 0..3) of column r of its tile.
-    const int64_t col = t * kTileRows + r;
-    if (a.splits == 1) {
-        if (tile_ok && col < a.n) {
-            const float bv = a.bias ? to_f32<ACT>(a.bias[col]) : 0.0f;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t row = m0 + mb * 16 + 4 * kq + i;
-                    if (row < a.m) a.y[row * a.ldy + col] = from_f32<ACT>(tot[mb][i] + bv);
-                }
-        }
-        return;
-    }
-
-    if (a.in_kernel) {
-        // K split finished in this launch: every split stores its FP32 sums in
-        // its slot, lane by lane as the registers hold them, written through
-        // to the device's coherence point (SC1: the XCDs' L2s are not
-        // coherent), and counts itself in the tile's counter; the split that
-        // completes the count adds the slots in split order, 0 + s_0 + s_1 +
-        // ... (its own sums from registers at their place: the reduce
-        // kernel's order, so the same bits), clears the counter for the next
-        // call and stores the outputs with the bias.  Nobody waits.
-        const int64_t blocks = a.tile_groups * gridDim.y, tile = tg * gridDim.y + mblk;
-        const int64_t slot_bytes = int64_t(BM) * kSkCols * 4;
-        const __amdgpu_buffer_rsrc_t sl = buffer_rsrc(a.slots, int64_t(a.splits) * blocks * slot_bytes);
-        const uint32_t lane_off = uint32_t((wave * MB * 64 + lane) * 16);
-        auto slot_of = [&](int sp) { return uint32_t((int64_t(sp) * blocks + tile) * slot_bytes) + lane_off; };
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, tot[mb]), sl, slot_of(split) + mb * 1024,
-                                                   0, kCoherent);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        int* const last = reinterpret_cast<int*>(&xa[0][0]);  // free: the K loop ended with a barrier
-        if (tid == 0) {
-            const unsigned before =
-                __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *last = before == unsigned(a.splits - 1);
-            if (*last) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        if (!*last) return;
-        f32x4_t sum[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) sum[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // eight splits' sums in flight at a time
-        for (int s0 = 0; s0 < a.splits; s0 += 8) {
-            f32x4_t part[8][MB];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const int sp = min(s0 + j, a.splits - 1);
-                    part[j][mb] = sp == split ? tot[mb]
-                                              : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                                sl, slot_of(sp) + mb * 1024, 0,
-                                                                                kCoherent));
-                }
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    if (s0 + j < a.splits) sum[mb] += part[j][mb];
-        }
-        if (tile_ok && col < a.n) {
-            const float bv = a.bias ? to_f32<ACT>(a.bias[col]) : 0.0f;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t row = m0 + mb * 16 + 4 * kq + i;
-                    if (row < a.m) a.y[row * a.ldy + col] = from_f32<ACT>(sum[mb][i] + bv);
-                }
-        }
-        return;
-    }
-
-    // K split: store the FP32 partial sums; the split-K reduce kernel adds
-    // them in split order, adds the bias and rounds (reduce.hip).
-    if (!tile_ok) return;
-    const int64_t npad = a.tile_groups * kSkCols;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = m0 + mb * 16 + 4 * kq + i;
-            if (row < a.m) a.partials[(int64_t(split) * a.m + row) * npad + col] = tot[mb][i];
-        }
+    skinny_finish<MB, ACT, kSkWaves>(a, tot, tg, mblk, split, reinterpret_cast<int*>(&xa[0][0]));
 }
 
-SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits) {
+// Without a fused activation: the workgroup's whole x slice in LDS.  4 MB
+// waves (one 16-row weight tile each, 64 MB output columns) and up to 16
+// groups of K (8 INT8 chunks).  Every wave first issues its share of the x
+// slice as direct global-to-LDS loads (per group, one 1 KB block per wave),
+// then every chunk and scale of its tile.  The x blocks land in issue order;
+// before groups 0, 1, 2, 4 and 8 each wave waits for its blocks up to the
+// end of that phase (groups 0, 1, 2-3, 4-7, 8-15; the chunk and scale loads
+// issued after them may still be in flight) and a barrier makes everyone's
+// visible.  No staging, no other barrier: group g waits for its own chunk
+// and scale alone, so the groups are computed while the weight stream is
+// still arriving.
+// The LDS holds x as MFMA A operands: block (group g, m-subtile mb, k-step
+// s) holds lane l's 16 bytes, x[16 mb + (l & 15)][128 g + 32 s + 8 (l >> 4)
+// .. + 7], at byte 16 l (linear: conflict-free reads).  Rows past M read
+// zero through the buffer range.
+template <int MB, int ACT, int GMAX, int BITS>
+__global__ __launch_bounds__(256 * MB) void skinny_direct_kernel(SkinnyArgs a) {
+    constexpr int WAVES = 4 * MB, NB = 4 * MB;  // NB: 1 KB x blocks per group, one per wave
+    constexpr int BM = 16 * MB;
+    constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
+    __shared__ __align__(16) uint8_t xl[GMAX * NB * 1024];
+
+    const Layout L(a.n, a.k, BITS);
+    const int split = int(blockIdx.x % unsigned(a.splits));
+    const int64_t tg = int64_t(blockIdx.x / unsigned(a.splits));
+    const int64_t mblk = blockIdx.y;
+    const int64_t m0 = mblk * BM;
+    const int64_t g0 = int64_t(split) * a.gps;
+    const int ng = int(min<int64_t>(a.gps, L.groups - g0));
+
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int64_t t = tg * WAVES + wave;
+    const int64_t tt = t < L.tiles ? t : L.tiles - 1;  // loads stay in bounds; results unused
+    const uint8_t* cbase = a.packed + (tt * L.groups + g0) * CB + lane * 16;
+    const float* sbase = reinterpret_cast<const float*>(a.packed + L.scale_offset()) + (tt * L.groups + g0) * kTileRows + r;
+    constexpr float off = code_offset<ACT, BITS>();
+    const uint32_t noff2 = uint32_t(from_f32<ACT>(-off)) * 0x00010001u;
+    const uint4 bneg = make_uint4(noff2, noff2, noff2, noff2);
+
+    // x blocks: this wave fills block `wave` (m-subtile wave / 4, k-step
+    // wave % 4) of every group; groups past the split's end reload its last.
+    const int64_t rows_valid = min<int64_t>(BM, a.m - m0);
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(a.x + m0 * a.ldx, rows_valid * a.ldx * 2);
+    const uint32_t xoff = uint32_t((16 * (wave >> 2) + r) * a.ldx * 2 + (32 * (wave & 3) + 8 * kq) * 2);
+#pragma unroll
+    for (int u = 0; u < GMAX; ++u) {
+        const int gc = u < ng ? u : ng - 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_ptr_t)(xl + (u * NB + wave) * 1024), 16, xoff,
+                                                 uniform(int((g0 + gc) * kGroup * 2)), 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 cw[GMAX][H];
+    float sc[GMAX];
+#pragma unroll
+    for (int u = 0; u < GMAX; ++u) {
+        const int gc = u < ng ? u : ng - 1;
+#pragma unroll
+        for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
+        sc[u] = sbase[int64_t(gc) * kTileRows];
+    }
+
+    f32x4_t tot[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) tot[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    static_for<0, GMAX>([&](auto gc) {
+        constexpr int gl = decltype(gc)::value;
+        // phase start: this wave's x blocks of the phase's groups have landed,
+        // then everyone's (the later blocks and all chunk and scale loads may
+        // still be in flight; a wave whose split ends early still takes part)
+        if constexpr (gl == 0 || gl == 1 || gl == 2 || gl == 4 || gl == 8) {
+            constexpr int end = gl < 2 ? gl + 1 : 2 * gl;
+            wait_vm<(GMAX - (end < GMAX ? end : GMAX)) + GMAX * (H + 1)>();
+            lds_barrier();
+        }
+        if (gl >= ng) return;
+        uint32_t words[4 * H];
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            words[4 * h] = cw[gl][h].x;
+            words[4 * h + 1] = cw[gl][h].y;
+            words[4 * h + 2] = cw[gl][h].z;
+            words[4 * h + 3] = cw[gl][h].w;
+        }
+        uint4 b01[2], b23[2];
+        bpairs2<BITS, ACT>(words, 0, b01);
+        bpairs2<BITS, ACT>(words, 2, b23);
+        const uint4 b[4] = {b01[0], b01[1], b23[0], b23[1]};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 av = *reinterpret_cast<const uint4*>(xl + ((gl * NB + mb * 4 + s) * 1024) + lane * 16);
+                acc = mfma16<ACT>(av, b[s], acc);
+                acc = mfma16<ACT>(av, bneg, acc);
+            }
+            tot[mb][0] = fmaf(sc[gl], acc[0], tot[mb][0]);
+            tot[mb][1] = fmaf(sc[gl], acc[1], tot[mb][1]);
+            tot[mb][2] = fmaf(sc[gl], acc[2], tot[mb][2]);
+            tot[mb][3] = fmaf(sc[gl], acc[3], tot[mb][3]);
+        }
+    });
+    // (the finish writes its flag only after a barrier all waves reach after
+    // their last read of the slice)
+    skinny_finish<MB, ACT, WAVES>(a, tot, tg, mblk, split, reinterpret_cast<int*>(xl));
+}
+
+namespace {
+
+// The plan for one kernel: 16-row m-subtiles per workgroup (mb) and the x
+// slice whole in LDS (direct) or staged per group.
+SkinnyPlan make_skinny_plan(int64_t m, const Layout& L, int mb, bool direct) {
     SkinnyPlan p{};
-    const Layout L(n, k, bits);
-    // Row blocks: these launches are latency-bound, so more and shorter
-    // workgroups win while the weights are small enough that reading them
-    // once per 16-row block stays cheap (from L2); larger layers take 32-row
-    // blocks.  Measured (MI355X, M 20..127): layers of <= 8 M weights run
-    // 1.3-1.8x faster with 16-row blocks than with 64-row blocks, layers of
-    // 33.5 M weights 10-20 % faster with 32-row blocks than with 16 or 64.
-    const bool small = n * k <= (int64_t(8) << 20);
-    p.mb = m <= 16 || small ? 1 : 2;
+    p.mb = mb;
     const int64_t bm = 16 * p.mb;
     p.mblocks = ceil_div(m, bm);
-    p.tile_groups = ceil_div(L.tiles, kSkWaves);
+    // the direct kernel: 4 waves per 16-row block (8 tiles share each x
+    // block of a 32-row block)
+    p.direct = direct;
+    p.waves = direct ? 4 * mb : kSkWaves;
+    const int64_t cols = 16 * p.waves;
+    p.tile_groups = ceil_div(L.tiles, int64_t(p.waves));
     // A workgroup holds all of its chunks in registers: up to 16 groups with
     // one or two 16-row m-subtiles, 8 with more.  Split K beyond that, and
     // further (halving the groups per workgroup) while fewer than 256
@@ -307,7 +432,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits) {
     // launch a split adds).
     const int64_t minwg = 256;
     // (INT8 chunks take twice the registers: half the groups)
-    const int64_t cap = (p.mb <= 2 ? 16 : 8) / (bits == 8 ? 2 : 1);
+    const int64_t cap = (p.mb <= 2 ? 16 : 8) / (L.cb == kChunkBytes8 ? 2 : 1);
     const int64_t base = p.tile_groups * p.mblocks;
     int64_t gps = L.groups < cap ? L.groups : cap;
     while (gps > 2 && base * ceil_div(L.groups, gps) < minwg) gps = ceil_div(gps, 2);
@@ -320,17 +445,48 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits) {
     // (16 x 16384 x 2048: 13.8 -> 11.9 us; 64 x 16384 x 2048: 20.4 -> 17.9;
     // 50 x 4096 x 1024: 9.2 -> 8.2).
     const int64_t blocks = p.tile_groups * p.mblocks;
-    const int64_t slot_bytes = int64_t(p.splits) * blocks * bm * kSkCols * 4;
+    const int64_t slot_bytes = int64_t(p.splits) * blocks * bm * cols * 4;
     p.in_kernel = p.splits > 1 && blocks <= int64_t(kSyncBytes / 4) && slot_bytes < (int64_t(1) << 31);
     p.workspace = p.splits == 1 ? 0
                   : p.in_kernel ? kSyncBytes + size_t(slot_bytes)
-                                : kSyncBytes + size_t(p.splits) * m * p.tile_groups * kSkCols * 4;
+                                : kSyncBytes + size_t(p.splits) * m * p.tile_groups * cols * 4;
     return p;
 }
 
-PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits) {
-    const SkinnyPlan p = plan_skinny(m, n, k, bits);
-    return {kSkWaves, 16 * p.mb, kSkCols, p.splits, p.gps, p.tile_groups * p.splits * p.mblocks,
+}  // namespace
+
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits, int act_fn) {
+    const Layout L(n, k, bits);
+    // Row blocks: these launches are latency-bound, so more and shorter
+    // workgroups win while the weights are small enough that reading them
+    // once per 16-row block stays cheap (from L2); larger layers take 32-row
+    // blocks.  Measured (MI355X, M 20..127): layers of <= 8 M weights run
+    // 1.3-1.8x faster with 16-row blocks than with 64-row blocks, layers of
+    // 33.5 M weights 10-20 % faster with 32-row blocks than with 16 or 64.
+    const bool small = n * k <= (int64_t(8) << 20);
+    const int mb = m <= 16 || small ? 1 : 2;
+    // Without a fused activation the direct kernel (x slice whole in LDS)
+    // where it measured faster (MI355X, bf16): 16-row blocks up to M = 64,
+    // 7-15 % (16 x 16384 x 2048: 11.9 -> 10.5 us; 16 x 2048 x 16384: 9.6 ->
+    // 8.2; 50 x 4096 x 1024: 8.0 -> 7.5; 64 x 1024 x 4096: 5.4 -> 4.9), not
+    // beyond (256 x 1024 x 4096: 9.1 -> 10.0); 32-row blocks only unsplit and
+    // in one round of workgroups (at most one per CU: 128 KB of LDS), 3-5 %
+    // (64 x 2048 x 16384: 15.9 -> 15.1); split or in more rounds they ran
+    // 4-45 % slower (64 x 16384 x 2048: 18.1 -> 19.9; 96 x 2048 x 16384:
+    // 20.4 -> 27.0).
+    if (act_fn == kActFnNone) {
+        if (mb == 1 && m <= 64) return make_skinny_plan(m, L, 1, true);
+        if (mb == 2) {
+            const SkinnyPlan d = make_skinny_plan(m, L, 2, true);
+            if (d.splits == 1 && d.tile_groups * d.mblocks <= 256) return d;
+        }
+    }
+    return make_skinny_plan(m, L, mb, false);
+}
+
+PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits, int act_fn) {
+    const SkinnyPlan p = plan_skinny(m, n, k, bits, act_fn);
+    return {p.waves, 16 * p.mb, 16 * p.waves, p.splits, p.gps, p.tile_groups * p.splits * p.mblocks,
             p.splits > 1 && !p.in_kernel};
 }
 
@@ -340,7 +496,18 @@ static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream
     // the plan keeps the register footprint GMAX * BITS / 4 chunks <= 16, and
     // <= 8 for MB > 2
     constexpr int kMaxRegChunks = MB <= 2 ? 16 : 8;
-    if (p.gmax == 4) {
+    if (p.direct) {
+        // (the plan takes it only without a fused activation, MB <= 2)
+        if constexpr (AF == kActFnNone && MB <= 2) {
+            const dim3 block(unsigned(256 * MB));
+            if (p.gmax == 4) skinny_direct_kernel<MB, ACT, 4, BITS><<<grid, block, 0, stream>>>(a);
+            else if (p.gmax == 8) skinny_direct_kernel<MB, ACT, 8, BITS><<<grid, block, 0, stream>>>(a);
+            else if constexpr (16 * BITS / 4 <= kMaxRegChunks) skinny_direct_kernel<MB, ACT, 16, BITS><<<grid, block, 0, stream>>>(a);
+            else return hipErrorInvalidValue;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (p.gmax == 4) {
         if constexpr (4 * BITS / 4 <= kMaxRegChunks) skinny_kernel<MB, ACT, AF, 4, BITS><<<grid, dim3(kSkThreads), 0, stream>>>(a);
         else return hipErrorInvalidValue;
     } else if (p.gmax == 8) {
@@ -352,7 +519,7 @@ static hipError_t launch_one(const SkinnyArgs& a, const SkinnyPlan& p, hipStream
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.in_kernel) return e;
-    return launch_splitk_reduce(a.partials, p.splits, a.m, a.n, p.tile_groups * kSkCols, a.bias, a.y, a.ldy,
+    return launch_splitk_reduce(a.partials, p.splits, a.m, a.n, p.tile_groups * 16 * p.waves, a.bias, a.y, a.ldy,
                                 ACT, stream);
 }
 
@@ -377,7 +544,7 @@ static hipError_t launch_mb(const SkinnyArgs& a, const SkinnyPlan& p, int act, i
 hipError_t launch_skinny(const void* x, int act, int act_fn, int bits, int64_t m, int64_t k, int64_t ldx,
                          const void* packed, int64_t n, const void* bias, void* y, int64_t ldy, void* workspace,
                          hipStream_t stream) {
-    const SkinnyPlan p = plan_skinny(m, n, k, bits);
+    const SkinnyPlan p = plan_skinny(m, n, k, bits, act_fn);
     SkinnyArgs a;
     a.x = static_cast<const uint16_t*>(x);
     a.ldx = ldx;
