@@ -77,7 +77,17 @@ def test_choose_path(lib):
     assert w4.choose_path(2, 2560, 2048) == w4.Path.GEMV
     assert w4.choose_path(2, 32768, 2048) == w4.Path.MGEMV
     assert w4.choose_path(2, 1024, 4096) == w4.Path.MGEMV
-    assert w4.choose_path(8, 16384, 2048) == w4.Path.MGEMV
+    # the mid-M kernel from M = 3 where it needs no K split (>= 16384 outputs,
+    # K <= 2048) and where the small-M kernel's split would need the reduce
+    # launch; the small-M kernel keeps M = 2 and the other split layers
+    assert w4.choose_path(8, 16384, 2048) == w4.Path.SKINNY
+    assert w4.choose_path(3, 32768, 2048) == w4.Path.SKINNY
+    assert w4.choose_path(2, 16384, 2048) == w4.Path.MGEMV
+    assert w4.choose_path(8, 4096, 16384) == w4.Path.SKINNY
+    assert w4.choose_path(4, 2048, 16384) == w4.Path.MGEMV
+    assert w4.choose_path(8, 2048, 16384) == w4.Path.MGEMV
+    assert w4.choose_path(4, 16384, 4096) == w4.Path.MGEMV
+    assert w4.choose_path(16, 2560, 2048) == w4.Path.MGEMV
     assert w4.choose_path(8, 32768, 2048) == w4.Path.SKINNY
     assert w4.choose_path(96, 32768, 2048) == w4.Path.SKINNY
     assert w4.choose_path(97, 32768, 2048) == w4.Path.GEMM

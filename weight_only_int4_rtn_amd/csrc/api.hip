@@ -276,9 +276,20 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     // to M = 512 (256 x 4096 x 1024: 9.3 vs 18.0); on larger layers up to
     // M = 96 (96 x 32768 x 2048: 38.8 vs 42.9; 96 x 2048 x 16384: 25.8 vs
     // 29.7; at M = 128 the GEMM leads, 46.3 vs 47.4 and 30.6 vs 32.4).
+    // With its x slice whole in LDS the mid-M kernel also takes M = 3-16 on
+    // layers it covers without a K split (>= 16384 outputs, K <= 2048: 3 x
+    // 32768 x 2048: 9.9 vs 10.7; 4 x 16384 x 2048: 6.6 vs 6.9; 8 x 16384 x
+    // 2048: 6.7 vs 8.0), and wherever the small-M kernel's K split would
+    // need the reduce launch (8 x 4096 x 16384: 12.7 vs 17.3); M = 2 is even
+    // (2 x 32768 x 2048: 9.8 vs 9.7), and split layers stay with the small-M
+    // kernel (4 x 2048 x 16384: 8.1 vs 9.1; 4 x 16384 x 4096: 11.2 vs 11.8).
     const bool small = n * k <= (int64_t(8) << 20);
     if (m <= 1 || (m == 2 && small && n >= 2048)) return W4A16_PATH_GEMV;
-    if (m <= 4 || (m <= 8 && n <= 16384) || (m <= 16 && small)) return W4A16_PATH_MGEMV;
+    if (m >= 3 && m <= 16 && k <= 2048 && n >= 16384) return W4A16_PATH_SKINNY;
+    if (m <= 4 || (m <= 8 && n <= 16384) || (m <= 16 && small)) {
+        const MgemvPlan p = plan_mgemv(m < 16 ? m : 16, n, k, 4);
+        if (m <= 2 || small || p.splits == 1 || p.exchange) return W4A16_PATH_MGEMV;
+    }
     if (k > kGemmMaxLd || m <= 96 || (small && m <= 512)) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
 }
