@@ -310,11 +310,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
 // once the memory pipeline is full: issuing every chunk up front kept each
 // wave from computing until its whole stream had almost arrived; PF 8 with
 // 16-row blocks and 4 with 32-row blocks measured 3-10 % faster than all
-// up front.)  The x blocks land in issue order; before groups 0, 1, 2, 4
-// and 8 each wave waits for its blocks up to the end of that phase (groups
-// 0, 1, 2-3, 4-7, 8-15; the chunk and scale loads issued after them may
-// still be in flight) and a barrier makes everyone's visible.  No staging,
-// no other barrier: group g waits for its own chunk and scale alone.
+// up front.)  The x blocks land in issue order; before groups 0, 2, 4 and 8
+// each wave waits for its blocks up to the end of that phase and a barrier
+// makes everyone's visible.  No staging, no other barrier: a group waits
+// for its own chunk and scale alone.
 // The LDS holds x as MFMA A operands: block (group g, m-subtile mb, k-step
 // s) holds lane l's 16 bytes, x[16 mb + (l & 15)][128 g + 32 s + 8 (l >> 4)
 // .. + 7], at byte 16 l (linear: conflict-free reads).  Rows past M read
@@ -372,53 +371,75 @@ __global__ __launch_bounds__(256 * MB) void skinny_direct_kernel(SkinnyArgs a) {
     f32x4_t tot[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) tot[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    static_for<0, GMAX>([&](auto gc) {
-        constexpr int gl = decltype(gc)::value;
-        // phase start: this wave's x blocks of the phase's groups have landed,
-        // then everyone's (the later blocks and all chunk and scale loads may
-        // still be in flight; a wave whose split ends early still takes part)
-        if constexpr (gl == 0 || gl == 1 || gl == 2 || gl == 4 || gl == 8) {
-            constexpr int end = gl < 2 ? gl + 1 : 2 * gl;
-            constexpr int chunks = PF + gl < GMAX ? PF + gl : GMAX;  // chunk loads issued so far
-            wait_vm<(GMAX - (end < GMAX ? end : GMAX)) + chunks * (H + 1)>();
-            lds_barrier();
-        }
-        // the chunk PF groups ahead goes out before this group's work
-        if constexpr (gl + PF < GMAX) load_chunk(gl + PF);
-        if (gl >= ng) return;
-        // this group's x fragments first: their LDS latency passes during the
-        // decode (3 % faster with 32-row blocks)
-        uint4 av[MB][4];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                av[mb][s] = *reinterpret_cast<const uint4*>(xl + ((gl * NB + mb * 4 + s) * 1024) + lane * 16);
-        __builtin_amdgcn_sched_barrier(0);
+    auto decode = [&](int u, uint4 (&b)[4]) {
         uint32_t words[4 * H];
 #pragma unroll
         for (int h = 0; h < H; ++h) {
-            words[4 * h] = cw[gl][h].x;
-            words[4 * h + 1] = cw[gl][h].y;
-            words[4 * h + 2] = cw[gl][h].z;
-            words[4 * h + 3] = cw[gl][h].w;
+            words[4 * h] = cw[u][h].x;
+            words[4 * h + 1] = cw[u][h].y;
+            words[4 * h + 2] = cw[u][h].z;
+            words[4 * h + 3] = cw[u][h].w;
         }
         uint4 b01[2], b23[2];
         bpairs2<BITS, ACT>(words, 0, b01);
         bpairs2<BITS, ACT>(words, 2, b23);
-        const uint4 b[4] = {b01[0], b01[1], b23[0], b23[1]};
+        b[0] = b01[0];
+        b[1] = b01[1];
+        b[2] = b23[0];
+        b[3] = b23[1];
+    };
+    // Groups in pairs: two independent accumulator chains, interleaved (1-4 %
+    // faster than one group at a time).
+    static_assert(GMAX % 2 == 0, "pairs");
+    static_for<0, GMAX / 2>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int g0 = 2 * j, g1 = 2 * j + 1;
+        // phase start (pairs 0, 1, 2, 4): this wave's x blocks of groups 0-1,
+        // 2-3, 4-7 or 8-15 have landed, then everyone's (the later blocks and
+        // the chunk and scale loads may still be in flight; a wave whose split
+        // ends early still takes part)
+        if constexpr (j == 0 || j == 1 || j == 2 || j == 4) {
+            constexpr int end0 = j == 0 ? 2 : 4 * j;
+            constexpr int end = end0 < GMAX ? end0 : GMAX;
+            constexpr int chunks = PF + g0 < GMAX ? PF + g0 : GMAX;
+            wait_vm<(GMAX - end) + chunks * (H + 1)>();
+            lds_barrier();
+        }
+        // the chunks PF groups ahead go out before this pair's work
+        if constexpr (g0 + PF < GMAX) load_chunk(g0 + PF);
+        if constexpr (g1 + PF < GMAX) load_chunk(g1 + PF);
+        if (g0 >= ng) return;
+        const bool two = g1 < ng;  // (else the second chain's sums are dropped)
+        // the pair's x fragments first: their LDS latency passes during the
+        // decode (3 % faster with 32-row blocks)
+        uint4 av0[MB][4], av1[MB][4];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                acc = mfma16<ACT>(av[mb][s], b[s], acc);
-                acc = mfma16<ACT>(av[mb][s], bneg, acc);
+                av0[mb][s] = *reinterpret_cast<const uint4*>(xl + ((g0 * NB + mb * 4 + s) * 1024) + lane * 16);
+                av1[mb][s] = *reinterpret_cast<const uint4*>(xl + ((g1 * NB + mb * 4 + s) * 1024) + lane * 16);
             }
-            tot[mb][0] = fmaf(sc[gl], acc[0], tot[mb][0]);
-            tot[mb][1] = fmaf(sc[gl], acc[1], tot[mb][1]);
-            tot[mb][2] = fmaf(sc[gl], acc[2], tot[mb][2]);
-            tot[mb][3] = fmaf(sc[gl], acc[3], tot[mb][3]);
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 b0[4], b1[4];
+        decode(g0, b0);
+        decode(g1, b1);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                acc0 = mfma16<ACT>(av0[mb][s], b0[s], acc0);
+                acc1 = mfma16<ACT>(av1[mb][s], b1[s], acc1);
+                acc0 = mfma16<ACT>(av0[mb][s], bneg, acc0);
+                acc1 = mfma16<ACT>(av1[mb][s], bneg, acc1);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[mb][i] = fmaf(sc[g0], acc0[i], tot[mb][i]);
+            if (two) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[mb][i] = fmaf(sc[g1], acc1[i], tot[mb][i]);
+            }
         }
     });
     // (the finish writes its flag only after a barrier all waves reach after
