@@ -52,3 +52,44 @@ def test_loads_stay_in_flight(src, tmp_path):
     assert counts, f"no kernels found in {src}"
     bad = {k: v for k, v in counts.items() if v > 2}
     assert not bad, f"{src}: kernels that wait for each load before the next: {bad}"
+
+
+def _lds_read_runs(asm):
+    """{kernel: [(address register, [(first, last) destination registers])]}
+    for every run of consecutive ds_read_b128 (an asm block of reads that
+    are all issued before one wait)."""
+    runs = {}
+    for name in re.findall(r"^(_ZN5w4a16\w+):", asm, re.M):
+        body = asm[asm.index(name + ":"):asm.index(".Lfunc_end", asm.index(name + ":"))].splitlines()
+        cur = []
+        out = []
+        for ln in body:
+            m = re.match(r"\s*ds_read_b128 v\[(\d+):(\d+)\], v(\d+)", ln)
+            if m:
+                cur.append((int(m.group(3)), int(m.group(1)), int(m.group(2))))
+            elif ln.strip() and not ln.strip().startswith(";"):
+                if len(cur) > 1:
+                    out.append(cur)
+                cur = []
+        runs[name] = out
+    return runs
+
+
+@pytest.mark.skipif(not shutil.which(libbuild.HIPCC) and not os.path.exists(libbuild.HIPCC), reason="hipcc not found")
+def test_lds_read_runs_keep_their_address(tmp_path):
+    """In a run of LDS reads issued back to back, no read may write the
+    address register of a later one: its returning data would change that
+    read's address (the mid-M kernel reads a pair of groups' x fragments in one
+    asm block; its outputs are early-clobber for this reason)."""
+    runs = _lds_read_runs(_assembly("skinny.hip", tmp_path))
+    assert any(runs.values()), "no runs of LDS reads found"
+    bad = {k: [r for r in v if _clobbers_later_address(r)] for k, v in runs.items()}
+    bad = {k: v for k, v in bad.items() if v}
+    assert not bad, f"LDS read runs that overwrite a later read's address register: {bad}"
+
+
+def _clobbers_later_address(run):
+    """True if a read's destination holds the address register of a read
+    after it in the run (the last read may overwrite its own address: it has
+    been read at issue)."""
+    return any(lo <= run[j][0] <= hi for i, (_, lo, hi) in enumerate(run) for j in range(i + 1, len(run)))

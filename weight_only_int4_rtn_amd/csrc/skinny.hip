@@ -301,29 +301,79 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     skinny_finish<MB, ACT, kSkWaves>(a, tot, tg, mblk, split, reinterpret_cast<int*>(&xa[0][0]));
 }
 
+// A pair of groups' x fragments from LDS (the direct kernel's layout below;
+// addr: this lane's byte address of the pair's first block, the second
+// group's blocks 4 MB KB later): 8 MB reads in one asm block that also waits
+// for them.  The compiler cannot tell LDS reads from the LDS the direct
+// global-to-LDS loads still in flight write, so before a plain read it waits
+// for every such load issued so far; these reads carry no such wait (the
+// caller's own wait and barrier order them after their blocks' loads).  The
+// outputs are early-clobber: no output may share the address register, which
+// a read's returning data could otherwise overwrite before the block's later
+// reads have issued.
+template <int MB>
+__device__ inline void read_pair(uint32_t addr, uint4 (&a0)[MB][4], uint4 (&a1)[MB][4]) {
+    if constexpr (MB == 1) {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+            "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+            "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+            "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0[0][0]), "=&v"(a0[0][1]), "=&v"(a0[0][2]), "=&v"(a0[0][3]), "=&v"(a1[0][0]), "=&v"(a1[0][1]),
+              "=&v"(a1[0][2]), "=&v"(a1[0][3])
+            : "v"(addr)
+            : "memory");
+    } else {
+        static_assert(MB == 2, "m-subtiles");
+        asm volatile(
+            "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
+            "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+            "ds_read_b128 %4, %16 offset:4096\n\tds_read_b128 %5, %16 offset:5120\n\t"
+            "ds_read_b128 %6, %16 offset:6144\n\tds_read_b128 %7, %16 offset:7168\n\t"
+            "ds_read_b128 %8, %16 offset:8192\n\tds_read_b128 %9, %16 offset:9216\n\t"
+            "ds_read_b128 %10, %16 offset:10240\n\tds_read_b128 %11, %16 offset:11264\n\t"
+            "ds_read_b128 %12, %16 offset:12288\n\tds_read_b128 %13, %16 offset:13312\n\t"
+            "ds_read_b128 %14, %16 offset:14336\n\tds_read_b128 %15, %16 offset:15360\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0[0][0]), "=&v"(a0[0][1]), "=&v"(a0[0][2]), "=&v"(a0[0][3]), "=&v"(a0[1][0]), "=&v"(a0[1][1]),
+              "=&v"(a0[1][2]), "=&v"(a0[1][3]), "=&v"(a1[0][0]), "=&v"(a1[0][1]), "=&v"(a1[0][2]), "=&v"(a1[0][3]),
+              "=&v"(a1[1][0]), "=&v"(a1[1][1]), "=&v"(a1[1][2]), "=&v"(a1[1][3])
+            : "v"(addr)
+            : "memory");
+    }
+}
+
 // Without a fused activation: the workgroup's whole x slice in LDS.  4 MB
 // waves (one 16-row weight tile each, 64 MB output columns) and up to 16
-// groups of K (8 INT8 chunks).  Every wave first issues its share of the x
-// slice as direct global-to-LDS loads (per group, one 1 KB block per wave),
-// then the chunks and scales of its tile's first PF groups; group g issues
-// the loads of group g + PF before its own work.  (A wave stalls at issue
-// once the memory pipeline is full: issuing every chunk up front kept each
-// wave from computing until its whole stream had almost arrived; PF 8 with
-// 16-row blocks and 4 with 32-row blocks measured 3-10 % faster than all
-// up front.)  The x blocks land in issue order; before groups 0, 2, 4 and 8
-// each wave waits for its blocks up to the end of that phase and a barrier
-// makes everyone's visible.  No staging, no other barrier: a group waits
-// for its own chunk and scale alone.
+// groups of K (8 INT8 chunks), taken in pairs: two independent accumulator
+// chains, interleaved (1-4 % faster than one group at a time).  Each wave
+// loads one 1 KB x block per group (direct global-to-LDS loads), and the
+// chunks and scales of its tile a window ahead of the pair being computed:
+// a wave stalls at issue once the memory pipeline is full, so issuing
+// every chunk up front kept each wave from computing until its whole stream
+// had almost arrived (the window measured 3-10 % faster).  Two schedules:
+//  * 16-row blocks: every x block first, then the chunks 8 groups ahead;
+//    before pairs 0, 1, 2 and 4 each wave waits for its x blocks of groups
+//    0-1, 2-3, 4-7 or 8-15 and a barrier makes everyone's visible;
+//  * 32-row blocks (8 waves): a pair's two x blocks and two chunks go out
+//    together, 2 pairs ahead; each pair waits for its own x blocks alone,
+//    then a barrier, and its fragments are read by read_pair (6-8 % faster
+//    than the first schedule here: 64 x 2048 x 16384 13.4 -> 12.5 us; 0-7 %
+//    slower with 16-row blocks).
 // The LDS holds x as MFMA A operands: block (group g, m-subtile mb, k-step
 // s) holds lane l's 16 bytes, x[16 mb + (l & 15)][128 g + 32 s + 8 (l >> 4)
-// .. + 7], at byte 16 l (linear: conflict-free reads).  Rows past M read
-// zero through the buffer range.
+// .. + 7], at byte 16 l of block 4 MB g + 4 mb + s (linear: conflict-free
+// reads).  Rows past M read zero through the buffer range.
 template <int MB, int ACT, int GMAX, int BITS>
 __global__ __launch_bounds__(256 * MB) void skinny_direct_kernel(SkinnyArgs a) {
     constexpr int WAVES = 4 * MB, NB = 4 * MB;  // NB: 1 KB x blocks per group, one per wave
     constexpr int BM = 16 * MB;
     constexpr int CB = chunk_bytes<BITS>(), H = BITS / 4;
-    constexpr int PF = MB == 1 ? 8 : 4;  // chunks in flight ahead of the group being computed
+    constexpr bool PAIRED = MB == 2;     // x loads in the window with the chunks
+    constexpr int PF = MB == 1 ? 8 : 4;  // groups whose chunks are in flight ahead of the pair computed
+    static_assert(GMAX % 2 == 0, "pairs");
+    constexpr int NP = GMAX / 2, PP = PF / 2 < NP ? PF / 2 : NP;  // pairs; pairs ahead
     __shared__ __align__(16) uint8_t xl[GMAX * NB * 1024];
 
     const Layout L(a.n, a.k, BITS);
@@ -350,13 +400,11 @@ __global__ __launch_bounds__(256 * MB) void skinny_direct_kernel(SkinnyArgs a) {
     const int64_t rows_valid = min<int64_t>(BM, a.m - m0);
     const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(a.x + m0 * a.ldx, rows_valid * a.ldx * 2);
     const uint32_t xoff = uint32_t((16 * (wave >> 2) + r) * a.ldx * 2 + (32 * (wave & 3) + 8 * kq) * 2);
-#pragma unroll
-    for (int u = 0; u < GMAX; ++u) {
+    auto load_x = [&](int u) {
         const int gc = u < ng ? u : ng - 1;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_ptr_t)(xl + (u * NB + wave) * 1024), 16, xoff,
                                                  uniform(int((g0 + gc) * kGroup * 2)), 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    };
     uint4 cw[GMAX][H];
     float sc[GMAX];
     auto load_chunk = [&](int u) {
@@ -365,8 +413,25 @@ __global__ __launch_bounds__(256 * MB) void skinny_direct_kernel(SkinnyArgs a) {
         for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
         sc[u] = sbase[int64_t(gc) * kTileRows];
     };
+    // a pair's loads in the window (PAIRED: with its x blocks)
+    constexpr int LP = (PAIRED ? 2 : 0) + 2 * (H + 1);  // loads per pair
+    auto load_pair = [&](int p) {
+        if constexpr (PAIRED) {
+            load_x(2 * p);
+            load_x(2 * p + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        load_chunk(2 * p);
+        load_chunk(2 * p + 1);
+        if constexpr (PAIRED) __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (!PAIRED) {
 #pragma unroll
-    for (int u = 0; u < (PF < GMAX ? PF : GMAX); ++u) load_chunk(u);
+        for (int u = 0; u < GMAX; ++u) load_x(u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int p = 0; p < PP; ++p) load_pair(p);
 
     f32x4_t tot[MB];
 #pragma unroll
@@ -388,39 +453,41 @@ __global__ __launch_bounds__(256 * MB) void skinny_direct_kernel(SkinnyArgs a) {
         b[2] = b23[0];
         b[3] = b23[1];
     };
-    // Groups in pairs: two independent accumulator chains, interleaved (1-4 %
-    // faster than one group at a time).
-    static_assert(GMAX % 2 == 0, "pairs");
-    static_for<0, GMAX / 2>([&](auto jc) {
+    static_for<0, NP>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int g0 = 2 * j, g1 = 2 * j + 1;
-        // phase start (pairs 0, 1, 2, 4): this wave's x blocks of groups 0-1,
-        // 2-3, 4-7 or 8-15 have landed, then everyone's (the later blocks and
-        // the chunk and scale loads may still be in flight; a wave whose split
-        // ends early still takes part)
-        if constexpr (j == 0 || j == 1 || j == 2 || j == 4) {
+        // this wave's x blocks of the groups about to be read have landed
+        // (the loads issued after them may still be in flight), then
+        // everyone's (a wave whose split ends early still takes part)
+        constexpr int issued = j + PP < NP ? j + PP : NP;  // pairs in the window issued so far
+        if constexpr (PAIRED) {
+            wait_vm<2 * (H + 1) + (issued - j - 1) * LP>();
+            lds_barrier();
+        } else if constexpr (j == 0 || j == 1 || j == 2 || j == 4) {
             constexpr int end0 = j == 0 ? 2 : 4 * j;
             constexpr int end = end0 < GMAX ? end0 : GMAX;
-            constexpr int chunks = PF + g0 < GMAX ? PF + g0 : GMAX;
-            wait_vm<(GMAX - end) + chunks * (H + 1)>();
+            wait_vm<(GMAX - end) + issued * LP>();
             lds_barrier();
         }
-        // the chunks PF groups ahead go out before this pair's work
-        if constexpr (g0 + PF < GMAX) load_chunk(g0 + PF);
-        if constexpr (g1 + PF < GMAX) load_chunk(g1 + PF);
+        // then the pair PP ahead goes out, before this pair's work
+        if constexpr (j + PP < NP) load_pair(j + PP);
         if (g0 >= ng) return;
         const bool two = g1 < ng;  // (else the second chain's sums are dropped)
         // the pair's x fragments first: their LDS latency passes during the
         // decode (3 % faster with 32-row blocks)
         uint4 av0[MB][4], av1[MB][4];
+        if constexpr (PAIRED) {
+            read_pair<MB>(uint32_t(reinterpret_cast<uintptr_t>(xl)) + uint32_t(g0 * NB * 1024 + lane * 16), av0, av1);
+        } else {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                av0[mb][s] = *reinterpret_cast<const uint4*>(xl + ((g0 * NB + mb * 4 + s) * 1024) + lane * 16);
-                av1[mb][s] = *reinterpret_cast<const uint4*>(xl + ((g1 * NB + mb * 4 + s) * 1024) + lane * 16);
-            }
-        __builtin_amdgcn_sched_barrier(0);
+                for (int s = 0; s < 4; ++s) {
+                    av0[mb][s] = *reinterpret_cast<const uint4*>(xl + ((g0 * NB + mb * 4 + s) * 1024) + lane * 16);
+                    av1[mb][s] = *reinterpret_cast<const uint4*>(xl + ((g1 * NB + mb * 4 + s) * 1024) + lane * 16);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         uint4 b0[4], b1[4];
         decode(g0, b0);
         decode(g1, b1);
