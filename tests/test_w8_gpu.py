@@ -222,6 +222,31 @@ def test_int8_exact_arithmetic_bit_exact(dev, path, dtype, m, n, k):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
 
 
+# The mid-M direct kernel's 32-row schedule on INT8 weights (8 waves, 128
+# columns; each pair's two-half chunks loaded with its x blocks): unsplit,
+# ragged last tile, rows past M.  Exact arithmetic, whole rows and columns at
+# the edges.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_int8_skinny_paired_plan_bit_exact(dev, dtype):
+    import weight_only_int4_rtn_amd as w4
+    m, n, k = 40, 16376, 1024
+    plan = w4.explain(m, n, k, path=w4.Path.SKINNY, bits=8)
+    assert (plan["waves"], plan["splits"]) == (8, 1), plan
+    w, x, b = exact_case8(m, n, k, seed=m + 7 * n + k, dtype=dtype, with_bias=True)
+    say(f"int8 skinny paired plan dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare8(w, dev)
+    y = run8(x.to(dev), packed, n, b.to(dev), "SKINNY").cpu().to(torch.float64).numpy()
+    edge_rows = sorted({0, 15, 16, 31, 32, m - 2, m - 1})
+    edge_cols = sorted({0, 15, 16, 127, 128, n - 17, n - 9, n - 1})
+    rows = np.concatenate([np.repeat(edge_rows, n), np.tile(np.arange(m), len(edge_cols))])
+    cols = np.concatenate([np.tile(np.arange(n), len(edge_rows)), np.repeat(edge_cols, m)])
+    want = to_rne16(oracle.linear_entries(bits(x), tag(dtype), q, s, bits(b), rows, cols), dtype)
+    got = y[rows, cols]
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (f"{bad.size} mismatches, first at row {rows[bad[0]]} col {cols[bad[0]]}: "
+                           f"got {got[bad[0]]} want {want[bad[0]]}")
+
+
 # The eight-wave GEMM on INT8 weights: ragged M and N over 256 x 256 tiles,
 # no split (one LDS-staged epilogue), an uneven long-K split (six parts of
 # 17 groups and one of 11), a single group, and a K split with odd group
