@@ -119,10 +119,12 @@ def test_gemm_tilings_bit_exact(dev, dtype, m, n, k):
 
 # Mid-M plans without a fused activation (x slice whole in LDS): 32-row
 # blocks on 8 waves (128 columns per workgroup), unsplit, ragged last tile and
-# rows past M; 16-row blocks with a K split finished in the launch whose last
-# part is one group short; a small layer in 16-row blocks, M not a multiple of
-# 16, split in four.  Exact arithmetic, whole rows and columns at the edges.
-SKINNY_SHAPES = [(37, 16376, 2048, 8, 1), (13, 2056, 16256, 4, 8), (61, 1000, 4096, 4, 4)]
+# rows past M, and split in eight (finished in the launch through 128-column
+# slots); 16-row blocks with a K split finished in the launch whose last part
+# is one group short; a small layer in 16-row blocks, M not a multiple of 16,
+# split in four.  Exact arithmetic, whole rows and columns at the edges.
+SKINNY_SHAPES = [(37, 16376, 2048, 8, 1), (61, 2040, 16384, 8, 8), (13, 2056, 16256, 4, 8),
+                 (61, 1000, 4096, 4, 4)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])

@@ -573,16 +573,17 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int bits, int act_fn) {
     // where it measured faster (MI355X, bf16): 16-row blocks up to M = 64,
     // 7-15 % (16 x 16384 x 2048: 11.9 -> 10.5 us; 16 x 2048 x 16384: 9.6 ->
     // 8.2; 50 x 4096 x 1024: 8.0 -> 7.5; 64 x 1024 x 4096: 5.4 -> 4.9), not
-    // beyond (256 x 1024 x 4096: 9.1 -> 10.0); 32-row blocks only unsplit and
-    // in one round of workgroups (at most one per CU: 128 KB of LDS), 3-5 %
-    // (64 x 2048 x 16384: 15.9 -> 15.1); split or in more rounds they ran
-    // 4-45 % slower (64 x 16384 x 2048: 18.1 -> 19.9; 96 x 2048 x 16384:
-    // 20.4 -> 27.0).
+    // beyond (256 x 1024 x 4096: 9.1 -> 10.0); 32-row blocks in one round of
+    // workgroups (at most one per CU: 128 KB of LDS) with at most 8 K
+    // splits (64 x 2048 x 16384: 15.9 -> 12.7; 64 x 16384 x 2048: 18.0 ->
+    // 17.3; 50 x 16384 x 2048: 17.8 -> 16.7); in more rounds or with 16
+    // splits they ran 4-45 % slower (32 x 16384 x 2048: 14.6 -> 15.2; 96 x
+    // 2048 x 16384: 20.4 -> 27.0).
     if (act_fn == kActFnNone) {
         if (mb == 1 && m <= 64) return make_skinny_plan(m, L, 1, true);
         if (mb == 2) {
             const SkinnyPlan d = make_skinny_plan(m, L, 2, true);
-            if (d.splits == 1 && d.tile_groups * d.mblocks <= 256) return d;
+            if (d.splits <= 8 && d.tile_groups * d.mblocks * d.splits <= 256) return d;
         }
     }
     return make_skinny_plan(m, L, mb, false);
