@@ -436,8 +436,10 @@ def test_explain_reports_the_plan(lib):
     assert p["path"] == w4.Path.GEMV and p["tile_n"] == 16 and p["splits"] == 1 and p["launches"] == 1
     assert p["workgroups"] == 2048 and p["workspace_bytes"] == 0
     p = w4.explain(1, 2048, 16384)          # K split over workgroups: exchange slots in the workspace
-    assert (p["waves"], p["splits"], p["groups_per_split"]) == (8, 4, 32) and p["workspace_bytes"] > 0
+    assert (p["waves"], p["splits"], p["groups_per_split"]) == (8, 2, 64) and p["workspace_bytes"] > 0
     assert p["workspace_bytes"] <= w4.workspace_bytes(1, 2048, 16384)
+    p = w4.explain(1, 4096, 16384)          # 256 row tiles: unsplit, 16 chunks per wave
+    assert (p["waves"], p["splits"], p["groups_per_split"], p["workgroups"]) == (8, 1, 128, 256)
     p = w4.explain(4, 2048, 16384, path=w4.Path.GEMV)  # whole tiles, 8 waves, 4 splits
     assert (p["tile_n"], p["waves"], p["splits"]) == (16, 8, 4)
     p = w4.explain(6, 1024, 2048)           # MGEMV: one launch per 16-row block

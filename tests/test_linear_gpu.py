@@ -117,6 +117,31 @@ def test_gemm_tilings_bit_exact(dev, dtype, m, n, k):
                            f"got {got[bad[0]]} want {want[bad[0]]}")
 
 
+# M = 1 plans of the v_dot2 kernel with more than 4 chunks per wave (issued
+# 4 ahead of the chunk computed): 16 chunks per wave unsplit (>= 256 row
+# tiles), ragged last tile; two splits of 64 + 63 groups (8 chunks per wave,
+# the last wave's last chunk past the split); 257 groups in five splits of
+# 64 (a tree of three levels, the last split one group).  Exact arithmetic,
+# every output bit for bit.
+GEMV_SHAPES = [(1, 4104, 16384, 8, 1, 128), (1, 2056, 16256, 8, 2, 64), (1, 1000, 32896, 8, 5, 64)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k,waves,splits,gps", GEMV_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k, *_ in GEMV_SHAPES])
+def test_gemv_plans_bit_exact(dev, dtype, m, n, k, waves, splits, gps):
+    lib = w4()
+    plan = lib.explain(m, n, k, path=lib.Path.GEMV)
+    assert (plan["waves"], plan["splits"], plan["groups_per_split"]) == (waves, splits, gps), plan
+    w, x, b = exact_case(m, n, k, seed=m + 5 * n + k, dtype=dtype, with_bias=True)
+    say(f"gemv plan case dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare(w, dev)
+    y = run(x.to(dev), packed, n, b.to(dev), "GEMV")
+    want = to_rne16(oracle.linear(bits(x), tag(dtype), q, s, bits(b)), dtype)
+    got = y.cpu().to(torch.float64).numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
 # Mid-M plans without a fused activation (x slice whole in LDS): 32-row
 # blocks on 8 waves (128 columns per workgroup), unsplit, ragged last tile and
 # rows past M, and split in eight (finished in the launch through 128-column

@@ -9,11 +9,12 @@
 // packed pair of 16-bit floats with one shift and one v_and_or, and multiplies
 // them into the activations with v_dot2 (FP32 accumulation).
 //
-// Latency: each thread first loads its part of the x slice, then every chunk
-// of its wave (nontemporal loads: the weights are read once), then stages x
-// in LDS.  Loads complete in issue order, so the staging waits only for x and
-// every chunk is used as soon as it lands: the nibble arithmetic overlaps the
-// weight stream instead of trailing it.
+// Latency: each thread first loads its part of the x slice, then the chunks
+// of its wave (nontemporal loads: the weights are read once; beyond 4 chunks
+// per wave, 4 ahead of the one computed), then stages x in LDS.  Loads
+// complete in issue order, so the staging waits only for x and every chunk is
+// used as soon as it lands: the nibble arithmetic overlaps the weight stream
+// instead of trailing it.
 //
 // The packed pairs hold 136 + q (bf16) or 1032 + q (f16) exactly; the offset
 // is removed once per group with the sum of the lane's 32 activations, which
@@ -126,8 +127,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(
         a.packed + L.scale_offset() + (t * L.groups + g0) * kChunkScaleBytes, int64_t(ng) * kChunkScaleBytes);
 
-#pragma unroll
-    for (int u = 0; u < CPW; ++u) {
+    // A wave of more than 4 chunks issues 4 up front and each further one
+    // while computing the chunk 4 before it: a wave stalls at issue once the
+    // memory pipeline is full, so with every chunk issued up front it would
+    // compute nothing until its stream had almost arrived (M = 1, 8 chunks
+    // per wave: 16384 x 2048 6.47 -> 5.91 us; windows of 2, 3 and 6 chunks
+    // 6.08-6.27).
+    constexpr int PF = CPW < 4 ? CPW : 4;
+    auto load_chunk = [&](int u) {
         const int gl = wave + u * WAVES;
         const int gc = gl < ng ? gl : ng - 1;  // a valid chunk; unused when gl >= ng
         if constexpr (M == 1) {
@@ -150,7 +157,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
         // every chunk and the products of the later chunks no longer overlap
         // the stream.
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_chunk(u);
 
     // Stage x into LDS and sum each lane-quarter's 32 activations of every
     // group: block b = 4s + kq of a group holds columns 32s + 8kq .. +7, so a
@@ -181,6 +190,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
         const int gl = wave + u * WAVES;
+        if (u + PF < CPW) load_chunk(u + PF);
         if (gl < ng) {
             uint32_t words[4 * H];
 #pragma unroll
@@ -270,13 +280,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 
 // --- planning ---------------------------------------------------------------
 //
-// One row tile per workgroup and at most 4 chunks per wave: a split longer
-// than 16 groups takes workgroups of 8 waves, so a workgroup covers up to 32
-// groups (K <= 4096) and a longer K is split into equal parts.  Measured on
-// the K 16384 down projection: the same split over 8 waves of 4 chunks
-// streams its weight about 1.6 us faster than over 4 waves of 8 chunks (more
-// waves, each with fewer loads in flight).  INT8 chunks are twice as long: 4
-// waves of at most 4 of them.
+// One row tile per workgroup.  Up to 16 groups per split: 4 waves of at most
+// 4 chunks.  Beyond that 8 waves: at M = 1 a split holds up to 64 groups (8
+// chunks per wave), or 128 (16) when the row tiles alone make 256
+// workgroups, chunks issued 4 ahead (above); at M = 2-4 up to 32 groups (4
+// chunks per wave, all up front).  Measured at M = 1 (MI355X, graph replay,
+// us): 16384 x 2048 (128 tiles) in two splits of 64 groups 5.91 against
+// four of 32 6.54 and one of 128 on 128 workgroups 6.93; 16384 x 4096 (256
+// tiles) unsplit 8.28 against two splits 8.87 and four 9.2; 32768 x 1024
+// in four splits of 64 6.38 against eight of 32 7.06.  INT8 chunks are
+// twice as long: 4 waves of at most 4 of them.
 //
 // Splitting only to fill the chip costs more than it gains: the exchange
 // adds a device round trip per tree level (about 0.45 us each, measured),
@@ -292,13 +305,13 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits) {
     const Layout L(n, k, bits);
     const int64_t G = L.groups;
     const int mm = int(m);
-    const int64_t cap = bits == 8 ? 4 * 4 : 8 * 4;
+    const int64_t cap = bits == 8 ? 4 * 4 : mm > 1 ? 8 * 4 : L.tiles >= 256 ? 8 * 16 : 8 * 8;
     const int64_t gps = G < cap ? G : cap;
     p.gps = int(gps);
     p.splits = int(ceil_div(G, gps));
     p.waves = (bits == 4 && gps > 16) ? 8 : 4;
     const int64_t per_wave = ceil_div(gps, p.waves);
-    p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : 4;
+    p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : per_wave <= 8 ? 8 : 16;
     p.lds = size_t(mm) * gps * kGroup * 2 + size_t(mm) * gps * 4 * 4 + size_t(p.waves) * mm * 16 * 4;
     const int64_t slots = L.tiles * (p.splits - 1) * mm * kTileRows;
     p.exchange = p.splits > 1 && slots * 8 <= int64_t(kSyncBytes);
@@ -319,9 +332,20 @@ static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s
     const Layout L(a.n, a.k, BITS);
     const dim3 grid(unsigned(L.tiles * p.splits)), block(unsigned(64 * p.waves));
     if (p.waves == 8) {
-        // 17..32 groups per split (INT4 only): 8 waves of 4 chunks
-        if constexpr (BITS == 4) gemv_kernel<M, ACT, 8, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a);
-        else return hipErrorInvalidValue;
+        // 17..128 groups per split (INT4 only): 8 waves of 4 chunks, or at
+        // M = 1 of 8 or 16
+        if constexpr (BITS == 4) {
+            if constexpr (M == 1) {
+                if (p.cpw == 16) gemv_kernel<M, ACT, 8, 16, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+                else if (p.cpw == 8) gemv_kernel<M, ACT, 8, 8, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+                else gemv_kernel<M, ACT, 8, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+            } else {
+                if (p.cpw != 4) return hipErrorInvalidValue;
+                gemv_kernel<M, ACT, 8, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+            }
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
         switch (p.cpw) {
             case 1: gemv_kernel<M, ACT, 4, 1, AF, BITS><<<grid, block, p.lds, stream>>>(a); break;
