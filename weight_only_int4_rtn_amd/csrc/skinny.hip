@@ -1,14 +1,16 @@
-// Mid-M forward (and any M): register-dequantized weights into MFMA.
+// Mid-M forward (and any M): register-dequantized weights into MFMA.  Two
+// kernels: skinny_direct_kernel (no fused activation; below) keeps the
+// workgroup's whole x slice in LDS; skinny_kernel stages x per group:
 //
 // A workgroup of 4 waves owns 4 adjacent 16-row weight tiles (64 output
 // columns), a block of up to 64 activation rows (MB 16-row blocks; the plan
 // takes 16 or 32) and a K split of up to 16 groups (8 for MB > 2, half as
 // many INT8 chunks).  Each wave first loads the x tiles of the first two
-// groups, then every 1 KB chunk of its tile in the split (one 128-bit load
-// per lane each), so the whole weight stream is in flight at once while the
-// first groups can start as soon as their own data lands (loads complete in
-// issue order; x issued after the chunks would wait for all of them:
-// measured 1-8 % slower).  Then per 128-column group:
+// groups, then the 1 KB chunks of its tile (one 128-bit load per lane each),
+// 8 groups (4 with 32-row blocks) ahead of the group computed, so the first
+// groups can start as soon as their own data lands (loads complete in issue
+// order; x issued after the chunks would wait for them: measured 1-8 %
+// slower).  Then per 128-column group:
 //   1. the activation block's 128 columns, loaded into registers two groups
 //      ahead, are staged in one of two LDS buffers (with a fused input
 //      activation applied on the way);
@@ -176,7 +178,7 @@ __device__ inline void skinny_finish(const SkinnyArgs& a, const f32x4_t (&tot)[M
 
 // AF: activation fused into the x staging (ActFn; SwiGLU gate values sit k
 // columns after the up values).  GMAX: most groups one workgroup covers (all
-// of its chunks are held in registers).  BITS: 4 (INT4 chunks) or 8 (INT8
+// of its chunks are held in registers, loaded a window ahead).  BITS: 4 (INT4 chunks) or 8 (INT8
 // chunks, two 1 KB halves each).
 template <int MB, int ACT, int AF, int GMAX, int BITS>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
@@ -246,17 +248,24 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
     if (ng > 1) load_x(1, 1);
     // keep the compiler from hoisting the chunk loads above the x loads
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < GMAX; ++u) {
+    // chunks in flight ahead of the group computed (the direct kernel's
+    // window; issuing every chunk up front left a wave stalled at issue until
+    // its stream had almost arrived: 8-11 % faster, 96 x 2048 x 16384 20.4 ->
+    // 18.2 us, 16 x 16384 x 2048 with SwiGLU 14.8 -> 13.6)
+    constexpr int SPF = MB == 1 ? 8 : 4;
+    auto load_chunk = [&](int u) {
         const int gc = u < ng ? u : ng - 1;  // a valid chunk; unused when u >= ng
 #pragma unroll
         for (int h = 0; h < H; ++h) cw[u][h] = load_stream16(cbase + int64_t(gc) * CB + h * kChunkBytes);
         sc[u] = sbase[int64_t(gc) * kTileRows];
-    }
+    };
+#pragma unroll
+    for (int u = 0; u < (SPF < GMAX ? SPF : GMAX); ++u) load_chunk(u);
     stage_x(0, 0);
     __syncthreads();
 #pragma unroll
     for (int gl = 0; gl < GMAX; ++gl) {
+        if (gl + SPF < GMAX) load_chunk(gl + SPF);
         if (gl >= ng) continue;  // (not break: the loop stays fully unrolled, arrays in registers)
         const int buf = gl & 1;
 
