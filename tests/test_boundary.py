@@ -89,8 +89,11 @@ def test_choose_path(lib):
     assert w4.choose_path(4, 16384, 4096) == w4.Path.MGEMV
     assert w4.choose_path(16, 2560, 2048) == w4.Path.MGEMV
     assert w4.choose_path(8, 32768, 2048) == w4.Path.SKINNY
-    assert w4.choose_path(96, 32768, 2048) == w4.Path.SKINNY
-    assert w4.choose_path(97, 32768, 2048) == w4.Path.GEMM
+    assert w4.choose_path(64, 32768, 2048) == w4.Path.SKINNY
+    assert w4.choose_path(65, 32768, 2048) == w4.Path.GEMM
+    assert w4.choose_path(128, 16384, 2048) == w4.Path.SKINNY
+    assert w4.choose_path(128, 2048, 16384) == w4.Path.SKINNY
+    assert w4.choose_path(129, 16384, 2048) == w4.Path.GEMM
     assert w4.choose_path(512, 4096, 1024) == w4.Path.SKINNY
     assert w4.choose_path(513, 4096, 1024) == w4.Path.GEMM
 

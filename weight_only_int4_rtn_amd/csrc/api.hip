@@ -273,9 +273,12 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     // outputs (8 x 16384 x 2048: 7.8 vs 9.1) and up to M = 4 on wider ones
     // (8 x 32768 x 2048: 14.0 vs 12.9).  The mid-M kernel beats the GEMM
     // (whose few tiles need a K split and a reduce launch) on small layers up
-    // to M = 512 (256 x 4096 x 1024: 9.3 vs 18.0); on larger layers up to
-    // M = 96 (96 x 32768 x 2048: 38.8 vs 42.9; 96 x 2048 x 16384: 25.8 vs
-    // 29.7; at M = 128 the GEMM leads, 46.3 vs 47.4 and 30.6 vs 32.4).
+    // to M = 512 (256 x 4096 x 1024: 9.3 vs 18.0); on layers of <= 32 M
+    // weights up to M = 128 (128 x 16384 x 2048: 22.2 vs 22.8; 128 x 2048 x
+    // 16384: 24.3 vs 27.0; at M = 160 the GEMM leads, 24.9 vs 29.0 and 30.7
+    // vs 33.0); on larger ones up to M = 64 (64 x 32768 x 2048: 24.0 vs 25.3;
+    // at M = 80 the GEMM leads, 25.6 vs 33.0; 96 x 4096 x 16384: 33.8 vs
+    // 39.1).
     // With its x slice whole in LDS the mid-M kernel also takes M = 3-16 on
     // layers it covers without a K split (>= 16384 outputs, K <= 2048: 3 x
     // 32768 x 2048: 9.9 vs 10.7; 4 x 16384 x 2048: 6.6 vs 6.9; 8 x 16384 x
@@ -290,7 +293,8 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
         const MgemvPlan p = plan_mgemv(m < 16 ? m : 16, n, k, 4);
         if (m <= 2 || small || p.splits == 1 || p.exchange) return W4A16_PATH_MGEMV;
     }
-    if (k > kGemmMaxLd || m <= 96 || (small && m <= 512)) return W4A16_PATH_SKINNY;
+    const bool mid = n * k <= (int64_t(32) << 20);
+    if (k > kGemmMaxLd || m <= 64 || (mid && m <= 128) || (small && m <= 512)) return W4A16_PATH_SKINNY;
     return W4A16_PATH_GEMM;
 }
 
