@@ -86,6 +86,8 @@ def test_choose_path(lib):
     assert w4.choose_path(8, 4096, 16384) == w4.Path.SKINNY
     assert w4.choose_path(4, 2048, 16384) == w4.Path.MGEMV
     assert w4.choose_path(8, 2048, 16384) == w4.Path.MGEMV
+    assert w4.choose_path(8, 16384, 4096) == w4.Path.SKINNY
+    assert w4.choose_path(6, 2048, 16384) == w4.Path.MGEMV
     assert w4.choose_path(4, 16384, 4096) == w4.Path.MGEMV
     assert w4.choose_path(16, 2560, 2048) == w4.Path.MGEMV
     assert w4.choose_path(8, 32768, 2048) == w4.Path.SKINNY

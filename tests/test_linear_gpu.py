@@ -61,9 +61,9 @@ def exact_case(m, n, k, seed, dtype, with_bias):
 
 # (1, 48, 2176): a 17-group K, the shortest split on 8 waves (3 chunks for
 # some waves, 2 for others); (1, 40, 8192): two 8-wave splits; (1, 72,
-# 32896): nine splits, the last holding one group; (6, 2056, 16384): 8-wave
-# splits of 21 groups on the MFMA small-M path, and on the v_dot2 path a
-# 4-row and a 2-row block of 8-wave splits of 32, ragged last tile.
+# 32896): nine splits, the last holding one group; (6, 2056, 16384): two
+# 8-wave splits of 64 groups on the MFMA small-M path, and on the v_dot2
+# path a 4-row and a 2-row block of 8-wave splits of 32, ragged last tile.
 EXACT_SHAPES = [(1, 16, 128), (2, 40, 384), (3, 1000, 2048), (4, 2056, 16384), (5, 72, 256),
                 (1, 48, 2176), (1, 40, 8192), (1, 72, 32896), (6, 2056, 16384),
                 (17, 130, 640), (33, 64, 1152), (63, 130, 512), (64, 2048, 8192), (65, 40, 256),
@@ -142,6 +142,31 @@ def test_gemv_plans_bit_exact(dev, dtype, m, n, k, waves, splits, gps):
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
 
 
+# Small-M MFMA plans: x operands loaded with each chunk (M > 4) on 8 waves of
+# 8 chunks in two K splits (one exchange level), ragged last row tile; the
+# same with a last split one group short and M odd; 4 waves unsplit at M =
+# 16; 8 waves of 4 chunk slots over 24 groups (some slots idle); x staged in
+# LDS (M = 3) split in four.  Exact arithmetic, every output.
+MGEMV_SHAPES = [(8, 2056, 16384, 8, 2, 64), (13, 1000, 16256, 8, 2, 64), (16, 2040, 2048, 4, 1, 16),
+                (6, 1032, 3072, 8, 1, 24), (3, 2056, 16384, 8, 4, 32)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k,waves,splits,gps", MGEMV_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k, *_ in MGEMV_SHAPES])
+def test_mgemv_plans_bit_exact(dev, dtype, m, n, k, waves, splits, gps):
+    lib = w4()
+    plan = lib.explain(m, n, k, path=lib.Path.MGEMV)
+    assert (plan["waves"], plan["splits"], plan["groups_per_split"]) == (waves, splits, gps), plan
+    w, x, b = exact_case(m, n, k, seed=m + 7 * n + k, dtype=dtype, with_bias=True)
+    say(f"mgemv plan case dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare(w, dev)
+    y = run(x.to(dev), packed, n, b.to(dev), "MGEMV")
+    want = to_rne16(oracle.linear(bits(x), tag(dtype), q, s, bits(b)), dtype)
+    got = y.cpu().to(torch.float64).numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
 # Mid-M plans without a fused activation (x slice whole in LDS): 32-row
 # blocks on 8 waves (128 columns per workgroup), unsplit, ragged last tile and
 # rows past M, and split in eight (finished in the launch through 128-column
@@ -213,13 +238,14 @@ def test_strided_output_bit_exact(dev):
 # have been: every result bit-exact, and the 1 MiB exchange-slot header zero
 # again after every call.  Small-M splits: GEMV into 4, 3 (a tree with an odd
 # child), 8 (too many slots: partial sums and the reduce kernel) and 5 parts;
-# MGEMV into 8 (three tree levels), 16 (partial sums) and 2 parts; stream-K
+# MGEMV into 2 (x operands with the chunks), 8 (the same, too many slots:
+# partial sums) and 8 parts (x staged in LDS, three tree levels); stream-K
 # GEMMs whose runs share tiles (their tile counters sit in the same header).
 SYNC_HEADER = 1 << 20
 SHARED_WS_CALLS = [("GEMV", 1, 2048, 16384), ("SKINNY", 50, 1000, 4096), ("GEMV", 3, 40, 12288),
                    ("MGEMV", 8, 2048, 16384), ("GEMM", 300, 4104, 640), ("GEMV", 4, 4688, 32768),
-                   ("MGEMV", 16, 1040, 16384), ("GEMM_STREAMK", 130, 2056, 2176), ("GEMV", 2, 100, 20480),
-                   ("MGEMV", 6, 520, 2048), ("GEMM_STREAMK", 97, 4104, 4096), ("GEMV", 1, 2048, 16384)]
+                   ("MGEMV", 16, 1200, 65536), ("GEMM_STREAMK", 130, 2056, 2176), ("GEMV", 2, 100, 20480),
+                   ("MGEMV", 4, 1024, 16384), ("GEMM_STREAMK", 97, 4104, 4096), ("GEMV", 1, 2048, 16384)]
 
 
 def test_shared_workspace_header_stays_clear(dev):

@@ -55,7 +55,21 @@ size_t path_workspace(w4a16_path_t path, int64_t m, int64_t n, int64_t k, int bi
             const size_t last = m > 4 && m % 4 ? plan_gemv(m % 4, n, k, bits).workspace : 0;
             return full > last ? full : last;
         }
-        case W4A16_PATH_MGEMV: return plan_mgemv(m < 16 ? m : 16, n, k, bits).workspace;
+        case W4A16_PATH_MGEMV: {
+            // row blocks of 16 and a last block of m % 16 rows, with or
+            // without a fused activation (staged or direct x operands): each
+            // plan has room
+            size_t most = 0;
+            const int64_t blocks[2] = {m < 16 ? m : 16, m > 16 ? m % 16 : 0};
+            for (const int64_t mm : blocks) {
+                if (mm == 0) continue;
+                for (const int fn : {int(kActFnNone), int(kActFnSwiglu)}) {
+                    const size_t w = plan_mgemv(mm, n, k, bits, fn).workspace;
+                    most = w > most ? w : most;
+                }
+            }
+            return most;
+        }
         case W4A16_PATH_SKINNY: {
             // the plans with and without a fused activation (different
             // workgroup widths): room for either
@@ -290,8 +304,16 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
     if (m <= 1 || (m == 2 && small && n >= 2048)) return W4A16_PATH_GEMV;
     if (m >= 3 && m <= 16 && k <= 2048 && n >= 16384) return W4A16_PATH_SKINNY;
     if (m <= 4 || (m <= 8 && n <= 16384) || (m <= 16 && small)) {
+        // Direct plans (x operands loaded with the chunks, M > 4) split K
+        // into at most a few exchange levels but put x through the vector
+        // memory path four times per chunk: on layers of more than 32 M
+        // weights the mid-M kernel, which shares x across its waves, leads
+        // (8 x 4096 x 16384: 13.3 vs 15.8 us; 8 x 16384 x 4096, unsplit:
+        // 12.4 vs 13.6); on 8 x 2048 x 16384 the small-M kernel leads, 8.8
+        // vs 9.4.
         const MgemvPlan p = plan_mgemv(m < 16 ? m : 16, n, k, 4);
-        if (m <= 2 || small || p.splits == 1 || p.exchange) return W4A16_PATH_MGEMV;
+        const bool fits = p.direct ? n * k <= (int64_t(32) << 20) : p.splits == 1 || p.exchange;
+        if (m <= 2 || small || fits) return W4A16_PATH_MGEMV;
     }
     const bool mid = n * k <= (int64_t(32) << 20);
     if (k > kGemmMaxLd || m <= 64 || (mid && m <= 128) || (small && m <= 512)) return W4A16_PATH_SKINNY;
@@ -464,7 +486,7 @@ w4a16_status_t w4a16_linear_explain(int bits, w4a16_act_t act, w4a16_path_t path
     int64_t launches = 1;
     switch (path) {
         case W4A16_PATH_GEMV: info = describe_gemv(m < 4 ? m : 4, n, k, bits); launches = ceil_div(m, 4); break;
-        case W4A16_PATH_MGEMV: info = describe_mgemv(m < 16 ? m : 16, n, k, bits); launches = ceil_div(m, 16); break;
+        case W4A16_PATH_MGEMV: info = describe_mgemv(m < 16 ? m : 16, n, k, bits, fn); launches = ceil_div(m, 16); break;
         case W4A16_PATH_SKINNY: info = describe_skinny(m, n, k, bits, fn); break;
         default: info = describe_gemm(m, n, k, bits, path == W4A16_PATH_GEMM_STREAMK); break;
     }

@@ -31,10 +31,11 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits = 4);
 
 struct MgemvPlan {
     int mmax, waves, gps, splits, cpw;
+    bool direct;    // x operands loaded with each chunk, else staged in LDS
     bool exchange;  // split finished through the header's exchange slots
     size_t lds, workspace;
 };
-MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits = 4);
+MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits = 4, int act_fn = 0);
 
 struct SkinnyPlan {
     int mb;             // 16-row m-subtiles per workgroup (1..4)
@@ -73,7 +74,7 @@ struct PlanInfo {
     bool stream_k;       // stream-K: splits = the most runs sharing a tile, gps = the longest run
 };
 PlanInfo describe_gemv(int64_t m, int64_t n, int64_t k, int bits);    // m <= 4 (one row block)
-PlanInfo describe_mgemv(int64_t m, int64_t n, int64_t k, int bits);   // m <= 16 (one row block)
+PlanInfo describe_mgemv(int64_t m, int64_t n, int64_t k, int bits, int act_fn);   // m <= 16 (one row block)
 PlanInfo describe_skinny(int64_t m, int64_t n, int64_t k, int bits, int act_fn);
 PlanInfo describe_gemm(int64_t m, int64_t n, int64_t k, int bits, bool streamk);
 
