@@ -146,9 +146,10 @@ def test_gemv_plans_bit_exact(dev, dtype, m, n, k, waves, splits, gps):
 # 8 chunks in two K splits (one exchange level), ragged last row tile; the
 # same with a last split one group short and M odd; 4 waves unsplit at M =
 # 16; 8 waves of 4 chunk slots over 24 groups (some slots idle); x staged in
-# LDS (M = 3) split in four.  Exact arithmetic, every output.
+# LDS (M = 3) split in four; M = 3 on a small layer (x with the chunks).
+# Exact arithmetic, every output.
 MGEMV_SHAPES = [(8, 2056, 16384, 8, 2, 64), (13, 1000, 16256, 8, 2, 64), (16, 2040, 2048, 4, 1, 16),
-                (6, 1032, 3072, 8, 1, 24), (3, 2056, 16384, 8, 4, 32)]
+                (6, 1032, 3072, 8, 1, 24), (3, 2056, 16384, 8, 4, 32), (3, 2056, 2048, 4, 1, 16)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
