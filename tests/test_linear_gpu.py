@@ -146,10 +146,11 @@ def test_gemv_plans_bit_exact(dev, dtype, m, n, k, waves, splits, gps):
 # 8 chunks in two K splits (one exchange level), ragged last row tile; the
 # same with a last split one group short and M odd; 4 waves unsplit at M =
 # 16; 8 waves of 4 chunk slots over 24 groups (some slots idle); x staged in
-# LDS (M = 3) split in four; M = 3 on a small layer (x with the chunks).
-# Exact arithmetic, every output.
-MGEMV_SHAPES = [(8, 2056, 16384, 8, 2, 64), (13, 1000, 16256, 8, 2, 64), (16, 2040, 2048, 4, 1, 16),
-                (6, 1032, 3072, 8, 1, 24), (3, 2056, 16384, 8, 4, 32), (3, 2056, 2048, 4, 1, 16)]
+# LDS (M = 3) split in four; M = 3 on a small layer (x with the chunks); 63
+# row tiles split in four to fill the chip.  Exact arithmetic, every output.
+MGEMV_SHAPES = [(8, 2056, 16384, 8, 2, 64), (13, 2056, 16256, 8, 2, 64), (16, 2040, 2048, 4, 1, 16),
+                (6, 2056, 3072, 8, 1, 24), (3, 2056, 16384, 8, 4, 32), (3, 2056, 2048, 4, 1, 16),
+                (16, 1000, 4096, 4, 4, 8)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
@@ -173,9 +174,10 @@ def test_mgemv_plans_bit_exact(dev, dtype, m, n, k, waves, splits, gps):
 # rows past M, and split in eight (finished in the launch through 128-column
 # slots); 16-row blocks with a K split finished in the launch whose last part
 # is one group short; a small layer in 16-row blocks, M not a multiple of 16,
-# split in four.  Exact arithmetic, whole rows and columns at the edges.
+# split in four; a small layer split in eight parts of 8 groups (512
+# workgroups).  Exact arithmetic, whole rows and columns at the edges.
 SKINNY_SHAPES = [(37, 16376, 2048, 8, 1), (61, 2040, 16384, 8, 8), (13, 2056, 16256, 4, 8),
-                 (61, 1000, 4096, 4, 4)]
+                 (61, 1000, 4096, 4, 4), (64, 1040, 8192, 4, 8)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])

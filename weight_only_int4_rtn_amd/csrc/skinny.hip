@@ -548,7 +548,15 @@ SkinnyPlan make_skinny_plan(int64_t m, const Layout& L, int mb, bool direct) {
     const int64_t cap = (p.mb <= 2 ? 16 : 8) / (L.cb == kChunkBytes8 ? 2 : 1);
     const int64_t base = p.tile_groups * p.mblocks;
     int64_t gps = L.groups < cap ? L.groups : cap;
-    while (gps > 2 && base * ceil_div(L.groups, gps) < minwg) gps = ceil_div(gps, 2);
+    // INT4 layers of <= 8 M weights: at most 8 groups per split, and not
+    // below 4 (MI355X, us: 128 x 1024 x 4096 in four splits of 8 9.5 vs two
+    // of 16 12.0; 64 x 2048 x 4096 8.1 vs 9.0; 64 x 1024 x 8192 9.1 vs 9.7;
+    // 16 x 1024 x 4096 in splits of 4 6.7 vs 2 8.8; from 8 to 4 groups per
+    // split slower: 50 x 1024 x 4096 8.1 vs 7.3)
+    const bool small = L.cb == kChunkBytes && L.tiles * kTileRows * L.groups * kGroup <= (int64_t(8) << 20);
+    if (small && gps > 8) gps = 8;
+    const int64_t floor_gps = small ? 4 : 2;
+    while (gps > floor_gps && base * ceil_div(L.groups, gps) < minwg) gps = ceil_div(gps, 2);
     p.gps = int(gps);
     p.gmax = gps <= 4 ? 4 : gps <= 8 ? 8 : 16;
     p.splits = int(ceil_div(L.groups, gps));
