@@ -308,9 +308,9 @@ w4a16_path_t w4a16_linear_choose_path(int64_t m, int64_t n, int64_t k) {
         // into at most a few exchange levels but put x through the vector
         // memory path four times per chunk: on layers of more than 32 M
         // weights the mid-M kernel, which shares x across its waves, leads
-        // (8 x 4096 x 16384: 13.3 vs 15.8 us; 8 x 16384 x 4096, unsplit:
-        // 12.4 vs 13.6); on 8 x 2048 x 16384 the small-M kernel leads, 8.8
-        // vs 9.4.
+        // (M x N x K = 8 x 4096 x 16384: 13.3 vs 15.8 us; 8 x 16384 x 4096,
+        // unsplit: 12.4 vs 13.6); on 8 x 2048 x 16384 the small-M kernel
+        // leads, 8.8 vs 9.4.
         const MgemvPlan p = plan_mgemv(m < 16 ? m : 16, n, k, 4);
         const bool fits = p.direct ? n * k <= (int64_t(32) << 20) : p.splits == 1 || p.exchange;
         if (m <= 2 || small || fits) return W4A16_PATH_MGEMV;

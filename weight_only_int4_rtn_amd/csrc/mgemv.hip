@@ -14,8 +14,8 @@
 //  - direct (otherwise): loaded straight from global memory with the chunk.
 //    Each group of a split is used by one wave only, so there is nothing to
 //    share: no staging barrier and no bound on the slice, hence fewer K
-//    splits (M = 8, 16384 x 2048: two splits instead of eight, 8.9 vs 9.7
-//    us).  The loads cost four instructions per chunk however few rows are
+//    splits (M = 8, K = 16384, N = 2048: two splits instead of eight, 8.9
+//    vs 9.7 us).  The loads cost four instructions per chunk however few rows are
 //    live, and a fused activation runs in every lane of the 16 rows, which
 //    is why small M keep the staged form (M = 4, same layer with SwiGLU:
 //    19.7 vs 10.4 us).
@@ -375,23 +375,23 @@ __global__ __launch_bounds__(64 * WAVES) void mgemv_direct_kernel(MgemvArgs a) {
 // issued a window ahead) or 16 INT8 groups (4 waves of up to 4 chunks of
 // twice the registers), balanced; a split of at most 16 INT4 groups runs on
 // 4 waves.  K is split only as far as a split's registers require: a split
-// merely to fill the chip adds an exchange level (M = 16, 2048 x 2560: 5.2 us
-// unsplit, 5.35 in two).
+// merely to fill the chip adds an exchange level (M = 16, K = 2048, N = 2560:
+// 5.2 us unsplit, 5.35 in two).
 MgemvPlan plan_mgemv(int64_t m, int64_t n, int64_t k, int bits, int act_fn) {
     MgemvPlan p{};
     const Layout L(n, k, bits);
     // small layers of >= 128 row tiles take the direct form from M = 1 (M = 3
-    // and 4, 2560 x 2048: 4.3 and 4.4 us against 4.6 staged); with fewer
-    // tiles the staged plan's K split fills more of the chip (4 x 1024 x
-    // 4096: 4.8 against 5.0 direct)
+    // and 4, K = 2048, N = 2560: 4.3 and 4.4 us against 4.6 staged); with
+    // fewer tiles the staged plan's K split fills more of the chip (M = 4,
+    // K = 4096, N = 1024: 4.8 against 5.0 direct)
     const bool small = n * k <= (int64_t(8) << 20) && L.tiles >= 128;
     p.direct = (act_fn == kActFnNone && (m > 4 || small)) || m > 8;
     if (p.direct) {
         const int64_t cap = bits == 8 ? 16 : 64;
         int64_t splits = ceil_div(L.groups, cap);
         // fewer than 128 row tiles: split K towards 256 workgroups, down to
-        // 8 groups per split (16 x 1024 x 4096: 5.7 us in four splits, 6.7
-        // unsplit on 64 workgroups)
+        // 8 groups per split (M = 16, K = 4096, N = 1024: 5.3 us in four
+        // splits, 6.7 unsplit on 64 workgroups)
         if (L.tiles < 128) {
             const int64_t want = ceil_div(int64_t(256), L.tiles), most = L.groups / 8;
             const int64_t more = want < most ? want : most;

@@ -549,10 +549,10 @@ SkinnyPlan make_skinny_plan(int64_t m, const Layout& L, int mb, bool direct) {
     const int64_t base = p.tile_groups * p.mblocks;
     int64_t gps = L.groups < cap ? L.groups : cap;
     // INT4 layers of <= 8 M weights: at most 8 groups per split, and not
-    // below 4 (MI355X, us: 128 x 1024 x 4096 in four splits of 8 9.5 vs two
-    // of 16 12.0; 64 x 2048 x 4096 8.1 vs 9.0; 64 x 1024 x 8192 9.1 vs 9.7;
-    // 16 x 1024 x 4096 in splits of 4 6.7 vs 2 8.8; from 8 to 4 groups per
-    // split slower: 50 x 1024 x 4096 8.1 vs 7.3)
+    // below 4 (MI355X, us, M x K x N: 128 x 4096 x 1024 in four splits of 8
+    // 9.5 vs two of 16 12.0; 64 x 4096 x 2048 8.1 vs 9.0; 64 x 8192 x 1024
+    // 9.1 vs 9.7; 16 x 4096 x 1024 in splits of 4 6.7 vs 2 8.8; from 8 to 4
+    // groups per split slower: 50 x 4096 x 1024 8.1 vs 7.3)
     const bool small = L.cb == kChunkBytes && L.tiles * kTileRows * L.groups * kGroup <= (int64_t(8) << 20);
     if (small && gps > 8) gps = 8;
     const int64_t floor_gps = small ? 4 : 2;
