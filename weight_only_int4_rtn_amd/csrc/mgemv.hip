@@ -260,10 +260,11 @@ __global__ __launch_bounds__(64 * WAVES) void mgemv_direct_kernel(MgemvArgs a) {
     // x) up front and each further chunk while computing the chunk PF before
     // it: a wave stalls at issue once the memory pipeline is full, so with
     // every chunk issued at once it would compute nothing until its stream
-    // had almost arrived.  The loads are unconditional straight-line code
-    // (clamped addresses), so each use waits for its own load.  A SwiGLU
-    // chunk holds twice the x registers: a window of 2 keeps the wave within
-    // 128 VGPRs.
+    // had almost arrived.  The chunk loads are unconditional straight-line
+    // code (clamped addresses) and the x loads are masked to the lanes of
+    // rows < M, which every wave has, so each use waits for its own load.  A
+    // SwiGLU chunk holds twice the x registers: a window of 2 keeps the wave
+    // within 128 VGPRs.
     constexpr int PF = CPW < (GATE ? 2 : 4) ? CPW : (GATE ? 2 : 4);
     uint4 cw[CPW][H];
     float sc[CPW];
