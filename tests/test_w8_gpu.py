@@ -247,6 +247,28 @@ def test_int8_skinny_paired_plan_bit_exact(dev, dtype):
                            f"got {got[bad[0]]} want {want[bad[0]]}")
 
 
+# The v_dot2 GEMV at M = 1 on INT8 weights: splits of 64 groups on 8 waves
+# of 8 two-half chunks (a window of 2 ahead), the last split one group
+# short, ragged last tile; 20 groups on 8 waves of 4 chunk slots (some
+# idle).  Exact arithmetic, every output.
+GEMV8_SHAPES = [(1, 2056, 16256, 8, 2, 64), (1, 1000, 2560, 8, 1, 20)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k,waves,splits,gps", GEMV8_SHAPES, ids=[f"m{m}_n{n}_k{k}" for m, n, k, *_ in GEMV8_SHAPES])
+def test_int8_gemv_plans_bit_exact(dev, dtype, m, n, k, waves, splits, gps):
+    import weight_only_int4_rtn_amd as w4
+    plan = w4.explain(m, n, k, path=w4.Path.GEMV, bits=8)
+    assert (plan["waves"], plan["splits"], plan["groups_per_split"]) == (waves, splits, gps), plan
+    w, x, b = exact_case8(m, n, k, seed=m + 11 * n + k, dtype=dtype, with_bias=True)
+    say(f"int8 gemv plan dtype={dtype} m={m} n={n} k={k}")
+    packed, q, s = prepare8(w, dev)
+    y = run8(x.to(dev), packed, n, b.to(dev), "GEMV").cpu().to(torch.float64).numpy()
+    want = to_rne16(oracle.linear(bits(x), tag(dtype), q, s, bits(b)), dtype)
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
 # The eight-wave GEMM on INT8 weights: ragged M and N over 256 x 256 tiles,
 # no split (one LDS-staged epilogue), an uneven long-K split (six parts of
 # 17 groups and one of 11), a single group, and a K split with odd group

@@ -132,8 +132,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
     // memory pipeline is full, so with every chunk issued up front it would
     // compute nothing until its stream had almost arrived (M = 1, 8 chunks
     // per wave: 16384 x 2048 6.47 -> 5.91 us; windows of 2, 3 and 6 chunks
-    // 6.08-6.27).
-    constexpr int PF = CPW < 4 ? CPW : 4;
+    // 6.08-6.27).  INT8 chunks are twice as long: a window of 2 (16384 x
+    // 2048 in two splits of 8 x 8 chunks: 8.3 us, 8.65 with a window of 4,
+    // 9.1 in eight splits of 4 x 4 all up front).
+    constexpr int PF = CPW < (BITS == 8 ? 2 : 4) ? CPW : (BITS == 8 ? 2 : 4);
     auto load_chunk = [&](int u) {
         const int gl = wave + u * WAVES;
         const int gc = gl < ng ? gl : ng - 1;  // a valid chunk; unused when gl >= ng
@@ -289,7 +291,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
 // four of 32 6.54 and one of 128 on 128 workgroups 6.93; 16384 x 4096 (256
 // tiles) unsplit 8.28 against two splits 8.87 and four 9.2; 32768 x 1024
 // in four splits of 64 6.38 against eight of 32 7.06.  INT8 chunks are
-// twice as long: 4 waves of at most 4 of them.
+// twice as long: 4 waves of at most 4 of them, but at M = 1 splits of up to
+// 64 groups on 8 waves with a window of 2 chunks (16384 x 2048: 8.3 us
+// against 9.1 in eight splits of 16; 32768 x 1024 8.7 vs 9.6; 16384 x 4096
+// 13.5 vs 14.8).
 //
 // Splitting only to fill the chip costs more than it gains: the exchange
 // adds a device round trip per tree level (about 0.45 us each, measured),
@@ -305,11 +310,11 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int bits) {
     const Layout L(n, k, bits);
     const int64_t G = L.groups;
     const int mm = int(m);
-    const int64_t cap = bits == 8 ? 4 * 4 : mm > 1 ? 8 * 4 : L.tiles >= 256 ? 8 * 16 : 8 * 8;
+    const int64_t cap = bits == 8 ? (mm == 1 ? 8 * 8 : 4 * 4) : mm > 1 ? 8 * 4 : L.tiles >= 256 ? 8 * 16 : 8 * 8;
     const int64_t gps = G < cap ? G : cap;
     p.gps = int(gps);
     p.splits = int(ceil_div(G, gps));
-    p.waves = (bits == 4 && gps > 16) ? 8 : 4;
+    p.waves = gps > 16 ? 8 : 4;
     const int64_t per_wave = ceil_div(gps, p.waves);
     p.cpw = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : per_wave <= 8 ? 8 : 16;
     p.lds = size_t(mm) * gps * kGroup * 2 + size_t(mm) * gps * 4 * 4 + size_t(p.waves) * mm * 16 * 4;
@@ -332,9 +337,13 @@ static hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s
     const Layout L(a.n, a.k, BITS);
     const dim3 grid(unsigned(L.tiles * p.splits)), block(unsigned(64 * p.waves));
     if (p.waves == 8) {
-        // 17..128 groups per split (INT4 only): 8 waves of 4 chunks, or at
-        // M = 1 of 8 or 16
-        if constexpr (BITS == 4) {
+        // 17..128 groups per split: INT4 8 waves of 4 chunks, or at M = 1 of
+        // 8 or 16; INT8 only at M = 1, 8 waves of 4 or 8 chunks
+        if constexpr (BITS == 8 && M == 1) {
+            if (p.cpw == 8) gemv_kernel<M, ACT, 8, 8, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+            else if (p.cpw == 4) gemv_kernel<M, ACT, 8, 4, AF, BITS><<<grid, block, p.lds, stream>>>(a);
+            else return hipErrorInvalidValue;
+        } else if constexpr (BITS == 4) {
             if constexpr (M == 1) {
                 if (p.cpw == 16) gemv_kernel<M, ACT, 8, 16, AF, BITS><<<grid, block, p.lds, stream>>>(a);
                 else if (p.cpw == 8) gemv_kernel<M, ACT, 8, 8, AF, BITS><<<grid, block, p.lds, stream>>>(a);
