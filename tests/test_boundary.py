@@ -449,6 +449,25 @@ def test_explain_reports_the_plan(lib):
     assert (p["tile_n"], p["waves"], p["splits"]) == (16, 8, 4)
     p = w4.explain(6, 1024, 2048)           # MGEMV: one launch per 16-row block
     assert p["path"] == w4.Path.MGEMV and p["tile_m"] == 6
+    # small-M MFMA plans: x with the chunks (M > 4) in splits of up to 64
+    # groups; towards 256 workgroups below 128 row tiles; x staged in LDS at
+    # M <= 4 on larger layers, and with a fused activation up to M = 8
+    p = w4.explain(8, 2048, 16384, path=w4.Path.MGEMV)
+    assert (p["waves"], p["splits"], p["groups_per_split"], p["workgroups"]) == (8, 2, 64, 256)
+    p = w4.explain(16, 1024, 4096, path=w4.Path.MGEMV)
+    assert (p["waves"], p["splits"], p["groups_per_split"], p["workgroups"]) == (4, 4, 8, 256)
+    p = w4.explain(4, 2048, 16384, path=w4.Path.MGEMV)
+    assert (p["waves"], p["splits"], p["groups_per_split"]) == (8, 4, 32)
+    p = w4.explain(6, 2048, 16384, path=w4.Path.MGEMV, act=w4.Act.SWIGLU)
+    assert (p["waves"], p["splits"], p["groups_per_split"]) == (8, 7, 21)  # x slice <= 2048 columns x 16 rows
+    # INT8 GEMV at M = 1: splits of up to 64 groups on 8 waves
+    p = w4.explain(1, 2048, 16384, bits=8)
+    assert (p["path"], p["waves"], p["splits"], p["groups_per_split"]) == (w4.Path.GEMV, 8, 2, 64)
+    # mid-M plans on INT4 layers of <= 8 M weights: at most 8 groups per split
+    p = w4.explain(128, 1024, 4096, path=w4.Path.SKINNY)
+    assert (p["splits"], p["groups_per_split"], p["workgroups"]) == (4, 8, 512)
+    p = w4.explain(16, 1024, 4096, path=w4.Path.SKINNY)
+    assert (p["splits"], p["groups_per_split"]) == (8, 4)
     assert w4.explain(40, 1024, 2048, path=w4.Path.GEMV)["launches"] >= 10
     p = w4.explain(300, 2056, 1152, act=w4.Act.GELU_TANH, path=w4.Path.GEMM)
     assert p["launches"] == (3 if p["splits"] > 1 else 2)  # activation, GEMM (+ reduce)
